@@ -1,0 +1,236 @@
+"""Brute-force cross-check of the oracle on tiny inputs (test infrastructure).
+
+Independent of oracle/kv4_oracle.c: it reads the packed cache with its own
+unpacker written from the layout description, evaluates every FP32 step the
+rules name with exact rational arithmetic followed by an explicit
+round-to-nearest-even to binary32, gets the Hadamard rotation from the
+recursive Sylvester construction H_2n = [[H, H], [H, -H]], and does every
+tolerance-level sum in FP64.  Slow by design: a few sequences, a few hundred
+positions.
+"""
+from __future__ import annotations
+
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+HD, PAGE, SINK, WINDOW = 128, 16, 16, 128
+
+
+# ------------------------------------------------------- exact rounding --
+
+def _round_binary(x: Fraction, mant: int, emin: int, emax: int) -> float:
+    if x == 0:
+        return 0.0
+    sign = -1.0 if x < 0 else 1.0
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ex = max(e, emin)
+    n = round(a / Fraction(2) ** (ex - mant))  # Fraction rounds half to even
+    if n == 2 ** (mant + 1):
+        n, ex = 2 ** mant, ex + 1
+    if ex > emax:
+        return sign * math.inf
+    return sign * float(Fraction(n) * Fraction(2) ** (ex - mant))
+
+
+def rn32(x) -> float:
+    return _round_binary(Fraction(x), 23, -126, 127)
+
+
+def rn16(x) -> float:
+    return _round_binary(Fraction(x), 10, -14, 15)
+
+
+def rnbf16(x) -> float:
+    return _round_binary(Fraction(x), 7, -126, 127)
+
+
+def f32_fma(a, b, c) -> float:
+    return rn32(Fraction(a) * Fraction(b) + Fraction(c))
+
+
+def f32_mul(a, b) -> float:
+    return rn32(Fraction(a) * Fraction(b))
+
+
+def f32_div(a, b) -> float:
+    return rn32(Fraction(a) / Fraction(b))
+
+
+def f32_sub(a, b) -> float:
+    return rn32(Fraction(a) - Fraction(b))
+
+
+def rint_even(x: float) -> int:
+    return int(round(x))  # Python rounds half to even
+
+
+def exp2_coeffs_exact() -> list[float]:
+    """fp32 RNE of ln2^k / k!, k = 0..7, from a 60-digit ln 2."""
+    getcontext().prec = 60
+    ln2 = Decimal(2).ln()
+    out = []
+    for k in range(8):
+        v = ln2 ** k / Decimal(math.factorial(k))
+        out.append(rn32(Fraction(v)))
+    return out
+
+
+_C = None
+
+
+def exp2s(y: float) -> float:
+    global _C
+    if _C is None:
+        _C = exp2_coeffs_exact()
+    if not (y >= -125.0):
+        return 0.0
+    n = rint_even(y)
+    f = y - n  # exact for binary32 y
+    p = _C[7]
+    for k in range(6, -1, -1):
+        p = f32_fma(p, f, _C[k])
+    return float(Fraction(p) * Fraction(2) ** n)
+
+
+# --------------------------------------------------------------- rotation --
+
+def sylvester(n: int) -> np.ndarray:
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def fwht_f32_recursive(x: np.ndarray) -> np.ndarray:
+    """H_n x by the recursion H_2n x = [H_n a + H_n b, H_n a - H_n b] with
+    FP32 adds; the outermost split is the stride-64 butterfly, applied last."""
+    x = np.asarray(x, dtype=np.float32)
+    n = x.shape[-1]
+    if n == 1:
+        return x.copy()
+    a = fwht_f32_recursive(x[..., : n // 2])
+    b = fwht_f32_recursive(x[..., n // 2:])
+    return np.concatenate([a + b, a - b], axis=-1).astype(np.float32)
+
+
+def inv_sqrt128_f32() -> np.float32:
+    """fp32 RNE of 2^-3.5 from a 60-digit square root."""
+    getcontext().prec = 60
+    return np.float32(rn32(Fraction(Decimal(1) / (Decimal(8) * Decimal(2).sqrt()))))
+
+
+# -------------------------------------------------------------- unpacking --
+
+def _f16(lo: int, hi: int) -> float:
+    return float(np.array([lo | (hi << 8)], np.uint16).view(np.float16)[0])
+
+
+def unpack_block(block: np.ndarray):
+    """block: uint8[2176] -> (kc[16][128], vc[16][128], kd[16], km[16], vd[16], vm[16])."""
+    kc = np.zeros((PAGE, HD), np.int64)
+    vc = np.zeros((PAGE, HD), np.int64)
+    for t in range(PAGE):
+        for ch in range(HD):
+            byte = int(block[64 * t + ch // 2])
+            kc[t, ch] = (byte >> (4 * (ch % 2))) & 15
+    for ch in range(HD):
+        for t in range(PAGE):
+            byte = int(block[1024 + 8 * ch + t // 2])
+            vc[t, ch] = (byte >> (4 * (t % 2))) & 15
+    meta = []
+    for base in (2048, 2112):
+        d = [_f16(int(block[base + 4 * t]), int(block[base + 4 * t + 1])) for t in range(PAGE)]
+        m = [_f16(int(block[base + 4 * t + 2]), int(block[base + 4 * t + 3])) for t in range(PAGE)]
+        meta += [d, m]
+    return kc, vc, *meta
+
+
+# ----------------------------------------------------------------- decode --
+
+def query_codes(q_bf16_bits: np.ndarray):
+    """Rotated, symmetric INT8 query codes by explicit FP32 steps."""
+    q = (q_bf16_bits.astype(np.uint32) << 16).view(np.float32)
+    r = (fwht_f32_recursive(q) * inv_sqrt128_f32()).astype(np.float32)
+    a = float(np.max(np.abs(r)))
+    s = f32_div(a, 127.0)
+    if s == 0.0:
+        return np.zeros(HD, np.int64), 0.0, 0
+    codes = np.array([min(127, max(-127, rint_even(f32_div(float(x), s)))) for x in r], np.int64)
+    return codes, s, int(codes.sum())
+
+
+def decode_one(pages, side_codes, side_scales, Hkv, q_bits, L, slot, g, table_row, scale_log2,
+               pv_exact=False):
+    """One (sequence, q-head): returns out[128] (f64), lse, and dicts of the
+    integer intermediates keyed by position / logical page."""
+    qc, s_q, S_q = query_codes(q_bits)
+    c_q = f32_mul(s_q, scale_log2)
+    qk, pcode, pv = {}, {}, {}
+    parts = []
+    # protected region: sinks and recent window
+    prot = list(range(0, min(SINK, L))) + list(range(max(SINK, L - WINDOW), L))
+    zs, rows = [], []
+    for p in prot:
+        row = p if p < SINK else SINK + p % WINDOW
+        k8 = side_codes[slot, g, row, 0].astype(np.int64)
+        d8 = int(np.dot(qc, k8))
+        qk[p] = d8
+        sk = float(np.array([side_scales[slot, g, row, 0]], np.uint16).view(np.float16)[0])
+        zs.append(f32_mul(f32_mul(float(d8), sk), c_q))
+        rows.append(row)
+    zmax = max(zs)
+    A = np.zeros(HD)
+    ell = 0.0
+    for z, row in zip(zs, rows):
+        e = exp2s(f32_sub(z, zmax))
+        sv = float(np.array([side_scales[slot, g, row, 1]], np.uint16).view(np.float16)[0])
+        v8 = side_codes[slot, g, row, 1].astype(np.int64)
+        vhat = np.array([rnbf16(f32_mul(sv, float(c))) for c in v8])
+        A += e * vhat
+        ell += e
+    parts.append((A, zmax, ell))
+    # main region, one tile per logical page
+    main_end = L - WINDOW
+    j = 1
+    while PAGE * j < main_end:
+        kc, vc, kd, km, vd, vm = unpack_block(pages[table_row[j], g])
+        n = min(PAGE, main_end - PAGE * j)
+        z = []
+        for t in range(n):
+            D = int(np.dot(qc, kc[t]))
+            qk[PAGE * j + t] = D
+            z.append(f32_mul(f32_fma(kd[t], float(D), f32_mul(km[t], float(S_q))), c_q))
+        zt = max(z)
+        e = [exp2s(f32_sub(zz, zt)) for zz in z]
+        u = [f32_mul(e[t], vd[t]) for t in range(n)]
+        umax = max(u)
+        ell = sum(e)
+        mu = sum(e[t] * vm[t] for t in range(n))
+        if pv_exact:
+            A = np.array([sum(e[t] * (vd[t] * vc[t, ch] + vm[t]) for t in range(n))
+                          for ch in range(HD)])
+        else:
+            if umax == 0.0:
+                uc = [0] * n
+            else:
+                inv = f32_div(127.0, umax)
+                uc = [min(127, max(0, rint_even(f32_mul(ut, inv)))) for ut in u]
+            acc = np.array([sum(uc[t] * int(vc[t, ch]) for t in range(n)) for ch in range(HD)])
+            for t in range(n):
+                pcode[PAGE * j + t] = uc[t]
+            pv[j] = acc
+            A = (umax / 127.0) * acc.astype(np.float64) + mu
+        parts.append((A, zt, ell))
+        j += 1
+    Z = max(p[1] for p in parts)
+    num = sum(2.0 ** (p[1] - Z) * p[0] for p in parts)
+    den = sum(2.0 ** (p[1] - Z) * p[2] for p in parts)
+    return num / den, math.log(2) * (Z + math.log2(den)), qk, pcode, pv
