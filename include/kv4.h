@@ -1,0 +1,175 @@
+/*
+ * kv4.h -- C ABI of the KV4-RL hybrid decode-attention library (MI355X, gfx950).
+ *
+ * The operations follow the KV4-RL pages (paper.rainbus.top summary,
+ * "方法步骤详情" steps 2-4 and "核心方法"; onedev.kr summary, "전제와 한계"):
+ *   - every cached position of K and V is group-affine INT4 (one group per
+ *     128-dim token-head vector, x^ = delta*c + m, FP16 delta and m computed on
+ *     line), 4.25 bits per element; keys are Hadamard-rotated after RoPE;
+ *   - the first 16 (sink) and last 128 (recent) positions also have an INT8
+ *     copy in a fixed-capacity side buffer; leaving the window rewrites nothing;
+ *   - one decode step quantizes the rotated query to INT8 once, runs integer
+ *     QK and integer PV over the INT4 main region and INT8 QK / BF16 V / FP32 PV
+ *     over the protected region, and merges the two exactly.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers (HIP global memory) unless a
+ *     comment says otherwise; descriptors and debug structs live on the host.
+ *   - The caller owns all memory.  The library never allocates, frees or
+ *     synchronizes, keeps no state between calls, and enqueues its work on the
+ *     given HIP stream (`hipStream_t` passed as void*; NULL = default stream).
+ *     Calls are stream-ordered: an append followed by a decode on the same
+ *     stream sees the appended token.
+ *   - Return value: KV4_OK (0) or a negative KV4_ERR_* code; no exception
+ *     crosses the ABI.  Host-checkable argument errors are reported before
+ *     anything is enqueued.  Device-side contracts (1 <= ctx_len <= max_ctx,
+ *     valid page ids, slot < max_slots, positions inside the page table) are
+ *     not checked on the device.
+ *   - BF16/FP16 tensors are 16-bit IEEE patterns; all device pointers must be
+ *     16-byte aligned.
+ */
+#ifndef KV4_H
+#define KV4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KV4_ABI_VERSION 1
+
+enum {
+  KV4_OK = 0,
+  KV4_ERR_NULLPTR = -1,     /* a required pointer is NULL */
+  KV4_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_size != 16, sink != 16,
+                               window != 128, Hq % Hkv != 0 or Hq / Hkv != 4,
+                               or abi_version mismatch */
+  KV4_ERR_SHAPE = -3,       /* a size is out of range (B <= 0, max_ctx > pt_stride*16, ...) */
+  KV4_ERR_WORKSPACE = -4,   /* workspace missing or smaller than kv4_decode_workspace_bytes */
+  KV4_ERR_HIP = -5          /* a HIP call failed; kv4_strerror gives the HIP message */
+};
+
+/* One layer's cache (host-side descriptor of caller-owned device memory).
+ *   pages        uint8 [num_pages][num_kv_heads][2176]: one block per
+ *                (physical page, kv-head) = K codes 1024 B (position t at bytes
+ *                64t..64t+63, channel 2i in the low nibble of byte i, 2i+1 in
+ *                the high nibble) | V codes 1024 B (channel j at bytes
+ *                8j..8j+7, position 2k in the low nibble of byte k, 2k+1 in
+ *                the high nibble) | 16 x {delta, m} FP16 for K | same for V.
+ *   side_codes   int8  [max_slots][num_kv_heads][144][2][128]: INT8 copies,
+ *                K (rotated) then V, of sink positions (row p for p < 16) and
+ *                recent positions (row 16 + p mod 128).
+ *   side_scales  fp16  [max_slots][num_kv_heads][144][2]: their scales. */
+typedef struct kv4_cache_desc {
+  int32_t abi_version; /* KV4_ABI_VERSION */
+  int32_t num_pages;
+  int32_t page_size;   /* must be 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;    /* must be 128 */
+  int32_t sink;        /* must be 16 */
+  int32_t window;      /* must be 128 */
+  int32_t max_slots;
+  void *pages;
+  void *side_codes;
+  void *side_scales;
+} kv4_cache_desc;
+
+/* Quantize-on-append of one token per sequence (steps 2-3 of the pages).
+ *   k, v        bf16 [B][num_kv_heads][128], post-RoPE keys and values
+ *   pos         int32 [B], position of the token in its sequence
+ *   slot        int32 [B], side-buffer slot of each sequence (NULL = b)
+ *   page_table  int32 [B][pt_stride], logical page -> physical page; entry
+ *               pos/16 must name a page owned by sequence b
+ * Writes the INT4 codes and FP16 delta/m of K (rotated) and V into slot pos%16
+ * of page page_table[b][pos/16], and the INT8 side row of pos (sinks for
+ * pos < 16, the recent ring otherwise).  The INT4 entry of the position
+ * leaving the window is not touched.  Two entries of one call must not write
+ * the same position. */
+int kv4_append(const kv4_cache_desc *cache, const void *k, const void *v, const int32_t *pos,
+               const int32_t *slot, const int32_t *page_table, int32_t pt_stride, int32_t B,
+               void *stream);
+
+/* Bulk re-prefill of carried prefixes (step 1 of the pages): quantizes T
+ * tokens exactly as T appends at positions start_pos[s] .. start_pos[s]+n_s-1
+ * would, leaving byte-identical pages and side rows.
+ *   k, v        bf16 [T][num_kv_heads][128], sequences back to back
+ *   cu_seqlens  int32 [nseq+1], token offsets (cu_seqlens[0] = 0)
+ *   start_pos   int32 [nseq], first position of each sequence's tokens
+ *   slot        int32 [nseq] (NULL = s);  page_table int32 [nseq][pt_stride]
+ *   max_seqlen  host upper bound of max_s (start_pos[s] % 16 + n_s), sizes the grid */
+int kv4_prefill_quantize(const kv4_cache_desc *cache, const void *k, const void *v,
+                         const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *slot,
+                         const int32_t *page_table, int32_t pt_stride, int32_t nseq,
+                         int32_t max_seqlen, void *stream);
+
+/* Bytes of device workspace kv4_decode_attention needs for B sequences and
+ * Hq query heads on the current device (0 on bad arguments). */
+size_t kv4_decode_workspace_bytes(const kv4_cache_desc *cache, int32_t B, int32_t Hq,
+                                  int32_t max_ctx);
+
+/* One decode step of hybrid attention (step 4 of the pages).
+ *   q          bf16 [B][Hq][128], post-RoPE queries; q-head h reads kv-head h/(Hq/Hkv)
+ *   ctx_len    int32 [B], context length INCLUDING this step's token: attends [0, ctx_len)
+ *   slot, page_table, pt_stride as for kv4_append
+ *   max_ctx    host upper bound of ctx_len (<= pt_stride * 16)
+ *   softmax_scale  logit scale (typically 1/sqrt(128))
+ *   out        fp32 [B][Hq][128], attention output
+ *   lse        fp32 [B][Hq], natural-log normaliser of the softmax
+ *   workspace  device scratch of at least kv4_decode_workspace_bytes bytes
+ * Positions [16, ctx_len-128) are read from the INT4 pages; [0, 16) and
+ * [max(16, ctx_len-128), ctx_len) from the INT8 side rows. */
+int kv4_decode_attention(const kv4_cache_desc *cache, const void *q, const int32_t *ctx_len,
+                         const int32_t *slot, const int32_t *page_table, int32_t pt_stride,
+                         int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale, float *out,
+                         float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Integer intermediates of a decode step, for bit-exact checking (device
+ * pointers; any may be NULL).  Same layouts as the arguments of
+ * kv4_decode_attention plus:
+ *   qcodes  int8  [B][Hq][128]   INT8 codes of the rotated query
+ *   qsum    int32 [B][Hq]        their sum
+ *   qk      int32 [B][Hq][max_ctx]  integer Q.K of each attended position
+ *   pcode   uint8 [B][Hq][max_ctx]  P-operand code of each main position
+ *   pv      int32 [B][Hq][max_pages][128]  integer P.V accumulators of the
+ *                                 main tile on logical page j (j >= 1) */
+typedef struct kv4_decode_debug {
+  int8_t *qcodes;
+  int32_t *qsum;
+  int32_t *qk;
+  uint8_t *pcode;
+  int32_t *pv;
+  int32_t max_ctx;
+  int32_t max_pages;
+} kv4_decode_debug;
+
+/* kv4_decode_attention running the same kernels instantiated with extra
+ * stores of the integer intermediates into *dbg (a host struct). */
+int kv4_decode_attention_debug(const kv4_cache_desc *cache, const void *q,
+                               const int32_t *ctx_len, const int32_t *slot,
+                               const int32_t *page_table, int32_t pt_stride, int32_t B,
+                               int32_t Hq, int32_t max_ctx, float softmax_scale, float *out,
+                               float *lse, void *workspace, size_t workspace_bytes,
+                               const kv4_decode_debug *dbg, void *stream);
+
+/* Static message for a status code (for KV4_ERR_HIP: the last HIP error seen
+ * by this thread). */
+const char *kv4_strerror(int status);
+
+/* ---- comparator, not part of the method: plain BF16 paged decode ----------
+ * The baseline the pages compare against is ordinary BF16 paged attention.
+ *   pages   bf16 [num_pages][Hkv][2][16][128]: per (page, kv-head) 16 K rows
+ *           then 16 V rows, unrotated
+ *   q, ctx_len, page_table, out, lse as for kv4_decode_attention; Hq/Hkv = 4 */
+size_t kv4bench_bf16_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx);
+int kv4bench_bf16_paged_decode(const void *pages, int32_t num_pages, int32_t Hkv, const void *q,
+                               const int32_t *ctx_len, const int32_t *page_table,
+                               int32_t pt_stride, int32_t B, int32_t Hq, int32_t max_ctx,
+                               float softmax_scale, float *out, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KV4_H */

@@ -1,0 +1,196 @@
+"""Python binding of libkv4 (include/kv4.h): KV4-RL hybrid decode attention on
+MI355X.
+
+Argument marshalling only.  Every step of the path runs in the library's HIP
+kernels; PyTorch only provides device memory and the current stream.  There is
+no fallback: if libkv4.so has not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkv4.so")
+ABI_VERSION = 1
+HEAD_DIM, PAGE, SINK, WINDOW, SIDE_ROWS, BLOCK_BYTES = 128, 16, 16, 128, 144, 2176
+
+# Every extern "C" function of include/kv4.h.
+EXPORTS = ("kv4_append", "kv4_prefill_quantize", "kv4_decode_workspace_bytes",
+           "kv4_decode_attention", "kv4_decode_attention_debug", "kv4_strerror",
+           "kv4bench_bf16_workspace_bytes", "kv4bench_bf16_paged_decode")
+
+_lib = None
+
+
+class Kv4Error(RuntimeError):
+    pass
+
+
+class _Desc(C.Structure):
+    _fields_ = [("abi_version", C.c_int32), ("num_pages", C.c_int32), ("page_size", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("sink", C.c_int32),
+                ("window", C.c_int32), ("max_slots", C.c_int32), ("pages", C.c_void_p),
+                ("side_codes", C.c_void_p), ("side_scales", C.c_void_p)]
+
+
+class _Debug(C.Structure):
+    _fields_ = [("qcodes", C.c_void_p), ("qsum", C.c_void_p), ("qk", C.c_void_p),
+                ("pcode", C.c_void_p), ("pv", C.c_void_p), ("max_ctx", C.c_int32),
+                ("max_pages", C.c_int32)]
+
+
+def lib():
+    """Load libkv4.so (built by int8_mixed_precision_kv4_amd/build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise Kv4Error(f"{LIB_PATH} is missing: build it with "
+                           "`python int8_mixed_precision_kv4_amd/build.py`")
+        L = C.CDLL(LIB_PATH)
+        P, I, F, Z = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
+        D = C.POINTER(_Desc)
+        L.kv4_append.argtypes = [D, P, P, P, P, P, I, I, P]
+        L.kv4_prefill_quantize.argtypes = [D, P, P, P, P, P, P, I, I, I, P]
+        L.kv4_decode_workspace_bytes.argtypes = [D, I, I, I]
+        L.kv4_decode_workspace_bytes.restype = Z
+        L.kv4_decode_attention.argtypes = [D, P, P, P, P, I, I, I, I, F, P, P, P, Z, P]
+        L.kv4_decode_attention_debug.argtypes = [D, P, P, P, P, I, I, I, I, F, P, P, P, Z,
+                                                 C.POINTER(_Debug), P]
+        L.kv4_strerror.argtypes = [C.c_int]
+        L.kv4_strerror.restype = C.c_char_p
+        L.kv4bench_bf16_workspace_bytes.argtypes = [I, I, I, I]
+        L.kv4bench_bf16_workspace_bytes.restype = Z
+        L.kv4bench_bf16_paged_decode.argtypes = [P, I, I, P, P, P, I, I, I, I, F, P, P, P, Z, P]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise Kv4Error(f"kv4 error {rc}: {lib().kv4_strerror(rc).decode()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA tensors"
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Kv4Cache:
+    """One layer's cache: paged INT4 pool + INT8 side buffer (device tensors)."""
+
+    def __init__(self, pages: torch.Tensor, side_codes: torch.Tensor, side_scales: torch.Tensor):
+        self.pages, self.side_codes, self.side_scales = pages, side_codes, side_scales
+        self.num_pages, self.num_kv_heads = int(pages.shape[0]), int(pages.shape[1])
+        self.max_slots = int(side_codes.shape[0])
+        assert pages.shape[2] == BLOCK_BYTES and pages.dtype == torch.uint8
+        assert tuple(side_codes.shape[1:]) == (self.num_kv_heads, SIDE_ROWS, 2, HEAD_DIM)
+        assert tuple(side_scales.shape[1:]) == (self.num_kv_heads, SIDE_ROWS, 2)
+        self._desc = _Desc(ABI_VERSION, self.num_pages, PAGE, self.num_kv_heads, HEAD_DIM, SINK,
+                           WINDOW, self.max_slots, pages.data_ptr(), side_codes.data_ptr(),
+                           side_scales.data_ptr())
+
+    @classmethod
+    def zeros(cls, num_pages: int, num_kv_heads: int, max_slots: int, device="cuda"):
+        return cls(torch.zeros((num_pages, num_kv_heads, BLOCK_BYTES), dtype=torch.uint8, device=device),
+                   torch.zeros((max_slots, num_kv_heads, SIDE_ROWS, 2, HEAD_DIM), dtype=torch.int8,
+                               device=device),
+                   torch.zeros((max_slots, num_kv_heads, SIDE_ROWS, 2), dtype=torch.int16,
+                               device=device))
+
+    def desc(self):
+        return C.byref(self._desc)
+
+
+def append(cache: Kv4Cache, k, v, pos, slot, page_table):
+    """kv4_append: k, v bf16 [B][Hkv][128]; pos, slot int32 [B]; page_table int32 [B][W]."""
+    _check(lib().kv4_append(cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(slot),
+                            _ptr(page_table), page_table.shape[1], pos.shape[0], _stream()))
+
+
+def prefill_quantize(cache: Kv4Cache, k, v, cu_seqlens, start_pos, slot, page_table,
+                     max_seqlen: int):
+    """kv4_prefill_quantize: k, v bf16 [T][Hkv][128]; cu_seqlens int32 [nseq+1]."""
+    _check(lib().kv4_prefill_quantize(cache.desc(), _ptr(k), _ptr(v), _ptr(cu_seqlens),
+                                      _ptr(start_pos), _ptr(slot), _ptr(page_table),
+                                      page_table.shape[1], start_pos.shape[0], int(max_seqlen),
+                                      _stream()))
+
+
+def decode_workspace_bytes(cache: Kv4Cache, B: int, Hq: int, max_ctx: int) -> int:
+    return int(lib().kv4_decode_workspace_bytes(cache.desc(), B, Hq, max_ctx))
+
+
+def decode_attention(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ctx: int,
+                     softmax_scale: float, out=None, lse=None, workspace=None):
+    """kv4_decode_attention: q bf16 [B][Hq][128] -> (out fp32 [B][Hq][128], lse fp32 [B][Hq])."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(cache, B, Hq, max_ctx), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().kv4_decode_attention(cache.desc(), _ptr(q), _ptr(ctx_len), _ptr(slot),
+                                      _ptr(page_table), page_table.shape[1], B, Hq, int(max_ctx),
+                                      float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                      workspace.numel(), _stream()))
+    return out, lse
+
+
+def decode_attention_debug(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ctx: int,
+                           softmax_scale: float):
+    """kv4_decode_attention_debug: also returns the integer intermediates
+    (qcodes, qsum, qk, pcode, pv) as device tensors."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    W = int(page_table.shape[1])
+    dev = q.device
+    dbg = dict(qcodes=torch.zeros((B, Hq, HEAD_DIM), dtype=torch.int8, device=dev),
+               qsum=torch.zeros((B, Hq), dtype=torch.int32, device=dev),
+               qk=torch.zeros((B, Hq, W * PAGE), dtype=torch.int32, device=dev),
+               pcode=torch.zeros((B, Hq, W * PAGE), dtype=torch.uint8, device=dev),
+               pv=torch.zeros((B, Hq, W, HEAD_DIM), dtype=torch.int32, device=dev))
+    d = _Debug(dbg["qcodes"].data_ptr(), dbg["qsum"].data_ptr(), dbg["qk"].data_ptr(),
+               dbg["pcode"].data_ptr(), dbg["pv"].data_ptr(), W * PAGE, W)
+    out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(decode_workspace_bytes(cache, B, Hq, max_ctx), dtype=torch.uint8, device=dev)
+    _check(lib().kv4_decode_attention_debug(cache.desc(), _ptr(q), _ptr(ctx_len), _ptr(slot),
+                                            _ptr(page_table), W, B, Hq, int(max_ctx),
+                                            float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                            ws.numel(), C.byref(d), _stream()))
+    return out, lse, dbg
+
+
+def bf16_workspace_bytes(B: int, Hq: int, Hkv: int, max_ctx: int) -> int:
+    return int(lib().kv4bench_bf16_workspace_bytes(B, Hq, Hkv, max_ctx))
+
+
+def bf16_paged_decode(pages, q, ctx_len, page_table, max_ctx: int, softmax_scale: float,
+                      out=None, lse=None, workspace=None):
+    """kv4bench_bf16_paged_decode (comparator): pages bf16 [P][Hkv][2][16][128]
+    with K token-major and V channel-major."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    Hkv = int(pages.shape[1])
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(bf16_workspace_bytes(B, Hq, Hkv, max_ctx), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().kv4bench_bf16_paged_decode(_ptr(pages), int(pages.shape[0]), Hkv, _ptr(q),
+                                            _ptr(ctx_len), _ptr(page_table), page_table.shape[1],
+                                            B, Hq, int(max_ctx), float(softmax_scale), _ptr(out),
+                                            _ptr(lse), _ptr(workspace), workspace.numel(),
+                                            _stream()))
+    return out, lse

@@ -1,0 +1,201 @@
+// kv4_device.hpp -- device-side building blocks shared by the KV4-RL kernels
+// (gfx950, wave64).  Numeric rules follow the KV4-RL pages (paper.rainbus.top
+// summary, "分组仿射 KV 量化" and "方法步骤详情" steps 2-4); where the pages are
+// silent the rule is stated where it is implemented.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kv4 {
+
+constexpr int HD = 128;          // one quantization group = one 128-dim token-head vector
+constexpr int PAGE = 16;         // positions per page
+constexpr int SINK = 16;         // protected leading positions
+constexpr int WINDOW = 128;      // protected recent positions
+constexpr int SIDE_ROWS = SINK + WINDOW;
+constexpr int BLOCK_BYTES = 2176;  // per (page, kv-head): 16 x (64 + 64 + 4 + 4)
+constexpr int OFF_VCODE = 1024;
+constexpr int OFF_KMETA = 2048;
+constexpr int OFF_VMETA = 2112;
+constexpr int GQA = 4;           // query heads per kv-head handled by the decode kernels
+
+// ---------------------------------------------------------------- formats --
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// IEEE binary16, round to nearest even (v_cvt_f16_f32 under the default mode,
+// subnormals kept).
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  _Float16 h = static_cast<_Float16>(x);
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_value(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+// Round a finite binary32 to bfloat16 (nearest, ties to even); value kept in FP32.
+__device__ __forceinline__ float round_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+  return __uint_as_float(u);
+}
+
+// ----------------------------------------------------------- cross-lane --
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// All-reduce over each row of 16 lanes: quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror, row_mirror.  Every lane ends with the result.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ------------------------------------------------------------- rotation --
+// Orthonormal Sylvester Hadamard H_128/sqrt(128) applied to a row vector held
+// by one wave, lane l holding elements 2l (x0) and 2l+1 (x1).  FP32 in-place
+// fast Walsh-Hadamard transform with element strides 1, 2, ..., 64 in that
+// order, butterfly (a, b) -> (a + b, a - b), then one multiply by fp32(2^-3.5).
+// The stride order fixes the FP32 sum tree of every output.
+constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;
+
+__device__ __forceinline__ void fwht128_wave(float& x0, float& x1) {
+  const float a = x0 + x1, b = x0 - x1;
+  x0 = a;
+  x1 = b;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {  // element stride 2h lives h lanes away
+    const float p0 = __shfl_xor(x0, h), p1 = __shfl_xor(x1, h);
+    const bool upper = (lane & h) != 0;
+    x0 = upper ? (p0 - x0) : (x0 + p0);
+    x1 = upper ? (p1 - x1) : (x1 + p1);
+  }
+  x0 = x0 * kInvSqrt128;
+  x1 = x1 * kInvSqrt128;
+}
+
+// ----------------------------------------------------------- quantizers --
+
+// Quotient RN(a/d) for a binary32 dividend and a divisor d with at most 11
+// significant bits (an FP16 value), given y = RN(1/d).  a/d is then never
+// closer than 2^-12 ulp to a rounding midpoint of binary32 (and never on
+// one), the residual a - d*RN(a*y) is exact in one FMA, and q0 + r*y is within
+// 2^-22 ulp of a/d, so a single rounding of it is the correctly rounded
+// quotient.  Three operations instead of a full IEEE division sequence.
+__device__ __forceinline__ float div_short_divisor(float a, float d, float y) {
+  const float q0 = a * y;
+  const float r = __builtin_fmaf(-q0, d, a);
+  return __builtin_fmaf(r, y, q0);
+}
+
+// Group-affine INT4 metadata of one vector from its FP32 min and max:
+// delta = fp16((max - min) / 15), offset m = fp16(min).
+struct Int4Meta {
+  uint32_t d16, m16;  // FP16 bit patterns
+  float d, m;         // their values
+  float dinv;         // RN(1/d), 0 when d == 0
+};
+__device__ __forceinline__ Int4Meta int4_meta(float mn, float mx) {
+  Int4Meta r;
+  const float range = mx - mn;
+  r.d16 = f16_bits(range / 15.0f);
+  r.m16 = f16_bits(mn);
+  r.d = f16_value(r.d16);
+  r.m = f16_value(r.m16);
+  r.dinv = (r.d == 0.0f) ? 0.0f : 1.0f / r.d;
+  return r;
+}
+// c = clamp(rint((x - m) / delta), 0, 15); a zero delta gives code 0.
+__device__ __forceinline__ uint32_t int4_code(float x, const Int4Meta& q) {
+  if (q.d == 0.0f) return 0u;
+  const float t = __builtin_rintf(div_short_divisor(x - q.m, q.d, q.dinv));
+  return static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), 15.0f));
+}
+
+// Symmetric INT8 side copy: s = fp16(max|x| / 127), c = clamp(rint(x / s), -127, 127).
+struct Int8Meta {
+  uint32_t s16;
+  float s, sinv;
+};
+__device__ __forceinline__ Int8Meta int8_meta(float amax) {
+  Int8Meta r;
+  r.s16 = f16_bits(amax / 127.0f);
+  r.s = f16_value(r.s16);
+  r.sinv = (r.s == 0.0f) ? 0.0f : 1.0f / r.s;
+  return r;
+}
+__device__ __forceinline__ int32_t int8_code(float x, const Int8Meta& q) {
+  if (q.s == 0.0f) return 0;
+  const float t = __builtin_rintf(div_short_divisor(x, q.s, q.sinv));
+  return static_cast<int32_t>(fminf(fmaxf(t, -127.0f), 127.0f));
+}
+
+// ----------------------------------------------------------------- exp2 --
+// Softmax weights: 2^y for y <= 0 evaluated the same way on every device so
+// that P-operand codes are reproducible: y < -125 gives 0; otherwise
+// n = rint(y), f = y - n (exact), degree-7 Taylor polynomial of 2^f in Horner
+// form with FMA, coefficients RN(ln2^k / k!), result p * 2^n.
+namespace detail {
+constexpr double kLn2 = 0.6931471805599453094172321214581766;
+constexpr float kC0 = 1.0f;
+constexpr float kC1 = static_cast<float>(kLn2);
+constexpr float kC2 = static_cast<float>(kLn2 * kLn2 / 2.0);
+constexpr float kC3 = static_cast<float>(kLn2 * kLn2 * kLn2 / 6.0);
+constexpr float kC4 = static_cast<float>(kLn2 * kLn2 * kLn2 * kLn2 / 24.0);
+constexpr float kC5 = static_cast<float>(kLn2 * kLn2 * kLn2 * kLn2 * kLn2 / 120.0);
+constexpr float kC6 = static_cast<float>(kLn2 * kLn2 * kLn2 * kLn2 * kLn2 * kLn2 / 720.0);
+constexpr float kC7 = static_cast<float>(kLn2 * kLn2 * kLn2 * kLn2 * kLn2 * kLn2 * kLn2 / 5040.0);
+}  // namespace detail
+
+__device__ __forceinline__ float exp2s(float y) {
+  using namespace detail;
+  const bool live = (y >= -125.0f);
+  const float yc = live ? y : 0.0f;
+  const float n = __builtin_rintf(yc);
+  const float f = yc - n;
+  float p = kC7;
+  p = __builtin_fmaf(p, f, kC6);
+  p = __builtin_fmaf(p, f, kC5);
+  p = __builtin_fmaf(p, f, kC4);
+  p = __builtin_fmaf(p, f, kC3);
+  p = __builtin_fmaf(p, f, kC2);
+  p = __builtin_fmaf(p, f, kC1);
+  p = __builtin_fmaf(p, f, kC0);
+  const float r = __builtin_ldexpf(p, static_cast<int>(n));
+  return live ? r : 0.0f;
+}
+
+}  // namespace kv4

@@ -1,0 +1,59 @@
+// kv4_internal.hpp -- kernel launchers shared between the translation units of
+// libkv4 (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kv4 {
+
+struct CacheView {
+  uint8_t* pages;
+  int8_t* side_codes;
+  uint16_t* side_scales;
+  int num_pages, Hkv, max_slots;
+};
+
+struct DecodeDebug {
+  int8_t* qcodes;
+  int32_t* qsum;
+  int32_t* qk;
+  uint8_t* pcode;
+  int32_t* pv;
+  int max_ctx, max_pages;
+};
+
+// Workspace carve-up of one decode call.
+struct DecodeWorkspace {
+  int32_t* plan;   // [B+1] prefix sums of (main pages x Hkv) over sequences
+  int8_t* qcodes;  // [B][Hq][128] INT8 codes of the rotated queries
+  float* qinfo;    // [B][Hq][4]  {c_q, S_q (int bits), s_q, 0}
+  float* prot;     // [B][Hq][kPart] partial of the protected region
+  float* parts;    // [n_waves + B*Hkv][4][kPart] partials of the main region
+  int n_waves;     // waves of the main-region grid
+};
+constexpr int kPart = 132;  // A[128], Z, l, 2 pad
+
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_waves);
+DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves);
+int main_region_waves();  // size of the main-region grid on the current device
+
+hipError_t launch_append(const CacheView& c, const uint16_t* k, const uint16_t* v,
+                         const int32_t* pos, const int32_t* slot, const int32_t* page_table,
+                         int pt_stride, int B, hipStream_t s);
+hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t* v,
+                          const int32_t* cu, const int32_t* start, const int32_t* slot,
+                          const int32_t* page_table, int pt_stride, int nseq, int max_seqlen,
+                          hipStream_t s);
+hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* ctx,
+                         const int32_t* slot, const int32_t* page_table, int pt_stride, int B,
+                         int Hq, float scale_log2, float* out, float* lse,
+                         const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s);
+hipError_t launch_bf16_decode(const uint16_t* pages, int num_pages, int Hkv, const uint16_t* q,
+                              const int32_t* ctx, const int32_t* page_table, int pt_stride, int B,
+                              int Hq, float scale_log2, float* out, float* lse, void* ws,
+                              int n_waves, hipStream_t s);
+size_t bf16_workspace_bytes(int B, int Hq, int Hkv, int n_waves);
+
+}  // namespace kv4

@@ -1,0 +1,161 @@
+// kv4_quantize.hip -- quantize-on-append and bulk re-prefill of the KV4-RL
+// cache (paper.rainbus.top summary, "方法步骤详情" steps 1-3).
+//
+// Each K vector is rotated (Hadamard after RoPE), then K and V are quantized
+// independently to group-affine INT4 (one group per 128-dim token-head
+// vector, FP16 delta and offset computed on line) into their page slot; sink
+// positions (< 16) and recent positions also get a symmetric INT8 copy in the
+// side buffer.  A position leaving the recent window keeps its INT4 entry; its
+// ring row is simply reused.
+#include "kv4_device.hpp"
+#include "kv4_internal.hpp"
+
+namespace kv4 {
+namespace {
+
+struct QuantArgs {
+  uint8_t* pages;
+  int8_t* side_codes;
+  uint16_t* side_scales;
+  int Hkv;
+  const uint32_t* k;  // bf16 pairs: lane l of a vector reads elements 2l, 2l+1
+  const uint32_t* v;
+  const int32_t* slot;
+  const int32_t* page_table;
+  int pt_stride;
+};
+
+__device__ __forceinline__ int side_row(int p) { return p < SINK ? p : SINK + (p % WINDOW); }
+
+// INT8 side row of one position (K rotated, V), held by one wave.
+__device__ __forceinline__ void write_side_row(const QuantArgs& a, int slot, int g, int pos,
+                                               float k0, float k1, float v0, float v1, int lane) {
+  const size_t r = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS + side_row(pos);
+  const Int8Meta ks = int8_meta(wave_max(fmaxf(fabsf(k0), fabsf(k1))));
+  const Int8Meta vs = int8_meta(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
+  const uint32_t kp = (static_cast<uint32_t>(int8_code(k0, ks)) & 0xFFu) |
+                      ((static_cast<uint32_t>(int8_code(k1, ks)) & 0xFFu) << 8);
+  const uint32_t vp = (static_cast<uint32_t>(int8_code(v0, vs)) & 0xFFu) |
+                      ((static_cast<uint32_t>(int8_code(v1, vs)) & 0xFFu) << 8);
+  uint16_t* codes = reinterpret_cast<uint16_t*>(a.side_codes + r * 2 * HD);
+  codes[lane] = static_cast<uint16_t>(kp);
+  codes[64 + lane] = static_cast<uint16_t>(vp);
+  if (lane == 0) {
+    a.side_scales[r * 2 + 0] = static_cast<uint16_t>(ks.s16);
+    a.side_scales[r * 2 + 1] = static_cast<uint16_t>(vs.s16);
+  }
+}
+
+// One token per sequence; one wave per (kv-head, sequence).
+__global__ __launch_bounds__(64) void append_kernel(QuantArgs a, const int32_t* __restrict__ pos_arr) {
+  const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int pos = pos_arr[b];
+  const int slot = a.slot ? a.slot[b] : b;
+  const size_t vec = static_cast<size_t>(b) * a.Hkv + g;
+  const uint32_t kw = a.k[vec * 64 + lane], vw = a.v[vec * 64 + lane];
+  float k0 = bf16_lo(kw), k1 = bf16_hi(kw);
+  const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
+  fwht128_wave(k0, k1);  // keys are stored in the rotated basis
+
+  const int phys = a.page_table[static_cast<size_t>(b) * a.pt_stride + (pos >> 4)];
+  const int t = pos & (PAGE - 1);
+  uint8_t* blk = a.pages + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
+
+  const Int4Meta kq = int4_meta(wave_min(fminf(k0, k1)), wave_max(fmaxf(k0, k1)));
+  const Int4Meta vq = int4_meta(wave_min(fminf(v0, v1)), wave_max(fmaxf(v0, v1)));
+  // K: token-major, channel 2l in the low nibble of byte l
+  blk[64 * t + lane] = static_cast<uint8_t>(int4_code(k0, kq) | (int4_code(k1, kq) << 4));
+  // V: channel-major, this position's nibble in bytes 8c + t/2 of channels 2l, 2l+1;
+  // the other nibble belongs to the neighbouring position and is kept.
+  const int sh = (t & 1) * 4;
+  const uint32_t keep = (t & 1) ? 0x0Fu : 0xF0u;
+  uint8_t* vb0 = blk + OFF_VCODE + 8 * (2 * lane) + (t >> 1);
+  uint8_t* vb1 = vb0 + 8;
+  *vb0 = static_cast<uint8_t>((*vb0 & keep) | (int4_code(v0, vq) << sh));
+  *vb1 = static_cast<uint8_t>((*vb1 & keep) | (int4_code(v1, vq) << sh));
+  if (lane == 0) {
+    *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
+    *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
+  }
+  write_side_row(a, slot, g, pos, k0, k1, v0, v1, lane);
+}
+
+// Re-prefill: one workgroup owns one (page, kv-head) block of one sequence, so
+// nibble bytes shared by neighbouring positions have a single writer.  Side
+// rows are written only where appends would leave them in the final state:
+// sinks, and the last 128 positions of the range (earlier ring rows would be
+// overwritten within the same range anyway).
+__global__ __launch_bounds__(256) void prefill_kernel(QuantArgs a, const int32_t* __restrict__ cu,
+                                                      const int32_t* __restrict__ start_pos) {
+  const int lp = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int n = cu[s + 1] - cu[s];
+  if (n <= 0) return;
+  const int start = start_pos[s], end = start + n;
+  const int page = (start >> 4) + lp;
+  if (page > ((end - 1) >> 4)) return;
+  const int t0 = max(start - page * PAGE, 0), t1 = min(end - page * PAGE, PAGE);
+  const int slot = a.slot ? a.slot[s] : s;
+  const int phys = a.page_table[static_cast<size_t>(s) * a.pt_stride + page];
+  uint8_t* blk = a.pages + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
+  const int keep_from = max(SINK, end - WINDOW);
+
+  __shared__ uint8_t vcodes[PAGE][HD];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int t = t0 + wave; t < t1; t += 4) {
+    const int p = page * PAGE + t;
+    const size_t vec = (static_cast<size_t>(cu[s]) + (p - start)) * a.Hkv + g;
+    const uint32_t kw = a.k[vec * 64 + lane], vw = a.v[vec * 64 + lane];
+    float k0 = bf16_lo(kw), k1 = bf16_hi(kw);
+    const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
+    fwht128_wave(k0, k1);
+    const Int4Meta kq = int4_meta(wave_min(fminf(k0, k1)), wave_max(fmaxf(k0, k1)));
+    const Int4Meta vq = int4_meta(wave_min(fminf(v0, v1)), wave_max(fmaxf(v0, v1)));
+    blk[64 * t + lane] = static_cast<uint8_t>(int4_code(k0, kq) | (int4_code(k1, kq) << 4));
+    vcodes[t][2 * lane] = static_cast<uint8_t>(int4_code(v0, vq));
+    vcodes[t][2 * lane + 1] = static_cast<uint8_t>(int4_code(v1, vq));
+    if (lane == 0) {
+      *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
+      *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
+    }
+    if (p < SINK || p >= keep_from) write_side_row(a, slot, g, p, k0, k1, v0, v1, lane);
+  }
+  __syncthreads();
+  // V codes, channel-major: thread -> channel j, positions 8*half .. 8*half+7
+  // (one dword); nibbles of positions outside [t0, t1) are kept.
+  const int j = threadIdx.x >> 1, half = threadIdx.x & 1;
+  uint32_t* vw = reinterpret_cast<uint32_t*>(blk + OFF_VCODE + 8 * j + 4 * half);
+  const bool whole = (t0 <= 8 * half) && (t1 >= 8 * half + 8);
+  uint32_t w = whole ? 0u : *vw;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = 8 * half + i;
+    if (t >= t0 && t < t1) w = (w & ~(0xFu << (4 * i))) | (static_cast<uint32_t>(vcodes[t][j]) << (4 * i));
+  }
+  *vw = w;
+}
+
+}  // namespace
+
+hipError_t launch_append(const CacheView& c, const uint16_t* k, const uint16_t* v,
+                         const int32_t* pos, const int32_t* slot, const int32_t* page_table,
+                         int pt_stride, int B, hipStream_t s) {
+  QuantArgs a{c.pages, c.side_codes, c.side_scales, c.Hkv,
+              reinterpret_cast<const uint32_t*>(k), reinterpret_cast<const uint32_t*>(v),
+              slot, page_table, pt_stride};
+  hipLaunchKernelGGL(append_kernel, dim3(c.Hkv, B), dim3(64), 0, s, a, pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t* v,
+                          const int32_t* cu, const int32_t* start, const int32_t* slot,
+                          const int32_t* page_table, int pt_stride, int nseq, int max_seqlen,
+                          hipStream_t s) {
+  QuantArgs a{c.pages, c.side_codes, c.side_scales, c.Hkv,
+              reinterpret_cast<const uint32_t*>(k), reinterpret_cast<const uint32_t*>(v),
+              slot, page_table, pt_stride};
+  const int pages = (max_seqlen + PAGE - 1) / PAGE + 1;
+  hipLaunchKernelGGL(prefill_kernel, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
+  return hipGetLastError();
+}
+
+}  // namespace kv4

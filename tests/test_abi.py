@@ -1,0 +1,56 @@
+"""The C-ABI library loads and exports every function include/kv4.h declares
+(no GPU needed: nothing is called)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kv4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(kv4[a-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("kv4_append", "kv4_prefill_quantize", "kv4_decode_attention",
+                     "kv4_decode_workspace_bytes", "kv4_strerror", "kv4bench_bf16_paged_decode"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    import int8_mixed_precision_kv4_amd as kv4
+    if not os.path.exists(kv4.LIB_PATH):
+        pytest.skip("libkv4.so not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(kv4.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(kv4.EXPORTS)
+
+
+def test_strerror_without_gpu():
+    import int8_mixed_precision_kv4_amd as kv4
+    if not os.path.exists(kv4.LIB_PATH):
+        pytest.skip("libkv4.so not built")
+    L = kv4.lib()
+    assert L.kv4_strerror(0) == b"success"
+    assert b"workspace" in L.kv4_strerror(-4)
+
+
+def test_host_validation_rejects_bad_arguments_without_gpu():
+    import int8_mixed_precision_kv4_amd as kv4
+    if not os.path.exists(kv4.LIB_PATH):
+        pytest.skip("libkv4.so not built")
+    L = kv4.lib()
+    # NULL descriptor and unsupported geometry are refused before any HIP call
+    assert L.kv4_append(None, None, None, None, None, None, 1, 1, None) == -1
+    d = kv4._Desc(1, 4, 32, 1, 128, 16, 128, 1, 1, 1, 1)  # page_size 32
+    assert L.kv4_append(ctypes.byref(d), 1, 1, 1, None, 1, 1, 1, None) == -2
+    d = kv4._Desc(1, 4, 16, 1, 128, 16, 128, 1, 1, 1, 1)
+    assert L.kv4_append(ctypes.byref(d), 1, 1, 1, None, 1, 1, 0, None) == -3
