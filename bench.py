@@ -1,0 +1,371 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV4-RL hybrid decode-attention path on one MI355X.
+
+Workload (qwen8b-shaped decode step): B=256 sequences, Hq/Hkv = 32/8, head_dim
+128, page 16, 36 layers, contexts = U[128,512] prompt + a length-biased
+lognormal(mean 3000, sd 2250) response position (+ this step's token).  One
+step = for each of the 36 layers: kv4_append of one token per sequence, then
+kv4_decode_attention.  Every layer has its own cache, so the step streams
+~28 GB of INT4 pages and never hits the 256 MB last-level cache.
+
+Prints one JSON line: decode-attention tokens/s (whole step), achieved HBM
+GB/s of the decode against the 8 TB/s peak, the roofline of the dominant
+kernel (timed with HIP events on its own stream), the in-build BF16 paged
+decode for the speed ratio, the re-prefill timing, and the CPU oracle timed on
+a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn tokens/s + achieved HBM GB/s (% of peak), B=256 mixed ctx, 1 GPU"
+PEAK_GBS = 8000.0
+WORKLOAD = 4
+LAYERS = 36
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "main_kernel_traffic_qwen8b.json")
+MAIN_SOURCES = [os.path.join(ROOT, "int8_mixed_precision_kv4_amd", "csrc", f)
+                for f in ("kv4_decode.hip", "kv4_device.hpp")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in MAIN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def metric_bytes(ctx, Hkv):
+    """Bytes per layer by the metric's formula: sum ctx*Hkv*128*2*4.25/8 plus
+    the side rows read (min(ctx,144) rows of 2x(128+2) bytes per kv-head)."""
+    import numpy as np
+    ctx = np.asarray(ctx, dtype=np.int64)
+    return int((ctx * Hkv * 136).sum() + (np.minimum(ctx, 144) * Hkv * 260).sum())
+
+
+def main_kernel_bytes(ctx, Hkv):
+    """Algorithmic bytes of the main-region kernel per launch: 136 B (64 B K
+    codes + 64 B V codes + 4 B + 4 B FP16 metadata) per main (position, kv-head)."""
+    import numpy as np
+    ctx = np.asarray(ctx, dtype=np.int64)
+    return int((np.maximum(ctx - 144, 0) * Hkv * 136).sum())
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs (hipEventCreate / hipEventElapsedTime) so the
+    library can record them on the stream the kernel is launched on."""
+
+    def __init__(self, n):
+        import ctypes
+        self.C = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e)
+
+    def pair(self, i):
+        return self.ev[2 * i], self.ev[2 * i + 1]
+
+    def elapsed_ms(self, i):
+        ms = self.C.c_float()
+        e0, e1 = self.pair(i)
+        assert self.hip.hipEventSynchronize(e1) == 0
+        assert self.hip.hipEventElapsedTime(self.C.byref(ms), e0, e1) == 0
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def build_layers(wl, dev, with_bf16=True):
+    import numpy as np
+    import torch
+
+    import int8_mixed_precision_kv4_amd as kv4
+    from synth import draw_values
+
+    n_tok = int(wl.ctx.sum())
+    off = np.zeros(wl.B + 1, np.int64)
+    off[1:] = np.cumsum(wl.ctx)
+    lead = wl.ctx - 1
+    rows_lead = torch.from_numpy(np.concatenate(
+        [np.arange(off[b], off[b] + lead[b]) for b in range(wl.B)])).to(dev)
+    rows_last = torch.from_numpy(off[:-1] + lead).to(dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lead)]).astype(np.int32)).to(dev)
+    zeros = torch.zeros(wl.B, dtype=torch.int32, device=dev)
+    table = torch.from_numpy(wl.page_table).to(dev)
+    slots = torch.from_numpy(wl.slots).to(dev)
+    # physical page and in-page slot of every position (for the BF16 pools)
+    pos_all = np.concatenate([np.arange(n) for n in wl.ctx])
+    seq_all = np.repeat(np.arange(wl.B), wl.ctx)
+    page_all = torch.from_numpy(wl.page_table[seq_all, pos_all // 16].astype(np.int64)).to(dev)
+    t_all = torch.from_numpy((pos_all % 16).astype(np.int64)).to(dev)
+    layers = []
+    for layer in range(wl.layers):
+        k, v, q = draw_values(wl.seed, layer, n_tok, wl.B, wl.Hq, wl.Hkv, device=dev)
+        cache = kv4.Kv4Cache.zeros(wl.num_pages, wl.Hkv, wl.max_slots, dev)
+        kv4.prefill_quantize(cache, k[rows_lead].contiguous(), v[rows_lead].contiguous(), cu, zeros,
+                             slots, table, int(lead.max()))
+        L = dict(cache=cache, q=q, k_app=k[rows_last].contiguous(), v_app=v[rows_last].contiguous())
+        if with_bf16:
+            pool = torch.empty((wl.num_pages, wl.Hkv, 2, 16, 128), dtype=torch.bfloat16, device=dev)
+            pool[page_all, :, 0, t_all, :] = k
+            vview = pool.view(wl.num_pages, wl.Hkv, 2, 2048)[:, :, 1].view(wl.num_pages, wl.Hkv, 128, 16)
+            vview[page_all, :, :, t_all] = v
+            L["bf16"] = pool
+        if layer == 0:
+            L["k_all"], L["v_all"] = k, v
+        else:
+            del k, v
+        layers.append(L)
+        if layer % 6 == 5:
+            log(f"built {layer + 1}/{wl.layers} layers")
+    torch.cuda.synchronize()
+    return layers, dict(table=table, slots=slots, offsets=off)
+
+
+def cpu_baseline(wl, layer0, shared, budget_s):
+    """The oracle as it stands, on the host cores, on layer 0 of the step (all
+    256 sequences): one append + one 32-head decode, repeated until about
+    budget_s seconds; extrapolated to the 36-layer step."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    def bf16_bits(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    sample = np.arange(wl.B)
+    ctx = wl.ctx[sample]
+    off = shared["offsets"]
+    need = (ctx + 15) // 16
+    table = np.zeros((len(sample), int(need.max())), np.int32)
+    table_flat = np.arange(int(need.sum()), dtype=np.int32)
+    o = 0
+    for i, n in enumerate(need):
+        table[i, :n] = table_flat[o:o + n]
+        o += n
+    k_all, v_all = layer0["k_all"], layer0["v_all"]
+    rows = np.concatenate([np.arange(off[b], off[b] + wl.ctx[b] - 1) for b in sample])
+    k = bf16_bits(k_all[rows].cpu())
+    v = bf16_bits(v_all[rows].cpu())
+    cu = np.concatenate([[0], np.cumsum(ctx - 1)]).astype(np.int32)
+    q = bf16_bits(layer0["q"][sample].cpu())
+    ka = bf16_bits(layer0["k_app"][sample].cpu())
+    va = bf16_bits(layer0["v_app"][sample].cpu())
+    threads = oracle.default_threads()
+    cache = oracle.Cache(int(need.sum()), wl.Hkv, len(sample))
+    slots = np.arange(len(sample), dtype=np.int32)
+    oracle.prefill(cache, k, v, cu, np.zeros(len(sample), np.int32), slots, table, threads)
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        oracle.append(cache, ka, va, (ctx - 1).astype(np.int32), slots, table)
+        out, lse, _ = oracle.decode(cache, q, ctx.astype(np.int32), slots, table, wl.Hq,
+                                    1.0 / math.sqrt(128), nthreads=threads)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    t_layer_sample = t_total / reps
+    t_step = t_layer_sample * (wl.ctx.sum() / ctx.sum()) * wl.layers
+    cpu = open("/proc/cpuinfo").read().split("model name")[1].split("\n")[0].strip(" :\t") \
+        if os.path.exists("/proc/cpuinfo") else "unknown"
+    return dict(value=round(wl.B / t_step, 3), unit="tokens/s", cores=threads, kind="oracle",
+                sample=(f"layer 0 of 36 (all {len(sample)} sequences, mean ctx {ctx.mean():.0f}): "
+                        f"append + 32-head decode, {reps} reps in {t_total:.1f}s; x36 layers"),
+                cpu=cpu), (sample, out, lse)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-copy", action="store_true", help="skip the 2 GiB device copy probe")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences and kv-heads shard with no exchange; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int8_mixed_precision_kv4_amd as kv4
+    from synth import make_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    kv4.lib()
+    wl = make_workload(WORKLOAD)
+    scale = 1.0 / math.sqrt(128)
+    log(f"workload qwen8b: B={wl.B} Hq/Hkv={wl.Hq}/{wl.Hkv} mean ctx {wl.ctx.mean():.0f} "
+        f"max {wl.max_ctx} pages/layer {wl.num_pages}")
+    layers, sh = build_layers(wl, dev, with_bf16=not args.no_bf16)
+    table, slots = sh["table"], sh["slots"]
+    ctx = torch.from_numpy(wl.ctx.astype(np.int32)).to(dev)
+    pos = (ctx - 1).contiguous()
+    B, Hq = wl.B, wl.Hq
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(kv4.decode_workspace_bytes(layers[0]["cache"], B, Hq, wl.max_ctx),
+                     dtype=torch.uint8, device=dev)
+
+    def step(decode_only=False):
+        for L in layers:
+            if not decode_only:
+                kv4.append(L["cache"], L["k_app"], L["v_app"], pos, slots, table)
+            kv4.decode_attention(L["cache"], L["q"], ctx, slots, table, wl.max_ctx, scale,
+                                 out, lse, ws)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    log("timing the 36-layer step (append + decode)")
+    t_step = timed(step, args.steps, args.warmup)
+    t_decode = timed(lambda: step(True), args.steps, 2)
+
+    # dominant kernel: main-region decode kernel, HIP events on its stream
+    log("timing the main-region kernel with HIP events")
+    evs = HipEvents(LAYERS * args.steps)
+    for r in range(args.steps):
+        for li, L in enumerate(layers):
+            e0, e1 = evs.pair(r * LAYERS + li)
+            kv4.decode_attention_timed(L["cache"], L["q"], ctx, slots, table, wl.max_ctx, scale,
+                                       out, lse, ws, e0, e1)
+    torch.cuda.synchronize()
+    main_ms = float(np.mean([evs.elapsed_ms(i) for i in range(LAYERS * args.steps)]))
+    evs.close()
+    main_bytes = main_kernel_bytes(wl.ctx, wl.Hkv)
+    achieved = main_bytes / (main_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("source_hash") == source_hash():
+            traffic = rec.get("bytes_per_launch")
+
+    extra = {}
+    if not args.no_bf16:
+        log("timing the BF16 paged decode comparator")
+        bws = torch.empty(kv4.bf16_workspace_bytes(B, Hq, wl.Hkv, wl.max_ctx), dtype=torch.uint8,
+                          device=dev)
+        bout = torch.empty_like(out)
+        blse = torch.empty_like(lse)
+
+        def bstep():
+            for L in layers:
+                kv4.bf16_paged_decode(L["bf16"], L["q"], ctx, table, wl.max_ctx, scale, bout, blse, bws)
+
+        t_bf16 = timed(bstep, args.steps, 2)
+        bf16_bytes = int((wl.ctx.astype(np.int64) * wl.Hkv * 512).sum())
+        # agreement of the two paths on the last layer (quantization error, information only)
+        kv4.decode_attention(layers[-1]["cache"], layers[-1]["q"], ctx, slots, table, wl.max_ctx,
+                             scale, out, lse, ws)
+        kv4.bf16_paged_decode(layers[-1]["bf16"], layers[-1]["q"], ctx, table, wl.max_ctx, scale,
+                              bout, blse, bws)
+        torch.cuda.synchronize()
+        extra.update(bf16_decode_ms_per_step=round(t_bf16 * 1e3, 3),
+                     bf16_hbm_gbps=round(bf16_bytes * LAYERS / t_bf16 / 1e9, 1),
+                     speedup_decode_vs_bf16=round(t_bf16 / t_decode, 3),
+                     kv4_vs_bf16_out_maxabs=float((out - bout).abs().max()))
+    if not args.no_prefill:
+        log("timing the 8 x 16384-token re-prefill")
+        from synth import draw_values
+        nseq, n = wl.prefill_nseq, wl.prefill_len
+        pk, pv, _ = draw_values(wl.seed, 1000, nseq * n, 1, 4, wl.Hkv, device=dev)
+        ppages = nseq * n // 16
+        pcache = kv4.Kv4Cache.zeros(ppages, wl.Hkv, nseq, dev)
+        ptable = torch.arange(ppages, dtype=torch.int32, device=dev).view(nseq, n // 16)
+        pcu = torch.arange(0, nseq * n + 1, n, dtype=torch.int32, device=dev)
+        pstart = torch.zeros(nseq, dtype=torch.int32, device=dev)
+        pslot = torch.arange(nseq, dtype=torch.int32, device=dev)
+        t_pre = timed(lambda: kv4.prefill_quantize(pcache, pk, pv, pcu, pstart, pslot, ptable, n),
+                      max(3, args.steps // 2), 2)
+        pbytes = nseq * n * wl.Hkv * (512 + 136)
+        extra.update(prefill_ms_per_layer=round(t_pre * 1e3, 3),
+                     prefill_gbps=round(pbytes / t_pre / 1e9, 1))
+        del pk, pv, pcache
+
+    if not args.no_copy:
+        # plain device-to-device copy of a known size: the box's practical HBM
+        # rate, and the scale of the FETCH_SIZE / WRITE_SIZE counters
+        src = torch.empty(2 ** 31, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        t_copy = timed(lambda: dst.copy_(src), 10, 2)
+        extra["copy_2GiB_gbps"] = round(2 * 2 ** 31 / t_copy / 1e9, 1)
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu:
+        log("oracle CPU baseline")
+        cpu, (sample, ref_out, ref_lse) = cpu_baseline(wl, layers[0], sh, args.cpu_budget)
+        kv4.decode_attention(layers[0]["cache"], layers[0]["q"], ctx, slots, table, wl.max_ctx,
+                             scale, out, lse, ws)
+        torch.cuda.synchronize()
+        got = out[torch.from_numpy(sample).to(dev)].cpu().numpy()
+        extra["sample_parity_out_maxabs"] = float(np.abs(got - ref_out).max())
+        extra["sample_parity_lse_maxabs"] = float(np.abs(lse[torch.from_numpy(sample).to(dev)].cpu().numpy() - ref_lse).max())
+
+    mb = metric_bytes(wl.ctx, wl.Hkv)
+    rec = {
+        "metric": METRIC,
+        "value": round(B / t_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": ("qwen8b decode step: B=256, Hq/Hkv=32/8, head_dim 128, page 16, "
+                                "36 layers, ctx = U[128,512] + length-biased lognormal(3000, 2250) "
+                                "position + 1; per layer kv4_append then kv4_decode_attention"),
+                   "B": B, "layers": LAYERS, "mean_ctx": round(float(wl.ctx.mean()), 1),
+                   "max_ctx": wl.max_ctx, "parallelism": "single GPU"},
+        "decode_tokens_per_s": round(B / t_decode, 1),
+        "decode_ms_per_step": round(t_decode * 1e3, 4),
+        "append_ms_per_step": round((t_step - t_decode) * 1e3, 4),
+        "hbm_gbps": round(mb * LAYERS / t_decode / 1e9, 1),
+        "hbm_frac_of_peak": round(mb * LAYERS / t_decode / 1e9 / PEAK_GBS, 4),
+        "metric_bytes_per_layer": mb,
+        "roofline": {"bound": "hbm", "kernel": "main_kernel (INT4 main region)",
+                     "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_us": round(main_ms * 1e3, 2), "alg_bytes_per_launch": main_bytes},
+        "cpu_baseline": cpu,
+    }
+    rec.update(extra)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -169,6 +169,17 @@ int kv4bench_bf16_paged_decode(const void *pages, int32_t num_pages, int32_t Hkv
                                float softmax_scale, float *out, float *lse, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Benchmark hook: kv4_decode_attention that also records two caller-created
+ * HIP events (hipEvent_t passed as void*) on `stream`, immediately before and
+ * after the main-region kernel, so the dominant kernel can be timed on the
+ * stream it runs on.  Either event may be NULL. */
+int kv4bench_decode_attention_timed(const kv4_cache_desc *cache, const void *q,
+                                    const int32_t *ctx_len, const int32_t *slot,
+                                    const int32_t *page_table, int32_t pt_stride, int32_t B,
+                                    int32_t Hq, int32_t max_ctx, float softmax_scale, float *out,
+                                    float *lse, void *workspace, size_t workspace_bytes,
+                                    void *ev_main_begin, void *ev_main_end, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,8 @@ HEAD_DIM, PAGE, SINK, WINDOW, SIDE_ROWS, BLOCK_BYTES = 128, 16, 16, 128, 144, 21
 # Every extern "C" function of include/kv4.h.
 EXPORTS = ("kv4_append", "kv4_prefill_quantize", "kv4_decode_workspace_bytes",
            "kv4_decode_attention", "kv4_decode_attention_debug", "kv4_strerror",
-           "kv4bench_bf16_workspace_bytes", "kv4bench_bf16_paged_decode")
+           "kv4bench_bf16_workspace_bytes", "kv4bench_bf16_paged_decode",
+           "kv4bench_decode_attention_timed")
 
 _lib = None
 
@@ -64,6 +65,8 @@ def lib():
         L.kv4bench_bf16_workspace_bytes.argtypes = [I, I, I, I]
         L.kv4bench_bf16_workspace_bytes.restype = Z
         L.kv4bench_bf16_paged_decode.argtypes = [P, I, I, P, P, P, I, I, I, I, F, P, P, P, Z, P]
+        L.kv4bench_decode_attention_timed.argtypes = [D, P, P, P, P, I, I, I, I, F, P, P, P, Z,
+                                                      P, P, P]
         _lib = L
     return _lib
 
@@ -194,3 +197,15 @@ def bf16_paged_decode(pages, q, ctx_len, page_table, max_ctx: int, softmax_scale
                                             _ptr(lse), _ptr(workspace), workspace.numel(),
                                             _stream()))
     return out, lse
+
+
+def decode_attention_timed(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ctx: int,
+                           softmax_scale: float, out, lse, workspace, ev_begin, ev_end):
+    """kv4bench_decode_attention_timed: as decode_attention, recording the two
+    raw hipEvent_t handles (ctypes.c_void_p) around the main-region kernel."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    _check(lib().kv4bench_decode_attention_timed(
+        cache.desc(), _ptr(q), _ptr(ctx_len), _ptr(slot), _ptr(page_table), page_table.shape[1],
+        B, Hq, int(max_ctx), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel(), ev_begin, ev_end,
+        _stream()))

@@ -72,7 +72,7 @@ int main_region_waves() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cached[dev] = cus * 16;  // 16 waves per compute unit: 4 per SIMD
+    cached[dev] = cus * 4 * KV4_MAIN_WAVES_PER_SIMD;  // 4 SIMDs per compute unit
   }
   return cached[dev];
 }
@@ -132,7 +132,8 @@ static int decode_common(const kv4_cache_desc* cache, const void* q, const int32
                          const int32_t* slot, const int32_t* page_table, int32_t pt_stride,
                          int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale, float* out,
                          float* lse, void* workspace, size_t workspace_bytes,
-                         const kv4_decode_debug* dbg, void* stream) {
+                         const kv4_decode_debug* dbg, void* stream, void* ev0 = nullptr,
+                         void* ev1 = nullptr) {
   int rc = check_decode(cache, q, ctx_len, page_table, pt_stride, B, Hq, max_ctx, out, lse);
   if (rc != KV4_OK) return rc;
   if (B > 65535) return KV4_ERR_SHAPE;
@@ -150,7 +151,8 @@ static int decode_common(const kv4_cache_desc* cache, const void* q, const int32
   hipError_t e = kv4::launch_decode(view(cache), static_cast<const uint16_t*>(q), ctx_len, slot,
                                     page_table, pt_stride, B, Hq, scale_log2(softmax_scale), out,
                                     lse, ws, dbg ? &d : nullptr,
-                                    static_cast<hipStream_t>(stream));
+                                    static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev0),
+                                    static_cast<hipEvent_t>(ev1));
   return e == hipSuccess ? KV4_OK : hip_fail(e);
 }
 
@@ -171,6 +173,17 @@ int kv4_decode_attention_debug(const kv4_cache_desc* cache, const void* q,
   if (!dbg) return KV4_ERR_NULLPTR;
   return decode_common(cache, q, ctx_len, slot, page_table, pt_stride, B, Hq, max_ctx,
                        softmax_scale, out, lse, workspace, workspace_bytes, dbg, stream);
+}
+
+int kv4bench_decode_attention_timed(const kv4_cache_desc* cache, const void* q,
+                                    const int32_t* ctx_len, const int32_t* slot,
+                                    const int32_t* page_table, int32_t pt_stride, int32_t B,
+                                    int32_t Hq, int32_t max_ctx, float softmax_scale, float* out,
+                                    float* lse, void* workspace, size_t workspace_bytes,
+                                    void* ev_main_begin, void* ev_main_end, void* stream) {
+  return decode_common(cache, q, ctx_len, slot, page_table, pt_stride, B, Hq, max_ctx,
+                       softmax_scale, out, lse, workspace, workspace_bytes, nullptr, stream,
+                       ev_main_begin, ev_main_end);
 }
 
 size_t kv4bench_bf16_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx) {

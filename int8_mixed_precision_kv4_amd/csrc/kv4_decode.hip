@@ -23,8 +23,6 @@
 namespace kv4 {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-
 struct DecArgs {
   const uint8_t* pages;
   const int8_t* side_codes;
@@ -44,7 +42,6 @@ struct DecArgs {
 
 // Main region M = [16, L-128) covers logical pages 1 .. (L-129)/16.
 __device__ __forceinline__ int main_pages(int L) { return L > SIDE_ROWS ? (L - 129) / PAGE : 0; }
-__device__ __forceinline__ int side_row(int p) { return p < SINK ? p : SINK + (p % WINDOW); }
 
 // plan[b] = sum over earlier sequences of main_pages * Hkv (one workgroup).
 __device__ void build_plan(const DecArgs& a) {
@@ -74,22 +71,46 @@ __device__ void build_plan(const DecArgs& a) {
 
 // ------------------------------------------------------------- protected --
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// QK MFMA output has head v of position l%16 in register v of lanes 0..15;
+// move head h to row h (lanes 16h..16h+15).
+__device__ __forceinline__ int qk_rows(v4i d) {
+  const auto r01 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(d[0]),
+                                                    static_cast<uint32_t>(d[1]), false, false);
+  const auto r23 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(d[2]),
+                                                    static_cast<uint32_t>(d[3]), false, false);
+  const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
+  return static_cast<int>(r[0]);
+}
+
+// Position held by side row r when the context is L (-1: row not in use).
+__device__ __forceinline__ int side_position(int r, int L) {
+  if (r < SINK) return r < L ? r : -1;
+  const int base = max(SINK, L - WINDOW);
+  const int p = base + ((r - SINK - base) % WINDOW + WINDOW) % WINDOW;
+  return p < L ? p : -1;
+}
+
 template <bool DEBUG>
 __global__ __launch_bounds__(256) void protected_kernel(DecArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int wave = wave_id(), lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int r16 = lane & 15, grp = lane >> 4;
   if (g == 0 && b == 0) build_plan(a);
 
-  __shared__ int32_t sq[GQA][HD / 4];      // query codes, 4 per dword, natural order
+  __shared__ __attribute__((aligned(16))) int8_t sq[GQA][HD];  // query codes, natural order
   __shared__ float scq[GQA];
-  __shared__ float sz[GQA][SIDE_ROWS];     // logits, then weights
-  __shared__ int32_t sv8[SIDE_ROWS][HD / 4];
-  __shared__ float ssv[SIDE_ROWS];
+  __shared__ float se[GQA][SIDE_ROWS];                           // logits, then weights
+  __shared__ __attribute__((aligned(16))) uint16_t svh[SIDE_ROWS][HD];  // BF16 V rows
 
   const int h = g * GQA + wave;
   const size_t bh = static_cast<size_t>(b) * a.Hq + h;
   const int L = a.ctx[b];
   const int slot = a.slot ? a.slot[b] : b;
+  const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
+  const int8_t* side = a.side_codes + row0 * 2 * HD;
+  const uint16_t* scales = a.side_scales + row0 * 2;
 
   // Rotate the query like the keys, then symmetric INT8 with an FP32 scale.
   {
@@ -107,7 +128,7 @@ __global__ __launch_bounds__(256) void protected_kernel(DecArgs a) {
     const float c_q = s_q * a.scale_log2;
     reinterpret_cast<uint16_t*>(sq[wave])[lane] =
         static_cast<uint16_t>((c0 & 0xFF) | ((c1 & 0xFF) << 8));
-    // even channels then odd channels, the operand order of the main kernel
+    // even channels then odd channels: the operand order of the main kernel
     int8_t* qs = a.ws.qcodes + bh * HD;
     qs[lane] = static_cast<int8_t>(c0);
     qs[64 + lane] = static_cast<int8_t>(c1);
@@ -124,68 +145,79 @@ __global__ __launch_bounds__(256) void protected_kernel(DecArgs a) {
       a.dbg.qcodes[bh * HD + 2 * lane + 1] = static_cast<int8_t>(c1);
     }
   }
+  // V rows dequantized once for the whole group: v^ = bf16(s_v * c); rows not
+  // in use are zero.  Chunk c = 16 codes of one row.
+  for (int c = tid; c < SIDE_ROWS * 8; c += 256) {
+    const int r = c >> 3, part = c & 7;
+    const bool live = side_position(r, L) >= 0;
+    const int4 codes = *reinterpret_cast<const int4*>(side + (r * 2 + 1) * HD + 16 * part);
+    const float sv = f16_value(scales[r * 2 + 1]);
+    const uint32_t w[4] = {static_cast<uint32_t>(codes.x), static_cast<uint32_t>(codes.y),
+                           static_cast<uint32_t>(codes.z), static_cast<uint32_t>(codes.w)};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int32_t c0 = static_cast<int8_t>((w[i >> 1] >> (16 * (i & 1))) & 0xFF);
+      const int32_t c1 = static_cast<int8_t>((w[i >> 1] >> (16 * (i & 1) + 8)) & 0xFF);
+      const uint32_t h0 = __float_as_uint(round_bf16(sv * static_cast<float>(c0))) >> 16;
+      const uint32_t h1 = __float_as_uint(round_bf16(sv * static_cast<float>(c1))) & 0xFFFF0000u;
+      o[i] = live ? (h0 | h1) : 0u;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(&svh[r][16 * part]);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
   __syncthreads();
 
-  // Protected positions: sinks [0, min(16,L)) then recent [max(16,L-128), L).
-  const int n = min(L, SIDE_ROWS);
-  const int sink_end = min(SINK, L), rec_begin = max(SINK, L - WINDOW);
-  if (tid < n) {
-    const int p = tid < sink_end ? tid : rec_begin + (tid - sink_end);
-    const size_t r = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS + side_row(p);
-    const int4* krow = reinterpret_cast<const int4*>(a.side_codes + r * 2 * HD);
-    const int4* vrow = krow + HD / 16;
-    int d[GQA] = {0, 0, 0, 0};
-#pragma unroll
-    for (int c = 0; c < HD / 16; ++c) {
-      const int4 kk = krow[c];
-      const int4 vv = vrow[c];
-#pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) {
-        d[hh] = __builtin_amdgcn_sdot4(kk.x, sq[hh][4 * c + 0], d[hh], false);
-        d[hh] = __builtin_amdgcn_sdot4(kk.y, sq[hh][4 * c + 1], d[hh], false);
-        d[hh] = __builtin_amdgcn_sdot4(kk.z, sq[hh][4 * c + 2], d[hh], false);
-        d[hh] = __builtin_amdgcn_sdot4(kk.w, sq[hh][4 * c + 3], d[hh], false);
-      }
-      sv8[tid][4 * c + 0] = vv.x;
-      sv8[tid][4 * c + 1] = vv.y;
-      sv8[tid][4 * c + 2] = vv.z;
-      sv8[tid][4 * c + 3] = vv.w;
-    }
-    const float sk = f16_value(a.side_scales[r * 2 + 0]);
-    ssv[tid] = f16_value(a.side_scales[r * 2 + 1]);
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) {
-      sz[hh][tid] = (static_cast<float>(d[hh]) * sk) * scq[hh];
-      if (DEBUG && a.dbg.qk)
-        a.dbg.qk[(static_cast<size_t>(b) * a.Hq + g * GQA + hh) * a.dbg.max_ctx + p] = d[hh];
-    }
+  // INT8 QK on MFMA: rows of 16 side rows per group; A = the 4 query codes.
+  v4i qa[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  if (r16 < GQA) {
+    qa[0] = *reinterpret_cast<const v4i*>(&sq[r16][16 * grp]);
+    qa[1] = *reinterpret_cast<const v4i*>(&sq[r16][64 + 16 * grp]);
+  }
+  const float c_q = scq[grp];
+  for (int rg = wave; rg < SIDE_ROWS / 16; rg += 4) {
+    const int r = 16 * rg + r16;
+    const int8_t* krow = side + r * 2 * HD;
+    v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+        qa[0], *reinterpret_cast<const v4i*>(krow + 16 * grp), v4i{0, 0, 0, 0}, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+        qa[1], *reinterpret_cast<const v4i*>(krow + 64 + 16 * grp), d, 0, 0, 0);
+    const int D8 = qk_rows(d);  // lane: head grp, row r
+    const int p = side_position(r, L);
+    const float sk = f16_value(scales[r * 2]);
+    se[grp][r] = (p >= 0) ? (static_cast<float>(D8) * sk) * c_q : -INFINITY;
+    if (DEBUG && a.dbg.qk && p >= 0)
+      a.dbg.qk[(static_cast<size_t>(b) * a.Hq + g * GQA + grp) * a.dbg.max_ctx + p] = D8;
   }
   __syncthreads();
 
   // FP32 softmax of this wave's head over the region.
   float zl = -INFINITY;
-  for (int i = lane; i < n; i += 64) zl = fmaxf(zl, sz[wave][i]);
+  for (int i = lane; i < SIDE_ROWS; i += 64) zl = fmaxf(zl, se[wave][i]);
   const float Z = wave_max(zl);
   float ls = 0.0f;
-  for (int i = lane; i < n; i += 64) {
-    const float e = exp2s(sz[wave][i] - Z);
-    sz[wave][i] = e;
+  for (int i = lane; i < SIDE_ROWS; i += 64) {
+    const float e = exp2s(se[wave][i] - Z);
+    se[wave][i] = e;
     ls += e;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
 
-  // PV with BF16-dequantized values, P kept in FP32; lane -> channels 2l, 2l+1.
+  // PV over the BF16 rows with FP32 weights; lane -> channels 2l, 2l+1.
   float a0 = 0.0f, a1 = 0.0f;
-  for (int i = 0; i < n; ++i) {
-    const float e = sz[wave][i];
-    const float sv = ssv[i];
-    const uint32_t cc = reinterpret_cast<const uint16_t*>(sv8[i])[lane];
-    const float v0 = round_bf16(sv * static_cast<float>(static_cast<int8_t>(cc & 0xFF)));
-    const float v1 = round_bf16(sv * static_cast<float>(static_cast<int8_t>(cc >> 8)));
-    a0 = __builtin_fmaf(e, v0, a0);
-    a1 = __builtin_fmaf(e, v1, a1);
+  for (int r = 0; r < SIDE_ROWS; r += 4) {
+    const float4 e4 = *reinterpret_cast<const float4*>(&se[wave][r]);
+    const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t vv = reinterpret_cast<const uint32_t*>(svh[r + i])[lane];
+      a0 = __builtin_fmaf(ev[i], __uint_as_float(vv << 16), a0);
+      a1 = __builtin_fmaf(ev[i], __uint_as_float(vv & 0xFFFF0000u), a1);
+    }
   }
   float* P = a.ws.prot + bh * kPart;
   reinterpret_cast<float2*>(P)[lane] = make_float2(a0, a1);
@@ -197,67 +229,223 @@ __global__ __launch_bounds__(256) void protected_kernel(DecArgs a) {
 
 // ------------------------------------------------------------------ main --
 
+__device__ __forceinline__ uint32_t lo_nibbles(uint32_t x) { return x & 0x0F0F0F0Fu; }
+__device__ __forceinline__ uint32_t hi_nibbles(uint32_t x) { return (x >> 4) & 0x0F0F0F0Fu; }
 __device__ __forceinline__ v4i nib_lo(uint4 x) {
-  const uint32_t m = 0x0F0F0F0Fu;
-  return v4i{static_cast<int>(x.x & m), static_cast<int>(x.y & m), static_cast<int>(x.z & m),
-             static_cast<int>(x.w & m)};
+  return v4i{static_cast<int>(lo_nibbles(x.x)), static_cast<int>(lo_nibbles(x.y)),
+             static_cast<int>(lo_nibbles(x.z)), static_cast<int>(lo_nibbles(x.w))};
 }
 __device__ __forceinline__ v4i nib_hi(uint4 x) {
-  const uint32_t m = 0x0F0F0F0Fu;
-  return v4i{static_cast<int>((x.x >> 4) & m), static_cast<int>((x.y >> 4) & m),
-             static_cast<int>((x.z >> 4) & m), static_cast<int>((x.w >> 4) & m)};
+  return v4i{static_cast<int>(hi_nibbles(x.x)), static_cast<int>(hi_nibbles(x.y)),
+             static_cast<int>(hi_nibbles(x.z)), static_cast<int>(hi_nibbles(x.w))};
 }
 // 16 positions of one channel (8 nibble bytes) -> 16 INT8 operand bytes; byte
 // i of the result holds position 8(i/8) + 2(i%4) + (i/4)%2.
 __device__ __forceinline__ v4i nib_positions(uint32_t lo8, uint32_t hi8) {
-  const uint32_t m = 0x0F0F0F0Fu;
-  return v4i{static_cast<int>(lo8 & m), static_cast<int>((lo8 >> 4) & m),
-             static_cast<int>(hi8 & m), static_cast<int>((hi8 >> 4) & m)};
+  return v4i{static_cast<int>(lo_nibbles(lo8)), static_cast<int>(hi_nibbles(lo8)),
+             static_cast<int>(lo_nibbles(hi8)), static_cast<int>(hi_nibbles(hi8))};
 }
 // inverse of that byte order
 __device__ __forceinline__ int pcode_slot(int t) { return 8 * (t >> 3) + 4 * (t & 1) + ((t & 7) >> 1); }
 
-// QK MFMA output has head v of position l%16 in register v of lanes 0..15;
-// move head h to row h (lanes 16h..16h+15).
-__device__ __forceinline__ int qk_rows(v4i d) {
-  const auto r01 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(d[0]),
-                                                    static_cast<uint32_t>(d[1]), false, false);
-  const auto r23 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(d[2]),
-                                                    static_cast<uint32_t>(d[3]), false, false);
-  const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
-  return static_cast<int>(r[0]);
+typedef const __attribute__((address_space(1))) uint8_t* gptr;
+typedef __attribute__((address_space(3))) void* lptr;
+
+// Per-wave LDS staging slot of one quad (4 pages of one segment):
+//   [0, 4096)     K codes, tile t at 1024 t + 16 lane
+//   [4096, 8192)  V codes, channel block s2 at 4096 + 1024 s2 + 16 lane
+//   [8192, 8704)  metadata, page t at 8192 + 128 t: 16 x {delta, m} K, then V
+// followed by 256 B where the P operand is assembled.
+constexpr int kSlotK = 0, kSlotV = 4096, kSlotMeta = 8192, kSlotP = 8704, kSlotBytes = 8960;
+
+struct QuadRegs {
+  uint4 kq[4], vq[4];
+  uint32_t km[4], vm[4];
+};
+
+// Issue the direct-to-LDS loads of one quad.  Tile t reads physical page
+// blk[t]; lane (r16, grp) fetches K bytes 64 r16 + 16 grp of every tile, and V
+// bytes 1024 + 16(16 s2 + r16) of tile grp (the k-group of the PV MFMA).
+__device__ __forceinline__ void quad_to_lds(uint8_t* slot, const gptr blk[4], int lane, int r16,
+                                            int grp) {
+  const int koff = 64 * r16 + 16 * grp;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    __builtin_amdgcn_global_load_lds(blk[t] + koff, (lptr)(slot + kSlotK + 1024 * t), 16, 0, 0);
+  const gptr vb = grp == 0 ? blk[0] : grp == 1 ? blk[1] : grp == 2 ? blk[2] : blk[3];
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2)
+    __builtin_amdgcn_global_load_lds(vb + OFF_VCODE + 16 * (16 * s2 + r16),
+                                     (lptr)(slot + kSlotV + 1024 * s2), 16, 0, 0);
+  if (lane < 32) {  // 4 pages x 128 B of metadata
+    const int t = lane >> 3;
+    const gptr mb = t == 0 ? blk[0] : t == 1 ? blk[1] : t == 2 ? blk[2] : blk[3];
+    __builtin_amdgcn_global_load_lds(mb + OFF_KMETA + 16 * (lane & 7), (lptr)(slot + kSlotMeta), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void quad_from_lds(QuadRegs& q, const uint8_t* slot, int lane, int r16) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    q.kq[t] = *reinterpret_cast<const uint4*>(slot + kSlotK + 1024 * t + 16 * lane);
+    q.vq[t] = *reinterpret_cast<const uint4*>(slot + kSlotV + 1024 * t + 16 * lane);
+    q.km[t] = *reinterpret_cast<const uint32_t*>(slot + kSlotMeta + 128 * t + 4 * r16);
+    q.vm[t] = *reinterpret_cast<const uint32_t*>(slot + kSlotMeta + 128 * t + 64 + 4 * r16);
+  }
+}
+
+// s_waitcnt encodings (gfx9): all direct-to-LDS loads landed; all LDS reads returned.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
+struct MainState {
+  float Zr, Ls, Ms;
+  float O[8];
+};
+
+// One quad of 4 tiles (pages) for the 4 heads of a group.  Lane = (head grp,
+// position r16) for the softmax; MFMA operand layouts as described above.
+template <bool DEBUG>
+__device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, const QuadRegs& q,
+                                             int np, v4i qa0, v4i qa1, float c_q, float S_q,
+                                             int j0, int main_end, size_t qb, uint8_t* stage,
+                                             int r16, int grp, int pslot) {
+  // integer QK of the four tiles
+  v4i d[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    d[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, nib_lo(q.kq[t]), v4i{0, 0, 0, 0}, 0, 0, 0);
+    d[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, nib_hi(q.kq[t]), d[t], 0, 0, 0);
+  }
+  float zmax[4], e[4], u[4], umax[4], emv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int D = qk_rows(d[t]);
+    const int pos = PAGE * (j0 + t) + r16;
+    const bool valid = (t < np) && (pos < main_end);
+    const float dk = f16_value(q.km[t] & 0xFFFFu), mk = f16_value(q.km[t] >> 16);
+    const float dv = f16_value(q.vm[t] & 0xFFFFu), mv = f16_value(q.vm[t] >> 16);
+    // q.k^ = s_q (delta * sum(qc*c) + m * sum(qc)); c_q carries s_q, the scale and log2(e)
+    const float z = valid ? __builtin_fmaf(dk, static_cast<float>(D), mk * S_q) * c_q : -INFINITY;
+    zmax[t] = row16_max(z);
+    e[t] = valid ? exp2s(z - zmax[t]) : 0.0f;
+    u[t] = valid ? e[t] * dv : 0.0f;    // V scale folded into P
+    emv[t] = valid ? e[t] * mv : 0.0f;  // V offset applied after the dot
+    umax[t] = __uint_as_float(row16_max_u32(__float_as_uint(u[t])));
+    if (DEBUG && valid && a.dbg.qk) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + pos] = D;
+  }
+  // 127 / u_max of the 16 (tile, head) pairs with one IEEE division:
+  // lane (h, r16) divides for tile r16 % 4, then quads broadcast.
+  const int tsel = r16 & 3;
+  const float xs = tsel == 0 ? umax[0] : tsel == 1 ? umax[1] : tsel == 2 ? umax[2] : umax[3];
+  const float qx = 127.0f / xs;
+  const float invx = (xs == 0.0f) ? 0.0f : qx;
+  const float inv[4] = {quad_bcast<0>(invx), quad_bcast<1>(invx), quad_bcast<2>(invx),
+                        quad_bcast<3>(invx)};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(u[t] * inv[t]), 0.0f, 127.0f);
+    const uint32_t uc = static_cast<uint32_t>(r);
+    stage[(t * 4 + grp) * 16 + pslot] = static_cast<uint8_t>(uc);
+    if (DEBUG && a.dbg.pcode) {
+      const int pos = PAGE * (j0 + t) + r16;
+      if (t < np && pos < main_end) a.dbg.pcode[(qb + grp) * a.dbg.max_ctx + pos] = static_cast<uint8_t>(uc);
+    }
+  }
+  // running reference max of each head; rescale what is accumulated
+  const float Zn = fmaxf(st.Zr, fmaxf(fmaxf(zmax[0], zmax[1]), fmaxf(zmax[2], zmax[3])));
+  const float al = __builtin_amdgcn_exp2f(st.Zr - Zn);
+#pragma unroll
+  for (int o = 0; o < 8; ++o) st.O[o] *= al;
+  st.Ls *= al;
+  st.Ms *= al;
+  st.Zr = Zn;
+  float wsu[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float wt = __builtin_amdgcn_exp2f(zmax[t] - Zn);
+    st.Ls = __builtin_fmaf(wt, e[t], st.Ls);
+    st.Ms = __builtin_fmaf(wt, emv[t], st.Ms);
+    wsu[t] = wt * (umax[t] * (1.0f / 127.0f));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // A operand of PV: row 4h + tile, k-group = tile (block diagonal)
+  v4i pa = *reinterpret_cast<const v4i*>(stage + (grp * 4 + (r16 >> 2)) * 16);
+  if ((r16 & 3) != grp) pa = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const v4i bv = e2 == 0 ? nib_positions(q.vq[s2].x, q.vq[s2].y) : nib_positions(q.vq[s2].z, q.vq[s2].w);
+      const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, bv, v4i{0, 0, 0, 0}, 0, 0, 0);
+      // lane: head grp, channel 2(16 s2 + r16) + e2, tile v in register v
+      const int o = 2 * s2 + e2;
+      float x = st.O[o];
+      x = __builtin_fmaf(wsu[0], static_cast<float>(acc[0]), x);
+      x = __builtin_fmaf(wsu[1], static_cast<float>(acc[1]), x);
+      x = __builtin_fmaf(wsu[2], static_cast<float>(acc[2]), x);
+      x = __builtin_fmaf(wsu[3], static_cast<float>(acc[3]), x);
+      st.O[o] = x;
+      if (DEBUG && a.dbg.pv) {
+        const int ch = 2 * (16 * s2 + r16) + e2;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (t < np) a.dbg.pv[((qb + grp) * a.dbg.max_pages + (j0 + t)) * HD + ch] = acc[t];
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
 }
 
 template <bool DEBUG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void main_kernel(DecArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t pstage[4][256];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WAVES_PER_SIMD, KV4_MAIN_WAVES_PER_SIMD))) void main_kernel(DecArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4][kSlotBytes];
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
   const int w = blockIdx.x * 4 + wave;
   const int nw = a.ws.n_waves;
   const int32_t* plan = a.ws.plan;
-  const int64_t T = plan[a.B];
+  const int64_t T = ld_const(plan + a.B);
   const int64_t start = static_cast<int64_t>(w) * T / nw;
   const int64_t end = static_cast<int64_t>(w + 1) * T / nw;
   if (start >= end) return;
   int lo = 0, hi = a.B;  // plan[lo] <= start < plan[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (plan[mid] <= start) lo = mid;
+    if (ld_const(plan + mid) <= start) lo = mid;
     else hi = mid;
   }
   int b = lo;
-  uint8_t* stage = pstage[wave];
+  uint8_t* slot = lds[wave];
+  uint8_t* stage = slot + kSlotP;
+  const int pslot = pcode_slot(r16);
+  const size_t pstride = static_cast<size_t>(a.Hkv) * BLOCK_BYTES;
   int64_t page = start;
 
   while (page < end) {
-    while (plan[b + 1] <= page) ++b;
-    const int mp = (plan[b + 1] - plan[b]) / a.Hkv;
-    const int g = static_cast<int>((page - plan[b]) / mp);
-    const int64_t seg0 = plan[b] + static_cast<int64_t>(g) * mp;
+    while (ld_const(plan + b + 1) <= page) ++b;
+    const int pb = ld_const(plan + b);
+    const int mp = (ld_const(plan + b + 1) - pb) / a.Hkv;
+    const int g = static_cast<int>((page - pb) / mp);
+    const int64_t seg0 = pb + static_cast<int64_t>(g) * mp;
     const int64_t stop = min(end, seg0 + mp);
-    const int main_end = a.ctx[b] - WINDOW;
+    const int main_end = ld_const(a.ctx + b) - WINDOW;
     const size_t qb = static_cast<size_t>(b) * a.Hq + g * GQA;
+    const int32_t* ptrow = a.page_table + static_cast<size_t>(b) * a.pt_stride;
+    const gptr gbase = (gptr)a.pages + static_cast<size_t>(g) * BLOCK_BYTES;
+    auto quad_np = [&](int64_t p) { return static_cast<int>(min(static_cast<int64_t>(4), stop - p)); };
+    auto quad_j0 = [&](int64_t p) { return 1 + static_cast<int>(p - seg0); };
+    auto issue = [&](int64_t p) {
+      const int j0 = quad_j0(p), np = quad_np(p);
+      gptr blk[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        blk[t] = gbase + static_cast<size_t>(ld_const(ptrow + j0 + min(t, np - 1))) * pstride;
+      quad_to_lds(slot, blk, lane, r16, grp);
+    };
+    issue(page);  // first quad of the segment in flight during the set-up below
 
     // A operand of QK: rows 0..3 = the group's heads, k = channels
     // (lane group grp covers channels 32grp..32grp+31, even / odd split).
@@ -267,121 +455,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       qa0 = *reinterpret_cast<const v4i*>(qs + 16 * grp);
       qa1 = *reinterpret_cast<const v4i*>(qs + 64 + 16 * grp);
     }
-    const float c_q = a.ws.qinfo[(qb + grp) * 4 + 0];
-    const float S_q = static_cast<float>(__float_as_int(a.ws.qinfo[(qb + grp) * 4 + 1]));
+    const float c_q = ld_const(a.ws.qinfo + (qb + grp) * 4 + 0);
+    const float S_q = static_cast<float>(__float_as_int(ld_const(a.ws.qinfo + (qb + grp) * 4 + 1)));
+    MainState st;
+    st.Zr = -INFINITY;
+    st.Ls = 0.0f;
+    st.Ms = 0.0f;
+#pragma unroll
+    for (int o = 0; o < 8; ++o) st.O[o] = 0.0f;
 
-    float Zr = -INFINITY, Ls = 0.0f, Ms = 0.0f;
-    float O[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int32_t* ptrow = a.page_table + static_cast<size_t>(b) * a.pt_stride;
-
+    // Pipeline: quad i is read out of the slot, quad i+1 streams into it
+    // while quad i is computed.
     for (int64_t p0 = page; p0 < stop; p0 += 4) {
-      const int np = static_cast<int>(min(static_cast<int64_t>(4), stop - p0));
-      const int j0 = 1 + static_cast<int>(p0 - seg0);  // logical page of tile 0
-      const uint8_t* blk[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int phys = ptrow[j0 + min(t, np - 1)];
-        blk[t] = a.pages + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
-      }
-      uint4 kq[4], vq[4];
-      uint32_t km[4], vm[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        kq[t] = *reinterpret_cast<const uint4*>(blk[t] + 64 * r16 + 16 * grp);
-        km[t] = *reinterpret_cast<const uint32_t*>(blk[t] + OFF_KMETA + 4 * r16);
-        vm[t] = *reinterpret_cast<const uint32_t*>(blk[t] + OFF_VMETA + 4 * r16);
-      }
-      const uint8_t* vb = grp == 0 ? blk[0] : grp == 1 ? blk[1] : grp == 2 ? blk[2] : blk[3];
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
-        vq[s2] = *reinterpret_cast<const uint4*>(vb + OFF_VCODE + 16 * (16 * s2 + r16));
-
-      float zmax[4], su[4], ecol[4], emv[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, nib_lo(kq[t]), v4i{0, 0, 0, 0}, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, nib_hi(kq[t]), d, 0, 0, 0);
-        const int D = qk_rows(d);  // lane: head grp, position r16 of tile t
-        const int pos = PAGE * (j0 + t) + r16;
-        const bool valid = (t < np) && (pos < main_end);
-        const float dk = f16_value(km[t] & 0xFFFFu), mk = f16_value(km[t] >> 16);
-        const float dv = f16_value(vm[t] & 0xFFFFu), mv = f16_value(vm[t] >> 16);
-        // q.k^ = s_q (delta * sum(qc*c) + m * sum(qc)); c_q carries s_q, the scale and log2(e)
-        float z = __builtin_fmaf(dk, static_cast<float>(D), mk * S_q) * c_q;
-        z = valid ? z : -INFINITY;
-        zmax[t] = row16_max(z);
-        const float e = valid ? exp2s(z - zmax[t]) : 0.0f;
-        const float u = valid ? e * dv : 0.0f;  // V scale folded into P
-        const float umax = row16_max(u);
-        uint32_t uc = 0;
-        if (umax != 0.0f) {
-          const float inv = 127.0f / umax;
-          uc = static_cast<uint32_t>(fminf(fmaxf(__builtin_rintf(u * inv), 0.0f), 127.0f));
-        }
-        su[t] = umax * (1.0f / 127.0f);
-        ecol[t] = e;
-        emv[t] = valid ? e * mv : 0.0f;  // V offset applied after the dot
-        stage[(t * 4 + grp) * 16 + pcode_slot(r16)] = static_cast<uint8_t>(uc);
-        if (DEBUG && valid) {
-          const size_t row = (qb + grp) * a.dbg.max_ctx + pos;
-          if (a.dbg.qk) a.dbg.qk[row] = D;
-          if (a.dbg.pcode) a.dbg.pcode[row] = static_cast<uint8_t>(uc);
-        }
-      }
-      // running reference max of each head; rescale what is accumulated
-      const float Zn = fmaxf(Zr, fmaxf(fmaxf(zmax[0], zmax[1]), fmaxf(zmax[2], zmax[3])));
-      const float al = __builtin_amdgcn_exp2f(Zr - Zn);
-#pragma unroll
-      for (int o = 0; o < 8; ++o) O[o] *= al;
-      Ls *= al;
-      Ms *= al;
-      Zr = Zn;
-      float wsu[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float wt = __builtin_amdgcn_exp2f(zmax[t] - Zr);
-        Ls = __builtin_fmaf(wt, ecol[t], Ls);
-        Ms = __builtin_fmaf(wt, emv[t], Ms);
-        wsu[t] = wt * su[t];
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // A operand of PV: row 4h + tau, k-group = tile; block diagonal in tiles
-      v4i pa = *reinterpret_cast<const v4i*>(stage + (grp * 4 + (r16 >> 2)) * 16);
-      if ((r16 & 3) != grp) pa = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          const v4i bv = e2 == 0 ? nib_positions(vq[s2].x, vq[s2].y) : nib_positions(vq[s2].z, vq[s2].w);
-          const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, bv, v4i{0, 0, 0, 0}, 0, 0, 0);
-          // lane: head grp, channel 2(16 s2 + r16) + e2, tile v in register v
-          float o = O[2 * s2 + e2];
-          o = __builtin_fmaf(wsu[0], static_cast<float>(acc[0]), o);
-          o = __builtin_fmaf(wsu[1], static_cast<float>(acc[1]), o);
-          o = __builtin_fmaf(wsu[2], static_cast<float>(acc[2]), o);
-          o = __builtin_fmaf(wsu[3], static_cast<float>(acc[3]), o);
-          O[2 * s2 + e2] = o;
-          if (DEBUG && a.dbg.pv) {
-            const int ch = 2 * (16 * s2 + r16) + e2;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              if (t < np)
-                a.dbg.pv[((qb + grp) * a.dbg.max_pages + (j0 + t)) * HD + ch] = acc[t];
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      QuadRegs q;
+      quad_from_lds(q, slot, lane, r16);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      if (p0 + 4 < stop) issue(p0 + 4);
+      compute_quad<DEBUG>(a, st, q, quad_np(p0), qa0, qa1, c_q, S_q, quad_j0(p0), main_end, qb,
+                          stage, r16, grp, pslot);
     }
     // partial of this (sequence, kv-head) segment: A = O + sum(w e m_v)
-    const float Lh = row16_sum(Ls), Mh = row16_sum(Ms);
+    const float Lh = row16_sum(st.Ls), Mh = row16_sum(st.Ms);
     float* P = a.ws.parts + ((static_cast<size_t>(w) + static_cast<size_t>(b) * a.Hkv + g) * GQA + grp) * kPart;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
-      *reinterpret_cast<float2*>(P + 2 * (16 * s2 + r16)) = make_float2(O[2 * s2] + Mh, O[2 * s2 + 1] + Mh);
+      *reinterpret_cast<float2*>(P + 2 * (16 * s2 + r16)) = make_float2(st.O[2 * s2] + Mh, st.O[2 * s2 + 1] + Mh);
     if (r16 == 0) {
-      P[128] = Zr;
+      P[128] = st.Zr;
       P[129] = Lh;
     }
     page = stop;
@@ -400,11 +501,12 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
   float Z = P0[128], l = P0[129];
   float2 A = reinterpret_cast<const float2*>(P0)[lane];
   const int32_t* plan = a.ws.plan;
-  const int64_t T = plan[a.B];
-  const int mp = (plan[b + 1] - plan[b]) / a.Hkv;
+  const int64_t T = ld_const(plan + a.B);
+  const int pb = ld_const(plan + b);
+  const int mp = (ld_const(plan + b + 1) - pb) / a.Hkv;
   if (mp > 0) {
     const int nw = a.ws.n_waves;
-    const int64_t s = plan[b] + static_cast<int64_t>(g) * mp, e = s + mp;
+    const int64_t s = pb + static_cast<int64_t>(g) * mp, e = s + mp;
     const int c_lo = static_cast<int>(((s + 1) * nw - 1) / T);
     const int c_hi = static_cast<int>((e * nw - 1) / T);
     for (int c = c_lo; c <= c_hi; ++c) {
@@ -456,7 +558,8 @@ DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves)
 hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* ctx,
                          const int32_t* slot, const int32_t* page_table, int pt_stride, int B,
                          int Hq, float scale_log2, float* out, float* lse,
-                         const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s) {
+                         const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
+                         hipEvent_t ev_main_begin, hipEvent_t ev_main_end) {
   DecArgs a{};
   a.pages = c.pages;
   a.side_codes = c.side_codes;
@@ -480,7 +583,15 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
     hipLaunchKernelGGL(main_kernel<true>, dim3(ws.n_waves / 4), block, 0, s, a);
   } else {
     hipLaunchKernelGGL(protected_kernel<false>, dim3(c.Hkv, B), block, 0, s, a);
+    if (ev_main_begin) {
+      const hipError_t e = hipEventRecord(ev_main_begin, s);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(main_kernel<false>, dim3(ws.n_waves / 4), block, 0, s, a);
+    if (ev_main_end) {
+      const hipError_t e = hipEventRecord(ev_main_end, s);
+      if (e != hipSuccess) return e;
+    }
   }
   hipLaunchKernelGGL(merge_kernel, dim3((Hq + 3) / 4, B), block, 0, s, a);
   return hipGetLastError();

@@ -67,6 +67,34 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Same all-reduce for non-negative floats, on their bit patterns (which order
+// like unsigned integers), so each step is one fused DPP v_max_u32.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x141, 0xF, 0xF, true)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x140, 0xF, 0xF, true)));
+  return v;
+}
+
+// Value of lane 4*(l/4) + I in every lane l (quad_perm [I,I,I,I]).
+template <int I>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), I * 0x55, 0xF, 0xF, true));
+}
+
+// Read memory that no wave writes during the kernel (inputs, or outputs of an
+// earlier launch) through the constant address space: wave-uniform reads then
+// become scalar loads, which do not wait behind the vector loads in flight.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

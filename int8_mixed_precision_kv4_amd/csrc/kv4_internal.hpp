@@ -35,6 +35,12 @@ struct DecodeWorkspace {
 };
 constexpr int kPart = 132;  // A[128], Z, l, 2 pad
 
+// Waves per SIMD of the main-region grid; every wave of the grid is resident
+// at once (the equal-chunk split assumes it).
+#ifndef KV4_MAIN_WAVES_PER_SIMD
+#define KV4_MAIN_WAVES_PER_SIMD 4
+#endif
+
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_waves);
 DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves);
 int main_region_waves();  // size of the main-region grid on the current device
@@ -49,7 +55,8 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t*
 hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* ctx,
                          const int32_t* slot, const int32_t* page_table, int pt_stride, int B,
                          int Hq, float scale_log2, float* out, float* lse,
-                         const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s);
+                         const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
+                         hipEvent_t ev_main_begin = nullptr, hipEvent_t ev_main_end = nullptr);
 hipError_t launch_bf16_decode(const uint16_t* pages, int num_pages, int Hkv, const uint16_t* q,
                               const int32_t* ctx, const int32_t* page_table, int pt_stride, int B,
                               int Hq, float scale_log2, float* out, float* lse, void* ws,
