@@ -10,12 +10,13 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkv4.so")
 SOURCES = ["kv4_api.hip", "kv4_quantize.hip", "kv4_decode.hip", "kv4_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off",                      # no silent FMA contraction: rounding is part of the rules
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-I" + INCLUDE,
 ]
 
 

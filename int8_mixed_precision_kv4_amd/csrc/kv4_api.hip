@@ -9,7 +9,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "../../include/kv4.h"
+#include "kv4.h"
 #include "kv4_device.hpp"
 #include "kv4_internal.hpp"
 

@@ -3,11 +3,9 @@
 // summary, "전제와 한계").
 //
 // Three launches on the caller's stream:
-//   1. protected_kernel, one workgroup per (kv-head, sequence): rotates and
-//      INT8-quantizes the 4 queries of the group (the codes are reused by the
-//      main region), runs INT8 QK against the side keys, an FP32 softmax, and
-//      PV over BF16-dequantized side values.  Workgroup (0,0) also writes the
-//      main-region work plan (prefix sums of main pages).
+//   1. query_kernel, one workgroup per (kv-head, sequence): rotates and
+//      INT8-quantizes the 4 queries of the group once for both regions.
+//      Workgroup (0,0) also writes the work plan (prefix sums of main pages).
 //   2. main_kernel, a fixed grid of independent waves: the concatenated list
 //      of main-region pages of all (sequence, kv-head) pairs is cut into equal
 //      contiguous chunks, one per wave (split-K with exact load balance).  Per
@@ -15,8 +13,10 @@
 //      applied after the dot, tile softmax, INT8 P operand with the V scale
 //      folded in, integer PV on MFMA, FP32 running merge.  A wave writes one
 //      partial per (sequence, kv-head) segment it touches.
-//   3. merge_kernel, one wave per (sequence, q-head): exact log-sum-exp merge
-//      of the protected partial and the main partials.
+//   3. protected_kernel, one workgroup per (kv-head, sequence): INT8 QK
+//      against the side keys, FP32 softmax, PV over BF16-dequantized side
+//      values, then the exact log-sum-exp merge of this protected partial with
+//      the main partials of the group, written as out and lse.
 #include "kv4_device.hpp"
 #include "kv4_internal.hpp"
 
@@ -69,9 +69,56 @@ __device__ void build_plan(const DecArgs& a) {
   }
 }
 
-// ------------------------------------------------------------- protected --
+// ---------------------------------------------------------------- query --
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) uint8_t* gptr;
+typedef __attribute__((address_space(3))) void* lptr;
+
+// s_waitcnt encodings (gfx9): all vector-memory loads (including direct-to-LDS
+// loads) landed; all LDS reads returned.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Query codes in the workspace, per (sequence, q-head): 128 B in MFMA operand
+// order (even channels, then odd channels) and 128 B in natural order.
+constexpr int kQStride = 2 * HD;
+
+template <bool DEBUG>
+__global__ __launch_bounds__(256) void query_kernel(DecArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  if (g == 0 && b == 0) build_plan(a);
+  const int h = g * GQA + wave;
+  const size_t bh = static_cast<size_t>(b) * a.Hq + h;
+  // Rotate the query like the keys, then symmetric INT8 with an FP32 scale.
+  const uint32_t qw = a.q[bh * 64 + lane];
+  float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
+  fwht128_wave(x0, x1);
+  const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+  const float s_q = amax / 127.0f;
+  int c0 = 0, c1 = 0;
+  if (s_q != 0.0f) {
+    c0 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x0 / s_q), -127.0f), 127.0f));
+    c1 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x1 / s_q), -127.0f), 127.0f));
+  }
+  const int S = wave_sum_i(c0 + c1);
+  int8_t* qs = a.ws.qcodes + bh * kQStride;
+  qs[lane] = static_cast<int8_t>(c0);
+  qs[64 + lane] = static_cast<int8_t>(c1);
+  reinterpret_cast<uint16_t*>(qs + HD)[lane] = static_cast<uint16_t>((c0 & 0xFF) | ((c1 & 0xFF) << 8));
+  if (lane == 0) {
+    a.ws.qinfo[bh * 4 + 0] = s_q * a.scale_log2;  // c_q: s_q, the scale and log2(e)
+    a.ws.qinfo[bh * 4 + 1] = __int_as_float(S);
+    a.ws.qinfo[bh * 4 + 2] = s_q;
+    a.ws.qinfo[bh * 4 + 3] = 0.0f;
+    if (DEBUG && a.dbg.qsum) a.dbg.qsum[bh] = S;
+  }
+  if (DEBUG && a.dbg.qcodes) {
+    a.dbg.qcodes[bh * HD + 2 * lane] = static_cast<int8_t>(c0);
+    a.dbg.qcodes[bh * HD + 2 * lane + 1] = static_cast<int8_t>(c1);
+  }
+}
 
 // QK MFMA output has head v of position l%16 in register v of lanes 0..15;
 // move head h to row h (lanes 16h..16h+15).
@@ -82,149 +129,6 @@ __device__ __forceinline__ int qk_rows(v4i d) {
                                                     static_cast<uint32_t>(d[3]), false, false);
   const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
   return static_cast<int>(r[0]);
-}
-
-// Position held by side row r when the context is L (-1: row not in use).
-__device__ __forceinline__ int side_position(int r, int L) {
-  if (r < SINK) return r < L ? r : -1;
-  const int base = max(SINK, L - WINDOW);
-  const int p = base + ((r - SINK - base) % WINDOW + WINDOW) % WINDOW;
-  return p < L ? p : -1;
-}
-
-template <bool DEBUG>
-__global__ __launch_bounds__(256) void protected_kernel(DecArgs a) {
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int wave = wave_id(), lane = threadIdx.x & 63, tid = threadIdx.x;
-  const int r16 = lane & 15, grp = lane >> 4;
-  if (g == 0 && b == 0) build_plan(a);
-
-  __shared__ __attribute__((aligned(16))) int8_t sq[GQA][HD];  // query codes, natural order
-  __shared__ float scq[GQA];
-  __shared__ float se[GQA][SIDE_ROWS];                           // logits, then weights
-  __shared__ __attribute__((aligned(16))) uint16_t svh[SIDE_ROWS][HD];  // BF16 V rows
-
-  const int h = g * GQA + wave;
-  const size_t bh = static_cast<size_t>(b) * a.Hq + h;
-  const int L = a.ctx[b];
-  const int slot = a.slot ? a.slot[b] : b;
-  const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
-  const int8_t* side = a.side_codes + row0 * 2 * HD;
-  const uint16_t* scales = a.side_scales + row0 * 2;
-
-  // Rotate the query like the keys, then symmetric INT8 with an FP32 scale.
-  {
-    const uint32_t qw = a.q[bh * 64 + lane];
-    float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
-    fwht128_wave(x0, x1);
-    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-    const float s_q = amax / 127.0f;
-    int c0 = 0, c1 = 0;
-    if (s_q != 0.0f) {
-      c0 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x0 / s_q), -127.0f), 127.0f));
-      c1 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x1 / s_q), -127.0f), 127.0f));
-    }
-    const int S = wave_sum_i(c0 + c1);
-    const float c_q = s_q * a.scale_log2;
-    reinterpret_cast<uint16_t*>(sq[wave])[lane] =
-        static_cast<uint16_t>((c0 & 0xFF) | ((c1 & 0xFF) << 8));
-    // even channels then odd channels: the operand order of the main kernel
-    int8_t* qs = a.ws.qcodes + bh * HD;
-    qs[lane] = static_cast<int8_t>(c0);
-    qs[64 + lane] = static_cast<int8_t>(c1);
-    if (lane == 0) {
-      a.ws.qinfo[bh * 4 + 0] = c_q;
-      a.ws.qinfo[bh * 4 + 1] = __int_as_float(S);
-      a.ws.qinfo[bh * 4 + 2] = s_q;
-      a.ws.qinfo[bh * 4 + 3] = 0.0f;
-      scq[wave] = c_q;
-      if (DEBUG && a.dbg.qsum) a.dbg.qsum[bh] = S;
-    }
-    if (DEBUG && a.dbg.qcodes) {
-      a.dbg.qcodes[bh * HD + 2 * lane] = static_cast<int8_t>(c0);
-      a.dbg.qcodes[bh * HD + 2 * lane + 1] = static_cast<int8_t>(c1);
-    }
-  }
-  // V rows dequantized once for the whole group: v^ = bf16(s_v * c); rows not
-  // in use are zero.  Chunk c = 16 codes of one row.
-  for (int c = tid; c < SIDE_ROWS * 8; c += 256) {
-    const int r = c >> 3, part = c & 7;
-    const bool live = side_position(r, L) >= 0;
-    const int4 codes = *reinterpret_cast<const int4*>(side + (r * 2 + 1) * HD + 16 * part);
-    const float sv = f16_value(scales[r * 2 + 1]);
-    const uint32_t w[4] = {static_cast<uint32_t>(codes.x), static_cast<uint32_t>(codes.y),
-                           static_cast<uint32_t>(codes.z), static_cast<uint32_t>(codes.w)};
-    uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int32_t c0 = static_cast<int8_t>((w[i >> 1] >> (16 * (i & 1))) & 0xFF);
-      const int32_t c1 = static_cast<int8_t>((w[i >> 1] >> (16 * (i & 1) + 8)) & 0xFF);
-      const uint32_t h0 = __float_as_uint(round_bf16(sv * static_cast<float>(c0))) >> 16;
-      const uint32_t h1 = __float_as_uint(round_bf16(sv * static_cast<float>(c1))) & 0xFFFF0000u;
-      o[i] = live ? (h0 | h1) : 0u;
-    }
-    uint4* dst = reinterpret_cast<uint4*>(&svh[r][16 * part]);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  }
-  __syncthreads();
-
-  // INT8 QK on MFMA: rows of 16 side rows per group; A = the 4 query codes.
-  v4i qa[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  if (r16 < GQA) {
-    qa[0] = *reinterpret_cast<const v4i*>(&sq[r16][16 * grp]);
-    qa[1] = *reinterpret_cast<const v4i*>(&sq[r16][64 + 16 * grp]);
-  }
-  const float c_q = scq[grp];
-  for (int rg = wave; rg < SIDE_ROWS / 16; rg += 4) {
-    const int r = 16 * rg + r16;
-    const int8_t* krow = side + r * 2 * HD;
-    v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-        qa[0], *reinterpret_cast<const v4i*>(krow + 16 * grp), v4i{0, 0, 0, 0}, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-        qa[1], *reinterpret_cast<const v4i*>(krow + 64 + 16 * grp), d, 0, 0, 0);
-    const int D8 = qk_rows(d);  // lane: head grp, row r
-    const int p = side_position(r, L);
-    const float sk = f16_value(scales[r * 2]);
-    se[grp][r] = (p >= 0) ? (static_cast<float>(D8) * sk) * c_q : -INFINITY;
-    if (DEBUG && a.dbg.qk && p >= 0)
-      a.dbg.qk[(static_cast<size_t>(b) * a.Hq + g * GQA + grp) * a.dbg.max_ctx + p] = D8;
-  }
-  __syncthreads();
-
-  // FP32 softmax of this wave's head over the region.
-  float zl = -INFINITY;
-  for (int i = lane; i < SIDE_ROWS; i += 64) zl = fmaxf(zl, se[wave][i]);
-  const float Z = wave_max(zl);
-  float ls = 0.0f;
-  for (int i = lane; i < SIDE_ROWS; i += 64) {
-    const float e = exp2s(se[wave][i] - Z);
-    se[wave][i] = e;
-    ls += e;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
-
-  // PV over the BF16 rows with FP32 weights; lane -> channels 2l, 2l+1.
-  float a0 = 0.0f, a1 = 0.0f;
-  for (int r = 0; r < SIDE_ROWS; r += 4) {
-    const float4 e4 = *reinterpret_cast<const float4*>(&se[wave][r]);
-    const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t vv = reinterpret_cast<const uint32_t*>(svh[r + i])[lane];
-      a0 = __builtin_fmaf(ev[i], __uint_as_float(vv << 16), a0);
-      a1 = __builtin_fmaf(ev[i], __uint_as_float(vv & 0xFFFF0000u), a1);
-    }
-  }
-  float* P = a.ws.prot + bh * kPart;
-  reinterpret_cast<float2*>(P)[lane] = make_float2(a0, a1);
-  if (lane == 0) {
-    P[128] = Z;
-    P[129] = ls;
-  }
 }
 
 // ------------------------------------------------------------------ main --
@@ -248,8 +152,6 @@ __device__ __forceinline__ v4i nib_positions(uint32_t lo8, uint32_t hi8) {
 // inverse of that byte order
 __device__ __forceinline__ int pcode_slot(int t) { return 8 * (t >> 3) + 4 * (t & 1) + ((t & 7) >> 1); }
 
-typedef const __attribute__((address_space(1))) uint8_t* gptr;
-typedef __attribute__((address_space(3))) void* lptr;
 
 // Per-wave LDS staging slot of one quad (4 pages of one segment):
 //   [0, 4096)     K codes, tile t at 1024 t + 16 lane
@@ -294,9 +196,6 @@ __device__ __forceinline__ void quad_from_lds(QuadRegs& q, const uint8_t* slot, 
   }
 }
 
-// s_waitcnt encodings (gfx9): all direct-to-LDS loads landed; all LDS reads returned.
-constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitLgkm0 = 0xC07F;
 
 struct MainState {
   float Zr, Ls, Ms;
@@ -451,7 +350,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     // (lane group grp covers channels 32grp..32grp+31, even / odd split).
     v4i qa0 = {0, 0, 0, 0}, qa1 = {0, 0, 0, 0};
     if (r16 < GQA) {
-      const int8_t* qs = a.ws.qcodes + (qb + r16) * HD;
+      const int8_t* qs = a.ws.qcodes + (qb + r16) * kQStride;
       qa0 = *reinterpret_cast<const v4i*>(qs + 16 * grp);
       qa1 = *reinterpret_cast<const v4i*>(qs + 64 + 16 * grp);
     }
@@ -477,7 +376,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     }
     // partial of this (sequence, kv-head) segment: A = O + sum(w e m_v)
     const float Lh = row16_sum(st.Ls), Mh = row16_sum(st.Ms);
-    float* P = a.ws.parts + ((static_cast<size_t>(w) + static_cast<size_t>(b) * a.Hkv + g) * GQA + grp) * kPart;
+    const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
+    float* P = a.ws.parts + ((static_cast<size_t>(w) + bg) * GQA + grp) * kPart;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
       *reinterpret_cast<float2*>(P + 2 * (16 * s2 + r16)) = make_float2(st.O[2 * s2] + Mh, st.O[2 * s2 + 1] + Mh);
@@ -489,41 +389,154 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   }
 }
 
-// ----------------------------------------------------------------- merge --
+// ------------------------------------------------------------ protected --
 
-__global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = blockIdx.x * 4 + wave, b = blockIdx.y;
-  if (h >= a.Hq) return;
-  const int g = h / GQA, hh = h % GQA;
+// Position held by side row r when the context is L (-1: row not in use).
+__device__ __forceinline__ int side_position(int r, int L) {
+  if (r < SINK) return r < L ? r : -1;
+  const int base = max(SINK, L - WINDOW);
+  const int p = base + ((r - SINK - base) % WINDOW + WINDOW) % WINDOW;
+  return p < L ? p : -1;
+}
+
+// Waves of the main grid whose page chunk contains page p of the plan (chunk
+// c covers [c T / nw, (c+1) T / nw); empty chunks own nothing).
+__device__ __forceinline__ int chunk_of(int64_t p, int64_t T, int nw) {
+  return static_cast<int>(((p + 1) * nw - 1) / T);
+}
+
+template <bool DEBUG>
+__global__ __launch_bounds__(256) void protected_kernel(DecArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int wave = wave_id(), lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int r16 = lane & 15, grp = lane >> 4;
+  __shared__ __attribute__((aligned(16))) int8_t sv8[SIDE_ROWS][HD];  // INT8 V rows
+  __shared__ float sz[GQA][SIDE_ROWS];                                // logits, then weights
+  __shared__ float ssv[SIDE_ROWS];                                    // V scales
+
+  const int h = g * GQA + wave;
   const size_t bh = static_cast<size_t>(b) * a.Hq + h;
-  const float* P0 = a.ws.prot + bh * kPart;
-  float Z = P0[128], l = P0[129];
-  float2 A = reinterpret_cast<const float2*>(P0)[lane];
-  const int32_t* plan = a.ws.plan;
-  const int64_t T = ld_const(plan + a.B);
-  const int pb = ld_const(plan + b);
-  const int mp = (ld_const(plan + b + 1) - pb) / a.Hkv;
+  const int L = ld_const(a.ctx + b);
+  const int slot = a.slot ? ld_const(a.slot + b) : b;
+  const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
+  const gptr side = (gptr)a.side_codes + row0 * 2 * HD;
+  const uint16_t* scales = a.side_scales + row0 * 2;
+
+  // V rows straight into LDS: each wave instruction moves 8 rows (1 KB).
+  for (int i = wave; i < SIDE_ROWS / 8; i += 4) {
+    const int r = 8 * i + (lane >> 3);
+    __builtin_amdgcn_global_load_lds(side + (2 * r + 1) * HD + 16 * (lane & 7),
+                                     (lptr)(&sv8[8 * i][0]), 16, 0, 0);
+  }
+  for (int r = tid; r < SIDE_ROWS; r += 256)  // rows not in use: 0 (their weight is 0 too)
+    ssv[r] = side_position(r, L) >= 0 ? f16_value(scales[2 * r + 1]) : 0.0f;
+
+  // Main partials of this head, fetched now so their latency overlaps the
+  // protected region (lane -> channels 2l, 2l+1).
+  const int pb = ld_const(a.ws.plan + b);
+  const int mp = (ld_const(a.ws.plan + b + 1) - pb) / a.Hkv;
+  const int64_t T = ld_const(a.ws.plan + a.B);
+  const int nw = a.ws.n_waves;
+  int c_lo = 0, c_hi = -1;
   if (mp > 0) {
-    const int nw = a.ws.n_waves;
-    const int64_t s = pb + static_cast<int64_t>(g) * mp, e = s + mp;
-    const int c_lo = static_cast<int>(((s + 1) * nw - 1) / T);
-    const int c_hi = static_cast<int>((e * nw - 1) / T);
-    for (int c = c_lo; c <= c_hi; ++c) {
-      if (static_cast<int64_t>(c) * T / nw >= static_cast<int64_t>(c + 1) * T / nw) continue;
-      const float* Pc = a.ws.parts + ((static_cast<size_t>(c) + static_cast<size_t>(b) * a.Hkv + g) * GQA + hh) * kPart;
-      const float Zc = Pc[128], lc = Pc[129];
-      const float2 Ac = reinterpret_cast<const float2*>(Pc)[lane];
-      const float Zn = fmaxf(Z, Zc);
-      const float w0 = __builtin_amdgcn_exp2f(Z - Zn), w1 = __builtin_amdgcn_exp2f(Zc - Zn);
-      A.x = A.x * w0 + Ac.x * w1;
-      A.y = A.y * w0 + Ac.y * w1;
-      l = l * w0 + lc * w1;
-      Z = Zn;
+    const int64_t s0 = pb + static_cast<int64_t>(g) * mp;
+    c_lo = chunk_of(s0, T, nw);
+    c_hi = chunk_of(s0 + mp - 1, T, nw);
+  }
+  const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
+  constexpr int kBatch = 4;  // main partials fetched together
+  float Zc[kBatch], lc[kBatch];
+  float2 Ac[kBatch];
+  bool okc[kBatch];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i;
+      okc[i] = (c <= c_hi) && (static_cast<int64_t>(c) * T / nw < static_cast<int64_t>(c + 1) * T / nw);
+      const float* Pc = a.ws.parts + ((static_cast<size_t>(okc[i] ? c : 0) + bg) * GQA + wave) * kPart;
+      Zc[i] = okc[i] ? Pc[128] : -INFINITY;
+      lc[i] = okc[i] ? Pc[129] : 0.0f;
+      Ac[i] = okc[i] ? reinterpret_cast<const float2*>(Pc)[lane] : make_float2(0.0f, 0.0f);
+    }
+  };
+  fetch(c_lo);
+
+  // INT8 QK on MFMA, 16 side rows per step; A = the 4 query codes (natural order).
+  v4i qa[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  if (r16 < GQA) {
+    const int8_t* qn = a.ws.qcodes + (static_cast<size_t>(b) * a.Hq + g * GQA + r16) * kQStride + HD;
+    qa[0] = *reinterpret_cast<const v4i*>(qn + 16 * grp);
+    qa[1] = *reinterpret_cast<const v4i*>(qn + 64 + 16 * grp);
+  }
+  const float c_q = ld_const(a.ws.qinfo + (static_cast<size_t>(b) * a.Hq + g * GQA + grp) * 4);
+  for (int rg = wave; rg < SIDE_ROWS / 16; rg += 4) {
+    const int r = 16 * rg + r16;
+    const gptr krow = side + r * 2 * HD;
+    v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+        qa[0], *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 16 * grp),
+        v4i{0, 0, 0, 0}, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+        qa[1], *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 64 + 16 * grp),
+        d, 0, 0, 0);
+    const int D8 = qk_rows(d);  // lane: head grp, row r
+    const int p = side_position(r, L);
+    const float sk = f16_value(scales[2 * r]);
+    sz[grp][r] = (p >= 0) ? (static_cast<float>(D8) * sk) * c_q : -INFINITY;
+    if (DEBUG && a.dbg.qk && p >= 0)
+      a.dbg.qk[(static_cast<size_t>(b) * a.Hq + g * GQA + grp) * a.dbg.max_ctx + p] = D8;
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // V rows are in LDS
+  __syncthreads();
+
+  // FP32 softmax of this wave's head over the region (rows not in use: 0).
+  float zl = -INFINITY;
+  for (int i = lane; i < SIDE_ROWS; i += 64) zl = fmaxf(zl, sz[wave][i]);
+  const float Z = wave_max(zl);
+  float ls = 0.0f;
+  for (int i = lane; i < SIDE_ROWS; i += 64) {
+    const float e = exp2s(sz[wave][i] - Z);
+    sz[wave][i] = e;
+    ls += e;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // PV with BF16-dequantized values v^ = bf16(s_v c) and FP32 weights.
+  float a0 = 0.0f, a1 = 0.0f;
+  for (int r = 0; r < SIDE_ROWS; r += 4) {
+    const float4 e4 = *reinterpret_cast<const float4*>(&sz[wave][r]);
+    const float4 s4 = *reinterpret_cast<const float4*>(&ssv[r]);
+    const float ev[4] = {e4.x, e4.y, e4.z, e4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t cc = reinterpret_cast<const uint16_t*>(sv8[r + i])[lane];
+      const float v0 = round_bf16(sv[i] * static_cast<float>(static_cast<int8_t>(cc & 0xFF)));
+      const float v1 = round_bf16(sv[i] * static_cast<float>(static_cast<int8_t>(cc >> 8)));
+      a0 = __builtin_fmaf(ev[i], v0, a0);
+      a1 = __builtin_fmaf(ev[i], v1, a1);
     }
   }
-  reinterpret_cast<float2*>(a.out + bh * HD)[lane] = make_float2(A.x / l, A.y / l);
-  if (lane == 0) a.lse[bh] = 0.69314718055994531f * (Z + log2f(l));
+  // exact log-sum-exp merge with the main partials of this head
+  float Zm = Z, lm = ls;
+  float2 Am = make_float2(a0, a1);
+  for (int c0 = c_lo; c0 <= c_hi; c0 += kBatch) {
+    if (c0 != c_lo) fetch(c0);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (!okc[i]) continue;
+      const float Zn = fmaxf(Zm, Zc[i]);
+      const float w0 = __builtin_amdgcn_exp2f(Zm - Zn), w1 = __builtin_amdgcn_exp2f(Zc[i] - Zn);
+      Am.x = Am.x * w0 + Ac[i].x * w1;
+      Am.y = Am.y * w0 + Ac[i].y * w1;
+      lm = lm * w0 + lc[i] * w1;
+      Zm = Zn;
+    }
+  }
+  reinterpret_cast<float2*>(a.out + bh * HD)[lane] = make_float2(Am.x / lm, Am.y / lm);
+  if (lane == 0) a.lse[bh] = 0.69314718055994531f * (Zm + log2f(lm));
 }
 
 }  // namespace
@@ -531,9 +544,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_waves) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   size_t n = up(static_cast<size_t>(B + 1) * 4);
-  n += up(static_cast<size_t>(B) * Hq * HD);
+  n += up(static_cast<size_t>(B) * Hq * kQStride);
   n += up(static_cast<size_t>(B) * Hq * 4 * 4);
-  n += up(static_cast<size_t>(B) * Hq * kPart * 4);
   n += up((static_cast<size_t>(n_waves) + static_cast<size_t>(B) * Hkv) * GQA * kPart * 4);
   return n;
 }
@@ -545,11 +557,9 @@ DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves)
   w.plan = reinterpret_cast<int32_t*>(p);
   p += up(static_cast<size_t>(B + 1) * 4);
   w.qcodes = reinterpret_cast<int8_t*>(p);
-  p += up(static_cast<size_t>(B) * Hq * HD);
+  p += up(static_cast<size_t>(B) * Hq * kQStride);
   w.qinfo = reinterpret_cast<float*>(p);
   p += up(static_cast<size_t>(B) * Hq * 4 * 4);
-  w.prot = reinterpret_cast<float*>(p);
-  p += up(static_cast<size_t>(B) * Hq * kPart * 4);
   w.parts = reinterpret_cast<float*>(p);
   w.n_waves = n_waves;
   return w;
@@ -577,23 +587,24 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   a.lse = lse;
   a.ws = ws;
   if (dbg) a.dbg = *dbg;
-  const dim3 block(256);
+  const dim3 block(256), groups(c.Hkv, B), grid(ws.n_waves / 4);
   if (dbg) {
-    hipLaunchKernelGGL(protected_kernel<true>, dim3(c.Hkv, B), block, 0, s, a);
-    hipLaunchKernelGGL(main_kernel<true>, dim3(ws.n_waves / 4), block, 0, s, a);
+    hipLaunchKernelGGL(query_kernel<true>, groups, block, 0, s, a);
+    hipLaunchKernelGGL(main_kernel<true>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(protected_kernel<true>, groups, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL(protected_kernel<false>, dim3(c.Hkv, B), block, 0, s, a);
+    hipLaunchKernelGGL(query_kernel<false>, groups, block, 0, s, a);
     if (ev_main_begin) {
       const hipError_t e = hipEventRecord(ev_main_begin, s);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(main_kernel<false>, dim3(ws.n_waves / 4), block, 0, s, a);
+    hipLaunchKernelGGL(main_kernel<false>, grid, block, 0, s, a);
     if (ev_main_end) {
       const hipError_t e = hipEventRecord(ev_main_end, s);
       if (e != hipSuccess) return e;
     }
+    hipLaunchKernelGGL(protected_kernel<false>, groups, block, 0, s, a);
   }
-  hipLaunchKernelGGL(merge_kernel, dim3((Hq + 3) / 4, B), block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -27,10 +27,11 @@ struct DecodeDebug {
 // Workspace carve-up of one decode call.
 struct DecodeWorkspace {
   int32_t* plan;   // [B+1] prefix sums of (main pages x Hkv) over sequences
-  int8_t* qcodes;  // [B][Hq][128] INT8 codes of the rotated queries
+  int8_t* qcodes;  // [B][Hq][256] INT8 codes of the rotated queries: MFMA
+                   // operand order (even channels, odd channels), then natural order
   float* qinfo;    // [B][Hq][4]  {c_q, S_q (int bits), s_q, 0}
-  float* prot;     // [B][Hq][kPart] partial of the protected region
-  float* parts;    // [n_waves + B*Hkv][4][kPart] partials of the main region
+  float* parts;    // [n_waves + B*Hkv][4][kPart] partials of the main region;
+                   // wave w writes segment (b, g) at w + b*Hkv + g
   int n_waves;     // waves of the main-region grid
 };
 constexpr int kPart = 132;  // A[128], Z, l, 2 pad
