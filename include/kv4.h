@@ -46,7 +46,8 @@ enum {
   KV4_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_size != 16, sink != 16,
                                window != 128, Hq % Hkv != 0 or Hq / Hkv != 4,
                                or abi_version mismatch */
-  KV4_ERR_SHAPE = -3,       /* a size is out of range (B <= 0, max_ctx > pt_stride*16, ...) */
+  KV4_ERR_SHAPE = -3,       /* a size is out of range (B <= 0, max_ctx > pt_stride*16,
+                               B * num_kv_heads * (max_ctx/16 + 1) > INT32_MAX, ...) */
   KV4_ERR_WORKSPACE = -4,   /* workspace missing or smaller than kv4_decode_workspace_bytes */
   KV4_ERR_HIP = -5          /* a HIP call failed; kv4_strerror gives the HIP message */
 };

@@ -55,6 +55,8 @@ int check_decode(const kv4_cache_desc* c, const void* q, const int32_t* ctx,
   if (B <= 0 || pt_stride <= 0 || max_ctx <= 0 ||
       static_cast<int64_t>(max_ctx) > static_cast<int64_t>(pt_stride) * 16)
     return KV4_ERR_SHAPE;
+  // main-region pages of all (sequence, kv-head) pairs are counted in int32
+  if (static_cast<int64_t>(B) * c->num_kv_heads * (max_ctx / 16 + 1) > INT32_MAX) return KV4_ERR_SHAPE;
   return KV4_OK;
 }
 

@@ -298,6 +298,42 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
   __builtin_amdgcn_wave_barrier();
 }
 
+// Work split of the main region: the global page list (sequence-major, then
+// kv-head, then logical page; T pages) is cut into one contiguous chunk per
+// wave, chunk c = [c q + min(c, r), (c+1) q + min(c+1, r)) with q = T / nw,
+// r = T % nw.  A wave writes one partial per segment its chunk touches, at
+// slot c + b*Hkv + g: chunks visit segments in list order, so slots never
+// collide and nw + B*Hkv slots suffice.
+struct Split {
+  int q, r;
+};
+__device__ __forceinline__ Split make_split(int T, int nw) { return Split{T / nw, T % nw}; }
+__device__ __forceinline__ int chunk_begin(const Split& s, int c) { return c * s.q + min(c, s.r); }
+// Chunk holding page p (0 <= p < T).
+__device__ __forceinline__ int chunk_of(const Split& s, int p) {
+  const int big = s.r * (s.q + 1);  // pages in the r chunks of q + 1 pages
+  return p < big ? p / (s.q + 1) : s.r + (p - big) / s.q;
+}
+
+// Sequence b holding page p of the plan (plan[b] <= p < plan[b+1]), searched
+// in [lo, B) with scalar loads: these are counted apart from the vector loads
+// in flight, so the search never waits for them.
+__device__ __forceinline__ int find_seq(const int32_t* plan, int B, int p, int lo) {
+  int hi = B;  // plan[lo] <= p < plan[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ld_const(plan + mid) <= p) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// One quad of the wave's page stream.
+struct QuadDesc {
+  int b, g, j0, np, slot, main_end;
+  bool first, last;  // first / last quad of its piece
+};
+
 template <bool DEBUG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WAVES_PER_SIMD, KV4_MAIN_WAVES_PER_SIMD))) void main_kernel(DecArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kSlotBytes];
@@ -306,87 +342,142 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   const int w = blockIdx.x * 4 + wave;
   const int nw = a.ws.n_waves;
   const int32_t* plan = a.ws.plan;
-  const int64_t T = ld_const(plan + a.B);
-  const int64_t start = static_cast<int64_t>(w) * T / nw;
-  const int64_t end = static_cast<int64_t>(w + 1) * T / nw;
-  if (start >= end) return;
-  int lo = 0, hi = a.B;  // plan[lo] <= start < plan[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (ld_const(plan + mid) <= start) lo = mid;
-    else hi = mid;
-  }
-  int b = lo;
+  const Split sp = make_split(ld_const(plan + a.B), nw);
   uint8_t* slot = lds[wave];
   uint8_t* stage = slot + kSlotP;
   const int pslot = pcode_slot(r16);
   const size_t pstride = static_cast<size_t>(a.Hkv) * BLOCK_BYTES;
-  int64_t page = start;
 
-  while (page < end) {
-    while (ld_const(plan + b + 1) <= page) ++b;
-    const int pb = ld_const(plan + b);
-    const int mp = (ld_const(plan + b + 1) - pb) / a.Hkv;
-    const int g = static_cast<int>((page - pb) / mp);
-    const int64_t seg0 = pb + static_cast<int64_t>(g) * mp;
-    const int64_t stop = min(end, seg0 + mp);
-    const int main_end = ld_const(a.ctx + b) - WINDOW;
-    const size_t qb = static_cast<size_t>(b) * a.Hq + g * GQA;
-    const int32_t* ptrow = a.page_table + static_cast<size_t>(b) * a.pt_stride;
-    const gptr gbase = (gptr)a.pages + static_cast<size_t>(g) * BLOCK_BYTES;
-    auto quad_np = [&](int64_t p) { return static_cast<int>(min(static_cast<int64_t>(4), stop - p)); };
-    auto quad_j0 = [&](int64_t p) { return 1 + static_cast<int>(p - seg0); };
-    auto issue = [&](int64_t p) {
-      const int j0 = quad_j0(p), np = quad_np(p);
-      gptr blk[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        blk[t] = gbase + static_cast<size_t>(ld_const(ptrow + j0 + min(t, np - 1))) * pstride;
-      quad_to_lds(slot, blk, lane, r16, grp);
-    };
-    issue(page);  // first quad of the segment in flight during the set-up below
+  // ---- issue cursor: page ip of the chunk [ip, iend) and the segment holding it
+  int ip = chunk_begin(sp, w);
+  const int iend = chunk_begin(sp, w + 1);
+  const int chunk0 = ip;
+  int ib = ip < iend ? find_seq(plan, a.B, ip, 0) : 0;
+  int seg0 = 0, seg_end = 0, seg_g = 0;  // segment holding ip: pages [seg0, seg_end), kv-head seg_g
+  // Q operands of the next piece (loaded with its first quad)
+  v4i nqa0 = {0, 0, 0, 0}, nqa1 = {0, 0, 0, 0};
+  float2 nqi = make_float2(0.0f, 0.0f);
 
-    // A operand of QK: rows 0..3 = the group's heads, k = channels
-    // (lane group grp covers channels 32grp..32grp+31, even / odd split).
-    v4i qa0 = {0, 0, 0, 0}, qa1 = {0, 0, 0, 0};
-    if (r16 < GQA) {
-      const int8_t* qs = a.ws.qcodes + (qb + r16) * kQStride;
-      qa0 = *reinterpret_cast<const v4i*>(qs + 16 * grp);
-      qa1 = *reinterpret_cast<const v4i*>(qs + 64 + 16 * grp);
+  // Stage 1: describe the next quad of the chunk and fetch its page-table
+  // entries (lanes 0..3, one per tile) into pt; false when the chunk is done.
+  // Runs two quads ahead of the compute.
+  auto plan_quad = [&](QuadDesc& d, int& pt) -> bool {
+    if (ip >= iend) return false;
+    if (ip >= seg_end || ip == chunk0) {  // entering a segment: locate it once
+      while (ld_const(plan + ib + 1) <= ip) ++ib;
+      const int pb = ld_const(plan + ib);
+      const int mp = (ld_const(plan + ib + 1) - pb) / a.Hkv;
+      seg_g = (ip - pb) / mp;
+      seg0 = pb + seg_g * mp;
+      seg_end = seg0 + mp;
     }
-    const float c_q = ld_const(a.ws.qinfo + (qb + grp) * 4 + 0);
-    const float S_q = static_cast<float>(__float_as_int(ld_const(a.ws.qinfo + (qb + grp) * 4 + 1)));
-    MainState st;
-    st.Zr = -INFINITY;
-    st.Ls = 0.0f;
-    st.Ms = 0.0f;
+    const int stop = min(iend, seg_end);
+    d.b = ib;
+    d.g = seg_g;
+    d.j0 = 1 + (ip - seg0);
+    d.np = min(4, stop - ip);
+    d.slot = w + ib * a.Hkv + seg_g;
+    d.first = (ip == chunk0) || (ip == seg0);
+    d.last = ip + d.np >= stop;
+    const int32_t* ptrow = a.page_table + static_cast<size_t>(ib) * a.pt_stride;
+    pt = ptrow[d.j0 + min(lane & 3, d.np - 1)];
+    ip += d.np;
+    return true;
+  };
+  // Stage 2: start the loads of a described quad (pages into the LDS slot,
+  // and for the first quad of a piece the Q operands of its group).
+  auto issue_quad = [&](QuadDesc& d, int pt) {
+    const gptr gbase = (gptr)a.pages + static_cast<size_t>(d.g) * BLOCK_BYTES;
+    gptr blk[4];
 #pragma unroll
-    for (int o = 0; o < 8; ++o) st.O[o] = 0.0f;
-
-    // Pipeline: quad i is read out of the slot, quad i+1 streams into it
-    // while quad i is computed.
-    for (int64_t p0 = page; p0 < stop; p0 += 4) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      QuadRegs q;
-      quad_from_lds(q, slot, lane, r16);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      if (p0 + 4 < stop) issue(p0 + 4);
-      compute_quad<DEBUG>(a, st, q, quad_np(p0), qa0, qa1, c_q, S_q, quad_j0(p0), main_end, qb,
-                          stage, r16, grp, pslot);
+    for (int t = 0; t < 4; ++t)
+      blk[t] = gbase + static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(pt, t))) * pstride;
+    quad_to_lds(slot, blk, lane, r16, grp);
+    if (d.first) {
+      // A operand of QK: rows 0..3 = the group's heads, k = channels (lane
+      // group grp covers channels 32grp..32grp+31, even / odd split).
+      const size_t qb = static_cast<size_t>(d.b) * a.Hq + d.g * GQA;
+      d.main_end = ld_const(a.ctx + d.b) - WINDOW;
+      if (r16 < GQA) {
+        const int8_t* qs = a.ws.qcodes + (qb + r16) * kQStride;
+        nqa0 = *reinterpret_cast<const v4i*>(qs + 16 * grp);
+        nqa1 = *reinterpret_cast<const v4i*>(qs + 64 + 16 * grp);
+      }
+      // raw {c_q, S_q bits}: converted when the piece starts computing, so
+      // that nothing waits for this load here
+      nqi = *reinterpret_cast<const float2*>(a.ws.qinfo + (qb + grp) * 4);
     }
-    // partial of this (sequence, kv-head) segment: A = O + sum(w e m_v)
-    const float Lh = row16_sum(st.Ls), Mh = row16_sum(st.Ms);
-    const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
-    float* P = a.ws.parts + ((static_cast<size_t>(w) + bg) * GQA + grp) * kPart;
+  };
+
+  // Pipeline: quad i is computed while quad i+1 streams into the LDS slot
+  // and the page-table entries of quad i+2 are fetched; pieces and ranges
+  // follow one another without a gap.
+  QuadDesc d1, d2;  // quads i+1 (in flight) and i+2 (described)
+  int pt1 = 0, pt2 = 0;
+  bool have1 = plan_quad(d1, pt1);
+  if (have1) issue_quad(d1, pt1);
+  bool have2 = have1 && plan_quad(d2, pt2);
+  MainState st;
+  v4i qa0 = {0, 0, 0, 0}, qa1 = {0, 0, 0, 0};
+  float c_q = 0.0f, S_q = 0.0f;
+  int main_end = 0;
+  // A finished piece's partial is stored one iteration late, after the next
+  // loads are issued, so the wait at the loop top never waits for its stores.
+  bool pend = false;
+  float* pend_P = nullptr;
+  float pend_A[8], pend_Z = 0.0f, pend_L = 0.0f;
+  auto store_partial = [&]() {
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
-      *reinterpret_cast<float2*>(P + 2 * (16 * s2 + r16)) = make_float2(st.O[2 * s2] + Mh, st.O[2 * s2 + 1] + Mh);
+      *reinterpret_cast<float2*>(pend_P + 2 * (16 * s2 + r16)) = make_float2(pend_A[2 * s2], pend_A[2 * s2 + 1]);
     if (r16 == 0) {
-      P[128] = st.Zr;
-      P[129] = Lh;
+      pend_P[128] = pend_Z;
+      pend_P[129] = pend_L;
     }
-    page = stop;
+  };
+  while (have1) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    QuadRegs q;
+    quad_from_lds(q, slot, lane, r16);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    const QuadDesc cd = d1;
+    if (cd.first) {
+      qa0 = nqa0;
+      qa1 = nqa1;
+      c_q = nqi.x;
+      S_q = static_cast<float>(__float_as_int(nqi.y));
+      main_end = cd.main_end;
+      st.Zr = -INFINITY;
+      st.Ls = 0.0f;
+      st.Ms = 0.0f;
+#pragma unroll
+      for (int o = 0; o < 8; ++o) st.O[o] = 0.0f;
+    }
+    have1 = have2;
+    if (have2) {
+      d1 = d2;
+      pt1 = pt2;
+      issue_quad(d1, pt1);
+      have2 = plan_quad(d2, pt2);
+    }
+    if (pend) {
+      store_partial();
+      pend = false;
+    }
+    const size_t qb = static_cast<size_t>(cd.b) * a.Hq + cd.g * GQA;
+    compute_quad<DEBUG>(a, st, q, cd.np, qa0, qa1, c_q, S_q, cd.j0, main_end, qb, stage, r16, grp,
+                        pslot);
+    if (cd.last) {  // partial of the piece: A = O + sum(w e m_v)
+      const float Mh = row16_sum(st.Ms);
+      pend_L = row16_sum(st.Ls);
+      pend_Z = st.Zr;
+      pend_P = a.ws.parts + (static_cast<size_t>(cd.slot) * GQA + grp) * kPart;
+#pragma unroll
+      for (int o = 0; o < 8; ++o) pend_A[o] = st.O[o] + Mh;
+      pend = true;
+    }
   }
+  if (pend) store_partial();
 }
 
 // ------------------------------------------------------------ protected --
@@ -399,154 +490,220 @@ __device__ __forceinline__ int side_position(int r, int L) {
   return p < L ? p : -1;
 }
 
-// Waves of the main grid whose page chunk contains page p of the plan (chunk
-// c covers [c T / nw, (c+1) T / nw); empty chunks own nothing).
-__device__ __forceinline__ int chunk_of(int64_t p, int64_t T, int nw) {
-  return static_cast<int>(((p + 1) * nw - 1) / T);
+// Round two FP32 values to BF16 (nearest even) with one v_cvt_pk_bf16_f32;
+// results kept in FP32.
+__device__ __forceinline__ void round_bf16x2(float& x, float& y) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{x, y}), b2));
+  x = __uint_as_float(u << 16);
+  y = __uint_as_float(u & 0xFFFF0000u);
 }
 
+// Protected region and merge, one workgroup per (kv-head g, sequence b).
+// QK: 9 MFMA row groups of 16 side rows, spread over the 4 waves.  Softmax:
+// wave h for head h.  PV: wave w takes rows [36w, 36w+36), lane (rp, cg) rows
+// 36w + rp + 2i and channels 4cg..4cg+3 for all 4 heads; the 2 row phases of
+// a wave are reduced with a permlane swap and the 4 waves through LDS.  Merge
+// and output: wave h, lane l -> channels 2l, 2l+1.
 template <bool DEBUG>
 __global__ __launch_bounds__(256) void protected_kernel(DecArgs a) {
+  constexpr int kRowsPerWave = SIDE_ROWS / 4;  // 36
   const int g = blockIdx.x, b = blockIdx.y;
   const int wave = wave_id(), lane = threadIdx.x & 63, tid = threadIdx.x;
   const int r16 = lane & 15, grp = lane >> 4;
-  __shared__ __attribute__((aligned(16))) int8_t sv8[SIDE_ROWS][HD];  // INT8 V rows
-  __shared__ float sz[GQA][SIDE_ROWS];                                // logits, then weights
-  __shared__ float ssv[SIDE_ROWS];                                    // V scales
+  __shared__ __attribute__((aligned(16))) float se[SIDE_ROWS][GQA];      // logits, then weights
+  __shared__ float ssv[SIDE_ROWS];                                         // V scales (0: row unused)
+  __shared__ __attribute__((aligned(16))) float red[4][GQA][HD];         // per-wave PV sums
+  __shared__ __attribute__((aligned(16))) float spart[GQA][4][kPart];   // main partials
 
-  const int h = g * GQA + wave;
-  const size_t bh = static_cast<size_t>(b) * a.Hq + h;
   const int L = ld_const(a.ctx + b);
   const int slot = a.slot ? ld_const(a.slot + b) : b;
   const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
   const gptr side = (gptr)a.side_codes + row0 * 2 * HD;
-  const uint16_t* scales = a.side_scales + row0 * 2;
+  typedef const __attribute__((address_space(1))) uint16_t* gptr16;
+  const gptr16 scales = (gptr16)(a.side_scales + row0 * 2);
+  const size_t qb = static_cast<size_t>(b) * a.Hq + g * GQA;
 
-  // V rows straight into LDS: each wave instruction moves 8 rows (1 KB).
-  for (int i = wave; i < SIDE_ROWS / 8; i += 4) {
-    const int r = 8 * i + (lane >> 3);
-    __builtin_amdgcn_global_load_lds(side + (2 * r + 1) * HD + 16 * (lane & 7),
-                                     (lptr)(&sv8[8 * i][0]), 16, 0, 0);
-  }
-  for (int r = tid; r < SIDE_ROWS; r += 256)  // rows not in use: 0 (their weight is 0 too)
-    ssv[r] = side_position(r, L) >= 0 ? f16_value(scales[2 * r + 1]) : 0.0f;
-
-  // Main partials of this head, fetched now so their latency overlaps the
-  // protected region (lane -> channels 2l, 2l+1).
-  const int pb = ld_const(a.ws.plan + b);
-  const int mp = (ld_const(a.ws.plan + b + 1) - pb) / a.Hkv;
-  const int64_t T = ld_const(a.ws.plan + a.B);
-  const int nw = a.ws.n_waves;
-  int c_lo = 0, c_hi = -1;
-  if (mp > 0) {
-    const int64_t s0 = pb + static_cast<int64_t>(g) * mp;
-    c_lo = chunk_of(s0, T, nw);
-    c_hi = chunk_of(s0 + mp - 1, T, nw);
-  }
-  const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
-  constexpr int kBatch = 4;  // main partials fetched together
-  float Zc[kBatch], lc[kBatch];
-  float2 Ac[kBatch];
-  bool okc[kBatch];
-  auto fetch = [&](int c0) {
+  // ---- every load first
+  // K operands and scales of this wave's row groups (rg = wave + 4k)
+  v4i kop[3][2];
+  float sk[3];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int c = c0 + i;
-      okc[i] = (c <= c_hi) && (static_cast<int64_t>(c) * T / nw < static_cast<int64_t>(c + 1) * T / nw);
-      const float* Pc = a.ws.parts + ((static_cast<size_t>(okc[i] ? c : 0) + bg) * GQA + wave) * kPart;
-      Zc[i] = okc[i] ? Pc[128] : -INFINITY;
-      lc[i] = okc[i] ? Pc[129] : 0.0f;
-      Ac[i] = okc[i] ? reinterpret_cast<const float2*>(Pc)[lane] : make_float2(0.0f, 0.0f);
+  for (int k = 0; k < 3; ++k) {
+    const int rg = wave + 4 * k;
+    if (rg < SIDE_ROWS / 16) {
+      const gptr krow = side + (16 * rg + r16) * 2 * HD;
+      kop[k][0] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 16 * grp);
+      kop[k][1] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 64 + 16 * grp);
+      sk[k] = f16_value(scales[2 * (16 * rg + r16)]);
     }
-  };
-  fetch(c_lo);
-
-  // INT8 QK on MFMA, 16 side rows per step; A = the 4 query codes (natural order).
+  }
+  // V codes of this wave's PV rows
+  const int rp = lane >> 5, cg = lane & 31;
+  uint32_t vop[kRowsPerWave / 2];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / 2; ++i) {
+    const int r = kRowsPerWave * wave + rp + 2 * i;
+    vop[i] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(side + (2 * r + 1) * HD + 4 * cg);
+  }
+  if (tid < SIDE_ROWS)
+    ssv[tid] = side_position(tid, L) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
+  // query codes (natural order) and c_q of the 4 heads
   v4i qa[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
   if (r16 < GQA) {
-    const int8_t* qn = a.ws.qcodes + (static_cast<size_t>(b) * a.Hq + g * GQA + r16) * kQStride + HD;
+    const int8_t* qn = a.ws.qcodes + (qb + r16) * kQStride + HD;
     qa[0] = *reinterpret_cast<const v4i*>(qn + 16 * grp);
     qa[1] = *reinterpret_cast<const v4i*>(qn + 64 + 16 * grp);
   }
-  const float c_q = ld_const(a.ws.qinfo + (static_cast<size_t>(b) * a.Hq + g * GQA + grp) * 4);
-  for (int rg = wave; rg < SIDE_ROWS / 16; rg += 4) {
-    const int r = 16 * rg + r16;
-    const gptr krow = side + r * 2 * HD;
-    v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-        qa[0], *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 16 * grp),
-        v4i{0, 0, 0, 0}, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-        qa[1], *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 64 + 16 * grp),
-        d, 0, 0, 0);
-    const int D8 = qk_rows(d);  // lane: head grp, row r
-    const int p = side_position(r, L);
-    const float sk = f16_value(scales[2 * r]);
-    sz[grp][r] = (p >= 0) ? (static_cast<float>(D8) * sk) * c_q : -INFINITY;
-    if (DEBUG && a.dbg.qk && p >= 0)
-      a.dbg.qk[(static_cast<size_t>(b) * a.Hq + g * GQA + grp) * a.dbg.max_ctx + p] = D8;
+  const float c_q = a.ws.qinfo[(qb + grp) * 4];
+  // main partials of head `wave` (lane -> channels 2l, 2l+1): one per chunk
+  // covering the segment's pages [s0, s0 + mp)
+  const int nw = a.ws.n_waves;
+  const Split sp = make_split(ld_const(a.ws.plan + a.B), nw);
+  const int pb = ld_const(a.ws.plan + b);
+  const int mp = (ld_const(a.ws.plan + b + 1) - pb) / a.Hkv;
+  int c_lo = 0, n_parts = 0;
+  if (mp > 0) {
+    const int s0 = pb + g * mp;
+    c_lo = chunk_of(sp, s0);
+    n_parts = chunk_of(sp, s0 + mp - 1) - c_lo + 1;
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // V rows are in LDS
+  const int bg = b * a.Hkv + g;
+  // slot of the k-th partial, or -1 for an empty chunk (only when T < nw)
+  auto part_slot = [&](int k) -> int {
+    const int c = c_lo + k;
+    return (k < n_parts && chunk_begin(sp, c) < chunk_begin(sp, c + 1)) ? c + bg : -1;
+  };
+  // A batch of up to 4 partials of head `wave` goes straight into LDS (528 B
+  // each: 33 lanes x 16 B).
+  constexpr int kBatch = 4;
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int sl = part_slot(k0 + i);
+      if (sl >= 0 && lane < kPart / 4) {
+        const gptr src = (gptr)(a.ws.parts + (static_cast<size_t>(sl) * GQA + wave) * kPart);
+        __builtin_amdgcn_global_load_lds(src + 16 * lane, (lptr)(&spart[wave][i][0]), 16, 0, 0);
+      }
+    }
+  };
+  fetch(0);
+
+  // ---- INT8 QK: lane (head grp, row 16 rg + r16)
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int rg = wave + 4 * k;
+    if (rg < SIDE_ROWS / 16) {
+      v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], kop[k][0], v4i{0, 0, 0, 0}, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], kop[k][1], d, 0, 0, 0);
+      const int D8 = qk_rows(d);
+      const int r = 16 * rg + r16;
+      const int p = side_position(r, L);
+      se[r][grp] = (p >= 0) ? (static_cast<float>(D8) * sk[k]) * c_q : -INFINITY;
+      if (DEBUG && a.dbg.qk && p >= 0) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + p] = D8;
+    }
+  }
   __syncthreads();
 
-  // FP32 softmax of this wave's head over the region (rows not in use: 0).
+  // ---- FP32 softmax of head `wave` over the region (rows not in use: 0)
   float zl = -INFINITY;
-  for (int i = lane; i < SIDE_ROWS; i += 64) zl = fmaxf(zl, sz[wave][i]);
+  for (int i = lane; i < SIDE_ROWS; i += 64) zl = fmaxf(zl, se[i][wave]);
   const float Z = wave_max(zl);
   float ls = 0.0f;
   for (int i = lane; i < SIDE_ROWS; i += 64) {
-    const float e = exp2s(sz[wave][i] - Z);
-    sz[wave][i] = e;
+    const float e = exp2s(se[i][wave] - Z);
+    se[i][wave] = e;
     ls += e;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __syncthreads();
 
-  // PV with BF16-dequantized values v^ = bf16(s_v c) and FP32 weights.
-  float a0 = 0.0f, a1 = 0.0f;
-  for (int r = 0; r < SIDE_ROWS; r += 4) {
-    const float4 e4 = *reinterpret_cast<const float4*>(&sz[wave][r]);
-    const float4 s4 = *reinterpret_cast<const float4*>(&ssv[r]);
-    const float ev[4] = {e4.x, e4.y, e4.z, e4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+  // ---- PV with v^ = bf16(s_v c) and FP32 weights
+  float acc[GQA][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t cc = reinterpret_cast<const uint16_t*>(sv8[r + i])[lane];
-      const float v0 = round_bf16(sv[i] * static_cast<float>(static_cast<int8_t>(cc & 0xFF)));
-      const float v1 = round_bf16(sv[i] * static_cast<float>(static_cast<int8_t>(cc >> 8)));
-      a0 = __builtin_fmaf(ev[i], v0, a0);
-      a1 = __builtin_fmaf(ev[i], v1, a1);
-    }
+  for (int h = 0; h < GQA; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[h][j] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / 2; ++i) {
+    const int r = kRowsPerWave * wave + rp + 2 * i;
+    const float4 e4 = *reinterpret_cast<const float4*>(&se[r][0]);
+    const float sv = ssv[r];
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = sv * static_cast<float>(static_cast<int8_t>((vop[i] >> (8 * j)) & 0xFF));
+    round_bf16x2(v[0], v[1]);
+    round_bf16x2(v[2], v[3]);
+    const float ev[GQA] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+    for (int h = 0; h < GQA; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[h][j] = __builtin_fmaf(ev[h], v[j], acc[h][j]);
   }
-  // exact log-sum-exp merge with the main partials of this head
+  // reduce over the two row phases: lanes 0-31 keep heads 0, 1, lanes 32-63
+  // heads 2, 3
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float hs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[k][j]),
+                                                        __float_as_uint(acc[k + 2][j]), false, false);
+      hs[j] = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+    }
+    *reinterpret_cast<float4*>(&red[wave][k + 2 * rp][4 * cg]) = make_float4(hs[0], hs[1], hs[2], hs[3]);
+  }
+  __syncthreads();
+
+  // ---- protected partial of head `wave`, then the exact log-sum-exp merge
+  float2 Am = make_float2(0.0f, 0.0f);
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2) {
+    const float2 x = reinterpret_cast<const float2*>(&red[w2][wave][0])[lane];
+    Am.x += x.x;
+    Am.y += x.y;
+  }
   float Zm = Z, lm = ls;
-  float2 Am = make_float2(a0, a1);
-  for (int c0 = c_lo; c0 <= c_hi; c0 += kBatch) {
-    if (c0 != c_lo) fetch(c0);
+  for (int k0 = 0; k0 < n_parts; k0 += kBatch) {
+    if (k0 != 0) {
+      __builtin_amdgcn_wave_barrier();  // the previous batch has been read
+      fetch(k0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (!okc[i]) continue;
-      const float Zn = fmaxf(Zm, Zc[i]);
-      const float w0 = __builtin_amdgcn_exp2f(Zm - Zn), w1 = __builtin_amdgcn_exp2f(Zc[i] - Zn);
-      Am.x = Am.x * w0 + Ac[i].x * w1;
-      Am.y = Am.y * w0 + Ac[i].y * w1;
-      lm = lm * w0 + lc[i] * w1;
+      if (part_slot(k0 + i) < 0) continue;
+      const float Zc = spart[wave][i][128], lc = spart[wave][i][129];
+      const float2 Ac = reinterpret_cast<const float2*>(&spart[wave][i][0])[lane];
+      const float Zn = fmaxf(Zm, Zc);
+      const float w0 = __builtin_amdgcn_exp2f(Zm - Zn), w1 = __builtin_amdgcn_exp2f(Zc - Zn);
+      Am.x = Am.x * w0 + Ac.x * w1;
+      Am.y = Am.y * w0 + Ac.y * w1;
+      lm = lm * w0 + lc * w1;
       Zm = Zn;
     }
   }
+  const size_t bh = qb + wave;
   reinterpret_cast<float2*>(a.out + bh * HD)[lane] = make_float2(Am.x / lm, Am.y / lm);
   if (lane == 0) a.lse[bh] = 0.69314718055994531f * (Zm + log2f(lm));
 }
 
 }  // namespace
 
+// Partial slots of the main region: chunk c writes segment (b, g) at c + b*Hkv + g.
+static size_t part_slots(int B, int Hkv, int n_waves) {
+  return static_cast<size_t>(n_waves) + static_cast<size_t>(B) * Hkv;
+}
+
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_waves) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   size_t n = up(static_cast<size_t>(B + 1) * 4);
   n += up(static_cast<size_t>(B) * Hq * kQStride);
   n += up(static_cast<size_t>(B) * Hq * 4 * 4);
-  n += up((static_cast<size_t>(n_waves) + static_cast<size_t>(B) * Hkv) * GQA * kPart * 4);
+  n += up(part_slots(B, Hkv, n_waves) * GQA * kPart * 4);
   return n;
 }
 
@@ -570,6 +727,7 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
                          int Hq, float scale_log2, float* out, float* lse,
                          const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
                          hipEvent_t ev_main_begin, hipEvent_t ev_main_end) {
+  if (ws.n_waves <= 0 || ws.n_waves % 4 != 0) return hipErrorInvalidValue;
   DecArgs a{};
   a.pages = c.pages;
   a.side_codes = c.side_codes;
