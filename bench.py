@@ -191,7 +191,56 @@ def cpu_baseline(wl, layer0, shared, budget_s):
                 cpu=cpu), (sample, out, lse)
 
 
+def traffic_from_counters(fetch_db, write_db, command):
+    """Write TRAFFIC_FILE from two rocprofv3 --pmc runs of this script (one
+    with FETCH_SIZE, one with WRITE_SIZE; KiB per dispatch).  Each counter is
+    scaled by what it reads for the 2 GiB device copy the script also runs,
+    whose true traffic is 2 GiB read and 2 GiB written."""
+    import re
+    import sqlite3
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select name, counter_name, counter_value from pmc_events").fetchall()
+        out = {}
+        for name, cn, val in rows:
+            if cn != counter:
+                continue
+            out.setdefault(name, []).append(float(val))
+        return out
+
+    def pick(d, pattern):
+        hits = [k for k in d if re.search(pattern, k)]
+        assert hits, (pattern, list(d)[:10])
+        return hits
+
+    fetch = per_kernel(fetch_db, "FETCH_SIZE")
+    write = per_kernel(write_db, "WRITE_SIZE")
+    main_k = pick(fetch, r"main_kernel<false>")[0]
+    # the 2 GiB device copy: the largest dispatch of the runtime's copy kernel
+    copy_f = max(v for k in pick(fetch, r"copyBuffer") for v in fetch[k])
+    copy_w = max(v for k in pick(write, r"copyBuffer") for v in write[k])
+    f_scale = 2 ** 31 / (copy_f * 1024)
+    w_scale = 2 ** 31 / (copy_w * 1024)
+    import numpy as np
+    f_main = float(np.mean(fetch[main_k])) * 1024 * f_scale
+    w_main = float(np.mean(write[main_k])) * 1024 * w_scale
+    rec = {"kernel": main_k, "workload": "qwen8b decode step, one layer",
+           "source_hash": source_hash(),
+           "fetch_bytes_per_launch": round(f_main), "write_bytes_per_launch": round(w_main),
+           "bytes_per_launch": round(f_main + w_main),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "copy_counter_kib": {"FETCH_SIZE": copy_f, "WRITE_SIZE": copy_w},
+           "launches": len(fetch[main_k]), "command": command}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--traffic-from":
+        traffic_from_counters(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
