@@ -250,6 +250,7 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the 2 GiB device copy probe")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -300,6 +301,28 @@ def main():
     t_step = timed(step, args.steps, args.warmup)
     t_decode = timed(lambda: step(True), args.steps, 2)
 
+    extra = {}
+    if not args.no_graph:
+        # the same 36-layer step captured once in a HIP graph and replayed
+        log("timing the step replayed from a HIP graph")
+        step()
+        torch.cuda.synchronize()
+        eager_out, eager_lse = out.clone(), lse.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        t_graph = timed(graph.replay, args.steps, 2)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(out, eager_out) and torch.equal(lse, eager_lse))
+        extra.update(graph_ms_per_step=round(t_graph * 1e3, 4),
+                     graph_tokens_per_s=round(B / t_graph, 1), graph_output_bit_identical=same)
+        del graph
+
     # dominant kernel: main-region decode kernel, HIP events on its stream
     log("timing the main-region kernel with HIP events")
     evs = HipEvents(LAYERS * args.steps)
@@ -319,7 +342,6 @@ def main():
         if rec.get("source_hash") == source_hash():
             traffic = rec.get("bytes_per_launch")
 
-    extra = {}
     if not args.no_bf16:
         log("timing the BF16 paged decode comparator")
         bws = torch.empty(kv4.bf16_workspace_bytes(B, Hq, wl.Hkv, wl.max_ctx), dtype=torch.uint8,

@@ -1,0 +1,135 @@
+"""GPU parity at the full sizes of the benchmark workloads.
+
+The whole batch is built and decoded on the GPU exactly as bench.py does it
+(values drawn on the device, re-prefill of the leading positions, this
+step's append, one decode launch over all B sequences in the timed launch
+configuration).  A sample of sequences is then rebuilt by the CPU oracle
+from the same values, and compared: page blocks and side rows bit-exact,
+query codes / int32 QK / P-operand codes / int32 PV accumulators bit-exact,
+out within 2e-3 and lse within 1e-4."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import int8_mixed_precision_kv4_amd as kv4
+import oracle
+from synth import draw_values, make_workload
+from tests.wl import bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL, LSE_TOL = 2e-3, 1e-4
+SCALE = 1.0 / math.sqrt(128)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _sample(ctx, n_random, seed):
+    """Shortest, longest, median and a few random sequences."""
+    order = np.argsort(ctx, kind="stable")
+    rng = np.random.default_rng(seed)
+    pick = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
+    pick.update(int(i) for i in rng.choice(len(ctx), size=min(n_random, len(ctx)), replace=False))
+    return np.array(sorted(pick))
+
+
+def _build_gpu(wl, layer, dev):
+    n_tok = int(wl.ctx.sum())
+    k, v, q = draw_values(wl.seed, layer, n_tok, wl.B, wl.Hq, wl.Hkv, device=dev)
+    off = np.zeros(wl.B + 1, np.int64)
+    off[1:] = np.cumsum(wl.ctx)
+    lead = wl.ctx - 1 if wl.append_step else wl.ctx
+    rows = torch.from_numpy(np.concatenate([np.arange(off[b], off[b] + lead[b]) for b in range(wl.B)])).to(dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lead)]).astype(np.int32)).to(dev)
+    table = torch.from_numpy(wl.page_table).to(dev)
+    slots = torch.from_numpy(wl.slots).to(dev)
+    cache = kv4.Kv4Cache.zeros(wl.num_pages, wl.Hkv, wl.max_slots, dev)
+    kv4.prefill_quantize(cache, k[rows].contiguous(), v[rows].contiguous(), cu,
+                         torch.zeros(wl.B, dtype=torch.int32, device=dev), slots, table, int(lead.max()))
+    if wl.append_step:
+        last = torch.from_numpy(off[:-1] + lead).to(dev)
+        kv4.append(cache, k[last].contiguous(), v[last].contiguous(),
+                   torch.from_numpy((wl.ctx - 1).astype(np.int32)).to(dev), slots, table)
+    return cache, k, v, q, off, table, slots
+
+
+def _oracle_for(wl, sample, k, v, q, off):
+    """Oracle cache and decode of the sampled sequences, from the device values."""
+    ctx = wl.ctx[sample]
+    need = (ctx + 15) // 16
+    table = np.zeros((len(sample), int(need.max())), np.int32)
+    o = 0
+    for i, n in enumerate(need):
+        table[i, :n] = np.arange(o, o + n)
+        o += n
+    lead = ctx - 1 if wl.append_step else ctx
+    rows_all = np.concatenate([np.arange(off[b], off[b] + wl.ctx[b]) for b in sample])
+    kh = bf16_bits(k[torch.from_numpy(rows_all).to(k.device)])
+    vh = bf16_bits(v[torch.from_numpy(rows_all).to(v.device)])
+    soff = np.zeros(len(sample) + 1, np.int64)
+    soff[1:] = np.cumsum(ctx)
+    lrows = np.concatenate([np.arange(soff[i], soff[i] + lead[i]) for i in range(len(sample))])
+    cu = np.concatenate([[0], np.cumsum(lead)]).astype(np.int32)
+    slots = np.arange(len(sample), dtype=np.int32)
+    cache = oracle.Cache(int(need.sum()), wl.Hkv, len(sample))
+    oracle.prefill(cache, kh[lrows], vh[lrows], cu, np.zeros(len(sample), np.int32), slots, table)
+    if wl.append_step:
+        last = soff[:-1] + lead
+        oracle.append(cache, kh[last], vh[last], lead.astype(np.int32), slots, table)
+    qh = bf16_bits(q[torch.from_numpy(sample).to(q.device)])
+    out, lse, dbg = oracle.decode(cache, qh, ctx.astype(np.int32), slots, table, wl.Hq, SCALE, debug=True)
+    return cache, table, out, lse, dbg
+
+
+@pytest.mark.parametrize("index,layer", [(2, 0), (3, 0), (4, 0), (4, 35)])
+def test_fullsize_sampled_parity(index, layer):
+    dev = torch.device("cuda")
+    wl = make_workload(index)
+    _say(f"[fullsize] workload {wl.name} B={wl.B} layer {layer} mean ctx {wl.ctx.mean():.0f} max {wl.ctx.max()}")
+    cache, k, v, q, off, table, slots = _build_gpu(wl, layer, dev)
+    ctx_d = torch.from_numpy(wl.ctx.astype(np.int32)).to(dev)
+    max_ctx = int(wl.ctx.max())
+    out, lse = kv4.decode_attention(cache, q, ctx_d, slots, table, max_ctx, SCALE)
+    out_d, lse_d, dbg = kv4.decode_attention_debug(cache, q, ctx_d, slots, table, max_ctx, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_d) and torch.equal(lse, lse_d)
+    sample = _sample(wl.ctx, 5, 100 + index + layer)
+    _say(f"[fullsize] oracle on sequences {sample.tolist()} (ctx {wl.ctx[sample].tolist()})")
+    ref, rtable, ref_out, ref_lse, ref_dbg = _oracle_for(wl, sample, k, v, q, off)
+
+    pages = cache.pages
+    for i, b in enumerate(sample):
+        n = int((wl.ctx[b] + 15) // 16)
+        got = pages[torch.from_numpy(wl.page_table[b, :n].astype(np.int64)).to(dev)].cpu().numpy()
+        want = ref.pages[rtable[i, :n]]
+        assert np.array_equal(got, want), f"pages of sequence {b} differ"
+        assert np.array_equal(cache.side_codes[int(wl.slots[b])].cpu().numpy(), ref.side_codes[i])
+        assert np.array_equal(cache.side_scales[int(wl.slots[b])].cpu().numpy().view(np.uint16),
+                              ref.side_scales[i])
+    sel = torch.from_numpy(sample).to(dev)
+    for key in ("qcodes", "qsum"):
+        assert np.array_equal(dbg[key][sel].cpu().numpy(), ref_dbg[key]), key
+    for i, b in enumerate(sample):
+        L = int(wl.ctx[b])
+        n = (L + 15) // 16
+        for key in ("qk", "pcode"):
+            got = dbg[key][int(b), :, :L].cpu().numpy()
+            assert np.array_equal(got, ref_dbg[key][i, :, :L]), f"{key} of sequence {b}"
+        got = dbg["pv"][int(b), :, :n].cpu().numpy()
+        assert np.array_equal(got, ref_dbg["pv"][i, :, :n]), f"pv of sequence {b}"
+    err = float(np.abs(out[sel].cpu().numpy() - ref_out).max())
+    lerr = float(np.abs(lse[sel].cpu().numpy() - ref_lse).max())
+    _say(f"[fullsize] {wl.name} layer {layer}: out {err:.2e} lse {lerr:.2e}")
+    assert err <= OUT_TOL and lerr <= LSE_TOL, (err, lerr)
+    # every output is finite and every lse at least the largest logit seen by any region
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
