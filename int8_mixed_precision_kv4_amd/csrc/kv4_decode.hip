@@ -6,17 +6,20 @@
 //   1. query_kernel, one workgroup per (kv-head, sequence): rotates and
 //      INT8-quantizes the 4 queries of the group once for both regions.
 //      Workgroup (0,0) also writes the work plan (prefix sums of main pages).
-//   2. main_kernel, a fixed grid of independent waves: the concatenated list
-//      of main-region pages of all (sequence, kv-head) pairs is cut into equal
-//      contiguous chunks, one per wave (split-K with exact load balance).  Per
-//      page: integer QK on MFMA (INT8 query x unpacked INT4 keys), delta/m
-//      applied after the dot, tile softmax, INT8 P operand with the V scale
-//      folded in, integer PV on MFMA, FP32 running merge.  A wave writes one
-//      partial per (sequence, kv-head) segment it touches.
-//   3. protected_kernel, one workgroup per (kv-head, sequence): INT8 QK
-//      against the side keys, FP32 softmax, PV over BF16-dequantized side
-//      values, then the exact log-sum-exp merge of this protected partial with
-//      the main partials of the group, written as out and lse.
+//   2. main_kernel.  Its first workgroups are a fixed set of independent
+//      waves: the concatenated list of main-region pages of all (sequence,
+//      kv-head) pairs is cut into equal contiguous chunks, one per wave
+//      (split-K with exact load balance).  Per page: integer QK on MFMA (INT8
+//      query x unpacked INT4 keys), delta/m applied after the dot, tile
+//      softmax, INT8 P operand with the V scale folded in, integer PV on MFMA,
+//      FP32 running merge; a wave writes one partial per segment it touches.
+//      Its last B*Hkv workgroups compute the protected region of one
+//      (sequence, kv-head) each (INT8 QK against the side keys, FP32 softmax,
+//      PV over BF16-dequantized side values); they are dispatched as the
+//      main-region waves retire, so they run in the main region's tail.
+//   3. merge_kernel, one workgroup per (kv-head, sequence): exact
+//      log-sum-exp merge of the protected partial with the main partials,
+//      written as out and lse.
 #include "kv4_device.hpp"
 #include "kv4_internal.hpp"
 
@@ -129,6 +132,169 @@ __device__ __forceinline__ int qk_rows(v4i d) {
                                                     static_cast<uint32_t>(d[3]), false, false);
   const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
   return static_cast<int>(r[0]);
+}
+
+// ------------------------------------------------------------ protected --
+
+// Position held by side row r when the context is L (-1: row not in use).
+__device__ __forceinline__ int side_position(int r, int L) {
+  if (r < SINK) return r < L ? r : -1;
+  const int base = max(SINK, L - WINDOW);
+  const int p = base + ((r - SINK - base) % WINDOW + WINDOW) % WINDOW;
+  return p < L ? p : -1;
+}
+
+// Round two FP32 values to BF16 (nearest even) with one v_cvt_pk_bf16_f32;
+// results kept in FP32.
+__device__ __forceinline__ void round_bf16x2(float& x, float& y) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{x, y}), b2));
+  x = __uint_as_float(u << 16);
+  y = __uint_as_float(u & 0xFFFF0000u);
+}
+
+// Protected-region partial of one (kv-head g, sequence b), computed by one
+// workgroup of the main kernel (the last B*Hkv workgroups of its grid, which
+// the dispatcher starts as main-region workgroups retire).  QK: 9 MFMA row
+// groups of 16 side rows spread over the 4 waves.  Softmax: wave h for head h.
+// PV: wave w takes rows [36w, 36w+36), lane (rp, cg) rows 36w + rp + 2i and
+// channels 4cg..4cg+3 for all 4 heads; the 2 row phases of a wave are reduced
+// with a permlane swap and the 4 waves through LDS.  Wave h writes the
+// partial (A[128], Z, l) of head h to the workspace.
+constexpr int kProtLds = SIDE_ROWS * GQA * 4 + SIDE_ROWS * 4 + 4 * GQA * HD * 4;  // 11072 B
+
+template <bool DEBUG>
+__device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b, uint8_t* lds_raw) {
+  constexpr int kRowsPerWave = SIDE_ROWS / 4;  // 36
+  const int wave = wave_id(), lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int r16 = lane & 15, grp = lane >> 4;
+  auto se = reinterpret_cast<float (*)[GQA]>(lds_raw);                                  // [144][4] logits, then weights
+  float* ssv = reinterpret_cast<float*>(lds_raw + SIDE_ROWS * GQA * 4);                   // [144] V scales (0: row unused)
+  auto red = reinterpret_cast<float (*)[GQA][HD]>(lds_raw + SIDE_ROWS * GQA * 4 + SIDE_ROWS * 4);  // [4][4][128]
+
+  const int L = ld_const(a.ctx + b);
+  const int slot = a.slot ? ld_const(a.slot + b) : b;
+  const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
+  const gptr side = (gptr)a.side_codes + row0 * 2 * HD;
+  typedef const __attribute__((address_space(1))) uint16_t* gptr16;
+  const gptr16 scales = (gptr16)(a.side_scales + row0 * 2);
+  const size_t qb = static_cast<size_t>(b) * a.Hq + g * GQA;
+
+  // ---- every load first
+  // K operands and scales of this wave's row groups (rg = wave + 4k)
+  v4i kop[3][2];
+  float sk[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int rg = wave + 4 * k;
+    if (rg < SIDE_ROWS / 16) {
+      const gptr krow = side + (16 * rg + r16) * 2 * HD;
+      kop[k][0] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 16 * grp);
+      kop[k][1] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 64 + 16 * grp);
+      sk[k] = f16_value(scales[2 * (16 * rg + r16)]);
+    }
+  }
+  // V codes of this wave's PV rows
+  const int rp = lane >> 5, cg = lane & 31;
+  uint32_t vop[kRowsPerWave / 2];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / 2; ++i) {
+    const int r = kRowsPerWave * wave + rp + 2 * i;
+    vop[i] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(side + (2 * r + 1) * HD + 4 * cg);
+  }
+  if (tid < SIDE_ROWS)
+    ssv[tid] = side_position(tid, L) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
+  // query codes (natural order) and c_q of the 4 heads
+  v4i qa[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  if (r16 < GQA) {
+    const int8_t* qn = a.ws.qcodes + (qb + r16) * kQStride + HD;
+    qa[0] = *reinterpret_cast<const v4i*>(qn + 16 * grp);
+    qa[1] = *reinterpret_cast<const v4i*>(qn + 64 + 16 * grp);
+  }
+  const float c_q = a.ws.qinfo[(qb + grp) * 4];
+
+  // ---- INT8 QK: lane (head grp, row 16 rg + r16)
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int rg = wave + 4 * k;
+    if (rg < SIDE_ROWS / 16) {
+      v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], kop[k][0], v4i{0, 0, 0, 0}, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], kop[k][1], d, 0, 0, 0);
+      const int D8 = qk_rows(d);
+      const int r = 16 * rg + r16;
+      const int p = side_position(r, L);
+      se[r][grp] = (p >= 0) ? (static_cast<float>(D8) * sk[k]) * c_q : -INFINITY;
+      if (DEBUG && a.dbg.qk && p >= 0) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + p] = D8;
+    }
+  }
+  __syncthreads();
+
+  // ---- FP32 softmax of head `wave` over the region (rows not in use: 0)
+  float zl = -INFINITY;
+  for (int i = lane; i < SIDE_ROWS; i += 64) zl = fmaxf(zl, se[i][wave]);
+  const float Z = wave_max(zl);
+  float ls = 0.0f;
+  for (int i = lane; i < SIDE_ROWS; i += 64) {
+    const float e = exp2s(se[i][wave] - Z);
+    se[i][wave] = e;
+    ls += e;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+  __syncthreads();
+
+  // ---- PV with v^ = bf16(s_v c) and FP32 weights
+  float acc[GQA][4];
+#pragma unroll
+  for (int h = 0; h < GQA; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[h][j] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / 2; ++i) {
+    const int r = kRowsPerWave * wave + rp + 2 * i;
+    const float4 e4 = *reinterpret_cast<const float4*>(&se[r][0]);
+    const float sv = ssv[r];
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = sv * static_cast<float>(static_cast<int8_t>((vop[i] >> (8 * j)) & 0xFF));
+    round_bf16x2(v[0], v[1]);
+    round_bf16x2(v[2], v[3]);
+    const float ev[GQA] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+    for (int h = 0; h < GQA; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[h][j] = __builtin_fmaf(ev[h], v[j], acc[h][j]);
+  }
+  // reduce over the two row phases: lanes 0-31 keep heads 0, 1, lanes 32-63
+  // heads 2, 3
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float hs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[k][j]),
+                                                        __float_as_uint(acc[k + 2][j]), false, false);
+      hs[j] = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+    }
+    *reinterpret_cast<float4*>(&red[wave][k + 2 * rp][4 * cg]) = make_float4(hs[0], hs[1], hs[2], hs[3]);
+  }
+  __syncthreads();
+
+  // ---- partial of head `wave`
+  float2 A = make_float2(0.0f, 0.0f);
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2) {
+    const float2 x = reinterpret_cast<const float2*>(&red[w2][wave][0])[lane];
+    A.x += x.x;
+    A.y += x.y;
+  }
+  float* P = a.ws.prot + (qb + wave) * kPart;
+  reinterpret_cast<float2*>(P)[lane] = A;
+  if (lane == 0) {
+    P[128] = Z;
+    P[129] = ls;
+  }
 }
 
 // ------------------------------------------------------------------ main --
@@ -315,14 +481,48 @@ __device__ __forceinline__ int chunk_of(const Split& s, int p) {
   return p < big ? p / (s.q + 1) : s.r + (p - big) / s.q;
 }
 
-// Sequence b holding page p of the plan (plan[b] <= p < plan[b+1]), searched
-// in [lo, B) with scalar loads: these are counted apart from the vector loads
-// in flight, so the search never waits for them.
-__device__ __forceinline__ int find_seq(const int32_t* plan, int B, int p, int lo) {
-  int hi = B;  // plan[lo] <= p < plan[hi]
+// The plan as seen by one main-kernel wave.  For up to 256 sequences the wave
+// holds entries 1..B in registers (entry i in lane (i-1) % 64 of register
+// (i-1) / 64), fetched with one round of vector loads; lookups are then
+// readlanes and ballots with no memory traffic.  Larger batches read the plan
+// through scalar loads.
+struct PlanView {
+  const int32_t* plan;
+  int B;
+  bool in_regs;
+  int v[4];
+};
+__device__ __forceinline__ PlanView load_plan(const int32_t* plan, int B, int lane) {
+  PlanView r;
+  r.plan = plan;
+  r.B = B;
+  r.in_regs = B <= 256;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r.v[k] = r.in_regs ? plan[min(1 + 64 * k + lane, B)] : 0;
+  return r;
+}
+// plan[i] for a wave-uniform 0 <= i <= B.
+__device__ __forceinline__ int plan_at(const PlanView& r, int i) {
+  if (!r.in_regs) return ld_const(r.plan + i);
+  if (i == 0) return 0;
+  const int l = (i - 1) & 63, k = (i - 1) >> 6;
+  const int x0 = __builtin_amdgcn_readlane(r.v[0], l), x1 = __builtin_amdgcn_readlane(r.v[1], l);
+  const int x2 = __builtin_amdgcn_readlane(r.v[2], l), x3 = __builtin_amdgcn_readlane(r.v[3], l);
+  return k == 0 ? x0 : k == 1 ? x1 : k == 2 ? x2 : x3;
+}
+// Sequence b holding page p (plan[b] <= p < plan[b+1]), at or after lo.
+__device__ __forceinline__ int find_seq(const PlanView& r, int p, int lo, int lane) {
+  if (r.in_regs) {  // count the entries 1..B that are <= p
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      cnt += __builtin_popcountll(__ballot(1 + 64 * k + lane <= r.B && r.v[k] <= p));
+    return cnt;
+  }
+  int hi = r.B;  // plan[lo] <= p < plan[hi]; scalar loads, counted apart from vector loads
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (ld_const(plan + mid) <= p) lo = mid;
+    if (ld_const(r.plan + mid) <= p) lo = mid;
     else hi = mid;
   }
   return lo;
@@ -337,10 +537,15 @@ struct QuadDesc {
 template <bool DEBUG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WAVES_PER_SIMD, KV4_MAIN_WAVES_PER_SIMD))) void main_kernel(DecArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kSlotBytes];
+  const int nw = a.ws.n_waves;
+  if (blockIdx.x >= nw / 4) {  // protected-region workgroups fill the tail of the grid
+    const int u = blockIdx.x - nw / 4;
+    protected_partial<DEBUG>(a, u % a.Hkv, u / a.Hkv, &lds[0][0]);
+    return;
+  }
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
   const int w = blockIdx.x * 4 + wave;
-  const int nw = a.ws.n_waves;
   const int32_t* plan = a.ws.plan;
   const Split sp = make_split(ld_const(plan + a.B), nw);
   uint8_t* slot = lds[wave];
@@ -352,7 +557,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   int ip = chunk_begin(sp, w);
   const int iend = chunk_begin(sp, w + 1);
   const int chunk0 = ip;
-  int ib = ip < iend ? find_seq(plan, a.B, ip, 0) : 0;
+  const PlanView pv = load_plan(plan, a.B, lane);
+  int ib = ip < iend ? find_seq(pv, ip, 0, lane) : 0;
   int seg0 = 0, seg_end = 0, seg_g = 0;  // segment holding ip: pages [seg0, seg_end), kv-head seg_g
   // Q operands of the next piece (loaded with its first quad)
   v4i nqa0 = {0, 0, 0, 0}, nqa1 = {0, 0, 0, 0};
@@ -364,9 +570,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   auto plan_quad = [&](QuadDesc& d, int& pt) -> bool {
     if (ip >= iend) return false;
     if (ip >= seg_end || ip == chunk0) {  // entering a segment: locate it once
-      while (ld_const(plan + ib + 1) <= ip) ++ib;
-      const int pb = ld_const(plan + ib);
-      const int mp = (ld_const(plan + ib + 1) - pb) / a.Hkv;
+      while (plan_at(pv, ib + 1) <= ip) ++ib;
+      const int pb = plan_at(pv, ib);
+      const int mp = (plan_at(pv, ib + 1) - pb) / a.Hkv;
       seg_g = (ip - pb) / mp;
       seg0 = pb + seg_g * mp;
       seg_end = seg0 + mp;
@@ -421,8 +627,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   v4i qa0 = {0, 0, 0, 0}, qa1 = {0, 0, 0, 0};
   float c_q = 0.0f, S_q = 0.0f;
   int main_end = 0;
-  // A finished piece's partial is stored one iteration late, after the next
-  // loads are issued, so the wait at the loop top never waits for its stores.
+  // A finished piece's partial is held in registers and stored only when the
+  // next piece finishes or the wave ends: stores count in the same vmcnt as
+  // the page loads and complete slowly under the read stream, so a wave with
+  // two pieces (the common case) never waits for one.
   bool pend = false;
   float* pend_P = nullptr;
   float pend_A[8], pend_Z = 0.0f, pend_L = 0.0f;
@@ -460,14 +668,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
       issue_quad(d1, pt1);
       have2 = plan_quad(d2, pt2);
     }
-    if (pend) {
-      store_partial();
-      pend = false;
-    }
     const size_t qb = static_cast<size_t>(cd.b) * a.Hq + cd.g * GQA;
     compute_quad<DEBUG>(a, st, q, cd.np, qa0, qa1, c_q, S_q, cd.j0, main_end, qb, stage, r16, grp,
                         pslot);
     if (cd.last) {  // partial of the piece: A = O + sum(w e m_v)
+      if (pend) store_partial();
       const float Mh = row16_sum(st.Ms);
       pend_L = row16_sum(st.Ls);
       pend_Z = st.Zr;
@@ -480,85 +685,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   if (pend) store_partial();
 }
 
-// ------------------------------------------------------------ protected --
-
-// Position held by side row r when the context is L (-1: row not in use).
-__device__ __forceinline__ int side_position(int r, int L) {
-  if (r < SINK) return r < L ? r : -1;
-  const int base = max(SINK, L - WINDOW);
-  const int p = base + ((r - SINK - base) % WINDOW + WINDOW) % WINDOW;
-  return p < L ? p : -1;
-}
-
-// Round two FP32 values to BF16 (nearest even) with one v_cvt_pk_bf16_f32;
-// results kept in FP32.
-__device__ __forceinline__ void round_bf16x2(float& x, float& y) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-  const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{x, y}), b2));
-  x = __uint_as_float(u << 16);
-  y = __uint_as_float(u & 0xFFFF0000u);
-}
-
-// Protected region and merge, one workgroup per (kv-head g, sequence b).
-// QK: 9 MFMA row groups of 16 side rows, spread over the 4 waves.  Softmax:
-// wave h for head h.  PV: wave w takes rows [36w, 36w+36), lane (rp, cg) rows
-// 36w + rp + 2i and channels 4cg..4cg+3 for all 4 heads; the 2 row phases of
-// a wave are reduced with a permlane swap and the 4 waves through LDS.  Merge
-// and output: wave h, lane l -> channels 2l, 2l+1.
-template <bool DEBUG>
-__global__ __launch_bounds__(256) void protected_kernel(DecArgs a) {
-  constexpr int kRowsPerWave = SIDE_ROWS / 4;  // 36
+// Exact log-sum-exp merge of the protected partial and the main partials of
+// each head, one workgroup per (kv-head g, sequence b), wave h for head h,
+// lane l for channels 2l, 2l+1.  Writes out and lse.
+__global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
-  const int wave = wave_id(), lane = threadIdx.x & 63, tid = threadIdx.x;
-  const int r16 = lane & 15, grp = lane >> 4;
-  __shared__ __attribute__((aligned(16))) float se[SIDE_ROWS][GQA];      // logits, then weights
-  __shared__ float ssv[SIDE_ROWS];                                         // V scales (0: row unused)
-  __shared__ __attribute__((aligned(16))) float red[4][GQA][HD];         // per-wave PV sums
-  __shared__ __attribute__((aligned(16))) float spart[GQA][4][kPart];   // main partials
-
-  const int L = ld_const(a.ctx + b);
-  const int slot = a.slot ? ld_const(a.slot + b) : b;
-  const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
-  const gptr side = (gptr)a.side_codes + row0 * 2 * HD;
-  typedef const __attribute__((address_space(1))) uint16_t* gptr16;
-  const gptr16 scales = (gptr16)(a.side_scales + row0 * 2);
-  const size_t qb = static_cast<size_t>(b) * a.Hq + g * GQA;
-
-  // ---- every load first
-  // K operands and scales of this wave's row groups (rg = wave + 4k)
-  v4i kop[3][2];
-  float sk[3];
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const int rg = wave + 4 * k;
-    if (rg < SIDE_ROWS / 16) {
-      const gptr krow = side + (16 * rg + r16) * 2 * HD;
-      kop[k][0] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 16 * grp);
-      kop[k][1] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 64 + 16 * grp);
-      sk[k] = f16_value(scales[2 * (16 * rg + r16)]);
-    }
-  }
-  // V codes of this wave's PV rows
-  const int rp = lane >> 5, cg = lane & 31;
-  uint32_t vop[kRowsPerWave / 2];
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave / 2; ++i) {
-    const int r = kRowsPerWave * wave + rp + 2 * i;
-    vop[i] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(side + (2 * r + 1) * HD + 4 * cg);
-  }
-  if (tid < SIDE_ROWS)
-    ssv[tid] = side_position(tid, L) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
-  // query codes (natural order) and c_q of the 4 heads
-  v4i qa[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  if (r16 < GQA) {
-    const int8_t* qn = a.ws.qcodes + (qb + r16) * kQStride + HD;
-    qa[0] = *reinterpret_cast<const v4i*>(qn + 16 * grp);
-    qa[1] = *reinterpret_cast<const v4i*>(qn + 64 + 16 * grp);
-  }
-  const float c_q = a.ws.qinfo[(qb + grp) * 4];
-  // main partials of head `wave` (lane -> channels 2l, 2l+1): one per chunk
-  // covering the segment's pages [s0, s0 + mp)
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const size_t bh = static_cast<size_t>(b) * a.Hq + g * GQA + wave;
+  const float* Pp = a.ws.prot + bh * kPart;
+  float2 Am = reinterpret_cast<const float2*>(Pp)[lane];
+  float Zm = Pp[128], lm = Pp[129];
+  // main partials: one per chunk covering the segment's pages [s0, s0 + mp)
   const int nw = a.ws.n_waves;
   const Split sp = make_split(ld_const(a.ws.plan + a.B), nw);
   const int pb = ld_const(a.ws.plan + b);
@@ -570,123 +707,30 @@ __global__ __launch_bounds__(256) void protected_kernel(DecArgs a) {
     n_parts = chunk_of(sp, s0 + mp - 1) - c_lo + 1;
   }
   const int bg = b * a.Hkv + g;
-  // slot of the k-th partial, or -1 for an empty chunk (only when T < nw)
-  auto part_slot = [&](int k) -> int {
-    const int c = c_lo + k;
-    return (k < n_parts && chunk_begin(sp, c) < chunk_begin(sp, c + 1)) ? c + bg : -1;
-  };
-  // A batch of up to 4 partials of head `wave` goes straight into LDS (528 B
-  // each: 33 lanes x 16 B).
   constexpr int kBatch = 4;
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int sl = part_slot(k0 + i);
-      if (sl >= 0 && lane < kPart / 4) {
-        const gptr src = (gptr)(a.ws.parts + (static_cast<size_t>(sl) * GQA + wave) * kPart);
-        __builtin_amdgcn_global_load_lds(src + 16 * lane, (lptr)(&spart[wave][i][0]), 16, 0, 0);
-      }
-    }
-  };
-  fetch(0);
-
-  // ---- INT8 QK: lane (head grp, row 16 rg + r16)
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const int rg = wave + 4 * k;
-    if (rg < SIDE_ROWS / 16) {
-      v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], kop[k][0], v4i{0, 0, 0, 0}, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], kop[k][1], d, 0, 0, 0);
-      const int D8 = qk_rows(d);
-      const int r = 16 * rg + r16;
-      const int p = side_position(r, L);
-      se[r][grp] = (p >= 0) ? (static_cast<float>(D8) * sk[k]) * c_q : -INFINITY;
-      if (DEBUG && a.dbg.qk && p >= 0) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + p] = D8;
-    }
-  }
-  __syncthreads();
-
-  // ---- FP32 softmax of head `wave` over the region (rows not in use: 0)
-  float zl = -INFINITY;
-  for (int i = lane; i < SIDE_ROWS; i += 64) zl = fmaxf(zl, se[i][wave]);
-  const float Z = wave_max(zl);
-  float ls = 0.0f;
-  for (int i = lane; i < SIDE_ROWS; i += 64) {
-    const float e = exp2s(se[i][wave] - Z);
-    se[i][wave] = e;
-    ls += e;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
-  __syncthreads();
-
-  // ---- PV with v^ = bf16(s_v c) and FP32 weights
-  float acc[GQA][4];
-#pragma unroll
-  for (int h = 0; h < GQA; ++h)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[h][j] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave / 2; ++i) {
-    const int r = kRowsPerWave * wave + rp + 2 * i;
-    const float4 e4 = *reinterpret_cast<const float4*>(&se[r][0]);
-    const float sv = ssv[r];
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = sv * static_cast<float>(static_cast<int8_t>((vop[i] >> (8 * j)) & 0xFF));
-    round_bf16x2(v[0], v[1]);
-    round_bf16x2(v[2], v[3]);
-    const float ev[GQA] = {e4.x, e4.y, e4.z, e4.w};
-#pragma unroll
-    for (int h = 0; h < GQA; ++h)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[h][j] = __builtin_fmaf(ev[h], v[j], acc[h][j]);
-  }
-  // reduce over the two row phases: lanes 0-31 keep heads 0, 1, lanes 32-63
-  // heads 2, 3
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    float hs[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[k][j]),
-                                                        __float_as_uint(acc[k + 2][j]), false, false);
-      hs[j] = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-    }
-    *reinterpret_cast<float4*>(&red[wave][k + 2 * rp][4 * cg]) = make_float4(hs[0], hs[1], hs[2], hs[3]);
-  }
-  __syncthreads();
-
-  // ---- protected partial of head `wave`, then the exact log-sum-exp merge
-  float2 Am = make_float2(0.0f, 0.0f);
-#pragma unroll
-  for (int w2 = 0; w2 < 4; ++w2) {
-    const float2 x = reinterpret_cast<const float2*>(&red[w2][wave][0])[lane];
-    Am.x += x.x;
-    Am.y += x.y;
-  }
-  float Zm = Z, lm = ls;
   for (int k0 = 0; k0 < n_parts; k0 += kBatch) {
-    if (k0 != 0) {
-      __builtin_amdgcn_wave_barrier();  // the previous batch has been read
-      fetch(k0);
+    float2 Ac[kBatch];
+    float Zc[kBatch], lc[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {  // loads of the batch first
+      const int c = c_lo + k0 + i;
+      const bool live = k0 + i < n_parts && chunk_begin(sp, c) < chunk_begin(sp, c + 1);
+      const float* Pc = a.ws.parts + ((static_cast<size_t>(live ? c : c_lo) + bg) * GQA + wave) * kPart;
+      Ac[i] = live ? reinterpret_cast<const float2*>(Pc)[lane] : make_float2(0.0f, 0.0f);
+      Zc[i] = live ? Pc[128] : -INFINITY;
+      lc[i] = live ? Pc[129] : 0.0f;
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (part_slot(k0 + i) < 0) continue;
-      const float Zc = spart[wave][i][128], lc = spart[wave][i][129];
-      const float2 Ac = reinterpret_cast<const float2*>(&spart[wave][i][0])[lane];
-      const float Zn = fmaxf(Zm, Zc);
-      const float w0 = __builtin_amdgcn_exp2f(Zm - Zn), w1 = __builtin_amdgcn_exp2f(Zc - Zn);
-      Am.x = Am.x * w0 + Ac.x * w1;
-      Am.y = Am.y * w0 + Ac.y * w1;
-      lm = lm * w0 + lc * w1;
+      if (Zc[i] == -INFINITY) continue;
+      const float Zn = fmaxf(Zm, Zc[i]);
+      const float w0 = __builtin_amdgcn_exp2f(Zm - Zn), w1 = __builtin_amdgcn_exp2f(Zc[i] - Zn);
+      Am.x = Am.x * w0 + Ac[i].x * w1;
+      Am.y = Am.y * w0 + Ac[i].y * w1;
+      lm = lm * w0 + lc[i] * w1;
       Zm = Zn;
     }
   }
-  const size_t bh = qb + wave;
   reinterpret_cast<float2*>(a.out + bh * HD)[lane] = make_float2(Am.x / lm, Am.y / lm);
   if (lane == 0) a.lse[bh] = 0.69314718055994531f * (Zm + log2f(lm));
 }
@@ -703,6 +747,7 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_waves) {
   size_t n = up(static_cast<size_t>(B + 1) * 4);
   n += up(static_cast<size_t>(B) * Hq * kQStride);
   n += up(static_cast<size_t>(B) * Hq * 4 * 4);
+  n += up(static_cast<size_t>(B) * Hq * kPart * 4);
   n += up(part_slots(B, Hkv, n_waves) * GQA * kPart * 4);
   return n;
 }
@@ -717,6 +762,8 @@ DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves)
   p += up(static_cast<size_t>(B) * Hq * kQStride);
   w.qinfo = reinterpret_cast<float*>(p);
   p += up(static_cast<size_t>(B) * Hq * 4 * 4);
+  w.prot = reinterpret_cast<float*>(p);
+  p += up(static_cast<size_t>(B) * Hq * kPart * 4);
   w.parts = reinterpret_cast<float*>(p);
   w.n_waves = n_waves;
   return w;
@@ -745,11 +792,12 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   a.lse = lse;
   a.ws = ws;
   if (dbg) a.dbg = *dbg;
-  const dim3 block(256), groups(c.Hkv, B), grid(ws.n_waves / 4);
+  // main-region workgroups, then one protected-region workgroup per (b, g)
+  const dim3 block(256), groups(c.Hkv, B), grid(ws.n_waves / 4 + B * c.Hkv);
   if (dbg) {
     hipLaunchKernelGGL(query_kernel<true>, groups, block, 0, s, a);
     hipLaunchKernelGGL(main_kernel<true>, grid, block, 0, s, a);
-    hipLaunchKernelGGL(protected_kernel<true>, groups, block, 0, s, a);
+    hipLaunchKernelGGL(merge_kernel, groups, block, 0, s, a);
   } else {
     hipLaunchKernelGGL(query_kernel<false>, groups, block, 0, s, a);
     if (ev_main_begin) {
@@ -761,7 +809,7 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
       const hipError_t e = hipEventRecord(ev_main_end, s);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(protected_kernel<false>, groups, block, 0, s, a);
+    hipLaunchKernelGGL(merge_kernel, groups, block, 0, s, a);
   }
   return hipGetLastError();
 }

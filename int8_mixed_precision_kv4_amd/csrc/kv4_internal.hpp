@@ -30,6 +30,7 @@ struct DecodeWorkspace {
   int8_t* qcodes;  // [B][Hq][256] INT8 codes of the rotated queries: MFMA
                    // operand order (even channels, odd channels), then natural order
   float* qinfo;    // [B][Hq][4]  {c_q, S_q (int bits), s_q, 0}
+  float* prot;     // [B][Hq][kPart] partials of the protected region
   float* parts;    // [slots][4][kPart] partials of the main region
   int n_waves;     // waves of the main-region grid
 };
