@@ -56,11 +56,13 @@ def metric_bytes(ctx, Hkv):
 
 
 def main_kernel_bytes(ctx, Hkv):
-    """Algorithmic bytes of the main-region kernel per launch: 136 B (64 B K
-    codes + 64 B V codes + 4 B + 4 B FP16 metadata) per main (position, kv-head)."""
+    """Algorithmic bytes of the main kernel per launch: 136 B (64 B K codes +
+    64 B V codes + 4 B + 4 B FP16 metadata) per main (position, kv-head), plus
+    the protected region its last workgroups read: 260 B (2 x 128 B INT8
+    codes + 2 x 2 B FP16 scales) per side (position, kv-head)."""
     import numpy as np
     ctx = np.asarray(ctx, dtype=np.int64)
-    return int((np.maximum(ctx - 144, 0) * Hkv * 136).sum())
+    return int((np.maximum(ctx - 144, 0) * Hkv * 136).sum() + (np.minimum(ctx, 144) * Hkv * 260).sum())
 
 
 class HipEvents:
@@ -428,7 +430,7 @@ def main():
         "hbm_gbps": round(mb * LAYERS / t_decode / 1e9, 1),
         "hbm_frac_of_peak": round(mb * LAYERS / t_decode / 1e9 / PEAK_GBS, 4),
         "metric_bytes_per_layer": mb,
-        "roofline": {"bound": "hbm", "kernel": "main_kernel (INT4 main region)",
+        "roofline": {"bound": "hbm", "kernel": "main_kernel (INT4 main region + INT8 protected region)",
                      "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(main_ms * 1e3, 2), "alg_bytes_per_launch": main_bytes},

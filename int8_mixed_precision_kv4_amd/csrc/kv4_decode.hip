@@ -92,6 +92,7 @@ __global__ __launch_bounds__(256) void query_kernel(DecArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   if (g == 0 && b == 0) build_plan(a);
+  if (threadIdx.x == 0) a.ws.mrange[b * a.Hkv + g] = make_int2(0, -1);  // no main partials unless written
   const int h = g * GQA + wave;
   const size_t bh = static_cast<size_t>(b) * a.Hq + h;
   // Rotate the query like the keys, then symmetric INT8 with an FP32 scale.
@@ -469,17 +470,13 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
 // wave, chunk c = [c q + min(c, r), (c+1) q + min(c+1, r)) with q = T / nw,
 // r = T % nw.  A wave writes one partial per segment its chunk touches, at
 // slot c + b*Hkv + g: chunks visit segments in list order, so slots never
-// collide and nw + B*Hkv slots suffice.
+// collide and nw + B*Hkv slots suffice.  The waves holding a segment's first
+// and last pages record their chunk indices for the merge.
 struct Split {
   int q, r;
 };
 __device__ __forceinline__ Split make_split(int T, int nw) { return Split{T / nw, T % nw}; }
 __device__ __forceinline__ int chunk_begin(const Split& s, int c) { return c * s.q + min(c, s.r); }
-// Chunk holding page p (0 <= p < T).
-__device__ __forceinline__ int chunk_of(const Split& s, int p) {
-  const int big = s.r * (s.q + 1);  // pages in the r chunks of q + 1 pages
-  return p < big ? p / (s.q + 1) : s.r + (p - big) / s.q;
-}
 
 // The plan as seen by one main-kernel wave.  For up to 256 sequences the wave
 // holds entries 1..B in registers (entry i in lane (i-1) % 64 of register
@@ -531,7 +528,8 @@ __device__ __forceinline__ int find_seq(const PlanView& r, int p, int lo, int la
 // One quad of the wave's page stream.
 struct QuadDesc {
   int b, g, j0, np, slot, main_end;
-  bool first, last;  // first / last quad of its piece
+  bool first, last;    // first / last quad of its piece
+  bool opens, closes;  // the piece starts at the segment's first page / ends at its last
 };
 
 template <bool DEBUG>
@@ -585,6 +583,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     d.slot = w + ib * a.Hkv + seg_g;
     d.first = (ip == chunk0) || (ip == seg0);
     d.last = ip + d.np >= stop;
+    d.opens = ip == seg0;
+    d.closes = stop == seg_end;
     const int32_t* ptrow = a.page_table + static_cast<size_t>(ib) * a.pt_stride;
     pt = ptrow[d.j0 + min(lane & 3, d.np - 1)];
     ip += d.np;
@@ -634,6 +634,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   bool pend = false;
   float* pend_P = nullptr;
   float pend_A[8], pend_Z = 0.0f, pend_L = 0.0f;
+  int pend_bg = 0;
+  bool pend_opens = false, pend_closes = false, piece_opens = false;
   auto store_partial = [&]() {
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
@@ -642,6 +644,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
       pend_P[128] = pend_Z;
       pend_P[129] = pend_L;
     }
+    // the chunks holding the segment's first and last pages bound its partials
+    if (lane == 0 && pend_opens) a.ws.mrange[pend_bg].x = w;
+    if (lane == 0 && pend_closes) a.ws.mrange[pend_bg].y = w;
   };
   while (have1) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -650,6 +655,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     const QuadDesc cd = d1;
     if (cd.first) {
+      piece_opens = cd.opens;
       qa0 = nqa0;
       qa1 = nqa1;
       c_q = nqi.x;
@@ -677,6 +683,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
       pend_L = row16_sum(st.Ls);
       pend_Z = st.Zr;
       pend_P = a.ws.parts + (static_cast<size_t>(cd.slot) * GQA + grp) * kPart;
+      pend_bg = cd.b * a.Hkv + cd.g;
+      pend_opens = piece_opens;
+      pend_closes = cd.closes;
 #pragma unroll
       for (int o = 0; o < 8; ++o) pend_A[o] = st.O[o] + Mh;
       pend = true;
@@ -695,18 +704,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
   const float* Pp = a.ws.prot + bh * kPart;
   float2 Am = reinterpret_cast<const float2*>(Pp)[lane];
   float Zm = Pp[128], lm = Pp[129];
-  // main partials: one per chunk covering the segment's pages [s0, s0 + mp)
-  const int nw = a.ws.n_waves;
-  const Split sp = make_split(ld_const(a.ws.plan + a.B), nw);
-  const int pb = ld_const(a.ws.plan + b);
-  const int mp = (ld_const(a.ws.plan + b + 1) - pb) / a.Hkv;
-  int c_lo = 0, n_parts = 0;
-  if (mp > 0) {
-    const int s0 = pb + g * mp;
-    c_lo = chunk_of(sp, s0);
-    n_parts = chunk_of(sp, s0 + mp - 1) - c_lo + 1;
-  }
+  // main partials: chunks c_lo..c_hi (recorded by the main kernel) at slots c + b*Hkv + g
   const int bg = b * a.Hkv + g;
+  const int2 cr = a.ws.mrange[bg];
+  const int c_lo = cr.x, n_parts = cr.y - cr.x + 1;
   constexpr int kBatch = 4;
   for (int k0 = 0; k0 < n_parts; k0 += kBatch) {
     float2 Ac[kBatch];
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {  // loads of the batch first
       const int c = c_lo + k0 + i;
-      const bool live = k0 + i < n_parts && chunk_begin(sp, c) < chunk_begin(sp, c + 1);
+      const bool live = k0 + i < n_parts;
       const float* Pc = a.ws.parts + ((static_cast<size_t>(live ? c : c_lo) + bg) * GQA + wave) * kPart;
       Ac[i] = live ? reinterpret_cast<const float2*>(Pc)[lane] : make_float2(0.0f, 0.0f);
       Zc[i] = live ? Pc[128] : -INFINITY;
@@ -748,6 +749,7 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_waves) {
   n += up(static_cast<size_t>(B) * Hq * kQStride);
   n += up(static_cast<size_t>(B) * Hq * 4 * 4);
   n += up(static_cast<size_t>(B) * Hq * kPart * 4);
+  n += up(static_cast<size_t>(B) * Hkv * 8);
   n += up(part_slots(B, Hkv, n_waves) * GQA * kPart * 4);
   return n;
 }
@@ -764,6 +766,8 @@ DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves)
   p += up(static_cast<size_t>(B) * Hq * 4 * 4);
   w.prot = reinterpret_cast<float*>(p);
   p += up(static_cast<size_t>(B) * Hq * kPart * 4);
+  w.mrange = reinterpret_cast<int2*>(p);
+  p += up(static_cast<size_t>(B) * Hkv * 8);
   w.parts = reinterpret_cast<float*>(p);
   w.n_waves = n_waves;
   return w;

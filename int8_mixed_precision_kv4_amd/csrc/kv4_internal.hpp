@@ -31,6 +31,7 @@ struct DecodeWorkspace {
                    // operand order (even channels, odd channels), then natural order
   float* qinfo;    // [B][Hq][4]  {c_q, S_q (int bits), s_q, 0}
   float* prot;     // [B][Hq][kPart] partials of the protected region
+  int2* mrange;    // [B*Hkv] first and last chunk holding pages of each segment (0, -1: none)
   float* parts;    // [slots][4][kPart] partials of the main region
   int n_waves;     // waves of the main-region grid
 };
