@@ -41,9 +41,15 @@ def log(msg):
 
 
 def source_hash() -> str:
+    """Hash of the main kernel's sources with comments and whitespace removed,
+    so that only a change of code invalidates the stored traffic figure."""
+    import re
     h = hashlib.sha256()
     for f in MAIN_SOURCES:
-        h.update(open(f, "rb").read())
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", "", text).encode())
     return h.hexdigest()[:16]
 
 

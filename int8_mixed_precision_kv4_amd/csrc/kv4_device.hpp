@@ -142,7 +142,10 @@ __device__ __forceinline__ void fwht128_wave(float& x0, float& x1) {
 // closer than 2^-12 ulp to a rounding midpoint of binary32 (and never on
 // one), the residual a - d*RN(a*y) is exact in one FMA, and q0 + r*y is within
 // 2^-22 ulp of a/d, so a single rounding of it is the correctly rounded
-// quotient.  Three operations instead of a full IEEE division sequence.
+// quotient.  This holds when a and a/d are normal; in the subnormal corner
+// the last bits may differ, but such quotients are far below 1/2, so the
+// integer codes taken from them do not.  Three operations instead of a full
+// IEEE division sequence.
 __device__ __forceinline__ float div_short_divisor(float a, float d, float y) {
   const float q0 = a * y;
   const float r = __builtin_fmaf(-q0, d, a);
