@@ -2,22 +2,22 @@
 // (paper.rainbus.top summary, "方法步骤详情" step 4 and "核心方法"; onedev.kr
 // summary, "전제와 한계").
 //
-// Three launches on the caller's stream:
-//   1. query_kernel, one workgroup per (kv-head, sequence): rotates and
-//      INT8-quantizes the 4 queries of the group once for both regions.
-//      Workgroup (0,0) also writes the work plan (prefix sums of main pages).
-//   2. main_kernel.  Its first workgroups are a fixed set of independent
+// Two launches on the caller's stream (three for more than 256 sequences,
+// when a one-workgroup plan_kernel first writes the work plan):
+//   1. main_kernel.  Its first workgroups are a fixed set of independent
 //      waves: the concatenated list of main-region pages of all (sequence,
 //      kv-head) pairs is cut into equal contiguous chunks, one per wave
-//      (split-K with exact load balance).  Per page: integer QK on MFMA (INT8
+//      (split-K with exact load balance); each wave builds the plan (prefix
+//      sums of main pages) in registers and rotates / INT8-quantizes the 4
+//      queries of each group it visits.  Per page: integer QK on MFMA (INT8
 //      query x unpacked INT4 keys), delta/m applied after the dot, tile
-//      softmax, INT8 P operand with the V scale folded in, integer PV on MFMA,
-//      FP32 running merge; a wave writes one partial per segment it touches.
-//      Its last B*Hkv workgroups compute the protected region of one
+//      softmax, INT8 P operand with the V scale folded in, integer PV on
+//      MFMA, FP32 running merge; a wave writes one partial per segment it
+//      touches.  Its last B*Hkv workgroups compute the protected region of one
 //      (sequence, kv-head) each (INT8 QK against the side keys, FP32 softmax,
 //      PV over BF16-dequantized side values); they are dispatched as the
 //      main-region waves retire, so they run in the main region's tail.
-//   3. merge_kernel, one workgroup per (kv-head, sequence): exact
+//   2. merge_kernel, one workgroup per (kv-head, sequence): exact
 //      log-sum-exp merge of the protected partial with the main partials,
 //      written as out and lse.
 #include "kv4_device.hpp"
@@ -83,45 +83,71 @@ typedef __attribute__((address_space(3))) void* lptr;
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitLgkm0 = 0xC07F;
 
-// Query codes in the workspace, per (sequence, q-head): 128 B in MFMA operand
-// order (even channels, then odd channels) and 128 B in natural order.
-constexpr int kQStride = 2 * HD;
+// Plan for batches of more than 256 sequences (smaller batches build it in
+// registers in every main-kernel wave): one workgroup.
+__global__ __launch_bounds__(256) void plan_kernel(DecArgs a) { build_plan(a); }
 
-template <bool DEBUG>
-__global__ __launch_bounds__(256) void query_kernel(DecArgs a) {
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  if (g == 0 && b == 0) build_plan(a);
-  if (threadIdx.x == 0) a.ws.mrange[b * a.Hkv + g] = make_int2(0, -1);  // no main partials unless written
-  const int h = g * GQA + wave;
-  const size_t bh = static_cast<size_t>(b) * a.Hq + h;
-  // Rotate the query like the keys, then symmetric INT8 with an FP32 scale.
-  const uint32_t qw = a.q[bh * 64 + lane];
-  float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
-  fwht128_wave(x0, x1);
-  const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+// Row-of-16 reductions of an int (lanes 16r .. 16r+15).
+__device__ __forceinline__ int row16_sum_i(int v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Rotated INT8 query of the 4 heads of a group, computed by one wave: lane
+// (head grp, r16) holds channels 8 r16 .. 8 r16 + 7 (raw = their BF16 values).
+// FWHT strides 1, 2, 4 inside the lane, then 8, 16, 32, 64 across lanes (xor
+// 1, 2, 4, 8 within the row of 16), in that order, then the 2^-3.5 scale;
+// s_q = max|x| / 127, codes = clamp(rint(x / s_q)), S_q = their sum.
+struct GroupQuery {
+  int c[8];
+  float c_q;
+  int S;
+};
+__device__ __forceinline__ GroupQuery quantize_group_query(uint4 raw, float scale_log2, int r16) {
+  float x[8];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(w[i]);
+    x[2 * i + 1] = bf16_hi(w[i]);
+  }
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((j & h) == 0) {
+        const float u = x[j], v = x[j + h];
+        x[j] = u + v;
+        x[j + h] = u - v;
+      }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const bool upper = (r16 & m) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = __shfl_xor(x[j], m);
+      x[j] = upper ? (p - x[j]) : (x[j] + p);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[j] = x[j] * kInvSqrt128;
+    amax = fmaxf(amax, fabsf(x[j]));
+  }
+  amax = row16_max(amax);
   const float s_q = amax / 127.0f;
-  int c0 = 0, c1 = 0;
-  if (s_q != 0.0f) {
-    c0 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x0 / s_q), -127.0f), 127.0f));
-    c1 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x1 / s_q), -127.0f), 127.0f));
+  GroupQuery g;
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    g.c[j] = s_q != 0.0f ? static_cast<int>(fminf(fmaxf(__builtin_rintf(x[j] / s_q), -127.0f), 127.0f)) : 0;
+    sum += g.c[j];
   }
-  const int S = wave_sum_i(c0 + c1);
-  int8_t* qs = a.ws.qcodes + bh * kQStride;
-  qs[lane] = static_cast<int8_t>(c0);
-  qs[64 + lane] = static_cast<int8_t>(c1);
-  reinterpret_cast<uint16_t*>(qs + HD)[lane] = static_cast<uint16_t>((c0 & 0xFF) | ((c1 & 0xFF) << 8));
-  if (lane == 0) {
-    a.ws.qinfo[bh * 4 + 0] = s_q * a.scale_log2;  // c_q: s_q, the scale and log2(e)
-    a.ws.qinfo[bh * 4 + 1] = __int_as_float(S);
-    a.ws.qinfo[bh * 4 + 2] = s_q;
-    a.ws.qinfo[bh * 4 + 3] = 0.0f;
-    if (DEBUG && a.dbg.qsum) a.dbg.qsum[bh] = S;
-  }
-  if (DEBUG && a.dbg.qcodes) {
-    a.dbg.qcodes[bh * HD + 2 * lane] = static_cast<int8_t>(c0);
-    a.dbg.qcodes[bh * HD + 2 * lane + 1] = static_cast<int8_t>(c1);
-  }
+  g.S = row16_sum_i(sum);
+  g.c_q = s_q * scale_log2;  // c_q: s_q, the scale and log2(e)
+  return g;
 }
 
 // QK MFMA output has head v of position l%16 in register v of lanes 0..15;
@@ -163,7 +189,7 @@ __device__ __forceinline__ void round_bf16x2(float& x, float& y) {
 // channels 4cg..4cg+3 for all 4 heads; the 2 row phases of a wave are reduced
 // with a permlane swap and the 4 waves through LDS.  Wave h writes the
 // partial (A[128], Z, l) of head h to the workspace.
-constexpr int kProtLds = SIDE_ROWS * GQA * 4 + SIDE_ROWS * 4 + 4 * GQA * HD * 4;  // 11072 B
+constexpr int kProtLds = SIDE_ROWS * GQA * 4 + SIDE_ROWS * 4 + 4 * GQA * HD * 4 + GQA * HD + GQA * 4;  // 11600 B
 
 template <bool DEBUG>
 __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b, uint8_t* lds_raw) {
@@ -173,6 +199,8 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   auto se = reinterpret_cast<float (*)[GQA]>(lds_raw);                                  // [144][4] logits, then weights
   float* ssv = reinterpret_cast<float*>(lds_raw + SIDE_ROWS * GQA * 4);                   // [144] V scales (0: row unused)
   auto red = reinterpret_cast<float (*)[GQA][HD]>(lds_raw + SIDE_ROWS * GQA * 4 + SIDE_ROWS * 4);  // [4][4][128]
+  int8_t* qn = reinterpret_cast<int8_t*>(lds_raw + SIDE_ROWS * GQA * 4 + SIDE_ROWS * 4 + 4 * GQA * HD * 4);  // [4][128]
+  float* cqs = reinterpret_cast<float*>(qn + GQA * HD);                                                    // [4]
 
   const int L = ld_const(a.ctx + b);
   const int slot = a.slot ? ld_const(a.slot + b) : b;
@@ -206,14 +234,38 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   }
   if (tid < SIDE_ROWS)
     ssv[tid] = side_position(tid, L) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
-  // query codes (natural order) and c_q of the 4 heads
+  // Query of head `wave`: rotate like the keys, then symmetric INT8 with an
+  // FP32 scale (lane l holds channels 2l, 2l+1); codes in natural order to LDS.
+  {
+    const size_t bh = qb + wave;
+    const uint32_t qw = a.q[bh * 64 + lane];
+    float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
+    fwht128_wave(x0, x1);
+    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    const float s_q = amax / 127.0f;
+    int c0 = 0, c1 = 0;
+    if (s_q != 0.0f) {
+      c0 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x0 / s_q), -127.0f), 127.0f));
+      c1 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x1 / s_q), -127.0f), 127.0f));
+    }
+    reinterpret_cast<uint16_t*>(qn + wave * HD)[lane] = static_cast<uint16_t>((c0 & 0xFF) | ((c1 & 0xFF) << 8));
+    if (lane == 0) cqs[wave] = s_q * a.scale_log2;
+    if (DEBUG) {
+      const int S = wave_sum_i(c0 + c1);
+      if (a.dbg.qsum && lane == 0) a.dbg.qsum[bh] = S;
+      if (a.dbg.qcodes) {
+        a.dbg.qcodes[bh * HD + 2 * lane] = static_cast<int8_t>(c0);
+        a.dbg.qcodes[bh * HD + 2 * lane + 1] = static_cast<int8_t>(c1);
+      }
+    }
+  }
+  __syncthreads();
   v4i qa[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
   if (r16 < GQA) {
-    const int8_t* qn = a.ws.qcodes + (qb + r16) * kQStride + HD;
-    qa[0] = *reinterpret_cast<const v4i*>(qn + 16 * grp);
-    qa[1] = *reinterpret_cast<const v4i*>(qn + 64 + 16 * grp);
+    qa[0] = *reinterpret_cast<const v4i*>(qn + r16 * HD + 16 * grp);
+    qa[1] = *reinterpret_cast<const v4i*>(qn + r16 * HD + 64 + 16 * grp);
   }
-  const float c_q = a.ws.qinfo[(qb + grp) * 4];
+  const float c_q = cqs[grp];
 
   // ---- INT8 QK: lane (head grp, row 16 rg + r16)
 #pragma unroll
@@ -324,8 +376,9 @@ __device__ __forceinline__ int pcode_slot(int t) { return 8 * (t >> 3) + 4 * (t 
 //   [0, 4096)     K codes, tile t at 1024 t + 16 lane
 //   [4096, 8192)  V codes, channel block s2 at 4096 + 1024 s2 + 16 lane
 //   [8192, 8704)  metadata, page t at 8192 + 128 t: 16 x {delta, m} K, then V
-// followed by 256 B where the P operand is assembled.
-constexpr int kSlotK = 0, kSlotV = 4096, kSlotMeta = 8192, kSlotP = 8704, kSlotBytes = 8960;
+// followed by 256 B where the P operand is assembled and 512 B where the
+// query codes of a group are rearranged into the MFMA operand order.
+constexpr int kSlotK = 0, kSlotV = 4096, kSlotMeta = 8192, kSlotP = 8704, kSlotQ = 8960, kSlotBytes = 9472;
 
 struct QuadRegs {
   uint4 kq[4], vq[4];
@@ -478,31 +531,55 @@ struct Split {
 __device__ __forceinline__ Split make_split(int T, int nw) { return Split{T / nw, T % nw}; }
 __device__ __forceinline__ int chunk_begin(const Split& s, int c) { return c * s.q + min(c, s.r); }
 
-// The plan as seen by one main-kernel wave.  For up to 256 sequences the wave
-// holds entries 1..B in registers (entry i in lane (i-1) % 64 of register
-// (i-1) / 64), fetched with one round of vector loads; lookups are then
-// readlanes and ballots with no memory traffic.  Larger batches read the plan
-// through scalar loads.
+// The plan as seen by one main-kernel wave.  For up to 256 sequences every
+// wave builds it in registers from the context lengths (entry i, 1 <= i <= B,
+// in lane (i-1) / 4 of register (i-1) % 4): one round of loads and a wave
+// prefix sum, then lookups are readlanes and ballots.  Larger batches read
+// the plan a separate launch wrote, through scalar loads.
 struct PlanView {
   const int32_t* plan;
-  int B;
+  int B, T;
   bool in_regs;
   int v[4];
 };
-__device__ __forceinline__ PlanView load_plan(const int32_t* plan, int B, int lane) {
+__device__ __forceinline__ PlanView plan_view(const DecArgs& a, int lane) {
   PlanView r;
-  r.plan = plan;
-  r.B = B;
-  r.in_regs = B <= 256;
+  r.plan = a.ws.plan;
+  r.B = a.B;
+  r.in_regs = a.B <= 256;
+  if (!r.in_regs) {
+    r.T = ld_const(a.ws.plan + a.B);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) r.v[k] = r.in_regs ? plan[min(1 + 64 * k + lane, B)] : 0;
+    for (int k = 0; k < 4; ++k) r.v[k] = 0;
+    return r;
+  }
+  int m[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * lane + k;
+    const int L = a.ctx[min(i, a.B - 1)];
+    m[k] = i < a.B ? main_pages(L) * a.Hkv : 0;
+  }
+  m[1] += m[0];
+  m[2] += m[1];
+  m[3] += m[2];
+  int x = m[3];  // inclusive prefix of the lane totals
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  const int excl = x - m[3];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r.v[k] = excl + m[k];
+  r.T = __builtin_amdgcn_readlane(r.v[3], 63);
   return r;
 }
 // plan[i] for a wave-uniform 0 <= i <= B.
 __device__ __forceinline__ int plan_at(const PlanView& r, int i) {
   if (!r.in_regs) return ld_const(r.plan + i);
   if (i == 0) return 0;
-  const int l = (i - 1) & 63, k = (i - 1) >> 6;
+  const int l = (i - 1) >> 2, k = (i - 1) & 3;
   const int x0 = __builtin_amdgcn_readlane(r.v[0], l), x1 = __builtin_amdgcn_readlane(r.v[1], l);
   const int x2 = __builtin_amdgcn_readlane(r.v[2], l), x3 = __builtin_amdgcn_readlane(r.v[3], l);
   return k == 0 ? x0 : k == 1 ? x1 : k == 2 ? x2 : x3;
@@ -513,7 +590,7 @@ __device__ __forceinline__ int find_seq(const PlanView& r, int p, int lo, int la
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      cnt += __builtin_popcountll(__ballot(1 + 64 * k + lane <= r.B && r.v[k] <= p));
+      cnt += __builtin_popcountll(__ballot(4 * lane + k + 1 <= r.B && r.v[k] <= p));
     return cnt;
   }
   int hi = r.B;  // plan[lo] <= p < plan[hi]; scalar loads, counted apart from vector loads
@@ -545,7 +622,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   const int r16 = lane & 15, grp = lane >> 4;
   const int w = blockIdx.x * 4 + wave;
   const int32_t* plan = a.ws.plan;
-  const Split sp = make_split(ld_const(plan + a.B), nw);
+  const PlanView pv = plan_view(a, lane);
+  const Split sp = make_split(pv.T, nw);
   uint8_t* slot = lds[wave];
   uint8_t* stage = slot + kSlotP;
   const int pslot = pcode_slot(r16);
@@ -555,12 +633,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   int ip = chunk_begin(sp, w);
   const int iend = chunk_begin(sp, w + 1);
   const int chunk0 = ip;
-  const PlanView pv = load_plan(plan, a.B, lane);
   int ib = ip < iend ? find_seq(pv, ip, 0, lane) : 0;
   int seg0 = 0, seg_end = 0, seg_g = 0;  // segment holding ip: pages [seg0, seg_end), kv-head seg_g
-  // Q operands of the next piece (loaded with its first quad)
+  // Q operands of the next piece: the raw query is loaded when its first quad
+  // is described (raw2, moved to raw1 with the quad), and rotated/quantized
+  // after the compute of the iteration that issued that quad.
   v4i nqa0 = {0, 0, 0, 0}, nqa1 = {0, 0, 0, 0};
   float2 nqi = make_float2(0.0f, 0.0f);
+  uint4 raw1 = make_uint4(0, 0, 0, 0), raw2 = make_uint4(0, 0, 0, 0);
+  auto group_query = [&](const QuadDesc& d, const uint4& raw) {
+    (void)d;
+    const GroupQuery gq = quantize_group_query(raw, a.scale_log2, r16);
+    // A operand of QK: rows 0..3 = the group's heads, k = channels (lane
+    // group grp covers channels 32grp..32grp+31, even / odd split); the codes
+    // go through the slot's query area to reach that layout.
+    uint8_t* qs = slot + kSlotQ + grp * HD;
+    const uint32_t even = (gq.c[0] & 0xFF) | ((gq.c[2] & 0xFF) << 8) | ((gq.c[4] & 0xFF) << 16) |
+                          (static_cast<uint32_t>(gq.c[6] & 0xFF) << 24);
+    const uint32_t odd = (gq.c[1] & 0xFF) | ((gq.c[3] & 0xFF) << 8) | ((gq.c[5] & 0xFF) << 16) |
+                         (static_cast<uint32_t>(gq.c[7] & 0xFF) << 24);
+    reinterpret_cast<uint32_t*>(qs)[r16] = even;
+    reinterpret_cast<uint32_t*>(qs + 64)[r16] = odd;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (r16 < GQA) {
+      nqa0 = *reinterpret_cast<const v4i*>(slot + kSlotQ + r16 * HD + 16 * grp);
+      nqa1 = *reinterpret_cast<const v4i*>(slot + kSlotQ + r16 * HD + 64 + 16 * grp);
+    }
+    nqi = make_float2(gq.c_q, __int_as_float(gq.S));
+  };
 
   // Stage 1: describe the next quad of the chunk and fetch its page-table
   // entries (lanes 0..3, one per tile) into pt; false when the chunk is done.
@@ -587,11 +689,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     d.closes = stop == seg_end;
     const int32_t* ptrow = a.page_table + static_cast<size_t>(ib) * a.pt_stride;
     pt = ptrow[d.j0 + min(lane & 3, d.np - 1)];
+    if (d.first)  // BF16 query of head grp, channels 8 r16 .. 8 r16 + 7
+      raw2 = reinterpret_cast<const uint4*>(a.q + ((static_cast<size_t>(ib) * a.Hq + seg_g * GQA + grp) * HD) / 2)[r16];
     ip += d.np;
     return true;
   };
-  // Stage 2: start the loads of a described quad (pages into the LDS slot,
-  // and for the first quad of a piece the Q operands of its group).
+  // Stage 2: start the page loads of a described quad into the LDS slot.
   auto issue_quad = [&](QuadDesc& d, int pt) {
     const gptr gbase = (gptr)a.pages + static_cast<size_t>(d.g) * BLOCK_BYTES;
     gptr blk[4];
@@ -599,20 +702,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     for (int t = 0; t < 4; ++t)
       blk[t] = gbase + static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(pt, t))) * pstride;
     quad_to_lds(slot, blk, lane, r16, grp);
-    if (d.first) {
-      // A operand of QK: rows 0..3 = the group's heads, k = channels (lane
-      // group grp covers channels 32grp..32grp+31, even / odd split).
-      const size_t qb = static_cast<size_t>(d.b) * a.Hq + d.g * GQA;
-      d.main_end = ld_const(a.ctx + d.b) - WINDOW;
-      if (r16 < GQA) {
-        const int8_t* qs = a.ws.qcodes + (qb + r16) * kQStride;
-        nqa0 = *reinterpret_cast<const v4i*>(qs + 16 * grp);
-        nqa1 = *reinterpret_cast<const v4i*>(qs + 64 + 16 * grp);
-      }
-      // raw {c_q, S_q bits}: converted when the piece starts computing, so
-      // that nothing waits for this load here
-      nqi = *reinterpret_cast<const float2*>(a.ws.qinfo + (qb + grp) * 4);
-    }
+    if (d.first) d.main_end = ld_const(a.ctx + d.b) - WINDOW;
   };
 
   // Pipeline: quad i is computed while quad i+1 streams into the LDS slot
@@ -621,7 +711,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   QuadDesc d1, d2;  // quads i+1 (in flight) and i+2 (described)
   int pt1 = 0, pt2 = 0;
   bool have1 = plan_quad(d1, pt1);
-  if (have1) issue_quad(d1, pt1);
+  raw1 = raw2;
+  if (have1) {
+    issue_quad(d1, pt1);
+    group_query(d1, raw1);  // d1 is the first quad of a piece
+  }
   bool have2 = have1 && plan_quad(d2, pt2);
   MainState st;
   v4i qa0 = {0, 0, 0, 0}, qa1 = {0, 0, 0, 0};
@@ -671,6 +765,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     if (have2) {
       d1 = d2;
       pt1 = pt2;
+      raw1 = raw2;
       issue_quad(d1, pt1);
       have2 = plan_quad(d2, pt2);
     }
@@ -690,6 +785,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
       for (int o = 0; o < 8; ++o) pend_A[o] = st.O[o] + Mh;
       pend = true;
     }
+    if (have1 && d1.first) group_query(d1, raw1);  // operands for the next iteration
   }
   if (pend) store_partial();
 }
@@ -706,8 +802,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
   float Zm = Pp[128], lm = Pp[129];
   // main partials: chunks c_lo..c_hi (recorded by the main kernel) at slots c + b*Hkv + g
   const int bg = b * a.Hkv + g;
-  const int2 cr = a.ws.mrange[bg];
-  const int c_lo = cr.x, n_parts = cr.y - cr.x + 1;
+  const int2 cr = a.ws.mrange[bg];  // written by the main kernel when the segment has pages
+  const int c_lo = cr.x, n_parts = main_pages(ld_const(a.ctx + b)) > 0 ? cr.y - cr.x + 1 : 0;
   constexpr int kBatch = 4;
   for (int k0 = 0; k0 < n_parts; k0 += kBatch) {
     float2 Ac[kBatch];
@@ -746,8 +842,6 @@ static size_t part_slots(int B, int Hkv, int n_waves) {
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_waves) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   size_t n = up(static_cast<size_t>(B + 1) * 4);
-  n += up(static_cast<size_t>(B) * Hq * kQStride);
-  n += up(static_cast<size_t>(B) * Hq * 4 * 4);
   n += up(static_cast<size_t>(B) * Hq * kPart * 4);
   n += up(static_cast<size_t>(B) * Hkv * 8);
   n += up(part_slots(B, Hkv, n_waves) * GQA * kPart * 4);
@@ -760,10 +854,6 @@ DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves)
   DecodeWorkspace w;
   w.plan = reinterpret_cast<int32_t*>(p);
   p += up(static_cast<size_t>(B + 1) * 4);
-  w.qcodes = reinterpret_cast<int8_t*>(p);
-  p += up(static_cast<size_t>(B) * Hq * kQStride);
-  w.qinfo = reinterpret_cast<float*>(p);
-  p += up(static_cast<size_t>(B) * Hq * 4 * 4);
   w.prot = reinterpret_cast<float*>(p);
   p += up(static_cast<size_t>(B) * Hq * kPart * 4);
   w.mrange = reinterpret_cast<int2*>(p);
@@ -798,12 +888,11 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   if (dbg) a.dbg = *dbg;
   // main-region workgroups, then one protected-region workgroup per (b, g)
   const dim3 block(256), groups(c.Hkv, B), grid(ws.n_waves / 4 + B * c.Hkv);
+  if (B > 256) hipLaunchKernelGGL(plan_kernel, dim3(1), block, 0, s, a);
   if (dbg) {
-    hipLaunchKernelGGL(query_kernel<true>, groups, block, 0, s, a);
     hipLaunchKernelGGL(main_kernel<true>, grid, block, 0, s, a);
     hipLaunchKernelGGL(merge_kernel, groups, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL(query_kernel<false>, groups, block, 0, s, a);
     if (ev_main_begin) {
       const hipError_t e = hipEventRecord(ev_main_begin, s);
       if (e != hipSuccess) return e;

@@ -26,10 +26,7 @@ struct DecodeDebug {
 
 // Workspace carve-up of one decode call.
 struct DecodeWorkspace {
-  int32_t* plan;   // [B+1] prefix sums of (main pages x Hkv) over sequences
-  int8_t* qcodes;  // [B][Hq][256] INT8 codes of the rotated queries: MFMA
-                   // operand order (even channels, odd channels), then natural order
-  float* qinfo;    // [B][Hq][4]  {c_q, S_q (int bits), s_q, 0}
+  int32_t* plan;   // [B+1] prefix sums of (main pages x Hkv) over sequences (B > 256 only)
   float* prot;     // [B][Hq][kPart] partials of the protected region
   int2* mrange;    // [B*Hkv] first and last chunk holding pages of each segment (0, -1: none)
   float* parts;    // [slots][4][kPart] partials of the main region
