@@ -612,6 +612,7 @@ struct QuadDesc {
 template <bool DEBUG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WAVES_PER_SIMD, KV4_MAIN_WAVES_PER_SIMD))) void main_kernel(DecArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kSlotBytes];
+  static_assert(kProtLds <= 4 * kSlotBytes, "the protected role reuses the main role's LDS");
   const int nw = a.ws.n_waves;
   if (blockIdx.x >= nw / 4) {  // protected-region workgroups fill the tail of the grid
     const int u = blockIdx.x - nw / 4;
@@ -621,7 +622,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
   const int w = blockIdx.x * 4 + wave;
-  const int32_t* plan = a.ws.plan;
   const PlanView pv = plan_view(a, lane);
   const Split sp = make_split(pv.T, nw);
   uint8_t* slot = lds[wave];
