@@ -25,7 +25,8 @@ _lib = None
 
 class _Cache(C.Structure):
     _fields_ = [("num_pages", C.c_int32), ("num_kv_heads", C.c_int32), ("max_slots", C.c_int32),
-                ("pages", C.c_void_p), ("side_codes", C.c_void_p), ("side_scales", C.c_void_p)]
+                ("pages", C.c_void_p), ("side_codes", C.c_void_p), ("side_scales", C.c_void_p),
+                ("sink", C.c_int32), ("window", C.c_int32)]
 
 
 class _Debug(C.Structure):
@@ -157,23 +158,32 @@ def scale_log2(softmax_scale: float) -> np.float32:
 # ------------------------------------------------------------------ cache --
 
 class Cache:
-    """One layer's cache in host memory (oracle side)."""
+    """One layer's cache in host memory (oracle side); sink / window are the
+    protection budget s, w (16 / 128 by default; s a multiple of 16,
+    s + w <= 144)."""
 
-    def __init__(self, num_pages: int, Hkv: int, max_slots: int):
+    def __init__(self, num_pages: int, Hkv: int, max_slots: int, sink: int = SINK,
+                 window: int = WINDOW):
         self.pages = np.zeros((num_pages, Hkv, BLOCK), np.uint8)
         self.side_codes = np.zeros((max_slots, Hkv, SIDE_ROWS, 2, HD), np.int8)
         self.side_scales = np.zeros((max_slots, Hkv, SIDE_ROWS, 2), np.uint16)
         self.num_pages, self.Hkv, self.max_slots = num_pages, Hkv, max_slots
+        if sink < 0 or window < 0 or sink % PAGE or sink + window > SIDE_ROWS:
+            raise ValueError(f"protection budget s={sink}, w={window}: need s % {PAGE} == 0 "
+                             f"and s + w <= {SIDE_ROWS}")
+        self.sink, self.window = sink, window
 
     def _struct(self):
         return _Cache(self.num_pages, self.Hkv, self.max_slots, _p(self.pages).value,
-                      _p(self.side_codes).value, _p(self.side_scales).value)
+                      _p(self.side_codes).value, _p(self.side_scales).value, self.sink,
+                      self.window)
 
     def copy(self) -> "Cache":
         c = Cache.__new__(Cache)
         c.pages, c.side_codes, c.side_scales = (self.pages.copy(), self.side_codes.copy(),
                                                 self.side_scales.copy())
         c.num_pages, c.Hkv, c.max_slots = self.num_pages, self.Hkv, self.max_slots
+        c.sink, c.window = self.sink, self.window
         return c
 
 
@@ -186,7 +196,8 @@ def append(cache: Cache, k, v, pos, slot, page_table):
     st = cache._struct()
     rc = lib().kv4ref_append(C.byref(st), _p(k), _p(v), _p(pos),
                              None if slot is None else _p(slot), _p(table), table.shape[1], B)
-    assert rc == 0
+    if rc != 0:
+        raise ValueError(f"kv4ref_append failed ({rc}): invalid protection budget")
 
 
 def prefill(cache: Cache, k, v, cu_seqlens, start_pos, slot, page_table, nthreads=None):
@@ -200,7 +211,8 @@ def prefill(cache: Cache, k, v, cu_seqlens, start_pos, slot, page_table, nthread
     rc = lib().kv4ref_prefill(C.byref(st), _p(k), _p(v), _p(cu), _p(start),
                               None if slot is None else _p(slot), _p(table), table.shape[1],
                               nseq, nthreads or default_threads())
-    assert rc == 0
+    if rc != 0:
+        raise ValueError(f"kv4ref_prefill failed ({rc}): invalid protection budget")
 
 
 def decode(cache: Cache, q, ctx_len, slot, page_table, Hq: int, softmax_scale: float,
@@ -228,5 +240,6 @@ def decode(cache: Cache, q, ctx_len, slot, page_table, Hq: int, softmax_scale: f
                              _p(table), table.shape[1], B, Hq, softmax_scale, int(pv_exact),
                              _p(out), _p(lse), C.byref(dstruct) if dstruct else None,
                              nthreads or default_threads())
-    assert rc == 0, rc
+    if rc != 0:
+        raise ValueError(f"kv4ref_decode failed ({rc}): invalid head counts or protection budget")
     return out, lse, dbg

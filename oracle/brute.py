@@ -168,25 +168,26 @@ def query_codes(q_bf16_bits: np.ndarray):
 
 
 def decode_one(pages, side_codes, side_scales, Hkv, q_bits, L, slot, g, table_row, scale_log2,
-               pv_exact=False):
+               pv_exact=False, sink=SINK, window=WINDOW):
     """One (sequence, q-head): returns out[128] (f64), lse, and dicts of the
-    integer intermediates keyed by position / logical page."""
+    integer intermediates keyed by position / logical page.  sink / window:
+    the protection budget s, w."""
     qc, s_q, S_q = query_codes(q_bits)
     c_q = f32_mul(s_q, scale_log2)
     qk, pcode, pv = {}, {}, {}
     parts = []
     # protected region: sinks and recent window
-    prot = list(range(0, min(SINK, L))) + list(range(max(SINK, L - WINDOW), L))
+    prot = list(range(0, min(sink, L))) + list(range(max(sink, L - window), L))
     zs, rows = [], []
     for p in prot:
-        row = p if p < SINK else SINK + p % WINDOW
+        row = p if p < sink else sink + p % window
         k8 = side_codes[slot, g, row, 0].astype(np.int64)
         d8 = int(np.dot(qc, k8))
         qk[p] = d8
         sk = float(np.array([side_scales[slot, g, row, 0]], np.uint16).view(np.float16)[0])
         zs.append(f32_mul(f32_mul(float(d8), sk), c_q))
         rows.append(row)
-    zmax = max(zs)
+    zmax = max(zs) if zs else -math.inf
     A = np.zeros(HD)
     ell = 0.0
     for z, row in zip(zs, rows):
@@ -196,10 +197,11 @@ def decode_one(pages, side_codes, side_scales, Hkv, q_bits, L, slot, g, table_ro
         vhat = np.array([rnbf16(f32_mul(sv, float(c))) for c in v8])
         A += e * vhat
         ell += e
-    parts.append((A, zmax, ell))
+    if prot:
+        parts.append((A, zmax, ell))
     # main region, one tile per logical page
-    main_end = L - WINDOW
-    j = 1
+    main_end = L - window
+    j = sink // PAGE
     while PAGE * j < main_end:
         kc, vc, kd, km, vd, vm = unpack_block(pages[table_row[j], g])
         n = min(PAGE, main_end - PAGE * j)

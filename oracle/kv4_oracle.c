@@ -32,9 +32,7 @@
 enum {
   HD = 128,          /* one quantization group = one 128-dim token-head vector */
   PAGE = 16,         /* positions per page */
-  SINK = 16,         /* s: protected leading positions */
-  WINDOW = 128,      /* w: protected recent positions */
-  SIDE_ROWS = 144,   /* s + w */
+  SIDE_ROWS = 144,   /* capacity of the side buffer per (slot, kv-head): s + w <= 144 */
   BLOCK = 2176,      /* bytes per (page, kv-head): 16 x (64+64+4+4) */
   OFF_KCODE = 0,     /* K codes, token-major, 64 B per position */
   OFF_VCODE = 1024,  /* V codes, channel-major, 8 B per channel */
@@ -291,7 +289,9 @@ float kv4ref_scale_log2(float softmax_scale) {
 /*   2k+1 in the high nibble of byte k) || 16 x {delta, m} FP16 for K ||      */
 /*   16 x {delta, m} FP16 for V (little-endian).  68 B per 128 elements:      */
 /*   4.25 bits per element.                                                   */
-/* Side rows: position p < 16 -> row p; p >= 16 -> row 16 + (p mod 128).     */
+/* Side rows (s sink positions, w recent positions; s = 16, w = 128 by       */
+/* default): position p < s -> row p; p >= s -> row s + (p mod w), or no row */
+/* when w = 0.                                                               */
 /* ------------------------------------------------------------------------ */
 
 static uint8_t *block_at(const kv4ref_cache *c, int32_t phys, int g) {
@@ -299,7 +299,16 @@ static uint8_t *block_at(const kv4ref_cache *c, int32_t phys, int g) {
   return c->pages + ((size_t)phys * (size_t)c->num_kv_heads + (size_t)g) * BLOCK;
 }
 
-static int side_row(int32_t p) { return p < SINK ? p : SINK + (p % WINDOW); }
+/* Protection budget: s a multiple of the page size, s + w within the buffer. */
+static int budget_ok(const kv4ref_cache *c) {
+  return c->sink >= 0 && c->window >= 0 && c->sink % PAGE == 0 && c->sink + c->window <= SIDE_ROWS;
+}
+
+/* Side row of position p, or -1 when p has none (p >= s and w = 0). */
+static int side_row(const kv4ref_cache *c, int32_t p) {
+  if (p < c->sink) return p;
+  return c->window > 0 ? c->sink + (p % c->window) : -1;
+}
 
 static int8_t *side_code_at(const kv4ref_cache *c, int32_t slot, int g, int row, int kv) {
   assert(slot >= 0 && slot < c->max_slots);
@@ -378,7 +387,8 @@ static void append_one(const kv4ref_cache *c, int g, const uint16_t *k16, const 
   put_meta(blk, OFF_KMETA, t, kd, km);
   put_meta(blk, OFF_VMETA, t, vd, vm);
 
-  int row = side_row(pos);
+  int row = side_row(c, pos);
+  if (row < 0) return;
   quant_int8(k, side_code_at(c, slot, g, row, 0), side_scale_at(c, slot, g, row, 0));
   quant_int8(v, side_code_at(c, slot, g, row, 1), side_scale_at(c, slot, g, row, 1));
 }
@@ -387,6 +397,7 @@ int kv4ref_append(const kv4ref_cache *c, const uint16_t *k, const uint16_t *v,
                   const int32_t *pos, const int32_t *slot, const int32_t *page_table,
                   int32_t pt_stride, int32_t B) {
   const int H = c->num_kv_heads;
+  if (!budget_ok(c)) return -1;
   for (int b = 0; b < B; b++) {
     int32_t s = slot ? slot[b] : b;
     for (int g = 0; g < H; g++) {
@@ -403,6 +414,7 @@ int kv4ref_prefill(const kv4ref_cache *c, const uint16_t *k, const uint16_t *v,
                    const int32_t *page_table, int32_t pt_stride, int32_t nseq, int32_t nthreads) {
   const int H = c->num_kv_heads;
   (void)nthreads;
+  if (!budget_ok(c)) return -1;
 #pragma omp parallel for schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
   for (int sq = 0; sq < nseq; sq++) {
     int32_t s = slot ? slot[sq] : sq;
@@ -420,9 +432,10 @@ int kv4ref_prefill(const kv4ref_cache *c, const uint16_t *k, const uint16_t *v,
 
 /* ------------------------------------------------------------------------ */
 /* Decode.                                                                    */
-/* Regions (L = context length including this step's token):                  */
-/*   sinks  S = [0, min(16, L)),  recent R = [max(16, L-128), L),             */
-/*   main   M = [16, L-128)  (empty when L <= 144).                           */
+/* Regions (L = context length including this step's token; s = 16 and     */
+/* w = 128 by default):                                                       */
+/*   sinks  S = [0, min(s, L)),  recent R = [max(s, L-w), L),                 */
+/*   main   M = [s, L-w)  (empty when L <= s + w).                            */
 /* A partial is (A[128], Z, l): unnormalised output, base-2 max logit and sum */
 /* of weights relative to Z.  Everything after the integer accumulators is    */
 /* evaluated in FP64 here.                                                    */
@@ -512,15 +525,20 @@ static void protected_region(const kv4ref_cache *c, int32_t slot, int g, int32_t
                              const int8_t qc[HD], float c_q, partial_t *out, int32_t *dbg_qk) {
   int32_t pos[SIDE_ROWS];
   int n = 0;
-  int sink_end = L < SINK ? L : SINK;
-  int rec_begin = (L - WINDOW) > SINK ? (L - WINDOW) : SINK;
+  const int sw = c->sink + c->window;
+  int sink_end = L < c->sink ? L : c->sink;
+  int rec_begin = (L - c->window) > c->sink ? (L - c->window) : c->sink;
   for (int p = 0; p < sink_end; p++) pos[n++] = p;
   for (int p = rec_begin; p < L; p++) pos[n++] = p;
-  assert(n == (L < SIDE_ROWS ? L : SIDE_ROWS));
+  assert(n == (L < sw ? L : sw));
+  out->Z = -INFINITY; /* an empty region (s = w = 0) contributes nothing */
+  out->l = 0.0;
+  for (int j = 0; j < HD; j++) out->A[j] = 0.0;
+  if (n == 0) return;
 
   float z[SIDE_ROWS];
   for (int i = 0; i < n; i++) {
-    int row = side_row(pos[i]);
+    int row = side_row(c, pos[i]);
     const int8_t *k8 = side_code_at(c, slot, g, row, 0);
     int32_t D8 = 0;
     for (int d = 0; d < HD; d++) D8 += (int32_t)qc[d] * (int32_t)k8[d];
@@ -532,10 +550,8 @@ static void protected_region(const kv4ref_cache *c, int32_t slot, int g, int32_t
   for (int i = 1; i < n; i++)
     if (z[i] > zmax) zmax = z[i];
   out->Z = zmax;
-  out->l = 0.0;
-  for (int j = 0; j < HD; j++) out->A[j] = 0.0;
   for (int i = 0; i < n; i++) {
-    int row = side_row(pos[i]);
+    int row = side_row(c, pos[i]);
     float e = exp2s(z[i] - zmax);
     const int8_t *v8 = side_code_at(c, slot, g, row, 1);
     float sv = kv4ref_f16_to_f32(*side_scale_at(c, slot, g, row, 1));
@@ -556,6 +572,7 @@ static void merge(const partial_t *p, int n, double *out, double *lse) {
   double o[HD];
   for (int j = 0; j < HD; j++) o[j] = 0.0;
   for (int r = 0; r < n; r++) {
+    if (p[r].l == 0.0) continue; /* empty region */
     double w = exp2(p[r].Z - Z);
     l += w * p[r].l;
     for (int j = 0; j < HD; j++) o[j] += w * p[r].A[j];
@@ -570,7 +587,7 @@ int kv4ref_decode(const kv4ref_cache *c, const uint16_t *q, const int32_t *ctx_l
                   const kv4ref_debug *dbg, int32_t nthreads) {
   exp2_init();
   const int Hkv = c->num_kv_heads;
-  if (Hkv <= 0 || Hq % Hkv != 0) return -1;
+  if (Hkv <= 0 || Hq % Hkv != 0 || !budget_ok(c)) return -1;
   const int G = Hq / Hkv; /* q-head h reads kv-head h / G */
   const float scale_log2 = kv4ref_scale_log2(softmax_scale);
   int bad = 0;
@@ -599,17 +616,20 @@ int kv4ref_decode(const kv4ref_cache *c, const uint16_t *q, const int32_t *ctx_l
     uint8_t *dpc = (dbg && dbg->pcode) ? dbg->pcode + (size_t)bh * dbg->max_ctx : NULL;
     int32_t *dpv = (dbg && dbg->pv) ? dbg->pv + (size_t)bh * dbg->max_pages * HD : NULL;
 
-    const int32_t main_end = L - WINDOW;           /* M = [16, main_end) */
-    const int ntiles = main_end > SINK ? (main_end - 1) / PAGE : 0; /* pages 1..ntiles */
+    const int32_t main_end = L - c->window;          /* M = [s, main_end) */
+    const int j0 = c->sink / PAGE;                    /* first main page */
+    const int j1 = main_end > c->sink ? (main_end - 1) / PAGE : j0 - 1; /* last main page */
+    const int ntiles = j1 - j0 + 1;
     partial_t *parts = (partial_t *)malloc(sizeof(partial_t) * (size_t)(ntiles + 1));
     protected_region(c, s, g, L, qc, c_q, &parts[0], dqk);
     const int32_t *row = page_table + (size_t)b * pt_stride;
-    for (int j = 1; j <= ntiles; j++) {
+    for (int j = j0; j <= j1; j++) {
       const uint8_t *blk = block_at(c, row[j], g);
       int t_end = main_end - PAGE * j;
       if (t_end > PAGE) t_end = PAGE;
-      main_tile(blk, t_end, qc, qsum, c_q, pv_exact, &parts[j], dqk ? dqk + PAGE * j : NULL,
-                dpc ? dpc + PAGE * j : NULL, dpv ? dpv + (size_t)j * HD : NULL);
+      main_tile(blk, t_end, qc, qsum, c_q, pv_exact, &parts[1 + j - j0],
+                dqk ? dqk + PAGE * j : NULL, dpc ? dpc + PAGE * j : NULL,
+                dpv ? dpv + (size_t)j * HD : NULL);
     }
     merge(parts, ntiles + 1, out + (size_t)bh * HD, lse + bh);
     free(parts);

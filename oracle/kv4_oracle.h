@@ -27,6 +27,8 @@ typedef struct kv4ref_cache {
   uint8_t *pages;
   int8_t *side_codes;
   uint16_t *side_scales;
+  int32_t sink;   /* s protected leading positions (16; a multiple of 16) */
+  int32_t window; /* w protected recent positions (128); s + w <= 144 */
 } kv4ref_cache;
 
 /* Optional integer intermediates of a decode step (any pointer may be NULL).
@@ -37,7 +39,7 @@ typedef struct kv4ref_cache {
  *                            in the protected region)
  *   pcode  [B][Hq][max_ctx]  uint8 P-operand code of every main position
  *   pv     [B][Hq][max_pages][128]  int32 integer P.V accumulators of the
- *                            main tile on logical page j (j >= 1) */
+ *                            main tile on logical page j (j >= s / 16) */
 typedef struct kv4ref_debug {
   int8_t *qcodes;
   int32_t *qsum;

@@ -43,11 +43,12 @@ def host_inputs(wl, layer: int = 0) -> HostInputs:
     return HostInputs(bf16_bits(k), bf16_bits(v), bf16_bits(q), off)
 
 
-def oracle_cache(wl, hi: HostInputs, nthreads=None) -> oracle.Cache:
+def oracle_cache(wl, hi: HostInputs, nthreads=None, sink=oracle.SINK,
+                 window=oracle.WINDOW) -> oracle.Cache:
     """Cache state right before attention: positions [0, ctx-1) by re-prefill,
     then this step's token appended (or all ctx positions by re-prefill for
-    decode-only workloads)."""
-    cache = oracle.Cache(wl.num_pages, wl.Hkv, wl.max_slots)
+    decode-only workloads); sink / window: the protection budget."""
+    cache = oracle.Cache(wl.num_pages, wl.Hkv, wl.max_slots, sink, window)
     lead = wl.ctx - 1 if wl.append_step else wl.ctx
     k, v, cu = hi.prefix(lead)
     oracle.prefill(cache, k, v, cu, np.zeros(wl.B, np.int32), wl.slots, wl.page_table, nthreads)
