@@ -147,6 +147,117 @@ def build_layers(wl, dev, with_bf16=True):
     return layers, dict(table=table, slots=slots, offsets=off)
 
 
+def fp64_attention(q, k, v, ctx, off, sample, scale):
+    """Exact attention of the sampled sequences in FP64 on the unquantized BF16
+    keys and values (the reference the variants' error is measured against):
+    out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over positions [0, ctx_b)."""
+    import torch
+    outs = []
+    Hq, Hkv = q.shape[1], k.shape[1]
+    for b in sample:
+        n = int(ctx[b])
+        K = k[int(off[b]):int(off[b]) + n].double()  # [n][Hkv][128]
+        V = v[int(off[b]):int(off[b]) + n].double()
+        Q = q[int(b)].double().view(Hkv, Hq // Hkv, 128)              # [Hkv][G][128]
+        Kt = K.permute(1, 2, 0).contiguous()                             # [Hkv][128][n]
+        Vg = V.permute(1, 0, 2).contiguous()                             # [Hkv][n][128]
+        p = torch.softmax(torch.matmul(Q, Kt) * scale, dim=-1)          # [Hkv][G][n]
+        outs.append(torch.matmul(p, Vg).reshape(Hq, 128))
+    return torch.stack(outs)
+
+
+def variant_leg(wl, layers, sh, ctx, scale, steps, t_bf16):
+    """Protection-budget variants through the same kernels (unprotected KV4,
+    all-sink, all-recent, and the default split): the side rows of every layer
+    are rebuilt for each budget (the INT4 pages do not depend on it), then the
+    36-layer decode is timed, the main kernel is timed with HIP events, and the
+    output of layer 0 on sampled sequences is compared with exact FP64
+    attention."""
+    import numpy as np
+    import torch
+
+    import int8_mixed_precision_kv4_amd as kv4
+    from synth import draw_values
+
+    dev = ctx.device
+    table, slots, off = sh["table"], sh["slots"], sh["offsets"]
+    B, Hq = wl.B, wl.Hq
+    lead = wl.ctx - 1
+    n_tok = int(wl.ctx.sum())
+    rows_lead = torch.from_numpy(np.concatenate(
+        [np.arange(off[b], off[b] + lead[b]) for b in range(B)])).to(dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lead)]).astype(np.int32)).to(dev)
+    zeros = torch.zeros(B, dtype=torch.int32, device=dev)
+    pos = (ctx - 1).contiguous()
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(kv4.decode_workspace_bytes(layers[0]["cache"], B, Hq, wl.max_ctx),
+                     dtype=torch.uint8, device=dev)
+    order = np.argsort(wl.ctx, kind="stable")
+    sample = np.unique(np.concatenate([order[:2], order[-2:], order[::max(1, B // 8)][:8]]))
+    k0, v0 = layers[0]["k_all"], layers[0]["v_all"]
+    ref = fp64_attention(layers[0]["q"], k0, v0, wl.ctx, off, sample, scale)
+    sel = torch.from_numpy(sample).to(dev)
+    res = {}
+    for s, w in ((0, 0), (144, 0), (0, 144), (16, 128)):
+        name = "kv4" if s + w == 0 else f"kv4rl_s{s}_w{w}"
+        log(f"variant {name}: rebuilding side rows of {wl.layers} layers")
+        caches = []
+        for li, L in enumerate(layers):
+            c = L["cache"]
+            vc = kv4.Kv4Cache(c.pages, c.side_codes, c.side_scales, sink=s, window=w)
+            if li == 0:
+                k, v = k0, v0
+            else:
+                k, v, _ = draw_values(wl.seed, li, n_tok, B, Hq, wl.Hkv, device=dev)
+            c.side_codes.zero_()
+            c.side_scales.zero_()
+            kv4.prefill_quantize(vc, k[rows_lead].contiguous(), v[rows_lead].contiguous(), cu, zeros,
+                                 slots, table, int(lead.max()))
+            kv4.append(vc, L["k_app"], L["v_app"], pos, slots, table)
+            del k, v
+            caches.append(vc)
+        torch.cuda.synchronize()
+
+        def dstep():
+            for vc, L in zip(caches, layers):
+                kv4.decode_attention(vc, L["q"], ctx, slots, table, wl.max_ctx, scale, out, lse, ws)
+
+        for _ in range(2):
+            dstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            dstep()
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / steps
+        evs = HipEvents(len(caches))
+        for i, (vc, L) in enumerate(zip(caches, layers)):
+            e0, e1 = evs.pair(i)
+            kv4.decode_attention_timed(vc, L["q"], ctx, slots, table, wl.max_ctx, scale, out, lse,
+                                       ws, e0, e1)
+        torch.cuda.synchronize()
+        main_us = float(np.mean([evs.elapsed_ms(i) for i in range(len(caches))])) * 1e3
+        evs.close()
+        kv4.decode_attention(caches[0], layers[0]["q"], ctx, slots, table, wl.max_ctx, scale, out,
+                             lse, ws)
+        torch.cuda.synchronize()
+        err = (out[sel].double() - ref).abs()
+        res[name] = dict(sink=s, window=w, decode_ms_per_step=round(t * 1e3, 3),
+                         decode_tokens_per_s=round(B / t, 1), main_kernel_us=round(main_us, 2),
+                         speedup_vs_bf16=round(t_bf16 / t, 3) if t_bf16 else None,
+                         err_vs_fp64_maxabs=float(err.max()), err_vs_fp64_meanabs=float(err.mean()))
+        log(f"variant {name}: {t * 1e3:.3f} ms/step, main {main_us:.1f} us, "
+            f"max err vs FP64 {float(err.max()):.3e}")
+    for name in res:
+        res[name]["throughput_vs_kv4"] = round(res["kv4"]["decode_ms_per_step"] /
+                                               res[name]["decode_ms_per_step"], 4)
+    return dict(workload="qwen8b decode step, 36 layers, decode only",
+                error_sample=(f"layer 0, sequences {sample.tolist()}, all {Hq} heads, vs exact FP64 "
+                              "attention on the unquantized BF16 K/V"),
+                budgets=res)
+
+
 def cpu_baseline(wl, layer0, shared, budget_s):
     """The oracle as it stands, on the host cores, on layer 0 of the step (all
     256 sequences): one append + one 32-head decode, repeated until about
@@ -259,6 +370,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the 2 GiB device copy probe")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the protection-budget variants (run last; they rebuild the side rows)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -350,6 +463,7 @@ def main():
         if rec.get("source_hash") == source_hash():
             traffic = rec.get("bytes_per_launch")
 
+    t_bf16 = None
     if not args.no_bf16:
         log("timing the BF16 paged decode comparator")
         bws = torch.empty(kv4.bf16_workspace_bytes(B, Hq, wl.Hkv, wl.max_ctx), dtype=torch.uint8,
@@ -410,6 +524,9 @@ def main():
         got = out[torch.from_numpy(sample).to(dev)].cpu().numpy()
         extra["sample_parity_out_maxabs"] = float(np.abs(got - ref_out).max())
         extra["sample_parity_lse_maxabs"] = float(np.abs(lse[torch.from_numpy(sample).to(dev)].cpu().numpy() - ref_lse).max())
+
+    if not args.no_variants:
+        extra["variants"] = variant_leg(wl, layers, sh, ctx, scale, max(3, args.steps // 2), t_bf16)
 
     mb = metric_bytes(wl.ctx, wl.Hkv)
     rec = {

@@ -6,8 +6,11 @@
  *   - every cached position of K and V is group-affine INT4 (one group per
  *     128-dim token-head vector, x^ = delta*c + m, FP16 delta and m computed on
  *     line), 4.25 bits per element; keys are Hadamard-rotated after RoPE;
- *   - the first 16 (sink) and last 128 (recent) positions also have an INT8
- *     copy in a fixed-capacity side buffer; leaving the window rewrites nothing;
+ *   - the first s (sink) and last w (recent) positions also have an INT8 copy
+ *     in a fixed-capacity side buffer (s = 16, w = 128 in the pages' main
+ *     configuration; other budgets, s = w = 0 included, are the allocation
+ *     comparisons of their figures 3 and 4(b)); leaving the window rewrites
+ *     nothing;
  *   - one decode step quantizes the rotated query to INT8 once, runs integer
  *     QK and integer PV over the INT4 main region and INT8 QK / BF16 V / FP32 PV
  *     over the protected region, and merges the two exactly.
@@ -43,9 +46,10 @@ extern "C" {
 enum {
   KV4_OK = 0,
   KV4_ERR_NULLPTR = -1,     /* a required pointer is NULL */
-  KV4_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_size != 16, sink != 16,
-                               window != 128, Hq % Hkv != 0 or Hq / Hkv != 4,
-                               or abi_version mismatch */
+  KV4_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_size != 16, sink < 0,
+                               window < 0, sink % 16 != 0, sink + window > 144,
+                               Hq % Hkv != 0 or Hq / Hkv != 4, or abi_version
+                               mismatch */
   KV4_ERR_SHAPE = -3,       /* a size is out of range (B <= 0, max_ctx > pt_stride*16,
                                B * num_kv_heads * (max_ctx/16 + 1) > INT32_MAX, ...) */
   KV4_ERR_WORKSPACE = -4,   /* workspace missing or smaller than kv4_decode_workspace_bytes */
@@ -60,8 +64,8 @@ enum {
  *                8j..8j+7, position 2k in the low nibble of byte k, 2k+1 in
  *                the high nibble) | 16 x {delta, m} FP16 for K | same for V.
  *   side_codes   int8  [max_slots][num_kv_heads][144][2][128]: INT8 copies,
- *                K (rotated) then V, of sink positions (row p for p < 16) and
- *                recent positions (row 16 + p mod 128).
+ *                K (rotated) then V, of sink positions (row p for p < s) and
+ *                recent positions (row s + p mod w); rows past s + w unused.
  *   side_scales  fp16  [max_slots][num_kv_heads][144][2]: their scales. */
 typedef struct kv4_cache_desc {
   int32_t abi_version; /* KV4_ABI_VERSION */
@@ -69,8 +73,10 @@ typedef struct kv4_cache_desc {
   int32_t page_size;   /* must be 16 */
   int32_t num_kv_heads;
   int32_t head_dim;    /* must be 128 */
-  int32_t sink;        /* must be 16 */
-  int32_t window;      /* must be 128 */
+  int32_t sink;        /* s: protected leading positions, a multiple of 16 (16) */
+  int32_t window;      /* w: protected recent positions (128); s + w <= 144.
+                          s = w = 0 is unprotected KV4.  A cache must be
+                          written and read with the same s and w. */
   int32_t max_slots;
   void *pages;
   void *side_codes;
@@ -85,7 +91,7 @@ typedef struct kv4_cache_desc {
  *               pos/16 must name a page owned by sequence b
  * Writes the INT4 codes and FP16 delta/m of K (rotated) and V into slot pos%16
  * of page page_table[b][pos/16], and the INT8 side row of pos (sinks for
- * pos < 16, the recent ring otherwise).  The INT4 entry of the position
+ * pos < s, the recent ring otherwise; none when pos >= s and w = 0).  The INT4 entry of the position
  * leaving the window is not touched.  Two entries of one call must not write
  * the same position. */
 int kv4_append(const kv4_cache_desc *cache, const void *k, const void *v, const int32_t *pos,
@@ -119,8 +125,8 @@ size_t kv4_decode_workspace_bytes(const kv4_cache_desc *cache, int32_t B, int32_
  *   out        fp32 [B][Hq][128], attention output
  *   lse        fp32 [B][Hq], natural-log normaliser of the softmax
  *   workspace  device scratch of at least kv4_decode_workspace_bytes bytes
- * Positions [16, ctx_len-128) are read from the INT4 pages; [0, 16) and
- * [max(16, ctx_len-128), ctx_len) from the INT8 side rows. */
+ * Positions [s, ctx_len-w) are read from the INT4 pages; [0, min(s, ctx_len))
+ * and [max(s, ctx_len-w), ctx_len) from the INT8 side rows. */
 int kv4_decode_attention(const kv4_cache_desc *cache, const void *q, const int32_t *ctx_len,
                          const int32_t *slot, const int32_t *page_table, int32_t pt_stride,
                          int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale, float *out,
@@ -134,7 +140,7 @@ int kv4_decode_attention(const kv4_cache_desc *cache, const void *q, const int32
  *   qk      int32 [B][Hq][max_ctx]  integer Q.K of each attended position
  *   pcode   uint8 [B][Hq][max_ctx]  P-operand code of each main position
  *   pv      int32 [B][Hq][max_pages][128]  integer P.V accumulators of the
- *                                 main tile on logical page j (j >= 1) */
+ *                                 main tile on logical page j (j >= s/16) */
 typedef struct kv4_decode_debug {
   int8_t *qcodes;
   int32_t *qsum;

@@ -88,26 +88,31 @@ def _stream():
 
 
 class Kv4Cache:
-    """One layer's cache: paged INT4 pool + INT8 side buffer (device tensors)."""
+    """One layer's cache: paged INT4 pool + INT8 side buffer (device tensors).
+    sink / window: the protection budget s, w (the library checks s % 16 == 0
+    and s + w <= 144)."""
 
-    def __init__(self, pages: torch.Tensor, side_codes: torch.Tensor, side_scales: torch.Tensor):
+    def __init__(self, pages: torch.Tensor, side_codes: torch.Tensor, side_scales: torch.Tensor,
+                 sink: int = SINK, window: int = WINDOW):
         self.pages, self.side_codes, self.side_scales = pages, side_codes, side_scales
+        self.sink, self.window = int(sink), int(window)
         self.num_pages, self.num_kv_heads = int(pages.shape[0]), int(pages.shape[1])
         self.max_slots = int(side_codes.shape[0])
         assert pages.shape[2] == BLOCK_BYTES and pages.dtype == torch.uint8
         assert tuple(side_codes.shape[1:]) == (self.num_kv_heads, SIDE_ROWS, 2, HEAD_DIM)
         assert tuple(side_scales.shape[1:]) == (self.num_kv_heads, SIDE_ROWS, 2)
-        self._desc = _Desc(ABI_VERSION, self.num_pages, PAGE, self.num_kv_heads, HEAD_DIM, SINK,
-                           WINDOW, self.max_slots, pages.data_ptr(), side_codes.data_ptr(),
+        self._desc = _Desc(ABI_VERSION, self.num_pages, PAGE, self.num_kv_heads, HEAD_DIM,
+                           self.sink, self.window, self.max_slots, pages.data_ptr(), side_codes.data_ptr(),
                            side_scales.data_ptr())
 
     @classmethod
-    def zeros(cls, num_pages: int, num_kv_heads: int, max_slots: int, device="cuda"):
+    def zeros(cls, num_pages: int, num_kv_heads: int, max_slots: int, device="cuda",
+              sink: int = SINK, window: int = WINDOW):
         return cls(torch.zeros((num_pages, num_kv_heads, BLOCK_BYTES), dtype=torch.uint8, device=device),
                    torch.zeros((max_slots, num_kv_heads, SIDE_ROWS, 2, HEAD_DIM), dtype=torch.int8,
                                device=device),
                    torch.zeros((max_slots, num_kv_heads, SIDE_ROWS, 2), dtype=torch.int16,
-                               device=device))
+                               device=device), sink, window)
 
     def desc(self):
         return C.byref(self._desc)

@@ -26,7 +26,7 @@ int hip_fail(hipError_t e) {
 int check_cache(const kv4_cache_desc* c) {
   if (!c) return KV4_ERR_NULLPTR;
   if (c->abi_version != KV4_ABI_VERSION || c->page_size != 16 || c->head_dim != 128 ||
-      c->sink != 16 || c->window != 128)
+      c->sink < 0 || c->window < 0 || c->sink % 16 != 0 || c->sink + c->window > kv4::SIDE_ROWS)
     return KV4_ERR_UNSUPPORTED;
   if (c->num_pages <= 0 || c->num_kv_heads <= 0 || c->max_slots <= 0) return KV4_ERR_SHAPE;
   if (!c->pages || !c->side_codes || !c->side_scales) return KV4_ERR_NULLPTR;
@@ -36,7 +36,7 @@ int check_cache(const kv4_cache_desc* c) {
 kv4::CacheView view(const kv4_cache_desc* c) {
   return kv4::CacheView{static_cast<uint8_t*>(c->pages), static_cast<int8_t*>(c->side_codes),
                         static_cast<uint16_t*>(c->side_scales), c->num_pages, c->num_kv_heads,
-                        c->max_slots};
+                        c->max_slots, c->sink, c->window};
 }
 
 // softmax in base 2: logits carry softmax_scale * log2(e)
@@ -87,8 +87,8 @@ const char* kv4_strerror(int status) {
     case KV4_OK: return "success";
     case KV4_ERR_NULLPTR: return "a required pointer is NULL";
     case KV4_ERR_UNSUPPORTED:
-      return "unsupported configuration (needs abi_version 1, page 16, head_dim 128, sink 16, "
-             "window 128, Hq/Hkv = 4)";
+      return "unsupported configuration (needs abi_version 1, page 16, head_dim 128, "
+             "sink a multiple of 16, sink + window <= 144, Hq/Hkv = 4)";
     case KV4_ERR_SHAPE: return "a size argument is out of range";
     case KV4_ERR_WORKSPACE: return "workspace missing or smaller than kv4_decode_workspace_bytes";
     case KV4_ERR_HIP: return g_hip_error;

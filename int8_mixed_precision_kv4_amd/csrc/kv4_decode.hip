@@ -36,6 +36,7 @@ struct DecArgs {
   const int32_t* slot;
   const int32_t* page_table;
   int pt_stride;
+  int sink, window;  // protection budget s, w
   float scale_log2;
   float* out;
   float* lse;
@@ -43,8 +44,11 @@ struct DecArgs {
   DecodeDebug dbg;
 };
 
-// Main region M = [16, L-128) covers logical pages 1 .. (L-129)/16.
-__device__ __forceinline__ int main_pages(int L) { return L > SIDE_ROWS ? (L - 129) / PAGE : 0; }
+// Main region M = [s, L-w) covers logical pages s/16 .. (L-w-1)/16 (s is a
+// multiple of 16, so the first page starts at s).
+__device__ __forceinline__ int main_pages(int L, int s, int w) {
+  return L - w > s ? (L - w - 1) / PAGE - s / PAGE + 1 : 0;
+}
 
 // plan[b] = sum over earlier sequences of main_pages * Hkv (one workgroup).
 __device__ void build_plan(const DecArgs& a) {
@@ -57,7 +61,7 @@ __device__ void build_plan(const DecArgs& a) {
   __syncthreads();
   for (int base = 0; base < a.B; base += 256) {
     const int b = base + threadIdx.x;
-    scan[threadIdx.x] = (b < a.B) ? main_pages(a.ctx[b]) * a.Hkv : 0;
+    scan[threadIdx.x] = (b < a.B) ? main_pages(a.ctx[b], a.sink, a.window) * a.Hkv : 0;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
       const int t = (threadIdx.x >= off) ? scan[threadIdx.x - off] : 0;
@@ -163,11 +167,13 @@ __device__ __forceinline__ int qk_rows(v4i d) {
 
 // ------------------------------------------------------------ protected --
 
-// Position held by side row r when the context is L (-1: row not in use).
-__device__ __forceinline__ int side_position(int r, int L) {
-  if (r < SINK) return r < L ? r : -1;
-  const int base = max(SINK, L - WINDOW);
-  const int p = base + ((r - SINK - base) % WINDOW + WINDOW) % WINDOW;
+// Position held by side row r when the context is L, for sinks [0, s) and a
+// ring of w recent positions in rows [s, s+w) (-1: row not in use).
+__device__ __forceinline__ int side_position(int r, int L, int s, int w) {
+  if (r < s) return r < L ? r : -1;
+  if (r >= s + w) return -1;
+  const int base = max(s, L - w);
+  const int p = base + ((r - s - base) % w + w) % w;
   return p < L ? p : -1;
 }
 
@@ -183,8 +189,9 @@ __device__ __forceinline__ void round_bf16x2(float& x, float& y) {
 
 // Protected-region partial of one (kv-head g, sequence b), computed by one
 // workgroup of the main kernel (the last B*Hkv workgroups of its grid, which
-// the dispatcher starts as main-region workgroups retire).  QK: 9 MFMA row
-// groups of 16 side rows spread over the 4 waves.  Softmax: wave h for head h.
+// the dispatcher starts as main-region workgroups retire; none when s = w = 0).
+// Only rows [0, s+w) are read.  QK: up to 9
+// MFMA row groups of 16 side rows spread over the 4 waves.  Softmax: wave h for head h.
 // PV: wave w takes rows [36w, 36w+36), lane (rp, cg) rows 36w + rp + 2i and
 // channels 4cg..4cg+3 for all 4 heads; the 2 row phases of a wave are reduced
 // with a permlane swap and the 4 waves through LDS.  Wave h writes the
@@ -203,6 +210,7 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   float* cqs = reinterpret_cast<float*>(qn + GQA * HD);                                                    // [4]
 
   const int L = ld_const(a.ctx + b);
+  const int nrows = a.sink + a.window;  // rows [0, s+w) can hold the region
   const int slot = a.slot ? ld_const(a.slot + b) : b;
   const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
   const gptr side = (gptr)a.side_codes + row0 * 2 * HD;
@@ -217,7 +225,9 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     const int rg = wave + 4 * k;
-    if (rg < SIDE_ROWS / 16) {
+    kop[k][0] = kop[k][1] = v4i{0, 0, 0, 0};
+    sk[k] = 0.0f;
+    if (rg < SIDE_ROWS / 16 && 16 * rg < nrows) {
       const gptr krow = side + (16 * rg + r16) * 2 * HD;
       kop[k][0] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 16 * grp);
       kop[k][1] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 64 + 16 * grp);
@@ -230,10 +240,10 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
 #pragma unroll
   for (int i = 0; i < kRowsPerWave / 2; ++i) {
     const int r = kRowsPerWave * wave + rp + 2 * i;
-    vop[i] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(side + (2 * r + 1) * HD + 4 * cg);
+    vop[i] = r < nrows ? *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(side + (2 * r + 1) * HD + 4 * cg) : 0u;
   }
   if (tid < SIDE_ROWS)
-    ssv[tid] = side_position(tid, L) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
+    ssv[tid] = side_position(tid, L, a.sink, a.window) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
   // Query of head `wave`: rotate like the keys, then symmetric INT8 with an
   // FP32 scale (lane l holds channels 2l, 2l+1); codes in natural order to LDS.
   {
@@ -276,7 +286,7 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
       d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], kop[k][1], d, 0, 0, 0);
       const int D8 = qk_rows(d);
       const int r = 16 * rg + r16;
-      const int p = side_position(r, L);
+      const int p = side_position(r, L, a.sink, a.window);
       se[r][grp] = (p >= 0) ? (static_cast<float>(D8) * sk[k]) * c_q : -INFINITY;
       if (DEBUG && a.dbg.qk && p >= 0) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + p] = D8;
     }
@@ -558,7 +568,7 @@ __device__ __forceinline__ PlanView plan_view(const DecArgs& a, int lane) {
   for (int k = 0; k < 4; ++k) {
     const int i = 4 * lane + k;
     const int L = a.ctx[min(i, a.B - 1)];
-    m[k] = i < a.B ? main_pages(L) * a.Hkv : 0;
+    m[k] = i < a.B ? main_pages(L, a.sink, a.window) * a.Hkv : 0;
   }
   m[1] += m[0];
   m[2] += m[1];
@@ -642,8 +652,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   float2 nqi = make_float2(0.0f, 0.0f);
   uint4 raw1 = make_uint4(0, 0, 0, 0), raw2 = make_uint4(0, 0, 0, 0);
   auto group_query = [&](const QuadDesc& d, const uint4& raw) {
-    (void)d;
     const GroupQuery gq = quantize_group_query(raw, a.scale_log2, r16);
+    if (DEBUG) {  // lane (grp, r16) holds rotated channels 8 r16 .. 8 r16 + 7 (same values from every piece)
+      const size_t bh = static_cast<size_t>(d.b) * a.Hq + d.g * GQA + grp;
+      if (a.dbg.qcodes)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a.dbg.qcodes[bh * HD + 8 * r16 + j] = static_cast<int8_t>(gq.c[j]);
+      if (a.dbg.qsum && r16 == 0) a.dbg.qsum[bh] = gq.S;
+    }
     // A operand of QK: rows 0..3 = the group's heads, k = channels (lane
     // group grp covers channels 32grp..32grp+31, even / odd split); the codes
     // go through the slot's query area to reach that layout.
@@ -680,7 +696,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     const int stop = min(iend, seg_end);
     d.b = ib;
     d.g = seg_g;
-    d.j0 = 1 + (ip - seg0);
+    d.j0 = a.sink / PAGE + (ip - seg0);
     d.np = min(4, stop - ip);
     d.slot = w + ib * a.Hkv + seg_g;
     d.first = (ip == chunk0) || (ip == seg0);
@@ -702,7 +718,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     for (int t = 0; t < 4; ++t)
       blk[t] = gbase + static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(pt, t))) * pstride;
     quad_to_lds(slot, blk, lane, r16, grp);
-    if (d.first) d.main_end = ld_const(a.ctx + d.b) - WINDOW;
+    if (d.first) d.main_end = ld_const(a.ctx + d.b) - a.window;
   };
 
   // Pipeline: quad i is computed while quad i+1 streams into the LDS slot
@@ -790,20 +806,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   if (pend) store_partial();
 }
 
-// Exact log-sum-exp merge of the protected partial and the main partials of
-// each head, one workgroup per (kv-head g, sequence b), wave h for head h,
-// lane l for channels 2l, 2l+1.  Writes out and lse.
+// Exact log-sum-exp merge of the protected partial (none when s = w = 0) and
+// the main partials of each head, one workgroup per (kv-head g, sequence b),
+// wave h for head h, lane l for channels 2l, 2l+1.  Writes out and lse.
 __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const size_t bh = static_cast<size_t>(b) * a.Hq + g * GQA + wave;
-  const float* Pp = a.ws.prot + bh * kPart;
-  float2 Am = reinterpret_cast<const float2*>(Pp)[lane];
-  float Zm = Pp[128], lm = Pp[129];
+  float2 Am = make_float2(0.0f, 0.0f);
+  float Zm = -INFINITY, lm = 0.0f;
+  if (a.sink + a.window > 0) {
+    const float* Pp = a.ws.prot + bh * kPart;
+    Am = reinterpret_cast<const float2*>(Pp)[lane];
+    Zm = Pp[128];
+    lm = Pp[129];
+  }
   // main partials: chunks c_lo..c_hi (recorded by the main kernel) at slots c + b*Hkv + g
   const int bg = b * a.Hkv + g;
   const int2 cr = a.ws.mrange[bg];  // written by the main kernel when the segment has pages
-  const int c_lo = cr.x, n_parts = main_pages(ld_const(a.ctx + b)) > 0 ? cr.y - cr.x + 1 : 0;
+  const int c_lo = cr.x, n_parts = main_pages(ld_const(a.ctx + b), a.sink, a.window) > 0 ? cr.y - cr.x + 1 : 0;
   constexpr int kBatch = 4;
   for (int k0 = 0; k0 < n_parts; k0 += kBatch) {
     float2 Ac[kBatch];
@@ -881,13 +902,16 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   a.slot = slot;
   a.page_table = page_table;
   a.pt_stride = pt_stride;
+  a.sink = c.sink;
+  a.window = c.window;
   a.scale_log2 = scale_log2;
   a.out = out;
   a.lse = lse;
   a.ws = ws;
   if (dbg) a.dbg = *dbg;
   // main-region workgroups, then one protected-region workgroup per (b, g)
-  const dim3 block(256), groups(c.Hkv, B), grid(ws.n_waves / 4 + B * c.Hkv);
+  const int prot_groups = c.sink + c.window > 0 ? B * c.Hkv : 0;
+  const dim3 block(256), groups(c.Hkv, B), grid(ws.n_waves / 4 + prot_groups);
   if (B > 256) hipLaunchKernelGGL(plan_kernel, dim3(1), block, 0, s, a);
   if (dbg) {
     hipLaunchKernelGGL(main_kernel<true>, grid, block, 0, s, a);

@@ -11,9 +11,7 @@ namespace kv4 {
 
 constexpr int HD = 128;          // one quantization group = one 128-dim token-head vector
 constexpr int PAGE = 16;         // positions per page
-constexpr int SINK = 16;         // protected leading positions
-constexpr int WINDOW = 128;      // protected recent positions
-constexpr int SIDE_ROWS = SINK + WINDOW;
+constexpr int SIDE_ROWS = 144;   // side-buffer rows per (slot, kv-head): sink + window <= 144
 constexpr int BLOCK_BYTES = 2176;  // per (page, kv-head): 16 x (64 + 64 + 4 + 4)
 constexpr int OFF_VCODE = 1024;
 constexpr int OFF_KMETA = 2048;

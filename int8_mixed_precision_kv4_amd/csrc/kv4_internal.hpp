@@ -13,6 +13,7 @@ struct CacheView {
   int8_t* side_codes;
   uint16_t* side_scales;
   int num_pages, Hkv, max_slots;
+  int sink, window;  // protection budget s, w (s % 16 == 0, s + w <= 144)
 };
 
 struct DecodeDebug {

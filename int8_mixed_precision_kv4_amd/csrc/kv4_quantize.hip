@@ -3,10 +3,11 @@
 //
 // Each K vector is rotated (Hadamard after RoPE), then K and V are quantized
 // independently to group-affine INT4 (one group per 128-dim token-head
-// vector, FP16 delta and offset computed on line) into their page slot; sink
-// positions (< 16) and recent positions also get a symmetric INT8 copy in the
-// side buffer.  A position leaving the recent window keeps its INT4 entry; its
-// ring row is simply reused.
+// vector, FP16 delta and offset computed on line) into their page slot; the s
+// sink positions and the w recent positions (s = 16, w = 128 by default) also
+// get a symmetric INT8 copy in the side buffer, sinks in rows [0, s) and
+// position p >= s in ring row s + (p mod w).  A position leaving the recent
+// window keeps its INT4 entry; its ring row is simply reused.
 #include "kv4_device.hpp"
 #include "kv4_internal.hpp"
 
@@ -23,14 +24,18 @@ struct QuantArgs {
   const int32_t* slot;
   const int32_t* page_table;
   int pt_stride;
+  int sink, window;
 };
 
-__device__ __forceinline__ int side_row(int p) { return p < SINK ? p : SINK + (p % WINDOW); }
+// Side row of position p; only called for p < sink or window > 0.
+__device__ __forceinline__ int side_row(const QuantArgs& a, int p) {
+  return p < a.sink ? p : a.sink + (p % a.window);
+}
 
 // INT8 side row of one position (K rotated, V), held by one wave.
 __device__ __forceinline__ void write_side_row(const QuantArgs& a, int slot, int g, int pos,
                                                float k0, float k1, float v0, float v1, int lane) {
-  const size_t r = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS + side_row(pos);
+  const size_t r = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS + side_row(a, pos);
   const Int8Meta ks = int8_meta(wave_max(fmaxf(fabsf(k0), fabsf(k1))));
   const Int8Meta vs = int8_meta(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
   const uint32_t kp = (static_cast<uint32_t>(int8_code(k0, ks)) & 0xFFu) |
@@ -77,14 +82,14 @@ __global__ __launch_bounds__(64) void append_kernel(QuantArgs a, const int32_t* 
     *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
     *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
   }
-  write_side_row(a, slot, g, pos, k0, k1, v0, v1, lane);
+  if (pos < a.sink || a.window > 0) write_side_row(a, slot, g, pos, k0, k1, v0, v1, lane);
 }
 
 // Re-prefill: one workgroup owns one (page, kv-head) block of one sequence, so
 // nibble bytes shared by neighbouring positions have a single writer.  Side
 // rows are written only where appends would leave them in the final state:
-// sinks, and the last 128 positions of the range (earlier ring rows would be
-// overwritten within the same range anyway).
+// sinks, and the last w positions of the range (earlier ring rows would be
+// overwritten within the same range anyway; none when w = 0).
 __global__ __launch_bounds__(256) void prefill_kernel(QuantArgs a, const int32_t* __restrict__ cu,
                                                       const int32_t* __restrict__ start_pos) {
   const int lp = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(QuantArgs a, const int32_t
   const int slot = a.slot ? a.slot[s] : s;
   const int phys = a.page_table[static_cast<size_t>(s) * a.pt_stride + page];
   uint8_t* blk = a.pages + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
-  const int keep_from = max(SINK, end - WINDOW);
+  const int keep_from = max(a.sink, end - a.window);  // == end when w = 0
 
   __shared__ uint8_t vcodes[PAGE][HD];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(QuantArgs a, const int32_t
       *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
       *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
     }
-    if (p < SINK || p >= keep_from) write_side_row(a, slot, g, p, k0, k1, v0, v1, lane);
+    if (p < a.sink || p >= keep_from) write_side_row(a, slot, g, p, k0, k1, v0, v1, lane);
   }
   __syncthreads();
   // V codes, channel-major: thread -> channel j, positions 8*half .. 8*half+7
@@ -141,7 +146,7 @@ hipError_t launch_append(const CacheView& c, const uint16_t* k, const uint16_t* 
                          int pt_stride, int B, hipStream_t s) {
   QuantArgs a{c.pages, c.side_codes, c.side_scales, c.Hkv,
               reinterpret_cast<const uint32_t*>(k), reinterpret_cast<const uint32_t*>(v),
-              slot, page_table, pt_stride};
+              slot, page_table, pt_stride, c.sink, c.window};
   hipLaunchKernelGGL(append_kernel, dim3(c.Hkv, B), dim3(64), 0, s, a, pos);
   return hipGetLastError();
 }
@@ -152,7 +157,7 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t*
                           hipStream_t s) {
   QuantArgs a{c.pages, c.side_codes, c.side_scales, c.Hkv,
               reinterpret_cast<const uint32_t*>(k), reinterpret_cast<const uint32_t*>(v),
-              slot, page_table, pt_stride};
+              slot, page_table, pt_stride, c.sink, c.window};
   const int pages = (max_seqlen + PAGE - 1) / PAGE + 1;
   hipLaunchKernelGGL(prefill_kernel, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
   return hipGetLastError();

@@ -24,9 +24,9 @@ def i32(a, dev):
 class GpuCase:
     """Device-side state of one workload layer."""
 
-    def __init__(self, wl, hi, dev="cuda", use_prefill=True):
+    def __init__(self, wl, hi, dev="cuda", use_prefill=True, sink=kv4.SINK, window=kv4.WINDOW):
         self.wl, self.hi, self.dev = wl, hi, torch.device(dev)
-        self.cache = kv4.Kv4Cache.zeros(wl.num_pages, wl.Hkv, wl.max_slots, self.dev)
+        self.cache = kv4.Kv4Cache.zeros(wl.num_pages, wl.Hkv, wl.max_slots, self.dev, sink, window)
         self.table = i32(wl.page_table, self.dev)
         self.slots = i32(wl.slots, self.dev)
         self.ctx = i32(wl.ctx, self.dev)

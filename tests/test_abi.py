@@ -54,3 +54,22 @@ def test_host_validation_rejects_bad_arguments_without_gpu():
     assert L.kv4_append(ctypes.byref(d), 1, 1, 1, None, 1, 1, 1, None) == -2
     d = kv4._Desc(1, 4, 16, 1, 128, 16, 128, 1, 1, 1, 1)
     assert L.kv4_append(ctypes.byref(d), 1, 1, 1, None, 1, 1, 0, None) == -3
+
+
+@pytest.mark.parametrize("sink,window,ok", [
+    (16, 128, True), (0, 0, True), (144, 0, True), (0, 144, True), (32, 64, True),
+    (8, 0, False), (16, 129, False), (-16, 0, False), (0, -1, False), (160, 0, False)])
+def test_host_validation_of_the_protection_budget(sink, window, ok):
+    """A budget is accepted when s is a non-negative multiple of 16, w >= 0 and
+    s + w <= 144 (then a NULL k is what fails); otherwise refused as
+    unsupported before any HIP call."""
+    import int8_mixed_precision_kv4_amd as kv4
+    if not os.path.exists(kv4.LIB_PATH):
+        pytest.skip("libkv4.so not built")
+    L = kv4.lib()
+    d = kv4._Desc(1, 4, 16, 1, 128, sink, window, 1, 1, 1, 1)
+    want = -1 if ok else -2
+    assert L.kv4_append(ctypes.byref(d), None, 1, 1, None, 1, 1, 1, None) == want
+    assert L.kv4_prefill_quantize(ctypes.byref(d), None, 1, 1, 1, None, 1, 1, 1, 1, None) == want
+    assert L.kv4_decode_attention(ctypes.byref(d), None, 1, None, 1, 1, 1, 4, 16, 1.0, 1, 1, 1, 1,
+                                  None) == want
