@@ -29,6 +29,10 @@ class _Cache(C.Structure):
                 ("sink", C.c_int32), ("window", C.c_int32)]
 
 
+class _Kv8Cache(C.Structure):
+    _fields_ = [("num_pages", C.c_int32), ("num_kv_heads", C.c_int32), ("pages", C.c_void_p)]
+
+
 class _Debug(C.Structure):
     _fields_ = [("qcodes", C.c_void_p), ("qsum", C.c_void_p), ("qk", C.c_void_p),
                 ("pcode", C.c_void_p), ("pv", C.c_void_p), ("max_ctx", C.c_int32),
@@ -56,6 +60,11 @@ def lib():
         _lib.kv4ref_quant_query.argtypes = [C.c_void_p] * 4 + [C.c_int64]
         _lib.kv4ref_exp2s_coeffs.argtypes = [C.c_void_p]
         _lib.kv4ref_append.argtypes = [C.POINTER(_Cache)] + [C.c_void_p] * 5 + [C.c_int32] * 2
+        K8 = C.POINTER(_Kv8Cache)
+        _lib.kv8ref_append.argtypes = [K8] + [C.c_void_p] * 4 + [C.c_int32] * 2
+        _lib.kv8ref_prefill.argtypes = [K8] + [C.c_void_p] * 5 + [C.c_int32] * 3
+        _lib.kv8ref_decode.argtypes = ([K8] + [C.c_void_p] * 3 + [C.c_int32] * 3 + [C.c_float]
+                                       + [C.c_void_p] * 2 + [C.POINTER(_Debug), C.c_int32])
         _lib.kv4ref_prefill.argtypes = ([C.POINTER(_Cache)] + [C.c_void_p] * 6
                                         + [C.c_int32] * 3)
         _lib.kv4ref_decode.argtypes = ([C.POINTER(_Cache)] + [C.c_void_p] * 4
@@ -242,4 +251,71 @@ def decode(cache: Cache, q, ctx_len, slot, page_table, Hq: int, softmax_scale: f
                              nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"kv4ref_decode failed ({rc}): invalid head counts or protection budget")
+    return out, lse, dbg
+
+
+# ------------------------------------------------------------ KV8 variant --
+
+KV8_BLOCK, KV8_OFF_V, KV8_OFF_SK, KV8_OFF_SV = 4160, 2048, 4096, 4128
+
+
+class Kv8Cache:
+    """KV8-everywhere pool (the INT8 comparison variant) in host memory:
+    [num_pages][Hkv][4160] = K codes int8 [16][128] (rotated keys) | V codes
+    int8 [128][16] | s_k FP16 [16] | s_v FP16 [16]."""
+
+    def __init__(self, num_pages: int, Hkv: int):
+        self.pages = np.zeros((num_pages, Hkv, KV8_BLOCK), np.uint8)
+        self.num_pages, self.Hkv = num_pages, Hkv
+
+    def _struct(self):
+        return _Kv8Cache(self.num_pages, self.Hkv, _p(self.pages).value)
+
+
+def kv8_append(cache: Kv8Cache, k, v, pos, page_table):
+    k, v = _c(k, np.uint16), _c(v, np.uint16)
+    pos, table = _c(pos, np.int32), _c(page_table, np.int32)
+    B = pos.shape[0]
+    assert k.shape == (B, cache.Hkv, HD) and v.shape == k.shape
+    st = cache._struct()
+    rc = lib().kv8ref_append(C.byref(st), _p(k), _p(v), _p(pos), _p(table), table.shape[1], B)
+    if rc != 0:
+        raise ValueError(f"kv8ref_append failed ({rc})")
+
+
+def kv8_prefill(cache: Kv8Cache, k, v, cu_seqlens, start_pos, page_table, nthreads=None):
+    k, v = _c(k, np.uint16), _c(v, np.uint16)
+    cu, start, table = (_c(cu_seqlens, np.int32), _c(start_pos, np.int32),
+                        _c(page_table, np.int32))
+    assert k.shape == (int(cu[-1]), cache.Hkv, HD)
+    st = cache._struct()
+    rc = lib().kv8ref_prefill(C.byref(st), _p(k), _p(v), _p(cu), _p(start), _p(table),
+                              table.shape[1], start.shape[0], nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"kv8ref_prefill failed ({rc})")
+
+
+def kv8_decode(cache: Kv8Cache, q, ctx_len, page_table, Hq: int, softmax_scale: float,
+               debug: bool = False, nthreads=None):
+    """Every position through the protected path's arithmetic.  Returns
+    (out [B][Hq][128] f64, lse [B][Hq] f64, dbg dict with qcodes, qsum, qk or None)."""
+    q = _c(q, np.uint16)
+    ctx, table = _c(ctx_len, np.int32), _c(page_table, np.int32)
+    B = ctx.shape[0]
+    assert q.shape == (B, Hq, HD)
+    out = np.zeros((B, Hq, HD), np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+    dbg = dstruct = None
+    if debug:
+        max_ctx = int(table.shape[1]) * PAGE
+        dbg = dict(qcodes=np.zeros((B, Hq, HD), np.int8), qsum=np.zeros((B, Hq), np.int32),
+                   qk=np.zeros((B, Hq, max_ctx), np.int32))
+        dstruct = _Debug(_p(dbg["qcodes"]).value, _p(dbg["qsum"]).value, _p(dbg["qk"]).value,
+                         None, None, max_ctx, table.shape[1])
+    st = cache._struct()
+    rc = lib().kv8ref_decode(C.byref(st), _p(q), _p(ctx), _p(table), table.shape[1], B, Hq,
+                             softmax_scale, _p(out), _p(lse), C.byref(dstruct) if dstruct else None,
+                             nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"kv8ref_decode failed ({rc})")
     return out, lse, dbg

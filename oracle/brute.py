@@ -236,3 +236,38 @@ def decode_one(pages, side_codes, side_scales, Hkv, q_bits, L, slot, g, table_ro
     num = sum(2.0 ** (p[1] - Z) * p[0] for p in parts)
     den = sum(2.0 ** (p[1] - Z) * p[2] for p in parts)
     return num / den, math.log(2) * (Z + math.log2(den)), qk, pcode, pv
+
+
+def unpack_kv8_block(block: np.ndarray):
+    """Independent reading of one KV8 block (4160 bytes): K codes [16][128]
+    token-major, V codes [128][16] channel-major, then 16 FP16 key scales and
+    16 FP16 value scales.  Returns (kc [16][128], vc [16][128], sk [16], sv [16])."""
+    b = np.asarray(block, np.uint8)
+    kc = b[:2048].view(np.int8).reshape(PAGE, HD).astype(np.int64)
+    vc = b[2048:4096].view(np.int8).reshape(HD, PAGE).T.astype(np.int64)
+    sk = [_f16(int(b[4096 + 2 * t]), int(b[4097 + 2 * t])) for t in range(PAGE)]
+    sv = [_f16(int(b[4128 + 2 * t]), int(b[4129 + 2 * t])) for t in range(PAGE)]
+    return kc, vc, sk, sv
+
+
+def kv8_decode_one(pages, q_bits, L, g, table_row, scale_log2):
+    """KV8 everywhere, one (sequence, q-head): every position through the
+    protected path's rules.  Returns out[128] (f64), lse, {position: D8}."""
+    qc, s_q, _ = query_codes(q_bits)
+    c_q = f32_mul(s_q, scale_log2)
+    zs, vrows, qk = [], [], {}
+    for p in range(L):
+        kc, vc, sk, sv = unpack_kv8_block(pages[table_row[p // PAGE], g])
+        t = p % PAGE
+        d8 = int(np.dot(qc, kc[t]))
+        qk[p] = d8
+        zs.append(f32_mul(f32_mul(float(d8), sk[t]), c_q))
+        vrows.append(np.array([rnbf16(f32_mul(sv[t], float(c))) for c in vc[t]]))
+    zmax = max(zs)
+    A = np.zeros(HD)
+    ell = 0.0
+    for z, vh in zip(zs, vrows):
+        e = exp2s(f32_sub(z, zmax))
+        A += e * vh
+        ell += e
+    return A / ell, math.log(2) * (zmax + math.log2(ell)), qk

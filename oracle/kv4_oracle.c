@@ -518,9 +518,46 @@ static void main_tile(const uint8_t *blk, int t_end, const int8_t qc[HD], int32_
   }
 }
 
-/* Protected region: the same INT8 query against the INT8 side keys,
- * z = (D8 * s_k) * c_q; FP32 softmax weights relative to the region max;
- * values dequantized to BF16, v^ = bf16(s_v * c); P stays FP32. */
+/* INT8 rows of one region: position, key and value codes and FP16 scales. */
+typedef struct {
+  int32_t pos;
+  const int8_t *k8, *v8;
+  uint16_t sk, sv;
+} int8_row_t;
+
+/* The protected path's arithmetic over n INT8 rows: the INT8 query against
+ * the INT8 keys, z = (D8 * s_k) * c_q; FP32 softmax weights relative to the
+ * region max; values dequantized to BF16, v^ = bf16(s_v * c); P stays FP32. */
+static void int8_region(const int8_row_t *rows, int n, const int8_t qc[HD], float c_q,
+                        partial_t *out, int32_t *dbg_qk) {
+  out->Z = -INFINITY; /* an empty region contributes nothing */
+  out->l = 0.0;
+  for (int j = 0; j < HD; j++) out->A[j] = 0.0;
+  if (n == 0) return;
+  float *z = (float *)malloc(sizeof(float) * (size_t)n);
+  for (int i = 0; i < n; i++) {
+    int32_t D8 = 0;
+    for (int d = 0; d < HD; d++) D8 += (int32_t)qc[d] * (int32_t)rows[i].k8[d];
+    z[i] = ((float)D8 * kv4ref_f16_to_f32(rows[i].sk)) * c_q;
+    if (dbg_qk) dbg_qk[rows[i].pos] = D8;
+  }
+  float zmax = -INFINITY;
+  for (int i = 0; i < n; i++)
+    if (z[i] > zmax) zmax = z[i];
+  out->Z = zmax;
+  for (int i = 0; i < n; i++) {
+    float e = exp2s(z[i] - zmax);
+    float sv = kv4ref_f16_to_f32(rows[i].sv);
+    out->l += (double)e;
+    for (int j = 0; j < HD; j++) {
+      float vhat = kv4ref_bf16_to_f32(kv4ref_f32_to_bf16(sv * (float)rows[i].v8[j]));
+      out->A[j] += (double)e * (double)vhat;
+    }
+  }
+  free(z);
+}
+
+/* Protected region: the sinks and the recent window, read from the side rows. */
 static void protected_region(const kv4ref_cache *c, int32_t slot, int g, int32_t L,
                              const int8_t qc[HD], float c_q, partial_t *out, int32_t *dbg_qk) {
   int32_t pos[SIDE_ROWS];
@@ -531,36 +568,16 @@ static void protected_region(const kv4ref_cache *c, int32_t slot, int g, int32_t
   for (int p = 0; p < sink_end; p++) pos[n++] = p;
   for (int p = rec_begin; p < L; p++) pos[n++] = p;
   assert(n == (L < sw ? L : sw));
-  out->Z = -INFINITY; /* an empty region (s = w = 0) contributes nothing */
-  out->l = 0.0;
-  for (int j = 0; j < HD; j++) out->A[j] = 0.0;
-  if (n == 0) return;
-
-  float z[SIDE_ROWS];
+  int8_row_t rows[SIDE_ROWS];
   for (int i = 0; i < n; i++) {
     int row = side_row(c, pos[i]);
-    const int8_t *k8 = side_code_at(c, slot, g, row, 0);
-    int32_t D8 = 0;
-    for (int d = 0; d < HD; d++) D8 += (int32_t)qc[d] * (int32_t)k8[d];
-    float sk = kv4ref_f16_to_f32(*side_scale_at(c, slot, g, row, 0));
-    z[i] = ((float)D8 * sk) * c_q;
-    if (dbg_qk) dbg_qk[pos[i]] = D8;
+    rows[i].pos = pos[i];
+    rows[i].k8 = side_code_at(c, slot, g, row, 0);
+    rows[i].v8 = side_code_at(c, slot, g, row, 1);
+    rows[i].sk = *side_scale_at(c, slot, g, row, 0);
+    rows[i].sv = *side_scale_at(c, slot, g, row, 1);
   }
-  float zmax = z[0];
-  for (int i = 1; i < n; i++)
-    if (z[i] > zmax) zmax = z[i];
-  out->Z = zmax;
-  for (int i = 0; i < n; i++) {
-    int row = side_row(c, pos[i]);
-    float e = exp2s(z[i] - zmax);
-    const int8_t *v8 = side_code_at(c, slot, g, row, 1);
-    float sv = kv4ref_f16_to_f32(*side_scale_at(c, slot, g, row, 1));
-    out->l += (double)e;
-    for (int j = 0; j < HD; j++) {
-      float vhat = kv4ref_bf16_to_f32(kv4ref_f32_to_bf16(sv * (float)v8[j]));
-      out->A[j] += (double)e * (double)vhat;
-    }
-  }
+  int8_region(rows, n, qc, c_q, out, dbg_qk);
 }
 
 /* Exact log-sum-exp merge of region partials. */
@@ -633,6 +650,122 @@ int kv4ref_decode(const kv4ref_cache *c, const uint16_t *q, const int32_t *ctx_l
     }
     merge(parts, ntiles + 1, out + (size_t)bh * HD, lse + bh);
     free(parts);
+  }
+  return bad ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* KV8 everywhere: the INT8 comparison variant of the quantization-target     */
+/* comparisons (KV4-RL pages, quantization-target comparison, figure 3).     */
+/* Every position is stored as the side rows store the protected positions  */
+/* (keys rotated, symmetric INT8 per 128-dim vector with an FP16 scale) and  */
+/* attended with the protected path's arithmetic.  Pool layout per (page,    */
+/* kv-head), 4160 B: K codes [16 positions][128] | V codes [128 channels][16 */
+/* positions] | s_k FP16 [16] | s_v FP16 [16].                               */
+/* ------------------------------------------------------------------------ */
+
+enum { KV8_BLOCK = 4160, KV8_OFF_V = 2048, KV8_OFF_SK = 4096, KV8_OFF_SV = 4128 };
+
+static uint8_t *kv8_block(const kv8ref_cache *c, int32_t phys, int g) {
+  assert(phys >= 0 && phys < c->num_pages);
+  return c->pages + ((size_t)phys * (size_t)c->num_kv_heads + (size_t)g) * KV8_BLOCK;
+}
+
+static void kv8_append_one(const kv8ref_cache *c, int g, const uint16_t *k16, const uint16_t *v16,
+                           int32_t pos, const int32_t *table_row) {
+  float k[HD], v[HD];
+  for (int i = 0; i < HD; i++) {
+    k[i] = kv4ref_bf16_to_f32(k16[i]);
+    v[i] = kv4ref_bf16_to_f32(v16[i]);
+  }
+  fwht128(k);
+  int8_t kc[HD], vc[HD];
+  uint16_t ks, vs;
+  quant_int8(k, kc, &ks);
+  quant_int8(v, vc, &vs);
+  uint8_t *blk = kv8_block(c, table_row[pos / PAGE], g);
+  const int t = pos % PAGE;
+  memcpy(blk + (size_t)t * HD, kc, HD);
+  for (int j = 0; j < HD; j++) blk[KV8_OFF_V + j * PAGE + t] = (uint8_t)vc[j];
+  memcpy(blk + KV8_OFF_SK + 2 * t, &ks, 2);
+  memcpy(blk + KV8_OFF_SV + 2 * t, &vs, 2);
+}
+
+int kv8ref_append(const kv8ref_cache *c, const uint16_t *k, const uint16_t *v, const int32_t *pos,
+                  const int32_t *page_table, int32_t pt_stride, int32_t B) {
+  const int H = c->num_kv_heads;
+  for (int b = 0; b < B; b++)
+    for (int g = 0; g < H; g++) {
+      size_t off = ((size_t)b * H + g) * HD;
+      kv8_append_one(c, g, k + off, v + off, pos[b], page_table + (size_t)b * pt_stride);
+    }
+  return 0;
+}
+
+int kv8ref_prefill(const kv8ref_cache *c, const uint16_t *k, const uint16_t *v,
+                   const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *page_table,
+                   int32_t pt_stride, int32_t nseq, int32_t nthreads) {
+  const int H = c->num_kv_heads;
+  (void)nthreads;
+#pragma omp parallel for schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int sq = 0; sq < nseq; sq++)
+    for (int32_t i = 0; i < cu_seqlens[sq + 1] - cu_seqlens[sq]; i++) {
+      size_t tok = (size_t)cu_seqlens[sq] + (size_t)i;
+      for (int g = 0; g < H; g++) {
+        size_t off = (tok * H + g) * HD;
+        kv8_append_one(c, g, k + off, v + off, start_pos[sq] + i, page_table + (size_t)sq * pt_stride);
+      }
+    }
+  return 0;
+}
+
+int kv8ref_decode(const kv8ref_cache *c, const uint16_t *q, const int32_t *ctx_len,
+                  const int32_t *page_table, int32_t pt_stride, int32_t B, int32_t Hq,
+                  float softmax_scale, double *out, double *lse, const kv4ref_debug *dbg,
+                  int32_t nthreads) {
+  exp2_init();
+  const int Hkv = c->num_kv_heads;
+  if (Hkv <= 0 || Hq % Hkv != 0) return -1;
+  const int G = Hq / Hkv;
+  const float scale_log2 = kv4ref_scale_log2(softmax_scale);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int bh = 0; bh < B * Hq; bh++) {
+    const int b = bh / Hq, h = bh % Hq, g = h / G;
+    const int32_t L = ctx_len[b];
+    if (L < 1 || (L + PAGE - 1) / PAGE > pt_stride) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    float qr[HD];
+    for (int i = 0; i < HD; i++) qr[i] = kv4ref_bf16_to_f32(q[(size_t)bh * HD + i]);
+    fwht128(qr);
+    int8_t qc[HD];
+    float s_q;
+    int32_t qsum;
+    quant_query(qr, qc, &s_q, &qsum);
+    if (dbg && dbg->qcodes) memcpy(dbg->qcodes + (size_t)bh * HD, qc, HD);
+    if (dbg && dbg->qsum) dbg->qsum[bh] = qsum;
+    int32_t *dqk = (dbg && dbg->qk) ? dbg->qk + (size_t)bh * dbg->max_ctx : NULL;
+    int8_row_t *rows = (int8_row_t *)malloc(sizeof(int8_row_t) * (size_t)L);
+    int8_t *vt = (int8_t *)malloc((size_t)L * HD); /* V codes of each position, channel order */
+    const int32_t *trow = page_table + (size_t)b * pt_stride;
+    for (int32_t p = 0; p < L; p++) {
+      const uint8_t *blk = kv8_block(c, trow[p / PAGE], g);
+      const int t = p % PAGE;
+      for (int j = 0; j < HD; j++) vt[(size_t)p * HD + j] = (int8_t)blk[KV8_OFF_V + j * PAGE + t];
+      rows[p].pos = p;
+      rows[p].k8 = (const int8_t *)blk + (size_t)t * HD;
+      rows[p].v8 = vt + (size_t)p * HD;
+      memcpy(&rows[p].sk, blk + KV8_OFF_SK + 2 * t, 2);
+      memcpy(&rows[p].sv, blk + KV8_OFF_SV + 2 * t, 2);
+    }
+    partial_t part;
+    int8_region(rows, L, qc, s_q * scale_log2, &part, dqk);
+    merge(&part, 1, out + (size_t)bh * HD, lse + bh);
+    free(vt);
+    free(rows);
   }
   return bad ? -2 : 0;
 }

@@ -82,6 +82,26 @@ int kv4ref_decode(const kv4ref_cache *c, const uint16_t *q, const int32_t *ctx_l
                   int32_t Hq, float softmax_scale, int32_t pv_exact, double *out, double *lse,
                   const kv4ref_debug *dbg, int32_t nthreads);
 
+/* KV8 everywhere (INT8 comparison variant): paged pool
+ * uint8 [num_pages][num_kv_heads][4160] = K codes int8 [16][128] (rotated) |
+ * V codes int8 [128][16] | s_k FP16 [16] | s_v FP16 [16]. */
+typedef struct kv8ref_cache {
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  uint8_t *pages;
+} kv8ref_cache;
+
+int kv8ref_append(const kv8ref_cache *c, const uint16_t *k, const uint16_t *v, const int32_t *pos,
+                  const int32_t *page_table, int32_t pt_stride, int32_t B);
+int kv8ref_prefill(const kv8ref_cache *c, const uint16_t *k, const uint16_t *v,
+                   const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *page_table,
+                   int32_t pt_stride, int32_t nseq, int32_t nthreads);
+/* Every position through the protected path's arithmetic; dbg: qcodes, qsum, qk. */
+int kv8ref_decode(const kv8ref_cache *c, const uint16_t *q, const int32_t *ctx_len,
+                  const int32_t *page_table, int32_t pt_stride, int32_t B, int32_t Hq,
+                  float softmax_scale, double *out, double *lse, const kv4ref_debug *dbg,
+                  int32_t nthreads);
+
 #ifdef __cplusplus
 }
 #endif
