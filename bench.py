@@ -249,6 +249,52 @@ def variant_leg(wl, layers, sh, ctx, scale, steps, t_bf16):
                          err_vs_fp64_maxabs=float(err.max()), err_vs_fp64_meanabs=float(err.mean()))
         log(f"variant {name}: {t * 1e3:.3f} ms/step, main {main_us:.1f} us, "
             f"max err vs FP64 {float(err.max()):.3e}")
+    # KV8 everywhere: every position in the side rows' INT8 representation,
+    # attended with the protected path's arithmetic (its own pool per layer)
+    for L in layers:
+        L.pop("bf16", None)
+    torch.cuda.empty_cache()
+    log(f"variant kv8: building the INT8 pools of {wl.layers} layers")
+    pools = []
+    rows_last = torch.from_numpy(off[:-1] + lead).to(dev)
+    for li, L in enumerate(layers):
+        if li == 0:
+            k, v = k0, v0
+        else:
+            k, v, _ = draw_values(wl.seed, li, n_tok, B, Hq, wl.Hkv, device=dev)
+        c8 = kv4.Kv8Cache.zeros(wl.num_pages, wl.Hkv, dev)
+        kv4.kv8_prefill_quantize(c8, k[rows_lead].contiguous(), v[rows_lead].contiguous(), cu, zeros,
+                                 table, int(lead.max()))
+        kv4.kv8_append(c8, k[rows_last].contiguous(), v[rows_last].contiguous(), pos, table)
+        del k, v
+        pools.append(c8)
+    torch.cuda.synchronize()
+    ws8 = torch.empty(kv4.kv8_decode_workspace_bytes(pools[0], B, Hq, wl.max_ctx), dtype=torch.uint8,
+                      device=dev)
+
+    def kv8_step():
+        for c8, L in zip(pools, layers):
+            kv4.kv8_decode_attention(c8, L["q"], ctx, table, wl.max_ctx, scale, out, lse, ws8)
+
+    for _ in range(2):
+        kv8_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        kv8_step()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    kv4.kv8_decode_attention(pools[0], layers[0]["q"], ctx, table, wl.max_ctx, scale, out, lse, ws8)
+    torch.cuda.synchronize()
+    err = (out[sel].double() - ref).abs()
+    kv8_bytes = int((wl.ctx.astype(np.int64) * wl.Hkv * 260).sum())
+    res["kv8"] = dict(decode_ms_per_step=round(t * 1e3, 3), decode_tokens_per_s=round(B / t, 1),
+                      hbm_gbps=round(kv8_bytes * len(pools) / t / 1e9, 1),
+                      speedup_vs_bf16=round(t_bf16 / t, 3) if t_bf16 else None,
+                      err_vs_fp64_maxabs=float(err.max()), err_vs_fp64_meanabs=float(err.mean()))
+    log(f"variant kv8: {t * 1e3:.3f} ms/step, max err vs FP64 {float(err.max()):.3e}")
+    del pools, ws8
+    torch.cuda.empty_cache()
     for name in res:
         res[name]["throughput_vs_kv4"] = round(res["kv4"]["decode_ms_per_step"] /
                                                res[name]["decode_ms_per_step"], 4)

@@ -187,6 +187,55 @@ int kv4bench_decode_attention_timed(const kv4_cache_desc *cache, const void *q,
                                     float *lse, void *workspace, size_t workspace_bytes,
                                     void *ev_main_begin, void *ev_main_end, void *stream);
 
+/* ---- variant: KV8 everywhere ----------------------------------------------
+ * The INT8 point of the pages' quantization-target comparison (KV4-RL,
+ * quantization-target comparison, figure 3): every position is stored the way
+ * the side buffer stores a protected position (key Hadamard-rotated after
+ * RoPE, symmetric INT8 per 128-dim vector with an FP16 scale) and attended
+ * with the protected path's arithmetic (the INT8 query against INT8 keys,
+ * FP32 softmax weights, values dequantized to BF16, FP32 accumulation).
+ *   pages  uint8 [num_pages][num_kv_heads][4160]: per (page, kv-head) K codes
+ *          int8 [16 positions][128] | V codes int8 [128 channels][16
+ *          positions] | s_k FP16 [16] | s_v FP16 [16]. */
+typedef struct kv8_cache_desc {
+  int32_t abi_version; /* KV4_ABI_VERSION */
+  int32_t num_pages;
+  int32_t page_size;   /* must be 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;    /* must be 128 */
+  void *pages;
+} kv8_cache_desc;
+
+/* As kv4_append (no side buffer, no slot): writes the INT8 codes and scales
+ * of position pos[b] into slot pos%16 of page page_table[b][pos/16]. */
+int kv8_append(const kv8_cache_desc *cache, const void *k, const void *v, const int32_t *pos,
+               const int32_t *page_table, int32_t pt_stride, int32_t B, void *stream);
+
+/* As kv4_prefill_quantize: byte-identical to appends of the same tokens. */
+int kv8_prefill_quantize(const kv8_cache_desc *cache, const void *k, const void *v,
+                         const int32_t *cu_seqlens, const int32_t *start_pos,
+                         const int32_t *page_table, int32_t pt_stride, int32_t nseq,
+                         int32_t max_seqlen, void *stream);
+
+/* Device workspace bytes of kv8_decode_attention (0 on bad arguments). */
+size_t kv8_decode_workspace_bytes(const kv8_cache_desc *cache, int32_t B, int32_t Hq,
+                                  int32_t max_ctx);
+
+/* One decode step over positions [0, ctx_len) of every sequence; arguments,
+ * layouts and errors as for kv4_decode_attention (no slot). */
+int kv8_decode_attention(const kv8_cache_desc *cache, const void *q, const int32_t *ctx_len,
+                         const int32_t *page_table, int32_t pt_stride, int32_t B, int32_t Hq,
+                         int32_t max_ctx, float softmax_scale, float *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* kv8_decode_attention with the debug stores: qcodes, qsum and qk of *dbg
+ * (pcode and pv are not used). */
+int kv8_decode_attention_debug(const kv8_cache_desc *cache, const void *q, const int32_t *ctx_len,
+                               const int32_t *page_table, int32_t pt_stride, int32_t B,
+                               int32_t Hq, int32_t max_ctx, float softmax_scale, float *out,
+                               float *lse, void *workspace, size_t workspace_bytes,
+                               const kv4_decode_debug *dbg, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

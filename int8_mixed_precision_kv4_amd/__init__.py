@@ -21,7 +21,9 @@ HEAD_DIM, PAGE, SINK, WINDOW, SIDE_ROWS, BLOCK_BYTES = 128, 16, 16, 128, 144, 21
 EXPORTS = ("kv4_append", "kv4_prefill_quantize", "kv4_decode_workspace_bytes",
            "kv4_decode_attention", "kv4_decode_attention_debug", "kv4_strerror",
            "kv4bench_bf16_workspace_bytes", "kv4bench_bf16_paged_decode",
-           "kv4bench_decode_attention_timed")
+           "kv4bench_decode_attention_timed", "kv8_append", "kv8_prefill_quantize",
+           "kv8_decode_workspace_bytes", "kv8_decode_attention", "kv8_decode_attention_debug")
+KV8_BLOCK_BYTES = 4160
 
 _lib = None
 
@@ -35,6 +37,11 @@ class _Desc(C.Structure):
                 ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("sink", C.c_int32),
                 ("window", C.c_int32), ("max_slots", C.c_int32), ("pages", C.c_void_p),
                 ("side_codes", C.c_void_p), ("side_scales", C.c_void_p)]
+
+
+class _Kv8Desc(C.Structure):
+    _fields_ = [("abi_version", C.c_int32), ("num_pages", C.c_int32), ("page_size", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("pages", C.c_void_p)]
 
 
 class _Debug(C.Structure):
@@ -67,6 +74,14 @@ def lib():
         L.kv4bench_bf16_paged_decode.argtypes = [P, I, I, P, P, P, I, I, I, I, F, P, P, P, Z, P]
         L.kv4bench_decode_attention_timed.argtypes = [D, P, P, P, P, I, I, I, I, F, P, P, P, Z,
                                                       P, P, P]
+        D8 = C.POINTER(_Kv8Desc)
+        L.kv8_append.argtypes = [D8, P, P, P, P, I, I, P]
+        L.kv8_prefill_quantize.argtypes = [D8, P, P, P, P, P, I, I, I, P]
+        L.kv8_decode_workspace_bytes.argtypes = [D8, I, I, I]
+        L.kv8_decode_workspace_bytes.restype = Z
+        L.kv8_decode_attention.argtypes = [D8, P, P, P, I, I, I, I, F, P, P, P, Z, P]
+        L.kv8_decode_attention_debug.argtypes = [D8, P, P, P, I, I, I, I, F, P, P, P, Z,
+                                                 C.POINTER(_Debug), P]
         _lib = L
     return _lib
 
@@ -214,3 +229,81 @@ def decode_attention_timed(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ct
         B, Hq, int(max_ctx), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel(), ev_begin, ev_end,
         _stream()))
+
+
+# ------------------------------------------------------------ KV8 variant --
+
+class Kv8Cache:
+    """KV8-everywhere pool (the INT8 comparison variant): pages uint8
+    [num_pages][Hkv][4160] = K codes [16][128] (rotated) | V codes [128][16] |
+    s_k FP16 [16] | s_v FP16 [16]."""
+
+    def __init__(self, pages: torch.Tensor):
+        assert pages.dtype == torch.uint8 and pages.dim() == 3 and pages.shape[2] == KV8_BLOCK_BYTES
+        self.pages = pages
+        self.num_pages, self.num_kv_heads = int(pages.shape[0]), int(pages.shape[1])
+        self._desc = _Kv8Desc(ABI_VERSION, self.num_pages, PAGE, self.num_kv_heads, HEAD_DIM,
+                              pages.data_ptr())
+
+    @classmethod
+    def zeros(cls, num_pages: int, num_kv_heads: int, device="cuda"):
+        return cls(torch.zeros((num_pages, num_kv_heads, KV8_BLOCK_BYTES), dtype=torch.uint8,
+                               device=device))
+
+    def desc(self):
+        return C.byref(self._desc)
+
+
+def kv8_append(cache: Kv8Cache, k, v, pos, page_table):
+    """kv8_append: k, v bf16 [B][Hkv][128]; pos int32 [B]; page_table int32 [B][W]."""
+    _check(lib().kv8_append(cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(page_table),
+                            page_table.shape[1], pos.shape[0], _stream()))
+
+
+def kv8_prefill_quantize(cache: Kv8Cache, k, v, cu_seqlens, start_pos, page_table, max_seqlen: int):
+    """kv8_prefill_quantize: k, v bf16 [T][Hkv][128]; cu_seqlens int32 [nseq+1]."""
+    _check(lib().kv8_prefill_quantize(cache.desc(), _ptr(k), _ptr(v), _ptr(cu_seqlens),
+                                      _ptr(start_pos), _ptr(page_table), page_table.shape[1],
+                                      start_pos.shape[0], int(max_seqlen), _stream()))
+
+
+def kv8_decode_workspace_bytes(cache: Kv8Cache, B: int, Hq: int, max_ctx: int) -> int:
+    return int(lib().kv8_decode_workspace_bytes(cache.desc(), B, Hq, max_ctx))
+
+
+def kv8_decode_attention(cache: Kv8Cache, q, ctx_len, page_table, max_ctx: int,
+                         softmax_scale: float, out=None, lse=None, workspace=None):
+    """kv8_decode_attention: q bf16 [B][Hq][128] -> (out fp32 [B][Hq][128], lse fp32 [B][Hq])."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(kv8_decode_workspace_bytes(cache, B, Hq, max_ctx), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().kv8_decode_attention(cache.desc(), _ptr(q), _ptr(ctx_len), _ptr(page_table),
+                                      page_table.shape[1], B, Hq, int(max_ctx), float(softmax_scale),
+                                      _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                      _stream()))
+    return out, lse
+
+
+def kv8_decode_attention_debug(cache: Kv8Cache, q, ctx_len, page_table, max_ctx: int,
+                               softmax_scale: float):
+    """kv8_decode_attention_debug: also returns qcodes, qsum and qk as device tensors."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    W = int(page_table.shape[1])
+    dev = q.device
+    dbg = dict(qcodes=torch.zeros((B, Hq, HEAD_DIM), dtype=torch.int8, device=dev),
+               qsum=torch.zeros((B, Hq), dtype=torch.int32, device=dev),
+               qk=torch.zeros((B, Hq, W * PAGE), dtype=torch.int32, device=dev))
+    d = _Debug(dbg["qcodes"].data_ptr(), dbg["qsum"].data_ptr(), dbg["qk"].data_ptr(), None, None,
+               W * PAGE, W)
+    out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(kv8_decode_workspace_bytes(cache, B, Hq, max_ctx), dtype=torch.uint8, device=dev)
+    _check(lib().kv8_decode_attention_debug(cache.desc(), _ptr(q), _ptr(ctx_len), _ptr(page_table),
+                                            W, B, Hq, int(max_ctx), float(softmax_scale), _ptr(out),
+                                            _ptr(lse), _ptr(ws), ws.numel(), C.byref(d), _stream()))
+    return out, lse, dbg

@@ -78,6 +78,9 @@ int main_region_waves() {
   }
   return cached[dev];
 }
+int kv8_region_waves() {
+  return main_region_waves() / KV4_MAIN_WAVES_PER_SIMD * KV8_MAIN_WAVES_PER_SIMD;
+}
 }  // namespace kv4
 
 extern "C" {
@@ -212,6 +215,99 @@ int kv4bench_bf16_paged_decode(const void* pages, int32_t num_pages, int32_t Hkv
                                          pt_stride, B, Hq, scale_log2(softmax_scale), out, lse,
                                          workspace, nw, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KV4_OK : hip_fail(e);
+}
+
+// ---- KV8 everywhere --------------------------------------------------------
+
+static int check_kv8(const kv8_cache_desc* c) {
+  if (!c) return KV4_ERR_NULLPTR;
+  if (c->abi_version != KV4_ABI_VERSION || c->page_size != 16 || c->head_dim != 128)
+    return KV4_ERR_UNSUPPORTED;
+  if (c->num_pages <= 0 || c->num_kv_heads <= 0) return KV4_ERR_SHAPE;
+  if (!c->pages) return KV4_ERR_NULLPTR;
+  return KV4_OK;
+}
+
+int kv8_append(const kv8_cache_desc* cache, const void* k, const void* v, const int32_t* pos,
+               const int32_t* page_table, int32_t pt_stride, int32_t B, void* stream) {
+  int rc = check_kv8(cache);
+  if (rc != KV4_OK) return rc;
+  if (!k || !v || !pos || !page_table) return KV4_ERR_NULLPTR;
+  if (B <= 0 || pt_stride <= 0 || B > 65535) return KV4_ERR_SHAPE;
+  hipError_t e = kv4::launch_kv8_append(static_cast<uint8_t*>(cache->pages), cache->num_kv_heads,
+                                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                        pos, page_table, pt_stride, B, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KV4_OK : hip_fail(e);
+}
+
+int kv8_prefill_quantize(const kv8_cache_desc* cache, const void* k, const void* v,
+                         const int32_t* cu_seqlens, const int32_t* start_pos,
+                         const int32_t* page_table, int32_t pt_stride, int32_t nseq,
+                         int32_t max_seqlen, void* stream) {
+  int rc = check_kv8(cache);
+  if (rc != KV4_OK) return rc;
+  if (!k || !v || !cu_seqlens || !start_pos || !page_table) return KV4_ERR_NULLPTR;
+  if (nseq <= 0 || nseq > 65535 || pt_stride <= 0 || max_seqlen <= 0) return KV4_ERR_SHAPE;
+  hipError_t e = kv4::launch_kv8_prefill(static_cast<uint8_t*>(cache->pages), cache->num_kv_heads,
+                                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                         cu_seqlens, start_pos, page_table, pt_stride, nseq,
+                                         max_seqlen, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KV4_OK : hip_fail(e);
+}
+
+size_t kv8_decode_workspace_bytes(const kv8_cache_desc* cache, int32_t B, int32_t Hq,
+                                  int32_t max_ctx) {
+  if (check_kv8(cache) != KV4_OK || B <= 0 || Hq <= 0 || max_ctx <= 0) return 0;
+  return kv4::decode_workspace_bytes(B, Hq, cache->num_kv_heads, kv4::kv8_region_waves());
+}
+
+static int kv8_decode_common(const kv8_cache_desc* cache, const void* q, const int32_t* ctx_len,
+                             const int32_t* page_table, int32_t pt_stride, int32_t B, int32_t Hq,
+                             int32_t max_ctx, float softmax_scale, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, const kv4_decode_debug* dbg,
+                             void* stream) {
+  int rc = check_kv8(cache);
+  if (rc != KV4_OK) return rc;
+  if (!q || !ctx_len || !page_table || !out || !lse) return KV4_ERR_NULLPTR;
+  const int Hkv = cache->num_kv_heads;
+  if (Hq <= 0 || Hq % Hkv != 0 || Hq / Hkv != kv4::GQA) return KV4_ERR_UNSUPPORTED;
+  if (B <= 0 || B > 65535 || pt_stride <= 0 || max_ctx <= 0 ||
+      static_cast<int64_t>(max_ctx) > static_cast<int64_t>(pt_stride) * 16)
+    return KV4_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * Hkv * (max_ctx / 16 + 1) > INT32_MAX) return KV4_ERR_SHAPE;
+  const int nw = kv4::kv8_region_waves();
+  if (!workspace || workspace_bytes < kv4::decode_workspace_bytes(B, Hq, Hkv, nw))
+    return KV4_ERR_WORKSPACE;
+  kv4::DecodeDebug d{};
+  if (dbg) {
+    if (dbg->max_ctx < max_ctx || dbg->max_pages < pt_stride) return KV4_ERR_SHAPE;
+    d = kv4::DecodeDebug{dbg->qcodes, dbg->qsum, dbg->qk, nullptr, nullptr, dbg->max_ctx,
+                         dbg->max_pages};
+  }
+  const kv4::DecodeWorkspace ws = kv4::carve_workspace(workspace, B, Hq, Hkv, nw);
+  hipError_t e = kv4::launch_kv8_decode(static_cast<const uint8_t*>(cache->pages), Hkv,
+                                        static_cast<const uint16_t*>(q), ctx_len, page_table,
+                                        pt_stride, B, Hq, scale_log2(softmax_scale), out, lse, ws,
+                                        dbg ? &d : nullptr, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KV4_OK : hip_fail(e);
+}
+
+int kv8_decode_attention(const kv8_cache_desc* cache, const void* q, const int32_t* ctx_len,
+                         const int32_t* page_table, int32_t pt_stride, int32_t B, int32_t Hq,
+                         int32_t max_ctx, float softmax_scale, float* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return kv8_decode_common(cache, q, ctx_len, page_table, pt_stride, B, Hq, max_ctx, softmax_scale,
+                           out, lse, workspace, workspace_bytes, nullptr, stream);
+}
+
+int kv8_decode_attention_debug(const kv8_cache_desc* cache, const void* q, const int32_t* ctx_len,
+                               const int32_t* page_table, int32_t pt_stride, int32_t B,
+                               int32_t Hq, int32_t max_ctx, float softmax_scale, float* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               const kv4_decode_debug* dbg, void* stream) {
+  if (!dbg) return KV4_ERR_NULLPTR;
+  return kv8_decode_common(cache, q, ctx_len, page_table, pt_stride, B, Hq, max_ctx, softmax_scale,
+                           out, lse, workspace, workspace_bytes, dbg, stream);
 }
 
 }  // extern "C"

@@ -528,6 +528,261 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
   __builtin_amdgcn_wave_barrier();
 }
 
+// ---------------------------------------------------------- page formats --
+// The main kernel streams units of kUnit pages of one segment through its
+// per-wave LDS slot; a format supplies the staging, the compute step, the
+// order of the query operand and the partial it leaves.
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// KV4-RL main region: quads of 4 INT4 pages (layouts above).
+struct Kv4Format {
+  static constexpr int kUnit = 4;
+  static constexpr int kWavesPerSimd = KV4_MAIN_WAVES_PER_SIMD;
+  static constexpr int kBlock = BLOCK_BYTES;
+  static constexpr bool kProtected = true;      // protected-region workgroups in the grid tail
+  static constexpr bool kNaturalQuery = false;  // QK operand: even / odd channels (nibble order)
+  typedef QuadRegs Regs;
+  typedef MainState State;
+  __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
+    quad_to_lds(slot, blk, lane, r16, grp);
+  }
+  __device__ static void from_lds(Regs& q, const uint8_t* slot, int lane, int r16, int grp) {
+    (void)grp;
+    quad_from_lds(q, slot, lane, r16);
+  }
+  __device__ static void reset(State& st) {
+    st.Zr = -INFINITY;
+    st.Ls = 0.0f;
+    st.Ms = 0.0f;
+#pragma unroll
+    for (int o = 0; o < 8; ++o) st.O[o] = 0.0f;
+  }
+  template <bool DEBUG>
+  __device__ static void compute(const DecArgs& a, State& st, const Regs& q, int np, v4i qa0, v4i qa1,
+                                 float c_q, float S_q, int j0, int main_end, size_t qb, uint8_t* slot,
+                                 int r16, int grp, int pslot) {
+    compute_quad<DEBUG>(a, st, q, np, qa0, qa1, c_q, S_q, j0, main_end, qb, slot + kSlotP, r16, grp,
+                        pslot);
+  }
+  // A = O + sum(w e m_v); lane (head grp, r16) holds channels 2(16 s2 + r16) + e2 in A[2 s2 + e2]
+  __device__ static void finish(const State& st, float A[8], float& Z, float& L) {
+    const float Mh = row16_sum(st.Ms);
+    L = row16_sum(st.Ls);
+    Z = st.Zr;
+#pragma unroll
+    for (int o = 0; o < 8; ++o) A[o] = st.O[o] + Mh;
+  }
+  // P0: the 4 heads' partials of the slot, kPart floats apart; this lane's head is grp
+  __device__ static void store(float* P0, const float A[8], int r16, int grp) {
+    float* P = P0 + grp * kPart;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+      *reinterpret_cast<float2*>(P + 2 * (16 * s2 + r16)) = make_float2(A[2 * s2], A[2 * s2 + 1]);
+  }
+};
+
+// KV8 everywhere: pairs of 2 INT8 pages, every position through the protected
+// path's arithmetic (INT8 QK on MFMA, FP32 softmax weights, v^ = bf16(s_v c),
+// FP32 P times BF16 v^ with FP32 accumulation).  P enters the BF16 MFMA as the
+// sum of two BF16 parts, hi = bf16(e) and lo = bf16(e - hi), which carries
+// e to 16 significant bits (relative error below 2^-16).  PV on
+// 16x16x32 MFMAs: MFMA r of accumulator acc keeps P only in rows 4r .. 4r+3
+// (head = row % 4) and takes channels 64 acc + 16 r + n as its columns, so
+// the four MFMAs fill all 16 rows of one accumulator with 4 heads x 64
+// channels.  Slot layout:
+//   [0, 4096)     K operands: page t, channel half h at 2048 t + 1024 h + 16 lane
+//                 (lane (r16, grp): position r16, channels 64 h + 16 grp .. + 15)
+//   [4096, 8192)  V codes, page t at 4096 + 2048 t (the block's channel-major copy)
+//   [8192, 8320)  scales, page t at 8192 + 64 t: s_k[16], s_v[16]
+//   [8320, 8832)  P operand [hi, lo][head][32 positions] BF16
+constexpr int k8K = 0, k8V = 4096, k8S = 8192, k8P = 8320;
+static_assert(k8P + 512 <= kSlotQ, "the KV8 slot must leave the query area free");
+
+struct Kv8Regs {
+  v4i kop[2][2];
+  uint2 vq[8];
+  uint32_t sk[2];
+  uint4 sv;
+};
+// O[acc]: lane (r16, grp) holds head h (register h), channel 64 acc + 16 grp + r16
+struct Kv8State {
+  float Zr, Ls;
+  v4f O[2];
+};
+
+// Two FP32 values as packed BF16 (nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{x, y}), b2));
+}
+
+template <bool DEBUG>
+__device__ __forceinline__ void compute_pair(const DecArgs& a, Kv8State& st, const Kv8Regs& r, int np,
+                                             v4i qa0, v4i qa1, float c_q, int j0, int L, size_t qb,
+                                             uint8_t* slot, int r16, int grp) {
+  // INT8 QK of the two pages; lane (head grp, position r16) after the move
+  v4i d[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    d[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, r.kop[t][0], v4i{0, 0, 0, 0}, 0, 0, 0);
+    d[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, r.kop[t][1], d[t], 0, 0, 0);
+  }
+  float z[2];
+  bool valid[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int D8 = qk_rows(d[t]);
+    const int pos = PAGE * (j0 + t) + r16;
+    valid[t] = (t < np) && (pos < L);
+    z[t] = valid[t] ? (static_cast<float>(D8) * f16_value(r.sk[t])) * c_q : -INFINITY;
+    if (DEBUG && valid[t] && a.dbg.qk) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + pos] = D8;
+  }
+  // running max of each head; weights relative to it, earlier sums rescaled
+  const float Zn = fmaxf(st.Zr, row16_max(fmaxf(z[0], z[1])));
+  const float al = __builtin_amdgcn_exp2f(st.Zr - Zn);
+  st.Zr = Zn;
+  float e[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) e[t] = valid[t] ? exp2s(z[t] - Zn) : 0.0f;
+  st.Ls = __builtin_fmaf(st.Ls, al, e[0] + e[1]);
+  // P operand through the slot: [hi, lo][head grp][16 t + r16]
+  uint16_t* pst = reinterpret_cast<uint16_t*>(slot + k8P);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t hi = pack_bf16x2(e[t], 0.0f) & 0xFFFFu;
+    const uint32_t lo = pack_bf16x2(e[t] - __uint_as_float(hi << 16), 0.0f) & 0xFFFFu;
+    pst[grp * 32 + 16 * t + r16] = static_cast<uint16_t>(hi);
+    pst[128 + grp * 32 + 16 * t + r16] = static_cast<uint16_t>(lo);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // A operand: lane (row r16, k-group grp) = head r16 % 4, positions 8 grp .. 8 grp + 7
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const u4 ph = *reinterpret_cast<const u4*>(pst + (r16 & 3) * 32 + 8 * grp);
+  const u4 pl = *reinterpret_cast<const u4*>(pst + 128 + (r16 & 3) * 32 + 8 * grp);
+  // B operand: lane (r16, grp) = channel 16 s + r16, positions 8 (grp & 1) + i of
+  // page grp >> 1; the V scale of a position outside the context is taken as 0
+  const int tp = grp >> 1;
+  const int pos0 = PAGE * (j0 + tp) + 8 * (grp & 1);
+  // packed FP16 scales, positions outside the context zeroed
+  uint32_t svw[4] = {r.sv.x, r.sv.y, r.sv.z, r.sv.w};
+  const int nval = tp < np ? min(8, max(0, L - pos0)) : 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t keep = (2 * i < nval ? 0x0000FFFFu : 0u) | (2 * i + 1 < nval ? 0xFFFF0000u : 0u);
+    svw[i] &= keep;
+  }
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  // rescale what is accumulated: head h in register h
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float alh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * h));
+    st.O[0][h] *= alh;
+    st.O[1][h] *= alh;
+  }
+  const u4 zero4 = u4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {  // channel block s = 4 acc + r
+    // v^ = bf16(s_v c); s_v c is exact in FP32 (an FMA with zero addend
+    // taking the FP16 scale directly)
+    const uint32_t w0 = r.vq[s].x, w1 = r.vq[s].y;
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const h2 sp = __builtin_bit_cast(h2, svw[i >> 1]);
+      const float si = static_cast<float>(sp[i & 1]);
+      const float c = static_cast<float>(static_cast<int8_t>((i < 4 ? w0 : w1) >> (8 * (i & 3))));
+      x[i] = __builtin_fmaf(si, c, 0.0f);
+    }
+    const u4 pk = u4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7])};
+    const v8bf vb = __builtin_bit_cast(v8bf, pk);
+    const bool mine = (r16 >> 2) == (s & 3);  // rows 4r .. 4r+3 carry P in MFMA r
+    const v8bf ah = __builtin_bit_cast(v8bf, mine ? ph : zero4);
+    const v8bf alo = __builtin_bit_cast(v8bf, mine ? pl : zero4);
+    v4f o = st.O[s >> 2];
+    o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, vb, o, 0, 0, 0);
+    st.O[s >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, vb, o, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // keep one block's operands live at a time
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+struct Kv8Format {
+  static constexpr int kUnit = 2;
+  static constexpr int kWavesPerSimd = KV8_MAIN_WAVES_PER_SIMD;
+  static constexpr int kBlock = KV8_BLOCK_BYTES;
+  static constexpr bool kProtected = false;
+  static constexpr bool kNaturalQuery = true;  // QK operand: channels in natural order
+  typedef Kv8Regs Regs;
+  typedef Kv8State State;
+  __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        __builtin_amdgcn_global_load_lds(blk[t] + HD * r16 + 64 * h + 16 * grp,
+                                         (lptr)(slot + k8K + 2048 * t + 1024 * h), 16, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(blk[t] + KV8_OFF_V + 1024 * i + 16 * lane,
+                                         (lptr)(slot + k8V + 2048 * t + 1024 * i), 16, 0, 0);
+    if (lane < 8)  // 2 pages x 64 B of scales
+      __builtin_amdgcn_global_load_lds((lane < 4 ? blk[0] : blk[1]) + KV8_OFF_SK + 16 * (lane & 3),
+                                       (lptr)(slot + k8S), 16, 0, 0);
+  }
+  __device__ static void from_lds(Regs& r, const uint8_t* slot, int lane, int r16, int grp) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        r.kop[t][h] = *reinterpret_cast<const v4i*>(slot + k8K + 2048 * t + 1024 * h + 16 * lane);
+    const uint8_t* vb = slot + k8V + 2048 * (grp >> 1) + 16 * r16 + 8 * (grp & 1);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r.vq[s] = *reinterpret_cast<const uint2*>(vb + 256 * s);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) r.sk[t] = *reinterpret_cast<const uint16_t*>(slot + k8S + 64 * t + 2 * r16);
+    r.sv = *reinterpret_cast<const uint4*>(slot + k8S + 64 * (grp >> 1) + 32 + 16 * (grp & 1));
+  }
+  __device__ static void reset(State& st) {
+    st.Zr = -INFINITY;
+    st.Ls = 0.0f;
+    st.O[0] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    st.O[1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  template <bool DEBUG>
+  __device__ static void compute(const DecArgs& a, State& st, const Regs& r, int np, v4i qa0, v4i qa1,
+                                 float c_q, float S_q, int j0, int main_end, size_t qb, uint8_t* slot,
+                                 int r16, int grp, int pslot) {
+    (void)S_q;
+    (void)pslot;
+    compute_pair<DEBUG>(a, st, r, np, qa0, qa1, c_q, j0, main_end, qb, slot, r16, grp);
+  }
+  // A[4 acc + h]: head h, channel 64 acc + 16 grp + r16
+  __device__ static void finish(const State& st, float A[8], float& Z, float& L) {
+    L = row16_sum(st.Ls);
+    Z = st.Zr;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      A[h] = st.O[0][h];
+      A[4 + h] = st.O[1][h];
+    }
+  }
+  // P0: the 4 heads' partials of the slot, kPart floats apart
+  __device__ static void store(float* P0, const float A[8], int r16, int grp) {
+#pragma unroll
+    for (int acc = 0; acc < 2; ++acc)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) P0[h * kPart + 64 * acc + 16 * grp + r16] = A[4 * acc + h];
+  }
+};
+
 // Work split of the main region: the global page list (sequence-major, then
 // kv-head, then logical page; T pages) is cut into one contiguous chunk per
 // wave, chunk c = [c q + min(c, r), (c+1) q + min(c+1, r)) with q = T / nw,
@@ -619,15 +874,17 @@ struct QuadDesc {
   bool opens, closes;  // the piece starts at the segment's first page / ends at its last
 };
 
-template <bool DEBUG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WAVES_PER_SIMD, KV4_MAIN_WAVES_PER_SIMD))) void main_kernel(DecArgs a) {
+template <class F, bool DEBUG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPerSimd, F::kWavesPerSimd))) void main_kernel(DecArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kSlotBytes];
   static_assert(kProtLds <= 4 * kSlotBytes, "the protected role reuses the main role's LDS");
   const int nw = a.ws.n_waves;
-  if (blockIdx.x >= nw / 4) {  // protected-region workgroups fill the tail of the grid
-    const int u = blockIdx.x - nw / 4;
-    protected_partial<DEBUG>(a, u % a.Hkv, u / a.Hkv, &lds[0][0]);
-    return;
+  if constexpr (F::kProtected) {
+    if (blockIdx.x >= nw / 4) {  // protected-region workgroups fill the tail of the grid
+      const int u = blockIdx.x - nw / 4;
+      protected_partial<DEBUG>(a, u % a.Hkv, u / a.Hkv, &lds[0][0]);
+      return;
+    }
   }
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
@@ -635,9 +892,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   const PlanView pv = plan_view(a, lane);
   const Split sp = make_split(pv.T, nw);
   uint8_t* slot = lds[wave];
-  uint8_t* stage = slot + kSlotP;
   const int pslot = pcode_slot(r16);
-  const size_t pstride = static_cast<size_t>(a.Hkv) * BLOCK_BYTES;
+  const size_t pstride = static_cast<size_t>(a.Hkv) * F::kBlock;
 
   // ---- issue cursor: page ip of the chunk [ip, iend) and the segment holding it
   int ip = chunk_begin(sp, w);
@@ -664,12 +920,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     // group grp covers channels 32grp..32grp+31, even / odd split); the codes
     // go through the slot's query area to reach that layout.
     uint8_t* qs = slot + kSlotQ + grp * HD;
-    const uint32_t even = (gq.c[0] & 0xFF) | ((gq.c[2] & 0xFF) << 8) | ((gq.c[4] & 0xFF) << 16) |
-                          (static_cast<uint32_t>(gq.c[6] & 0xFF) << 24);
-    const uint32_t odd = (gq.c[1] & 0xFF) | ((gq.c[3] & 0xFF) << 8) | ((gq.c[5] & 0xFF) << 16) |
-                         (static_cast<uint32_t>(gq.c[7] & 0xFF) << 24);
-    reinterpret_cast<uint32_t*>(qs)[r16] = even;
-    reinterpret_cast<uint32_t*>(qs + 64)[r16] = odd;
+    if constexpr (F::kNaturalQuery) {  // channels 8 r16 .. 8 r16 + 7 in place
+      const uint32_t lo = (gq.c[0] & 0xFF) | ((gq.c[1] & 0xFF) << 8) | ((gq.c[2] & 0xFF) << 16) |
+                          (static_cast<uint32_t>(gq.c[3] & 0xFF) << 24);
+      const uint32_t hi = (gq.c[4] & 0xFF) | ((gq.c[5] & 0xFF) << 8) | ((gq.c[6] & 0xFF) << 16) |
+                          (static_cast<uint32_t>(gq.c[7] & 0xFF) << 24);
+      reinterpret_cast<uint2*>(qs)[r16] = make_uint2(lo, hi);
+    } else {
+      const uint32_t even = (gq.c[0] & 0xFF) | ((gq.c[2] & 0xFF) << 8) | ((gq.c[4] & 0xFF) << 16) |
+                            (static_cast<uint32_t>(gq.c[6] & 0xFF) << 24);
+      const uint32_t odd = (gq.c[1] & 0xFF) | ((gq.c[3] & 0xFF) << 8) | ((gq.c[5] & 0xFF) << 16) |
+                           (static_cast<uint32_t>(gq.c[7] & 0xFF) << 24);
+      reinterpret_cast<uint32_t*>(qs)[r16] = even;
+      reinterpret_cast<uint32_t*>(qs + 64)[r16] = odd;
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -697,7 +961,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     d.b = ib;
     d.g = seg_g;
     d.j0 = a.sink / PAGE + (ip - seg0);
-    d.np = min(4, stop - ip);
+    d.np = min(F::kUnit, stop - ip);
     d.slot = w + ib * a.Hkv + seg_g;
     d.first = (ip == chunk0) || (ip == seg0);
     d.last = ip + d.np >= stop;
@@ -712,12 +976,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   };
   // Stage 2: start the page loads of a described quad into the LDS slot.
   auto issue_quad = [&](QuadDesc& d, int pt) {
-    const gptr gbase = (gptr)a.pages + static_cast<size_t>(d.g) * BLOCK_BYTES;
-    gptr blk[4];
+    const gptr gbase = (gptr)a.pages + static_cast<size_t>(d.g) * F::kBlock;
+    gptr blk[F::kUnit];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < F::kUnit; ++t)
       blk[t] = gbase + static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(pt, t))) * pstride;
-    quad_to_lds(slot, blk, lane, r16, grp);
+    F::to_lds(slot, blk, lane, r16, grp);
     if (d.first) d.main_end = ld_const(a.ctx + d.b) - a.window;
   };
 
@@ -733,7 +997,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
     group_query(d1, raw1);  // d1 is the first quad of a piece
   }
   bool have2 = have1 && plan_quad(d2, pt2);
-  MainState st;
+  typename F::State st;
   v4i qa0 = {0, 0, 0, 0}, qa1 = {0, 0, 0, 0};
   float c_q = 0.0f, S_q = 0.0f;
   int main_end = 0;
@@ -747,12 +1011,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   int pend_bg = 0;
   bool pend_opens = false, pend_closes = false, piece_opens = false;
   auto store_partial = [&]() {
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
-      *reinterpret_cast<float2*>(pend_P + 2 * (16 * s2 + r16)) = make_float2(pend_A[2 * s2], pend_A[2 * s2 + 1]);
+    F::store(pend_P, pend_A, r16, grp);
     if (r16 == 0) {
-      pend_P[128] = pend_Z;
-      pend_P[129] = pend_L;
+      pend_P[grp * kPart + 128] = pend_Z;
+      pend_P[grp * kPart + 129] = pend_L;
     }
     // the chunks holding the segment's first and last pages bound its partials
     if (lane == 0 && pend_opens) a.ws.mrange[pend_bg].x = w;
@@ -760,8 +1022,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
   };
   while (have1) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    QuadRegs q;
-    quad_from_lds(q, slot, lane, r16);
+    typename F::Regs q;
+    F::from_lds(q, slot, lane, r16, grp);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     const QuadDesc cd = d1;
     if (cd.first) {
@@ -771,11 +1033,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
       c_q = nqi.x;
       S_q = static_cast<float>(__float_as_int(nqi.y));
       main_end = cd.main_end;
-      st.Zr = -INFINITY;
-      st.Ls = 0.0f;
-      st.Ms = 0.0f;
-#pragma unroll
-      for (int o = 0; o < 8; ++o) st.O[o] = 0.0f;
+      F::reset(st);
     }
     have1 = have2;
     if (have2) {
@@ -786,19 +1044,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV4_MAIN_WA
       have2 = plan_quad(d2, pt2);
     }
     const size_t qb = static_cast<size_t>(cd.b) * a.Hq + cd.g * GQA;
-    compute_quad<DEBUG>(a, st, q, cd.np, qa0, qa1, c_q, S_q, cd.j0, main_end, qb, stage, r16, grp,
-                        pslot);
-    if (cd.last) {  // partial of the piece: A = O + sum(w e m_v)
+    F::template compute<DEBUG>(a, st, q, cd.np, qa0, qa1, c_q, S_q, cd.j0, main_end, qb, slot, r16,
+                               grp, pslot);
+    if (cd.last) {  // partial of the piece
       if (pend) store_partial();
-      const float Mh = row16_sum(st.Ms);
-      pend_L = row16_sum(st.Ls);
-      pend_Z = st.Zr;
-      pend_P = a.ws.parts + (static_cast<size_t>(cd.slot) * GQA + grp) * kPart;
+      F::finish(st, pend_A, pend_Z, pend_L);
+      pend_P = a.ws.parts + static_cast<size_t>(cd.slot) * GQA * kPart;
       pend_bg = cd.b * a.Hkv + cd.g;
       pend_opens = piece_opens;
       pend_closes = cd.closes;
-#pragma unroll
-      for (int o = 0; o < 8; ++o) pend_A[o] = st.O[o] + Mh;
       pend = true;
     }
     if (have1 && d1.first) group_query(d1, raw1);  // operands for the next iteration
@@ -914,20 +1168,49 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   const dim3 block(256), groups(c.Hkv, B), grid(ws.n_waves / 4 + prot_groups);
   if (B > 256) hipLaunchKernelGGL(plan_kernel, dim3(1), block, 0, s, a);
   if (dbg) {
-    hipLaunchKernelGGL(main_kernel<true>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((main_kernel<Kv4Format, true>), grid, block, 0, s, a);
     hipLaunchKernelGGL(merge_kernel, groups, block, 0, s, a);
   } else {
     if (ev_main_begin) {
       const hipError_t e = hipEventRecord(ev_main_begin, s);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(main_kernel<false>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((main_kernel<Kv4Format, false>), grid, block, 0, s, a);
     if (ev_main_end) {
       const hipError_t e = hipEventRecord(ev_main_end, s);
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(merge_kernel, groups, block, 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv8_decode(const uint8_t* pages, int Hkv, const uint16_t* q, const int32_t* ctx,
+                             const int32_t* page_table, int pt_stride, int B, int Hq,
+                             float scale_log2, float* out, float* lse, const DecodeWorkspace& ws,
+                             const DecodeDebug* dbg, hipStream_t s) {
+  if (ws.n_waves <= 0 || ws.n_waves % 4 != 0) return hipErrorInvalidValue;
+  DecArgs a{};
+  a.pages = pages;
+  a.Hkv = Hkv;
+  a.Hq = Hq;
+  a.B = B;
+  a.q = reinterpret_cast<const uint32_t*>(q);
+  a.ctx = ctx;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.sink = 0;  // every page in the streamed region, no protected partial
+  a.window = 0;
+  a.scale_log2 = scale_log2;
+  a.out = out;
+  a.lse = lse;
+  a.ws = ws;
+  if (dbg) a.dbg = *dbg;
+  const dim3 block(256), groups(Hkv, B), grid(ws.n_waves / 4);
+  if (B > 256) hipLaunchKernelGGL(plan_kernel, dim3(1), block, 0, s, a);
+  if (dbg) hipLaunchKernelGGL((main_kernel<Kv8Format, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((main_kernel<Kv8Format, false>), grid, block, 0, s, a);
+  hipLaunchKernelGGL(merge_kernel, groups, block, 0, s, a);
   return hipGetLastError();
 }
 

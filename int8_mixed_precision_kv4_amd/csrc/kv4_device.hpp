@@ -17,6 +17,12 @@ constexpr int OFF_VCODE = 1024;
 constexpr int OFF_KMETA = 2048;
 constexpr int OFF_VMETA = 2112;
 constexpr int GQA = 4;           // query heads per kv-head handled by the decode kernels
+// KV8-everywhere pool block per (page, kv-head): K codes [16][128] | V codes
+// [128][16] | s_k FP16 [16] | s_v FP16 [16]
+constexpr int KV8_BLOCK_BYTES = 4160;
+constexpr int KV8_OFF_V = 2048;
+constexpr int KV8_OFF_SK = 4096;
+constexpr int KV8_OFF_SV = 4128;
 
 // ---------------------------------------------------------------- formats --
 

@@ -40,10 +40,16 @@ constexpr int kPart = 132;  // A[128], Z, l, 2 pad
 #ifndef KV4_MAIN_WAVES_PER_SIMD
 #define KV4_MAIN_WAVES_PER_SIMD 4
 #endif
+// The KV8-everywhere instantiation holds more operands per wave (138 VGPRs)
+// and runs 3 waves per SIMD.
+#ifndef KV8_MAIN_WAVES_PER_SIMD
+#define KV8_MAIN_WAVES_PER_SIMD 3
+#endif
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_waves);
 DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves);
 int main_region_waves();  // size of the main-region grid on the current device
+int kv8_region_waves();   // the same for the KV8-everywhere instantiation
 
 hipError_t launch_append(const CacheView& c, const uint16_t* k, const uint16_t* v,
                          const int32_t* pos, const int32_t* slot, const int32_t* page_table,
@@ -52,6 +58,18 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t*
                           const int32_t* cu, const int32_t* start, const int32_t* slot,
                           const int32_t* page_table, int pt_stride, int nseq, int max_seqlen,
                           hipStream_t s);
+hipError_t launch_kv8_append(uint8_t* pages, int Hkv, const uint16_t* k, const uint16_t* v,
+                             const int32_t* pos, const int32_t* page_table, int pt_stride, int B,
+                             hipStream_t s);
+hipError_t launch_kv8_prefill(uint8_t* pages, int Hkv, const uint16_t* k, const uint16_t* v,
+                              const int32_t* cu, const int32_t* start, const int32_t* page_table,
+                              int pt_stride, int nseq, int max_seqlen, hipStream_t s);
+// KV8-everywhere decode: the main kernel's plan and pipeline over every page,
+// no protected region (workspace as for launch_decode)
+hipError_t launch_kv8_decode(const uint8_t* pages, int Hkv, const uint16_t* q, const int32_t* ctx,
+                             const int32_t* page_table, int pt_stride, int B, int Hq,
+                             float scale_log2, float* out, float* lse, const DecodeWorkspace& ws,
+                             const DecodeDebug* dbg, hipStream_t s);
 hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* ctx,
                          const int32_t* slot, const int32_t* page_table, int pt_stride, int B,
                          int Hq, float scale_log2, float* out, float* lse,

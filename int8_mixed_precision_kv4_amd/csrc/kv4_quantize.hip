@@ -139,7 +139,84 @@ __global__ __launch_bounds__(256) void prefill_kernel(QuantArgs a, const int32_t
   *vw = w;
 }
 
+// ------------------------------------------------------------ KV8 pool --
+// KV8 everywhere (the INT8 comparison variant): every position in the side
+// rows' representation (rotated key, symmetric INT8 per 128-dim vector, FP16
+// scale), in a paged pool whose block per (page, kv-head) is K codes
+// [16][128] token-major | V codes [128][16] channel-major | s_k[16] | s_v[16].
+// Every byte belongs to one position, so tokens are written independently.
+
+struct Kv8Args {
+  uint8_t* pages;
+  int Hkv;
+  const uint32_t* k;
+  const uint32_t* v;
+  const int32_t* page_table;
+  int pt_stride;
+};
+
+__device__ __forceinline__ void kv8_write(const Kv8Args& a, int g, int phys, int t, uint32_t kw,
+                                          uint32_t vw, int lane) {
+  float k0 = bf16_lo(kw), k1 = bf16_hi(kw);
+  const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
+  fwht128_wave(k0, k1);
+  const Int8Meta ks = int8_meta(wave_max(fmaxf(fabsf(k0), fabsf(k1))));
+  const Int8Meta vs = int8_meta(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
+  uint8_t* blk = a.pages + (static_cast<size_t>(phys) * a.Hkv + g) * KV8_BLOCK_BYTES;
+  reinterpret_cast<uint16_t*>(blk + HD * t)[lane] =
+      static_cast<uint16_t>((static_cast<uint32_t>(int8_code(k0, ks)) & 0xFFu) |
+                            ((static_cast<uint32_t>(int8_code(k1, ks)) & 0xFFu) << 8));
+  blk[KV8_OFF_V + PAGE * (2 * lane) + t] = static_cast<uint8_t>(int8_code(v0, vs));
+  blk[KV8_OFF_V + PAGE * (2 * lane + 1) + t] = static_cast<uint8_t>(int8_code(v1, vs));
+  if (lane == 0) {
+    reinterpret_cast<uint16_t*>(blk + KV8_OFF_SK)[t] = static_cast<uint16_t>(ks.s16);
+    reinterpret_cast<uint16_t*>(blk + KV8_OFF_SV)[t] = static_cast<uint16_t>(vs.s16);
+  }
+}
+
+// One token per sequence; one wave per (kv-head, sequence).
+__global__ __launch_bounds__(64) void kv8_append_kernel(Kv8Args a, const int32_t* __restrict__ pos_arr) {
+  const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int pos = pos_arr[b];
+  const size_t vec = static_cast<size_t>(b) * a.Hkv + g;
+  const int phys = a.page_table[static_cast<size_t>(b) * a.pt_stride + (pos >> 4)];
+  kv8_write(a, g, phys, pos & (PAGE - 1), a.k[vec * 64 + lane], a.v[vec * 64 + lane], lane);
+}
+
+// Re-prefill: one wave per (token, kv-head); workgroup (x, g, s) covers
+// tokens 4x .. 4x+3 of sequence s.
+__global__ __launch_bounds__(256) void kv8_prefill_kernel(Kv8Args a, const int32_t* __restrict__ cu,
+                                                          const int32_t* __restrict__ start_pos) {
+  const int g = blockIdx.y, s = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = 4 * blockIdx.x + wave;
+  if (i >= cu[s + 1] - cu[s]) return;
+  const int p = start_pos[s] + i;
+  const size_t vec = (static_cast<size_t>(cu[s]) + i) * a.Hkv + g;
+  const int phys = a.page_table[static_cast<size_t>(s) * a.pt_stride + (p >> 4)];
+  kv8_write(a, g, phys, p & (PAGE - 1), a.k[vec * 64 + lane], a.v[vec * 64 + lane], lane);
+}
+
 }  // namespace
+
+hipError_t launch_kv8_append(uint8_t* pages, int Hkv, const uint16_t* k, const uint16_t* v,
+                             const int32_t* pos, const int32_t* page_table, int pt_stride, int B,
+                             hipStream_t s) {
+  Kv8Args a{pages, Hkv, reinterpret_cast<const uint32_t*>(k), reinterpret_cast<const uint32_t*>(v),
+            page_table, pt_stride};
+  hipLaunchKernelGGL(kv8_append_kernel, dim3(Hkv, B), dim3(64), 0, s, a, pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv8_prefill(uint8_t* pages, int Hkv, const uint16_t* k, const uint16_t* v,
+                              const int32_t* cu, const int32_t* start, const int32_t* page_table,
+                              int pt_stride, int nseq, int max_seqlen, hipStream_t s) {
+  Kv8Args a{pages, Hkv, reinterpret_cast<const uint32_t*>(k), reinterpret_cast<const uint32_t*>(v),
+            page_table, pt_stride};
+  hipLaunchKernelGGL(kv8_prefill_kernel, dim3((max_seqlen + 3) / 4, Hkv, nseq), dim3(256), 0, s, a,
+                     cu, start);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const CacheView& c, const uint16_t* k, const uint16_t* v,
                          const int32_t* pos, const int32_t* slot, const int32_t* page_table,

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "kv4.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(kv4[a-z0-9_]*)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(kv[48][a-z0-9_]*)\s*\(",
                                  text, flags=re.M)))
 
 
