@@ -381,7 +381,7 @@ def traffic_from_counters(fetch_db, write_db, command):
 
     fetch = per_kernel(fetch_db, "FETCH_SIZE")
     write = per_kernel(write_db, "WRITE_SIZE")
-    main_k = pick(fetch, r"main_kernel<false>")[0]
+    main_k = pick(fetch, r"main_kernel<.*Kv4Format, false>")[0]
     # the 2 GiB device copy: the largest dispatch of the runtime's copy kernel
     copy_f = max(v for k in pick(fetch, r"copyBuffer") for v in fetch[k])
     copy_w = max(v for k in pick(write, r"copyBuffer") for v in write[k])
