@@ -416,6 +416,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the 2 GiB device copy probe")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
+    ap.add_argument("--workload", choices=("qwen8b", "refill"), default="qwen8b",
+                    help="qwen8b: contexts from the length-biased sampler; refill: the B=256 batch "
+                         "of one steady-state step of a simulated continuous-refill run, same law")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the protection-budget variants (run last; they rebuild the side rows)")
     args = ap.parse_args()
@@ -434,6 +437,9 @@ def main():
     dev = torch.device("cuda:0")
     kv4.lib()
     wl = make_workload(WORKLOAD)
+    if args.workload == "refill":
+        from synth.concentration import LengthLaw, refill_snapshot
+        wl = make_workload(WORKLOAD, ctx=refill_snapshot(LengthLaw.lognormal(3000, 2250), wl.B, wl.seed))
     scale = 1.0 / math.sqrt(128)
     log(f"workload qwen8b: B={wl.B} Hq/Hkv={wl.Hq}/{wl.Hkv} mean ctx {wl.ctx.mean():.0f} "
         f"max {wl.max_ctx} pages/layer {wl.num_pages}")
@@ -590,7 +596,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": ("qwen8b decode step: B=256, Hq/Hkv=32/8, head_dim 128, page 16, "
                                 "36 layers, ctx = U[128,512] + length-biased lognormal(3000, 2250) "
-                                "position + 1; per layer kv4_append then kv4_decode_attention"),
+                                "position + 1; per layer kv4_append then kv4_decode_attention"
+                                + ("; contexts replayed from one steady-state step of a simulated "
+                                   "continuous-refill run" if args.workload == "refill" else "")),
                    "B": B, "layers": LAYERS, "mean_ctx": round(float(wl.ctx.mean()), 1),
                    "max_ctx": wl.max_ctx, "parallelism": "single GPU"},
         "decode_tokens_per_s": round(B / t_decode, 1),
