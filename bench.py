@@ -348,12 +348,17 @@ def cpu_baseline(wl, layer0, shared, budget_s):
         reps += 1
     t_layer_sample = t_total / reps
     t_step = t_layer_sample * (wl.ctx.sum() / ctx.sum()) * wl.layers
+    # the same layer once on one thread
+    t0 = time.perf_counter()
+    oracle.append(cache, ka, va, (ctx - 1).astype(np.int32), slots, table)
+    oracle.decode(cache, q, ctx.astype(np.int32), slots, table, wl.Hq, 1.0 / math.sqrt(128), nthreads=1)
+    t_single = time.perf_counter() - t0
     cpu = open("/proc/cpuinfo").read().split("model name")[1].split("\n")[0].strip(" :\t") \
         if os.path.exists("/proc/cpuinfo") else "unknown"
     return dict(value=round(wl.B / t_step, 3), unit="tokens/s", cores=threads, kind="oracle",
                 sample=(f"layer 0 of 36 (all {len(sample)} sequences, mean ctx {ctx.mean():.0f}): "
                         f"append + 32-head decode, {reps} reps in {t_total:.1f}s; x36 layers"),
-                cpu=cpu), (sample, out, lse)
+                cpu=cpu, single_thread_layer_s=round(t_single, 3)), (sample, out, lse)
 
 
 def traffic_from_counters(fetch_db, write_db, command):

@@ -133,3 +133,35 @@ def test_fullsize_sampled_parity(index, layer):
     assert err <= OUT_TOL and lerr <= LSE_TOL, (err, lerr)
     # every output is finite and every lse at least the largest logit seen by any region
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("first", [0, 9, 18, 27])
+def test_benchmark_workload_every_layer(first):
+    """All 36 layers of the 256-sequence benchmark workload, built and decoded
+    on the GPU as bench.py does (each layer its own values and cache); per
+    layer the shortest sequence and one drawn at random are rebuilt by the
+    oracle: their pages, side rows and query codes bit-exact, out and lse
+    within the bar."""
+    dev = torch.device("cuda")
+    wl = make_workload(4)
+    order = np.argsort(wl.ctx, kind="stable")
+    for layer in range(first, first + 9):
+        cache, k, v, q, off, table, slots = _build_gpu(wl, layer, dev)
+        ctx_d = torch.from_numpy(wl.ctx.astype(np.int32)).to(dev)
+        out, lse = kv4.decode_attention(cache, q, ctx_d, slots, table, int(wl.ctx.max()), SCALE)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(1000 + layer)
+        sample = np.unique([int(order[0]), int(rng.integers(wl.B))])
+        ref, rtable, ref_out, ref_lse, ref_dbg = _oracle_for(wl, sample, k, v, q, off)
+        for i, b in enumerate(sample):
+            n = int((wl.ctx[b] + 15) // 16)
+            got = cache.pages[torch.from_numpy(wl.page_table[b, :n].astype(np.int64)).to(dev)].cpu().numpy()
+            assert np.array_equal(got, ref.pages[rtable[i, :n]]), f"layer {layer}: pages of {b}"
+            assert np.array_equal(cache.side_codes[int(wl.slots[b])].cpu().numpy(), ref.side_codes[i])
+        sel = torch.from_numpy(sample).to(dev)
+        err = float(np.abs(out[sel].cpu().numpy() - ref_out).max())
+        lerr = float(np.abs(lse[sel].cpu().numpy() - ref_lse).max())
+        _say(f"[layers] layer {layer} sequences {sample.tolist()}: out {err:.2e} lse {lerr:.2e}")
+        assert err <= OUT_TOL and lerr <= LSE_TOL, (layer, err, lerr)
+        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+        del cache, k, v, q
