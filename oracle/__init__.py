@@ -60,6 +60,11 @@ def lib():
         _lib.kv4ref_quant_query.argtypes = [C.c_void_p] * 4 + [C.c_int64]
         _lib.kv4ref_exp2s_coeffs.argtypes = [C.c_void_p]
         _lib.kv4ref_append.argtypes = [C.POINTER(_Cache)] + [C.c_void_p] * 5 + [C.c_int32] * 2
+        KC = C.POINTER(_Cache)
+        _lib.mxref_append.argtypes = [KC] + [C.c_void_p] * 5 + [C.c_int32] * 2
+        _lib.mxref_prefill.argtypes = [KC] + [C.c_void_p] * 6 + [C.c_int32] * 3
+        _lib.mxref_decode.argtypes = ([KC] + [C.c_void_p] * 4 + [C.c_int32] * 3 + [C.c_float]
+                                      + [C.c_void_p] * 2 + [C.c_int32])
         K8 = C.POINTER(_Kv8Cache)
         _lib.kv8ref_append.argtypes = [K8] + [C.c_void_p] * 4 + [C.c_int32] * 2
         _lib.kv8ref_prefill.argtypes = [K8] + [C.c_void_p] * 5 + [C.c_int32] * 3
@@ -319,3 +324,54 @@ def kv8_decode(cache: Kv8Cache, q, ctx_len, page_table, Hq: int, softmax_scale: 
     if rc != 0:
         raise ValueError(f"kv8ref_decode failed ({rc})")
     return out, lse, dbg
+
+
+# ---------------------------------------------------------- MXFP4 variant --
+
+MX_OFF_V, MX_OFF_KS, MX_OFF_VS = 1024, 2048, 2112
+
+
+def mx_append(cache: Cache, k, v, pos, slot, page_table):
+    """The MXFP4 variant's append: main-region block in OCP MXFP4, side rows as kv4 append."""
+    k, v = _c(k, np.uint16), _c(v, np.uint16)
+    pos, table = _c(pos, np.int32), _c(page_table, np.int32)
+    slot = None if slot is None else _c(slot, np.int32)
+    B = pos.shape[0]
+    assert k.shape == (B, cache.Hkv, HD) and v.shape == k.shape
+    st = cache._struct()
+    rc = lib().mxref_append(C.byref(st), _p(k), _p(v), _p(pos), None if slot is None else _p(slot),
+                            _p(table), table.shape[1], B)
+    if rc != 0:
+        raise ValueError(f"mxref_append failed ({rc}): invalid protection budget")
+
+
+def mx_prefill(cache: Cache, k, v, cu_seqlens, start_pos, slot, page_table, nthreads=None):
+    k, v = _c(k, np.uint16), _c(v, np.uint16)
+    cu, start, table = (_c(cu_seqlens, np.int32), _c(start_pos, np.int32), _c(page_table, np.int32))
+    slot = None if slot is None else _c(slot, np.int32)
+    assert k.shape == (int(cu[-1]), cache.Hkv, HD)
+    st = cache._struct()
+    rc = lib().mxref_prefill(C.byref(st), _p(k), _p(v), _p(cu), _p(start),
+                             None if slot is None else _p(slot), _p(table), table.shape[1],
+                             start.shape[0], nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"mxref_prefill failed ({rc}): invalid protection budget")
+
+
+def mx_decode(cache: Cache, q, ctx_len, slot, page_table, Hq: int, softmax_scale: float,
+              nthreads=None):
+    """Returns (out [B][Hq][128] f64, lse [B][Hq] f64) of the MXFP4 variant."""
+    q = _c(q, np.uint16)
+    ctx, table = _c(ctx_len, np.int32), _c(page_table, np.int32)
+    slot = None if slot is None else _c(slot, np.int32)
+    B = ctx.shape[0]
+    assert q.shape == (B, Hq, HD)
+    out = np.zeros((B, Hq, HD), np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+    st = cache._struct()
+    rc = lib().mxref_decode(C.byref(st), _p(q), _p(ctx), None if slot is None else _p(slot),
+                            _p(table), table.shape[1], B, Hq, softmax_scale, _p(out), _p(lse),
+                            nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"mxref_decode failed ({rc})")
+    return out, lse

@@ -271,3 +271,102 @@ def kv8_decode_one(pages, q_bits, L, g, table_row, scale_log2):
         A += e * vh
         ell += e
     return A / ell, math.log(2) * (zmax + math.log2(ell)), qk
+
+
+
+# ------------------------------------------------------- MXFP4 variant --
+
+E2M1_GRID = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+             Fraction(4), Fraction(6)]  # magnitudes of codes 0..7
+
+
+def mx_quant_block(x):
+    """OCP MXFP4 block by exact rationals: E = floor(log2 amax) - 2 (clamped to
+    [-127, 127]; -127 for an all-zero block), code = the grid magnitude nearest
+    to |x| / 2^E (ties to the even code), saturated at 6, sign from x.
+    Returns (codes [32], E8M0 byte)."""
+    xs = [Fraction(float(v)) for v in x]
+    amax = max(abs(v) for v in xs)
+    if amax == 0:
+        E = -127
+    else:
+        E = 0
+        while Fraction(2) ** (E + 1) <= amax:
+            E += 1
+        while Fraction(2) ** E > amax:
+            E -= 1
+        E = max(-127, min(127, E - 2))
+    codes = []
+    for v, f in zip(xs, x):
+        y = abs(v) / Fraction(2) ** E
+        best = min(range(8), key=lambda c: (abs(E2M1_GRID[c] - y), c % 2))
+        if y > 6:
+            best = 7
+        codes.append(best | (8 if math.copysign(1.0, float(f)) < 0 else 0))
+    return codes, E + 127
+
+
+def e2m1(code) -> float:
+    return float((-1 if code & 8 else 1) * E2M1_GRID[code & 7])
+
+
+def unpack_mx_block(block: np.ndarray):
+    """Independent reading of one MXFP4 block: (k [16][128], v [16][128]) dequantized exactly."""
+    b = np.asarray(block, np.uint8)
+    k = np.zeros((PAGE, HD))
+    v = np.zeros((PAGE, HD))
+    for t in range(PAGE):
+        for j in range(HD):
+            kc = (int(b[64 * t + j // 2]) >> (4 * (j % 2))) & 15
+            vc = (int(b[1024 + 8 * j + t // 2]) >> (4 * (t % 2))) & 15
+            k[t, j] = e2m1(kc) * 2.0 ** (int(b[2048 + 4 * t + j // 32]) - 127)
+            v[t, j] = e2m1(vc) * 2.0 ** (int(b[2112 + 4 * t + j // 32]) - 127)
+    return k, v
+
+
+def mx_decode_one(pages, side_codes, side_scales, q_bits, L, slot, g, table_row, scale_log2,
+                  sink=SINK, window=WINDOW):
+    """MXFP4 variant, one (sequence, q-head): protected region as decode_one,
+    main region [s, L-w) with z = fp32(bf16(q_rot) . k^) * c, FP32 exp2s weights
+    relative to the region max, exact v^; exact merge."""
+    qc, s_q, _ = query_codes(q_bits)
+    c_q = f32_mul(s_q, scale_log2)
+    q = (q_bits.astype(np.uint32) << 16).view(np.float32)
+    r = (fwht_f32_recursive(q) * inv_sqrt128_f32()).astype(np.float32)
+    qb = np.array([rnbf16(float(x)) for x in r])
+    parts = []
+    prot = list(range(0, min(sink, L))) + list(range(max(sink, L - window), L))
+    zs, rows = [], []
+    for p in prot:
+        row = p if p < sink else sink + p % window
+        d8 = int(np.dot(qc, side_codes[slot, g, row, 0].astype(np.int64)))
+        sk = float(np.array([side_scales[slot, g, row, 0]], np.uint16).view(np.float16)[0])
+        zs.append(f32_mul(f32_mul(float(d8), sk), c_q))
+        rows.append(row)
+    if zs:
+        zmax = max(zs)
+        A, ell = np.zeros(HD), 0.0
+        for z, row in zip(zs, rows):
+            e = exp2s(f32_sub(z, zmax))
+            sv = float(np.array([side_scales[slot, g, row, 1]], np.uint16).view(np.float16)[0])
+            A += e * np.array([rnbf16(f32_mul(sv, float(c))) for c in side_codes[slot, g, row, 1]])
+            ell += e
+        parts.append((A, zmax, ell))
+    mz, mv = [], []
+    for p in range(sink, max(sink, L - window)):
+        kk, vv = unpack_mx_block(pages[table_row[p // PAGE], g])
+        d = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(qb, kk[p % PAGE]))
+        mz.append(f32_mul(rn32(d), scale_log2))
+        mv.append(vv[p % PAGE])
+    if mz:
+        zmax = max(mz)
+        A, ell = np.zeros(HD), 0.0
+        for z, vv in zip(mz, mv):
+            e = exp2s(f32_sub(z, zmax))
+            A += e * vv
+            ell += e
+        parts.append((A, zmax, ell))
+    Z = max(p[1] for p in parts)
+    num = sum(2.0 ** (p[1] - Z) * p[0] for p in parts)
+    den = sum(2.0 ** (p[1] - Z) * p[2] for p in parts)
+    return num / den, math.log(2) * (Z + math.log2(den))

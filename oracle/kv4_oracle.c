@@ -769,3 +769,189 @@ int kv8ref_decode(const kv8ref_cache *c, const uint16_t *q, const int32_t *ctx_l
   }
   return bad ? -2 : 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4 variant (KV4-RL pages, comparison of 4-bit formats, appendix D.4):  */
+/* the main region stored in OCP MXFP4 instead of INT4 group-affine; the     */
+/* rotation, the INT8 side buffer, the protected path and the merge are as   */
+/* above.  Block per (page, kv-head), 2176 B: K codes [16][64] (E2M1, channel */
+/* 2i low nibble of byte i) | V codes [128][8] (channel-major, position 2k   */
+/* low nibble of byte k) | K scales E8M0 [16 positions][4 blocks] | V scales */
+/* E8M0 [16][4]; block b = channels 32b .. 32b+31.                           */
+/* ------------------------------------------------------------------------ */
+
+enum { MX_OFF_V = 1024, MX_OFF_KS = 2048, MX_OFF_VS = 2112 };
+
+/* E2M1 value of a 4-bit code: sign, 2 exponent bits (bias 1), 1 mantissa bit. */
+static double e2m1_value(int code) {
+  const int e = (code >> 1) & 3, m = code & 1;
+  const double mag = e == 0 ? 0.5 * m : (1.0 + 0.5 * m) * ldexp(1.0, e - 1);
+  return (code & 8) ? -mag : mag;
+}
+
+/* Nearest E2M1 code of y (ties to the even mantissa), saturating at +-6; the
+ * sign bit follows y's sign (so -0.2 gives the code of -0). */
+static int e2m1_code(double y) {
+  const double a = fabs(y);
+  int best = 0;
+  for (int c = 1; c < 8; c++) {
+    const double d = fabs(e2m1_value(c) - a), db = fabs(e2m1_value(best) - a);
+    if (d < db || (d == db && (c & 1) == 0)) best = c;
+  }
+  if (a > 6.0) best = 7;
+  return best | (signbit(y) ? 8 : 0);
+}
+
+/* OCP MX block quantizer: E = floor(log2(amax)) - 2 (2 = largest E2M1
+ * exponent), clamped to [-127, 127], E = -127 for an all-zero block; codes =
+ * E2M1 of x / 2^E.  Returns the E8M0 byte E + 127. */
+static uint8_t mx_block(const float *x, uint8_t *codes /* 32 */) {
+  float amax = 0.0f;
+  for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(x[i]));
+  int E = -127;
+  if (amax > 0.0f) {
+    int ex;
+    frexpf(amax, &ex); /* amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+    E = ex - 1 - 2;
+    if (E < -127) E = -127;
+    if (E > 127) E = 127;
+  }
+  for (int i = 0; i < 32; i++) codes[i] = (uint8_t)e2m1_code(ldexp((double)x[i], -E));
+  return (uint8_t)(E + 127);
+}
+
+static void mx_append_one(const kv4ref_cache *c, int g, const uint16_t *k16, const uint16_t *v16,
+                          int32_t pos, int32_t slot, const int32_t *table_row) {
+  float k[HD], v[HD];
+  for (int i = 0; i < HD; i++) {
+    k[i] = kv4ref_bf16_to_f32(k16[i]);
+    v[i] = kv4ref_bf16_to_f32(v16[i]);
+  }
+  fwht128(k);
+  uint8_t *blk = block_at(c, table_row[pos / PAGE], g);
+  const int t = pos % PAGE;
+  for (int b = 0; b < 4; b++) {
+    uint8_t kc[32], vc[32];
+    blk[MX_OFF_KS + 4 * t + b] = mx_block(k + 32 * b, kc);
+    blk[MX_OFF_VS + 4 * t + b] = mx_block(v + 32 * b, vc);
+    for (int i = 0; i < 16; i++) blk[64 * t + 16 * b + i] = (uint8_t)(kc[2 * i] | (kc[2 * i + 1] << 4));
+    for (int i = 0; i < 32; i++) {
+      uint8_t *byte = blk + MX_OFF_V + 8 * (32 * b + i) + t / 2;
+      *byte = (t & 1) ? (uint8_t)((*byte & 0x0F) | (vc[i] << 4)) : (uint8_t)((*byte & 0xF0) | vc[i]);
+    }
+  }
+  int row = side_row(c, pos);
+  if (row < 0) return;
+  quant_int8(k, side_code_at(c, slot, g, row, 0), side_scale_at(c, slot, g, row, 0));
+  quant_int8(v, side_code_at(c, slot, g, row, 1), side_scale_at(c, slot, g, row, 1));
+}
+
+int mxref_append(const kv4ref_cache *c, const uint16_t *k, const uint16_t *v, const int32_t *pos,
+                 const int32_t *slot, const int32_t *page_table, int32_t pt_stride, int32_t B) {
+  const int H = c->num_kv_heads;
+  if (!budget_ok(c)) return -1;
+  for (int b = 0; b < B; b++)
+    for (int g = 0; g < H; g++) {
+      size_t off = ((size_t)b * H + g) * HD;
+      mx_append_one(c, g, k + off, v + off, pos[b], slot ? slot[b] : b,
+                    page_table + (size_t)b * pt_stride);
+    }
+  return 0;
+}
+
+int mxref_prefill(const kv4ref_cache *c, const uint16_t *k, const uint16_t *v,
+                  const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *slot,
+                  const int32_t *page_table, int32_t pt_stride, int32_t nseq, int32_t nthreads) {
+  const int H = c->num_kv_heads;
+  (void)nthreads;
+  if (!budget_ok(c)) return -1;
+#pragma omp parallel for schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int sq = 0; sq < nseq; sq++)
+    for (int32_t i = 0; i < cu_seqlens[sq + 1] - cu_seqlens[sq]; i++) {
+      size_t tok = (size_t)cu_seqlens[sq] + (size_t)i;
+      for (int g = 0; g < H; g++) {
+        size_t off = (tok * H + g) * HD;
+        mx_append_one(c, g, k + off, v + off, start_pos[sq] + i, slot ? slot[sq] : sq,
+                      page_table + (size_t)sq * pt_stride);
+      }
+    }
+  return 0;
+}
+
+/* Dequantized MXFP4 entry t of a block (exact). */
+static void mx_unpack(const uint8_t *blk, int t, double k[HD], double v[HD]) {
+  for (int j = 0; j < HD; j++) {
+    const int kc = (blk[64 * t + j / 2] >> (4 * (j & 1))) & 15;
+    const int vcd = (blk[MX_OFF_V + 8 * j + t / 2] >> (4 * (t & 1))) & 15;
+    k[j] = ldexp(e2m1_value(kc), (int)blk[MX_OFF_KS + 4 * t + j / 32] - 127);
+    v[j] = ldexp(e2m1_value(vcd), (int)blk[MX_OFF_VS + 4 * t + j / 32] - 127);
+  }
+}
+
+/* Main region of the MXFP4 variant, one partial: z = (bf16(q_rot) . k^) *
+ * scale_log2 (the dot exact, rounded once to FP32), e = exp2s(z - z_max) in
+ * FP32, A = sum e v^ with the exactly dequantized values. */
+static void mx_main(const kv4ref_cache *c, const int32_t *trow, int g, int32_t m0, int32_t m1,
+                    const float qb[HD], float scale_log2, partial_t *out) {
+  out->Z = -INFINITY;
+  out->l = 0.0;
+  for (int j = 0; j < HD; j++) out->A[j] = 0.0;
+  const int n = m1 - m0;
+  if (n <= 0) return;
+  float *z = (float *)malloc(sizeof(float) * (size_t)n);
+  double *vals = (double *)malloc(sizeof(double) * (size_t)n * HD);
+  float zmax = -INFINITY;
+  for (int i = 0; i < n; i++) {
+    const int p = m0 + i;
+    double kk[HD];
+    mx_unpack(block_at(c, trow[p / PAGE], g), p % PAGE, kk, vals + (size_t)i * HD);
+    double d = 0.0;
+    for (int j = 0; j < HD; j++) d += (double)qb[j] * kk[j]; /* exact: few significant bits */
+    z[i] = (float)d * scale_log2;
+    if (z[i] > zmax) zmax = z[i];
+  }
+  out->Z = zmax;
+  for (int i = 0; i < n; i++) {
+    const float e = exp2s(z[i] - zmax);
+    out->l += (double)e;
+    for (int j = 0; j < HD; j++) out->A[j] += (double)e * vals[(size_t)i * HD + j];
+  }
+  free(vals);
+  free(z);
+}
+
+int mxref_decode(const kv4ref_cache *c, const uint16_t *q, const int32_t *ctx_len,
+                 const int32_t *slot, const int32_t *page_table, int32_t pt_stride, int32_t B,
+                 int32_t Hq, float softmax_scale, double *out, double *lse, int32_t nthreads) {
+  exp2_init();
+  const int Hkv = c->num_kv_heads;
+  if (Hkv <= 0 || Hq % Hkv != 0 || !budget_ok(c)) return -1;
+  const int G = Hq / Hkv;
+  const float scale_log2 = kv4ref_scale_log2(softmax_scale);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int bh = 0; bh < B * Hq; bh++) {
+    const int b = bh / Hq, h = bh % Hq, g = h / G;
+    const int32_t L = ctx_len[b];
+    if (L < 1 || (L + PAGE - 1) / PAGE > pt_stride) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    float qr[HD];
+    for (int i = 0; i < HD; i++) qr[i] = kv4ref_bf16_to_f32(q[(size_t)bh * HD + i]);
+    fwht128(qr);
+    int8_t qc[HD];
+    float s_q, qb[HD];
+    int32_t qsum;
+    quant_query(qr, qc, &s_q, &qsum);
+    for (int i = 0; i < HD; i++) qb[i] = kv4ref_bf16_to_f32(kv4ref_f32_to_bf16(qr[i]));
+    partial_t parts[2];
+    protected_region(c, slot ? slot[b] : b, g, L, qc, s_q * scale_log2, &parts[0], NULL);
+    const int32_t main_end = L - c->window;
+    mx_main(c, page_table + (size_t)b * pt_stride, g, c->sink, main_end > c->sink ? main_end : c->sink,
+            qb, scale_log2, &parts[1]);
+    merge(parts, 2, out + (size_t)bh * HD, lse + bh);
+  }
+  return bad ? -2 : 0;
+}

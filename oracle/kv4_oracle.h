@@ -102,6 +102,18 @@ int kv8ref_decode(const kv8ref_cache *c, const uint16_t *q, const int32_t *ctx_l
                   float softmax_scale, double *out, double *lse, const kv4ref_debug *dbg,
                   int32_t nthreads);
 
+/* MXFP4 variant: the same cache (pages of 2176 B, side buffer, budget) with
+ * the main region in OCP MXFP4: K codes [16][64] | V codes [128][8] | K scales
+ * E8M0 [16][4] | V scales E8M0 [16][4]. */
+int mxref_append(const kv4ref_cache *c, const uint16_t *k, const uint16_t *v, const int32_t *pos,
+                 const int32_t *slot, const int32_t *page_table, int32_t pt_stride, int32_t B);
+int mxref_prefill(const kv4ref_cache *c, const uint16_t *k, const uint16_t *v,
+                  const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *slot,
+                  const int32_t *page_table, int32_t pt_stride, int32_t nseq, int32_t nthreads);
+int mxref_decode(const kv4ref_cache *c, const uint16_t *q, const int32_t *ctx_len,
+                 const int32_t *slot, const int32_t *page_table, int32_t pt_stride, int32_t B,
+                 int32_t Hq, float softmax_scale, double *out, double *lse, int32_t nthreads);
+
 #ifdef __cplusplus
 }
 #endif
