@@ -249,6 +249,45 @@ def variant_leg(wl, layers, sh, ctx, scale, steps, t_bf16):
                          err_vs_fp64_maxabs=float(err.max()), err_vs_fp64_meanabs=float(err.mean()))
         log(f"variant {name}: {t * 1e3:.3f} ms/step, main {main_us:.1f} us, "
             f"max err vs FP64 {float(err.max()):.3e}")
+    # MXFP4 main region (OCP MXFP4 pages, the same side rows and budget):
+    # the layers' caches are rewritten in that format in place
+    log(f"variant mxfp4: rewriting the pages of {wl.layers} layers in MXFP4")
+    rows_last = torch.from_numpy(off[:-1] + lead).to(dev)
+    for li, L in enumerate(layers):
+        if li == 0:
+            k, v = k0, v0
+        else:
+            k, v, _ = draw_values(wl.seed, li, n_tok, B, Hq, wl.Hkv, device=dev)
+        c = L["cache"]
+        mc = kv4.Kv4Cache(c.pages, c.side_codes, c.side_scales)
+        kv4.mx_prefill_quantize(mc, k[rows_lead].contiguous(), v[rows_lead].contiguous(), cu, zeros,
+                                slots, table, int(lead.max()))
+        kv4.mx_append(mc, L["k_app"], L["v_app"], pos, slots, table)
+        del k, v
+    torch.cuda.synchronize()
+
+    def mx_step():
+        for L in layers:
+            kv4.mx_decode_attention(L["cache"], L["q"], ctx, slots, table, wl.max_ctx, scale, out, lse, ws)
+
+    for _ in range(2):
+        mx_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mx_step()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    kv4.mx_decode_attention(layers[0]["cache"], layers[0]["q"], ctx, slots, table, wl.max_ctx, scale, out,
+                            lse, ws)
+    torch.cuda.synchronize()
+    err = (out[sel].double() - ref).abs()
+    res["mxfp4_rl"] = dict(sink=16, window=128, decode_ms_per_step=round(t * 1e3, 3),
+                           decode_tokens_per_s=round(B / t, 1),
+                           speedup_vs_bf16=round(t_bf16 / t, 3) if t_bf16 else None,
+                           err_vs_fp64_maxabs=float(err.max()), err_vs_fp64_meanabs=float(err.mean()))
+    log(f"variant mxfp4: {t * 1e3:.3f} ms/step, max err vs FP64 {float(err.max()):.3e}")
+
     # KV8 everywhere: every position in the side rows' INT8 representation,
     # attended with the protected path's arithmetic (its own pool per layer)
     for L in layers:
@@ -256,7 +295,6 @@ def variant_leg(wl, layers, sh, ctx, scale, steps, t_bf16):
     torch.cuda.empty_cache()
     log(f"variant kv8: building the INT8 pools of {wl.layers} layers")
     pools = []
-    rows_last = torch.from_numpy(off[:-1] + lead).to(dev)
     for li, L in enumerate(layers):
         if li == 0:
             k, v = k0, v0

@@ -187,6 +187,33 @@ int kv4bench_decode_attention_timed(const kv4_cache_desc *cache, const void *q,
                                     float *lse, void *workspace, size_t workspace_bytes,
                                     void *ev_main_begin, void *ev_main_end, void *stream);
 
+/* ---- variant: MXFP4 main region ----------------------------------------------
+ * The 4-bit format comparison of the pages (KV4-RL, appendix D.4: NVFP4 and
+ * MXFP4 against INT4 group-affine): the same cache descriptor, budget, side
+ * buffer and protected path, with each page block (2176 B) holding the main
+ * region in OCP MXFP4 instead: K codes [16 positions][64 B] (E2M1, channel 2i
+ * in the low nibble of byte i, keys Hadamard-rotated) | V codes [128
+ * channels][8 B] (position 2k low nibble of byte k) | K scales E8M0 [16][4] |
+ * V scales E8M0 [16][4], one scale per 32-channel block: E = floor(log2 amax)
+ * - 2 (clamped to [-127, 127], -127 for an all-zero block), code = E2M1 of
+ * x / 2^E rounded to nearest even and saturated at 6.  The main region is
+ * attended on the exactly dequantized values: logits from the BF16-rounded
+ * rotated query, FP32 softmax weights, FP32 accumulation.  A cache must be
+ * written and read by the same variant. */
+int kv4mx_append(const kv4_cache_desc *cache, const void *k, const void *v, const int32_t *pos,
+                 const int32_t *slot, const int32_t *page_table, int32_t pt_stride, int32_t B,
+                 void *stream);
+int kv4mx_prefill_quantize(const kv4_cache_desc *cache, const void *k, const void *v,
+                           const int32_t *cu_seqlens, const int32_t *start_pos, const int32_t *slot,
+                           const int32_t *page_table, int32_t pt_stride, int32_t nseq,
+                           int32_t max_seqlen, void *stream);
+/* Workspace as kv4_decode_workspace_bytes; arguments and errors as for
+ * kv4_decode_attention. */
+int kv4mx_decode_attention(const kv4_cache_desc *cache, const void *q, const int32_t *ctx_len,
+                           const int32_t *slot, const int32_t *page_table, int32_t pt_stride,
+                           int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale, float *out,
+                           float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---- variant: KV8 everywhere ----------------------------------------------
  * The INT8 point of the pages' quantization-target comparison (KV4-RL,
  * quantization-target comparison, figure 3): every position is stored the way

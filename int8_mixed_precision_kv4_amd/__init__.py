@@ -22,7 +22,8 @@ EXPORTS = ("kv4_append", "kv4_prefill_quantize", "kv4_decode_workspace_bytes",
            "kv4_decode_attention", "kv4_decode_attention_debug", "kv4_strerror",
            "kv4bench_bf16_workspace_bytes", "kv4bench_bf16_paged_decode",
            "kv4bench_decode_attention_timed", "kv8_append", "kv8_prefill_quantize",
-           "kv8_decode_workspace_bytes", "kv8_decode_attention", "kv8_decode_attention_debug")
+           "kv8_decode_workspace_bytes", "kv8_decode_attention", "kv8_decode_attention_debug",
+           "kv4mx_append", "kv4mx_prefill_quantize", "kv4mx_decode_attention")
 KV8_BLOCK_BYTES = 4160
 
 _lib = None
@@ -74,6 +75,9 @@ def lib():
         L.kv4bench_bf16_paged_decode.argtypes = [P, I, I, P, P, P, I, I, I, I, F, P, P, P, Z, P]
         L.kv4bench_decode_attention_timed.argtypes = [D, P, P, P, P, I, I, I, I, F, P, P, P, Z,
                                                       P, P, P]
+        L.kv4mx_append.argtypes = [D, P, P, P, P, P, I, I, P]
+        L.kv4mx_prefill_quantize.argtypes = [D, P, P, P, P, P, P, I, I, I, P]
+        L.kv4mx_decode_attention.argtypes = [D, P, P, P, P, I, I, I, I, F, P, P, P, Z, P]
         D8 = C.POINTER(_Kv8Desc)
         L.kv8_append.argtypes = [D8, P, P, P, P, I, I, P]
         L.kv8_prefill_quantize.argtypes = [D8, P, P, P, P, P, I, I, I, P]
@@ -307,3 +311,39 @@ def kv8_decode_attention_debug(cache: Kv8Cache, q, ctx_len, page_table, max_ctx:
                                             W, B, Hq, int(max_ctx), float(softmax_scale), _ptr(out),
                                             _ptr(lse), _ptr(ws), ws.numel(), C.byref(d), _stream()))
     return out, lse, dbg
+
+
+# ---------------------------------------------------------- MXFP4 variant --
+# The same Kv4Cache (descriptor, side buffer, budget); the page blocks hold the
+# main region in OCP MXFP4.  A cache is written and read by one variant.
+
+def mx_append(cache: Kv4Cache, k, v, pos, slot, page_table):
+    """kv4mx_append: as append, main-region entry in MXFP4."""
+    _check(lib().kv4mx_append(cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(slot),
+                              _ptr(page_table), page_table.shape[1], pos.shape[0], _stream()))
+
+
+def mx_prefill_quantize(cache: Kv4Cache, k, v, cu_seqlens, start_pos, slot, page_table,
+                        max_seqlen: int):
+    _check(lib().kv4mx_prefill_quantize(cache.desc(), _ptr(k), _ptr(v), _ptr(cu_seqlens),
+                                        _ptr(start_pos), _ptr(slot), _ptr(page_table),
+                                        page_table.shape[1], start_pos.shape[0], int(max_seqlen),
+                                        _stream()))
+
+
+def mx_decode_attention(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ctx: int,
+                        softmax_scale: float, out=None, lse=None, workspace=None):
+    """kv4mx_decode_attention: q bf16 [B][Hq][128] -> (out fp32 [B][Hq][128], lse fp32 [B][Hq])."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(cache, B, Hq, max_ctx), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().kv4mx_decode_attention(cache.desc(), _ptr(q), _ptr(ctx_len), _ptr(slot),
+                                        _ptr(page_table), page_table.shape[1], B, Hq, int(max_ctx),
+                                        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                        workspace.numel(), _stream()))
+    return out, lse

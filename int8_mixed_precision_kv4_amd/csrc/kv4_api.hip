@@ -138,7 +138,7 @@ static int decode_common(const kv4_cache_desc* cache, const void* q, const int32
                          int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale, float* out,
                          float* lse, void* workspace, size_t workspace_bytes,
                          const kv4_decode_debug* dbg, void* stream, void* ev0 = nullptr,
-                         void* ev1 = nullptr) {
+                         void* ev1 = nullptr, bool mx = false) {
   int rc = check_decode(cache, q, ctx_len, page_table, pt_stride, B, Hq, max_ctx, out, lse);
   if (rc != KV4_OK) return rc;
   if (B > 65535) return KV4_ERR_SHAPE;
@@ -157,7 +157,7 @@ static int decode_common(const kv4_cache_desc* cache, const void* q, const int32
                                     page_table, pt_stride, B, Hq, scale_log2(softmax_scale), out,
                                     lse, ws, dbg ? &d : nullptr,
                                     static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev0),
-                                    static_cast<hipEvent_t>(ev1));
+                                    static_cast<hipEvent_t>(ev1), mx);
   return e == hipSuccess ? KV4_OK : hip_fail(e);
 }
 
@@ -215,6 +215,45 @@ int kv4bench_bf16_paged_decode(const void* pages, int32_t num_pages, int32_t Hkv
                                          pt_stride, B, Hq, scale_log2(softmax_scale), out, lse,
                                          workspace, nw, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KV4_OK : hip_fail(e);
+}
+
+// ---- MXFP4 variant -----------------------------------------------------------
+
+int kv4mx_append(const kv4_cache_desc* cache, const void* k, const void* v, const int32_t* pos,
+                 const int32_t* slot, const int32_t* page_table, int32_t pt_stride, int32_t B,
+                 void* stream) {
+  int rc = check_cache(cache);
+  if (rc != KV4_OK) return rc;
+  if (!k || !v || !pos || !page_table) return KV4_ERR_NULLPTR;
+  if (B <= 0 || pt_stride <= 0 || B > 65535) return KV4_ERR_SHAPE;
+  hipError_t e = kv4::launch_append(view(cache), static_cast<const uint16_t*>(k),
+                                    static_cast<const uint16_t*>(v), pos, slot, page_table,
+                                    pt_stride, B, static_cast<hipStream_t>(stream), true);
+  return e == hipSuccess ? KV4_OK : hip_fail(e);
+}
+
+int kv4mx_prefill_quantize(const kv4_cache_desc* cache, const void* k, const void* v,
+                           const int32_t* cu_seqlens, const int32_t* start_pos, const int32_t* slot,
+                           const int32_t* page_table, int32_t pt_stride, int32_t nseq,
+                           int32_t max_seqlen, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != KV4_OK) return rc;
+  if (!k || !v || !cu_seqlens || !start_pos || !page_table) return KV4_ERR_NULLPTR;
+  if (nseq <= 0 || nseq > 65535 || pt_stride <= 0 || max_seqlen <= 0) return KV4_ERR_SHAPE;
+  hipError_t e = kv4::launch_prefill(view(cache), static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), cu_seqlens, start_pos, slot,
+                                     page_table, pt_stride, nseq, max_seqlen,
+                                     static_cast<hipStream_t>(stream), true);
+  return e == hipSuccess ? KV4_OK : hip_fail(e);
+}
+
+int kv4mx_decode_attention(const kv4_cache_desc* cache, const void* q, const int32_t* ctx_len,
+                           const int32_t* slot, const int32_t* page_table, int32_t pt_stride,
+                           int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(cache, q, ctx_len, slot, page_table, pt_stride, B, Hq, max_ctx,
+                       softmax_scale, out, lse, workspace, workspace_bytes, nullptr, stream, nullptr,
+                       nullptr, true);
 }
 
 // ---- KV8 everywhere --------------------------------------------------------

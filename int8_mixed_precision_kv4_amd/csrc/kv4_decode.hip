@@ -108,8 +108,7 @@ struct GroupQuery {
   float c_q;
   int S;
 };
-__device__ __forceinline__ GroupQuery quantize_group_query(uint4 raw, float scale_log2, int r16) {
-  float x[8];
+__device__ __forceinline__ void rotate_group_query(uint4 raw, int r16, float x[8]) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -134,12 +133,15 @@ __device__ __forceinline__ GroupQuery quantize_group_query(uint4 raw, float scal
       x[j] = upper ? (p - x[j]) : (x[j] + p);
     }
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = x[j] * kInvSqrt128;
+}
+__device__ __forceinline__ GroupQuery quantize_group_query(uint4 raw, float scale_log2, int r16) {
+  float x[8];
+  rotate_group_query(raw, r16, x);
   float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    x[j] = x[j] * kInvSqrt128;
-    amax = fmaxf(amax, fabsf(x[j]));
-  }
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
   amax = row16_max(amax);
   const float s_q = amax / 127.0f;
   GroupQuery g;
@@ -537,12 +539,14 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // KV4-RL main region: quads of 4 INT4 pages (layouts above).
+enum class QueryMode { Int8EvenOdd, Int8Natural, Bf16 };
+
 struct Kv4Format {
+  static constexpr QueryMode kQuery = QueryMode::Int8EvenOdd;
   static constexpr int kUnit = 4;
   static constexpr int kWavesPerSimd = KV4_MAIN_WAVES_PER_SIMD;
   static constexpr int kBlock = BLOCK_BYTES;
   static constexpr bool kProtected = true;      // protected-region workgroups in the grid tail
-  static constexpr bool kNaturalQuery = false;  // QK operand: even / odd channels (nibble order)
   typedef QuadRegs Regs;
   typedef MainState State;
   __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
@@ -713,11 +717,11 @@ __device__ __forceinline__ void compute_pair(const DecArgs& a, Kv8State& st, con
 }
 
 struct Kv8Format {
+  static constexpr QueryMode kQuery = QueryMode::Int8Natural;
   static constexpr int kUnit = 2;
   static constexpr int kWavesPerSimd = KV8_MAIN_WAVES_PER_SIMD;
   static constexpr int kBlock = KV8_BLOCK_BYTES;
   static constexpr bool kProtected = false;
-  static constexpr bool kNaturalQuery = true;  // QK operand: channels in natural order
   typedef Kv8Regs Regs;
   typedef Kv8State State;
   __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
@@ -781,6 +785,169 @@ struct Kv8Format {
 #pragma unroll
       for (int h = 0; h < 4; ++h) P0[h * kPart + 64 * acc + 16 * grp + r16] = A[4 * acc + h];
   }
+};
+
+// MXFP4 variant of the main region (KV4-RL pages, comparison of 4-bit formats,
+// appendix D.4): pairs of 2 pages in OCP MXFP4, attended on their exactly
+// dequantized values.  QK: the BF16-rounded rotated query against K codes
+// converted to BF16 by the hardware FP4 conversion with the block's E8M0 scale
+// (v_cvt_scalef32_pk_bf16_fp4; a lane's 8 channels share one block), BF16
+// MFMA 16x16x32 with FP32 accumulation.  PV: the FP32 weight of a position
+// times 2^(V block exponent) is split into two BF16 parts per V block and
+// meets the unscaled V codes (converted at unit scale) on the same MFMA, rows
+// rotated as for KV8.  Slot layout:
+//   [0, 2048)     K codes in operand order, page t at 1024 t: lane (r16, c)
+//                 holds channel block c of position r16 at 16 (r16 + 16 c)
+//   [2048, 4096)  V codes, page t at 2048 + 1024 t (the block's channel-major copy)
+//   [4096, 4352)  scales, page t at 4096 + 128 t: K E8M0 [16][4], V E8M0 [16][4]
+//   [4352, 6400)  P operand [V block][hi, lo][head][32 positions] BF16
+//   [6400, 7424)  BF16 rotated query [head][128]
+constexpr int kmxK = 0, kmxV = 2048, kmxS = 4096, kmxP = 4352, kmxQ = 6400;
+static_assert(kmxQ + 1024 <= kSlotBytes, "the MXFP4 slot must fit the per-wave LDS slot");
+
+struct MxRegs {
+  uint32_t k[2][4];  // 8 FP4 codes: channels 32 m + 8 grp .. of position r16
+  uint32_t ks[2], vs[2];
+  uint32_t vq[8];    // 8 FP4 codes: positions 8 (grp & 1) .. of channel 16 s + r16, page grp >> 1
+};
+
+__device__ __forceinline__ float e8m0_value(uint32_t e) {
+  return __uint_as_float(e ? (e << 23) : 0x00400000u);  // 2^(e - 127); e = 0 is the subnormal 2^-127
+}
+
+// 8 FP4 codes (4 bytes, low nibble first) times scale, as 8 BF16.
+__device__ __forceinline__ v8bf fp4x8_bf16(uint32_t w, float scale) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const b2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const b2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const b2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <bool DEBUG>
+__device__ __forceinline__ void compute_mx_pair(const DecArgs& a, Kv8State& st, const MxRegs& r,
+                                                int np, int j0, int main_end, size_t qb,
+                                                uint8_t* slot, int r16, int grp) {
+  (void)qb;
+  // QK on BF16 MFMAs; lane (head grp, position r16) after the move
+  v8bf qa[4] = {v8bf{}, v8bf{}, v8bf{}, v8bf{}};
+  if (r16 < GQA) {  // A operand: head r16, channels 32 m + 8 grp .. + 7
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      qa[m] = *reinterpret_cast<const v8bf*>(slot + kmxQ + 2 * (HD * r16 + 32 * m + 8 * grp));
+  }
+  float z[2];
+  bool valid[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    v4f d = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], fp4x8_bf16(r.k[t][m], e8m0_value((r.ks[t] >> (8 * m)) & 0xFFu)),
+                                                  d, 0, 0, 0);
+    const auto r01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[0]), __float_as_uint(d[1]), false, false);
+    const auto r23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[2]), __float_as_uint(d[3]), false, false);
+    const float D = __uint_as_float(__builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false)[0]);
+    const int pos = PAGE * (j0 + t) + r16;
+    valid[t] = (t < np) && (pos < main_end);
+    z[t] = valid[t] ? D * a.scale_log2 : -INFINITY;
+  }
+  const float Zn = fmaxf(st.Zr, row16_max(fmaxf(z[0], z[1])));
+  const float al = __builtin_amdgcn_exp2f(st.Zr - Zn);
+  st.Zr = Zn;
+  float e[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) e[t] = valid[t] ? exp2s(z[t] - Zn) : 0.0f;
+  st.Ls = __builtin_fmaf(st.Ls, al, e[0] + e[1]);
+  // P operand per V block b: e 2^(E_v(b) - 127), split into two BF16 parts
+  uint16_t* pst = reinterpret_cast<uint16_t*>(slot + kmxP);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float p = __builtin_ldexpf(e[t], static_cast<int>((r.vs[t] >> (8 * b)) & 0xFFu) - 127);
+      const uint32_t hi = pack_bf16x2(p, 0.0f) & 0xFFFFu;
+      const uint32_t lo = pack_bf16x2(p - __uint_as_float(hi << 16), 0.0f) & 0xFFFFu;
+      pst[((2 * b) * 4 + grp) * 32 + 16 * t + r16] = static_cast<uint16_t>(hi);
+      pst[((2 * b + 1) * 4 + grp) * 32 + 16 * t + r16] = static_cast<uint16_t>(lo);
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float alh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * h));
+    st.O[0][h] *= alh;
+    st.O[1][h] *= alh;
+  }
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const u4 zero4 = u4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    // A operand of V block b: head r16 % 4, positions 8 grp .. 8 grp + 7
+    const u4 ph = *reinterpret_cast<const u4*>(pst + ((2 * b) * 4 + (r16 & 3)) * 32 + 8 * grp);
+    const u4 pl = *reinterpret_cast<const u4*>(pst + ((2 * b + 1) * 4 + (r16 & 3)) * 32 + 8 * grp);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int s = 2 * b + half;  // channels 16 s .. 16 s + 15 = 4 acc + r
+      const v8bf vb = fp4x8_bf16(r.vq[s], 1.0f);
+      const bool mine = (r16 >> 2) == (s & 3);
+      v4f o = st.O[s >> 2];
+      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, mine ? ph : zero4), vb, o, 0, 0, 0);
+      st.O[s >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, mine ? pl : zero4), vb, o,
+                                                             0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+struct MxFormat {
+  static constexpr QueryMode kQuery = QueryMode::Bf16;
+  static constexpr int kUnit = 2;
+  static constexpr int kWavesPerSimd = KV4_MAIN_WAVES_PER_SIMD;
+  static constexpr int kBlock = BLOCK_BYTES;
+  static constexpr bool kProtected = true;
+  typedef MxRegs Regs;
+  typedef Kv8State State;
+  __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      __builtin_amdgcn_global_load_lds(blk[t] + 64 * r16 + 16 * grp, (lptr)(slot + kmxK + 1024 * t), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(blk[t] + OFF_VCODE + 16 * lane, (lptr)(slot + kmxV + 1024 * t), 16, 0, 0);
+    }
+    if (lane < 16)  // 2 pages x 128 B of scales
+      __builtin_amdgcn_global_load_lds((lane < 8 ? blk[0] : blk[1]) + OFF_KMETA + 16 * (lane & 7),
+                                       (lptr)(slot + kmxS), 16, 0, 0);
+  }
+  __device__ static void from_lds(Regs& r, const uint8_t* slot, int lane, int r16, int grp) {
+    (void)lane;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        r.k[t][m] = *reinterpret_cast<const uint32_t*>(slot + kmxK + 1024 * t + 16 * (r16 + 16 * m) + 4 * grp);
+      r.ks[t] = *reinterpret_cast<const uint32_t*>(slot + kmxS + 128 * t + 4 * r16);
+      r.vs[t] = *reinterpret_cast<const uint32_t*>(slot + kmxS + 128 * t + 64 + 4 * r16);
+    }
+    const uint8_t* vb = slot + kmxV + 1024 * (grp >> 1) + 8 * r16 + 4 * (grp & 1);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r.vq[s] = *reinterpret_cast<const uint32_t*>(vb + 128 * s);
+  }
+  __device__ static void reset(State& st) { Kv8Format::reset(st); }
+  template <bool DEBUG>
+  __device__ static void compute(const DecArgs& a, State& st, const Regs& r, int np, v4i qa0, v4i qa1,
+                                 float c_q, float S_q, int j0, int main_end, size_t qb, uint8_t* slot,
+                                 int r16, int grp, int pslot) {
+    (void)qa0;
+    (void)qa1;
+    (void)c_q;
+    (void)S_q;
+    (void)pslot;
+    compute_mx_pair<DEBUG>(a, st, r, np, j0, main_end, qb, slot, r16, grp);
+  }
+  __device__ static void finish(const State& st, float A[8], float& Z, float& L) { Kv8Format::finish(st, A, Z, L); }
+  __device__ static void store(float* P0, const float A[8], int r16, int grp) { Kv8Format::store(P0, A, r16, grp); }
 };
 
 // Work split of the main region: the global page list (sequence-major, then
@@ -908,6 +1075,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
   float2 nqi = make_float2(0.0f, 0.0f);
   uint4 raw1 = make_uint4(0, 0, 0, 0), raw2 = make_uint4(0, 0, 0, 0);
   auto group_query = [&](const QuadDesc& d, const uint4& raw) {
+    if constexpr (F::kQuery == QueryMode::Bf16) {
+      // the rotated query rounded to BF16, natural order: head grp, channels 8 r16 ..
+      (void)d;
+      float x[8];
+      rotate_group_query(raw, r16, x);
+      const uint4 w = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                                 pack_bf16x2(x[6], x[7]));
+      *reinterpret_cast<uint4*>(slot + kmxQ + 2 * (HD * grp + 8 * r16)) = w;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      return;
+    }
     const GroupQuery gq = quantize_group_query(raw, a.scale_log2, r16);
     if (DEBUG) {  // lane (grp, r16) holds rotated channels 8 r16 .. 8 r16 + 7 (same values from every piece)
       const size_t bh = static_cast<size_t>(d.b) * a.Hq + d.g * GQA + grp;
@@ -920,7 +1100,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
     // group grp covers channels 32grp..32grp+31, even / odd split); the codes
     // go through the slot's query area to reach that layout.
     uint8_t* qs = slot + kSlotQ + grp * HD;
-    if constexpr (F::kNaturalQuery) {  // channels 8 r16 .. 8 r16 + 7 in place
+    if constexpr (F::kQuery == QueryMode::Int8Natural) {  // channels 8 r16 .. 8 r16 + 7 in place
       const uint32_t lo = (gq.c[0] & 0xFF) | ((gq.c[1] & 0xFF) << 8) | ((gq.c[2] & 0xFF) << 16) |
                           (static_cast<uint32_t>(gq.c[3] & 0xFF) << 24);
       const uint32_t hi = (gq.c[4] & 0xFF) | ((gq.c[5] & 0xFF) << 8) | ((gq.c[6] & 0xFF) << 16) |
@@ -1142,8 +1322,9 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
                          const int32_t* slot, const int32_t* page_table, int pt_stride, int B,
                          int Hq, float scale_log2, float* out, float* lse,
                          const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
-                         hipEvent_t ev_main_begin, hipEvent_t ev_main_end) {
+                         hipEvent_t ev_main_begin, hipEvent_t ev_main_end, bool mx) {
   if (ws.n_waves <= 0 || ws.n_waves % 4 != 0) return hipErrorInvalidValue;
+  if (mx && dbg) return hipErrorInvalidValue;  // no debug instantiation of the MXFP4 variant
   DecArgs a{};
   a.pages = c.pages;
   a.side_codes = c.side_codes;
@@ -1175,7 +1356,8 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
       const hipError_t e = hipEventRecord(ev_main_begin, s);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((main_kernel<Kv4Format, false>), grid, block, 0, s, a);
+    if (mx) hipLaunchKernelGGL((main_kernel<MxFormat, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((main_kernel<Kv4Format, false>), grid, block, 0, s, a);
     if (ev_main_end) {
       const hipError_t e = hipEventRecord(ev_main_end, s);
       if (e != hipSuccess) return e;

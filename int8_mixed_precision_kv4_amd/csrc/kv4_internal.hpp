@@ -51,13 +51,14 @@ DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves)
 int main_region_waves();  // size of the main-region grid on the current device
 int kv8_region_waves();   // the same for the KV8-everywhere instantiation
 
+// mx: write the main-region entry in the MXFP4 variant's format instead of INT4
 hipError_t launch_append(const CacheView& c, const uint16_t* k, const uint16_t* v,
                          const int32_t* pos, const int32_t* slot, const int32_t* page_table,
-                         int pt_stride, int B, hipStream_t s);
+                         int pt_stride, int B, hipStream_t s, bool mx = false);
 hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t* v,
                           const int32_t* cu, const int32_t* start, const int32_t* slot,
                           const int32_t* page_table, int pt_stride, int nseq, int max_seqlen,
-                          hipStream_t s);
+                          hipStream_t s, bool mx = false);
 hipError_t launch_kv8_append(uint8_t* pages, int Hkv, const uint16_t* k, const uint16_t* v,
                              const int32_t* pos, const int32_t* page_table, int pt_stride, int B,
                              hipStream_t s);
@@ -74,7 +75,8 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
                          const int32_t* slot, const int32_t* page_table, int pt_stride, int B,
                          int Hq, float scale_log2, float* out, float* lse,
                          const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
-                         hipEvent_t ev_main_begin = nullptr, hipEvent_t ev_main_end = nullptr);
+                         hipEvent_t ev_main_begin = nullptr, hipEvent_t ev_main_end = nullptr,
+                         bool mx = false);
 hipError_t launch_bf16_decode(const uint16_t* pages, int num_pages, int Hkv, const uint16_t* q,
                               const int32_t* ctx, const int32_t* page_table, int pt_stride, int B,
                               int Hq, float scale_log2, float* out, float* lse, void* ws,

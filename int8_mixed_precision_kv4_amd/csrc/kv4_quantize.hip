@@ -51,7 +51,42 @@ __device__ __forceinline__ void write_side_row(const QuantArgs& a, int slot, int
   }
 }
 
+// MXFP4 variant of the main-region entry (KV4-RL pages, comparison of 4-bit
+// formats): OCP MX blocks of 32 channels (16 lanes), E = floor(log2 amax) - 2
+// clamped to [-127, 127] (-127 for an all-zero block), codes = E2M1 of
+// x / 2^E, nearest with ties to even and saturation at 6, by the hardware
+// conversion at unit scale after an exact ldexp.  Block layout: K codes [16][64]
+// | V codes [128][8] | K scales E8M0 [16][4] | V scales E8M0 [16][4].
+constexpr int MX_OFF_KS = 2048, MX_OFF_VS = 2112;
+
+struct MxCodes {
+  uint32_t kbyte, v0, v1;  // K: channels 2l (low) and 2l+1; V: code of channel 2l, 2l+1
+  uint32_t ke8, ve8;       // E8M0 bytes of this lane's block (channels 32(l/16) ..)
+};
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (amax == 0.0f) return -127;
+  const int ef = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);  // 0 for a subnormal: clamps
+  return max(ef - 127 - 2, -127);
+}
+__device__ __forceinline__ uint32_t mx_pair(float x0, float x1, int E) {
+  const float y0 = __builtin_ldexpf(x0, -E), y1 = __builtin_ldexpf(x1, -E);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0) & 0xFFu;
+}
+__device__ __forceinline__ MxCodes mx_codes(float k0, float k1, float v0, float v1) {
+  const int ek = mx_exponent(row16_max(fmaxf(fabsf(k0), fabsf(k1))));
+  const int ev = mx_exponent(row16_max(fmaxf(fabsf(v0), fabsf(v1))));
+  MxCodes c;
+  c.kbyte = mx_pair(k0, k1, ek);
+  const uint32_t vb = mx_pair(v0, v1, ev);
+  c.v0 = vb & 0xFu;
+  c.v1 = vb >> 4;
+  c.ke8 = static_cast<uint32_t>(ek + 127);
+  c.ve8 = static_cast<uint32_t>(ev + 127);
+  return c;
+}
+
 // One token per sequence; one wave per (kv-head, sequence).
+template <bool MX>
 __global__ __launch_bounds__(64) void append_kernel(QuantArgs a, const int32_t* __restrict__ pos_arr) {
   const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int pos = pos_arr[b];
@@ -66,22 +101,37 @@ __global__ __launch_bounds__(64) void append_kernel(QuantArgs a, const int32_t* 
   const int t = pos & (PAGE - 1);
   uint8_t* blk = a.pages + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
 
-  const Int4Meta kq = int4_meta(wave_min(fminf(k0, k1)), wave_max(fmaxf(k0, k1)));
-  const Int4Meta vq = int4_meta(wave_min(fminf(v0, v1)), wave_max(fmaxf(v0, v1)));
+  uint32_t kbyte, vc0, vc1;
+  if constexpr (MX) {
+    const MxCodes mc = mx_codes(k0, k1, v0, v1);
+    kbyte = mc.kbyte;
+    vc0 = mc.v0;
+    vc1 = mc.v1;
+    if ((lane & 15) == 0) {
+      blk[MX_OFF_KS + 4 * t + (lane >> 4)] = static_cast<uint8_t>(mc.ke8);
+      blk[MX_OFF_VS + 4 * t + (lane >> 4)] = static_cast<uint8_t>(mc.ve8);
+    }
+  } else {
+    const Int4Meta kq = int4_meta(wave_min(fminf(k0, k1)), wave_max(fmaxf(k0, k1)));
+    const Int4Meta vq = int4_meta(wave_min(fminf(v0, v1)), wave_max(fmaxf(v0, v1)));
+    kbyte = static_cast<uint32_t>(int4_code(k0, kq) | (int4_code(k1, kq) << 4));
+    vc0 = static_cast<uint32_t>(int4_code(v0, vq));
+    vc1 = static_cast<uint32_t>(int4_code(v1, vq));
+    if (lane == 0) {
+      *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
+      *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
+    }
+  }
   // K: token-major, channel 2l in the low nibble of byte l
-  blk[64 * t + lane] = static_cast<uint8_t>(int4_code(k0, kq) | (int4_code(k1, kq) << 4));
+  blk[64 * t + lane] = static_cast<uint8_t>(kbyte);
   // V: channel-major, this position's nibble in bytes 8c + t/2 of channels 2l, 2l+1;
   // the other nibble belongs to the neighbouring position and is kept.
   const int sh = (t & 1) * 4;
   const uint32_t keep = (t & 1) ? 0x0Fu : 0xF0u;
   uint8_t* vb0 = blk + OFF_VCODE + 8 * (2 * lane) + (t >> 1);
   uint8_t* vb1 = vb0 + 8;
-  *vb0 = static_cast<uint8_t>((*vb0 & keep) | (int4_code(v0, vq) << sh));
-  *vb1 = static_cast<uint8_t>((*vb1 & keep) | (int4_code(v1, vq) << sh));
-  if (lane == 0) {
-    *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
-    *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
-  }
+  *vb0 = static_cast<uint8_t>((*vb0 & keep) | (vc0 << sh));
+  *vb1 = static_cast<uint8_t>((*vb1 & keep) | (vc1 << sh));
   if (pos < a.sink || a.window > 0) write_side_row(a, slot, g, pos, k0, k1, v0, v1, lane);
 }
 
@@ -90,6 +140,7 @@ __global__ __launch_bounds__(64) void append_kernel(QuantArgs a, const int32_t* 
 // rows are written only where appends would leave them in the final state:
 // sinks, and the last w positions of the range (earlier ring rows would be
 // overwritten within the same range anyway; none when w = 0).
+template <bool MX>
 __global__ __launch_bounds__(256) void prefill_kernel(QuantArgs a, const int32_t* __restrict__ cu,
                                                       const int32_t* __restrict__ start_pos) {
   const int lp = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
@@ -113,14 +164,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(QuantArgs a, const int32_t
     float k0 = bf16_lo(kw), k1 = bf16_hi(kw);
     const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
     fwht128_wave(k0, k1);
-    const Int4Meta kq = int4_meta(wave_min(fminf(k0, k1)), wave_max(fmaxf(k0, k1)));
-    const Int4Meta vq = int4_meta(wave_min(fminf(v0, v1)), wave_max(fmaxf(v0, v1)));
-    blk[64 * t + lane] = static_cast<uint8_t>(int4_code(k0, kq) | (int4_code(k1, kq) << 4));
-    vcodes[t][2 * lane] = static_cast<uint8_t>(int4_code(v0, vq));
-    vcodes[t][2 * lane + 1] = static_cast<uint8_t>(int4_code(v1, vq));
-    if (lane == 0) {
-      *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
-      *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
+    if constexpr (MX) {
+      const MxCodes mc = mx_codes(k0, k1, v0, v1);
+      blk[64 * t + lane] = static_cast<uint8_t>(mc.kbyte);
+      vcodes[t][2 * lane] = static_cast<uint8_t>(mc.v0);
+      vcodes[t][2 * lane + 1] = static_cast<uint8_t>(mc.v1);
+      if ((lane & 15) == 0) {
+        blk[MX_OFF_KS + 4 * t + (lane >> 4)] = static_cast<uint8_t>(mc.ke8);
+        blk[MX_OFF_VS + 4 * t + (lane >> 4)] = static_cast<uint8_t>(mc.ve8);
+      }
+    } else {
+      const Int4Meta kq = int4_meta(wave_min(fminf(k0, k1)), wave_max(fmaxf(k0, k1)));
+      const Int4Meta vq = int4_meta(wave_min(fminf(v0, v1)), wave_max(fmaxf(v0, v1)));
+      blk[64 * t + lane] = static_cast<uint8_t>(int4_code(k0, kq) | (int4_code(k1, kq) << 4));
+      vcodes[t][2 * lane] = static_cast<uint8_t>(int4_code(v0, vq));
+      vcodes[t][2 * lane + 1] = static_cast<uint8_t>(int4_code(v1, vq));
+      if (lane == 0) {
+        *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
+        *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
+      }
     }
     if (p < a.sink || p >= keep_from) write_side_row(a, slot, g, p, k0, k1, v0, v1, lane);
   }
@@ -220,23 +282,25 @@ hipError_t launch_kv8_prefill(uint8_t* pages, int Hkv, const uint16_t* k, const 
 
 hipError_t launch_append(const CacheView& c, const uint16_t* k, const uint16_t* v,
                          const int32_t* pos, const int32_t* slot, const int32_t* page_table,
-                         int pt_stride, int B, hipStream_t s) {
+                         int pt_stride, int B, hipStream_t s, bool mx) {
   QuantArgs a{c.pages, c.side_codes, c.side_scales, c.Hkv,
               reinterpret_cast<const uint32_t*>(k), reinterpret_cast<const uint32_t*>(v),
               slot, page_table, pt_stride, c.sink, c.window};
-  hipLaunchKernelGGL(append_kernel, dim3(c.Hkv, B), dim3(64), 0, s, a, pos);
+  if (mx) hipLaunchKernelGGL(append_kernel<true>, dim3(c.Hkv, B), dim3(64), 0, s, a, pos);
+  else hipLaunchKernelGGL(append_kernel<false>, dim3(c.Hkv, B), dim3(64), 0, s, a, pos);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t* v,
                           const int32_t* cu, const int32_t* start, const int32_t* slot,
                           const int32_t* page_table, int pt_stride, int nseq, int max_seqlen,
-                          hipStream_t s) {
+                          hipStream_t s, bool mx) {
   QuantArgs a{c.pages, c.side_codes, c.side_scales, c.Hkv,
               reinterpret_cast<const uint32_t*>(k), reinterpret_cast<const uint32_t*>(v),
               slot, page_table, pt_stride, c.sink, c.window};
   const int pages = (max_seqlen + PAGE - 1) / PAGE + 1;
-  hipLaunchKernelGGL(prefill_kernel, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
+  if (mx) hipLaunchKernelGGL(prefill_kernel<true>, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
+  else hipLaunchKernelGGL(prefill_kernel<false>, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
   return hipGetLastError();
 }
 
