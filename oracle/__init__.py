@@ -61,6 +61,9 @@ def lib():
         _lib.kv4ref_exp2s_coeffs.argtypes = [C.c_void_p]
         _lib.kv4ref_append.argtypes = [C.POINTER(_Cache)] + [C.c_void_p] * 5 + [C.c_int32] * 2
         KC = C.POINTER(_Cache)
+        _lib.kv4ref_prefill_attention.argtypes = ([KC] + [C.c_void_p] * 5 + [C.c_int32] * 3
+                                                  + [C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
+                                                     C.POINTER(_Debug), C.c_int32])
         _lib.mxref_append.argtypes = [KC] + [C.c_void_p] * 5 + [C.c_int32] * 2
         _lib.mxref_prefill.argtypes = [KC] + [C.c_void_p] * 6 + [C.c_int32] * 3
         _lib.mxref_decode.argtypes = ([KC] + [C.c_void_p] * 4 + [C.c_int32] * 3 + [C.c_float]
@@ -375,3 +378,37 @@ def mx_decode(cache: Cache, q, ctx_len, slot, page_table, Hq: int, softmax_scale
     if rc != 0:
         raise ValueError(f"mxref_decode failed ({rc})")
     return out, lse
+
+
+# ------------------------------------------------- re-prefill attention --
+
+def prefill_attention(cache: Cache, q, cu_seqlens, start_pos, slot, page_table, Hq: int,
+                      softmax_scale: float, pv_exact: bool = False, debug: bool = False,
+                      nthreads=None):
+    """Chunk attention after the chunk's K/V were written: token i of sequence s
+    attends [0, start[s] + i] with the protected set of the cache ending at
+    start[s] + n_s.  q [T][Hq][128]; returns (out [T][Hq][128], lse [T][Hq], dbg)."""
+    q = _c(q, np.uint16)
+    cu, start, table = (_c(cu_seqlens, np.int32), _c(start_pos, np.int32), _c(page_table, np.int32))
+    slot = None if slot is None else _c(slot, np.int32)
+    T = int(cu[-1])
+    assert q.shape == (T, Hq, HD)
+    out = np.zeros((T, Hq, HD), np.float64)
+    lse = np.zeros((T, Hq), np.float64)
+    dbg = dstruct = None
+    if debug:
+        max_ctx = int(table.shape[1]) * PAGE
+        dbg = dict(qcodes=np.zeros((T, Hq, HD), np.int8), qsum=np.zeros((T, Hq), np.int32),
+                   qk=np.zeros((T, Hq, max_ctx), np.int32), pcode=np.zeros((T, Hq, max_ctx), np.uint8),
+                   pv=np.zeros((T, Hq, table.shape[1], HD), np.int32))
+        dstruct = _Debug(_p(dbg["qcodes"]).value, _p(dbg["qsum"]).value, _p(dbg["qk"]).value,
+                         _p(dbg["pcode"]).value, _p(dbg["pv"]).value, max_ctx, table.shape[1])
+    st = cache._struct()
+    rc = lib().kv4ref_prefill_attention(C.byref(st), _p(q), _p(cu), _p(start),
+                                        None if slot is None else _p(slot), _p(table), table.shape[1],
+                                        start.shape[0], Hq, softmax_scale, int(pv_exact), _p(out),
+                                        _p(lse), C.byref(dstruct) if dstruct else None,
+                                        nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"kv4ref_prefill_attention failed ({rc})")
+    return out, lse, dbg

@@ -168,16 +168,18 @@ def query_codes(q_bf16_bits: np.ndarray):
 
 
 def decode_one(pages, side_codes, side_scales, Hkv, q_bits, L, slot, g, table_row, scale_log2,
-               pv_exact=False, sink=SINK, window=WINDOW):
-    """One (sequence, q-head): returns out[128] (f64), lse, and dicts of the
-    integer intermediates keyed by position / logical page.  sink / window:
-    the protection budget s, w."""
+               pv_exact=False, sink=SINK, window=WINDOW, E=None):
+    """One (query, q-head) attending [0, L): returns out[128] (f64), lse, and
+    dicts of the integer intermediates keyed by position / logical page.
+    sink / window: the protection budget s, w; E: the end of the cache (the
+    recent window is [E - w, E)), L for a decode step."""
+    E = L if E is None else E
     qc, s_q, S_q = query_codes(q_bits)
     c_q = f32_mul(s_q, scale_log2)
     qk, pcode, pv = {}, {}, {}
     parts = []
     # protected region: sinks and recent window
-    prot = list(range(0, min(sink, L))) + list(range(max(sink, L - window), L))
+    prot = list(range(0, min(sink, L))) + list(range(max(sink, E - window), L))
     zs, rows = [], []
     for p in prot:
         row = p if p < sink else sink + p % window
@@ -200,7 +202,7 @@ def decode_one(pages, side_codes, side_scales, Hkv, q_bits, L, slot, g, table_ro
     if prot:
         parts.append((A, zmax, ell))
     # main region, one tile per logical page
-    main_end = L - window
+    main_end = min(L, E - window)
     j = sink // PAGE
     while PAGE * j < main_end:
         kc, vc, kd, km, vd, vm = unpack_block(pages[table_row[j], g])

@@ -471,8 +471,8 @@ static void main_tile(const uint8_t *blk, int t_end, const int8_t qc[HD], int32_
     get_meta(blk, OFF_VMETA, t, &dv[t], &mv[t]);
     if (dbg_qk) dbg_qk[t] = D;
   }
-  float zmax = z[0];
-  for (int t = 1; t < t_end; t++)
+  float zmax = -INFINITY; /* t_end >= 1 */
+  for (int t = 0; t < t_end; t++)
     if (z[t] > zmax) zmax = z[t];
   float umax = 0.0f;
   for (int t = 0; t < t_end; t++) {
@@ -557,17 +557,19 @@ static void int8_region(const int8_row_t *rows, int n, const int8_t qc[HD], floa
   free(z);
 }
 
-/* Protected region: the sinks and the recent window, read from the side rows. */
-static void protected_region(const kv4ref_cache *c, int32_t slot, int g, int32_t L,
+/* Protected region of a query that attends [0, L) while the cache holds
+ * positions [0, E) (E = L for a decode step): the sinks below L and the
+ * window positions [max(s, E-w), L), read from the side rows. */
+static void protected_region(const kv4ref_cache *c, int32_t slot, int g, int32_t L, int32_t E,
                              const int8_t qc[HD], float c_q, partial_t *out, int32_t *dbg_qk) {
   int32_t pos[SIDE_ROWS];
   int n = 0;
   const int sw = c->sink + c->window;
   int sink_end = L < c->sink ? L : c->sink;
-  int rec_begin = (L - c->window) > c->sink ? (L - c->window) : c->sink;
+  int rec_begin = (E - c->window) > c->sink ? (E - c->window) : c->sink;
   for (int p = 0; p < sink_end; p++) pos[n++] = p;
   for (int p = rec_begin; p < L; p++) pos[n++] = p;
-  assert(n == (L < sw ? L : sw));
+  assert(n <= sw && (E != L || n == (L < sw ? L : sw)));
   int8_row_t rows[SIDE_ROWS];
   for (int i = 0; i < n; i++) {
     int row = side_row(c, pos[i]);
@@ -598,6 +600,40 @@ static void merge(const partial_t *p, int n, double *out, double *lse) {
   *lse = M_LN2 * (Z + log2(l));
 }
 
+/* One (query, q-head): attends [0, L) of the cache holding [0, E).  Main
+ * region M = [s, min(L, E-w)); the rest as protected_region. */
+static void decode_one_query(const kv4ref_cache *c, const uint16_t *q16, int32_t L, int32_t E,
+                             int32_t slot, int g, const int32_t *row, float scale_log2,
+                             int32_t pv_exact, double *out, double *lse, int8_t *dqc, int32_t *dqs,
+                             int32_t *dqk, uint8_t *dpc, int32_t *dpv) {
+  float qr[HD];
+  for (int i = 0; i < HD; i++) qr[i] = kv4ref_bf16_to_f32(q16[i]);
+  fwht128(qr); /* same rotation as the keys: scores are preserved */
+  int8_t qc[HD];
+  float s_q;
+  int32_t qsum;
+  quant_query(qr, qc, &s_q, &qsum);
+  const float c_q = s_q * scale_log2;
+  if (dqc) memcpy(dqc, qc, HD);
+  if (dqs) *dqs = qsum;
+  int32_t main_end = E - c->window; /* M = [s, main_end) */
+  if (main_end > L) main_end = L;
+  const int j0 = c->sink / PAGE;                                          /* first main page */
+  const int j1 = main_end > c->sink ? (main_end - 1) / PAGE : j0 - 1;   /* last main page */
+  const int ntiles = j1 - j0 + 1;
+  partial_t *parts = (partial_t *)malloc(sizeof(partial_t) * (size_t)(ntiles + 1));
+  protected_region(c, slot, g, L, E, qc, c_q, &parts[0], dqk);
+  for (int j = j0; j <= j1; j++) {
+    const uint8_t *blk = block_at(c, row[j], g);
+    int t_end = main_end - PAGE * j;
+    if (t_end > PAGE) t_end = PAGE;
+    main_tile(blk, t_end, qc, qsum, c_q, pv_exact, &parts[1 + j - j0], dqk ? dqk + PAGE * j : NULL,
+              dpc ? dpc + PAGE * j : NULL, dpv ? dpv + (size_t)j * HD : NULL);
+  }
+  merge(parts, ntiles + 1, out, lse);
+  free(parts);
+}
+
 int kv4ref_decode(const kv4ref_cache *c, const uint16_t *q, const int32_t *ctx_len,
                   const int32_t *slot, const int32_t *page_table, int32_t pt_stride, int32_t B,
                   int32_t Hq, float softmax_scale, int32_t pv_exact, double *out, double *lse,
@@ -613,43 +649,58 @@ int kv4ref_decode(const kv4ref_cache *c, const uint16_t *q, const int32_t *ctx_l
   for (int bh = 0; bh < B * Hq; bh++) {
     const int b = bh / Hq, h = bh % Hq, g = h / G;
     const int32_t L = ctx_len[b];
-    const int32_t s = slot ? slot[b] : b;
     if (L < 1 || (L + PAGE - 1) / PAGE > pt_stride) {
 #pragma omp atomic write
       bad = 1;
       continue;
     }
-    float qr[HD];
-    for (int i = 0; i < HD; i++) qr[i] = kv4ref_bf16_to_f32(q[(size_t)bh * HD + i]);
-    fwht128(qr); /* same rotation as the keys: scores are preserved */
-    int8_t qc[HD];
-    float s_q;
-    int32_t qsum;
-    quant_query(qr, qc, &s_q, &qsum);
-    const float c_q = s_q * scale_log2;
-    if (dbg && dbg->qcodes) memcpy(dbg->qcodes + (size_t)bh * HD, qc, HD);
-    if (dbg && dbg->qsum) dbg->qsum[bh] = qsum;
-    int32_t *dqk = (dbg && dbg->qk) ? dbg->qk + (size_t)bh * dbg->max_ctx : NULL;
-    uint8_t *dpc = (dbg && dbg->pcode) ? dbg->pcode + (size_t)bh * dbg->max_ctx : NULL;
-    int32_t *dpv = (dbg && dbg->pv) ? dbg->pv + (size_t)bh * dbg->max_pages * HD : NULL;
+    decode_one_query(c, q + (size_t)bh * HD, L, L, slot ? slot[b] : b, g,
+                     page_table + (size_t)b * pt_stride, scale_log2, pv_exact, out + (size_t)bh * HD,
+                     lse + bh, (dbg && dbg->qcodes) ? dbg->qcodes + (size_t)bh * HD : NULL,
+                     (dbg && dbg->qsum) ? dbg->qsum + bh : NULL,
+                     (dbg && dbg->qk) ? dbg->qk + (size_t)bh * dbg->max_ctx : NULL,
+                     (dbg && dbg->pcode) ? dbg->pcode + (size_t)bh * dbg->max_ctx : NULL,
+                     (dbg && dbg->pv) ? dbg->pv + (size_t)bh * dbg->max_pages * HD : NULL);
+  }
+  return bad ? -2 : 0;
+}
 
-    const int32_t main_end = L - c->window;          /* M = [s, main_end) */
-    const int j0 = c->sink / PAGE;                    /* first main page */
-    const int j1 = main_end > c->sink ? (main_end - 1) / PAGE : j0 - 1; /* last main page */
-    const int ntiles = j1 - j0 + 1;
-    partial_t *parts = (partial_t *)malloc(sizeof(partial_t) * (size_t)(ntiles + 1));
-    protected_region(c, s, g, L, qc, c_q, &parts[0], dqk);
-    const int32_t *row = page_table + (size_t)b * pt_stride;
-    for (int j = j0; j <= j1; j++) {
-      const uint8_t *blk = block_at(c, row[j], g);
-      int t_end = main_end - PAGE * j;
-      if (t_end > PAGE) t_end = PAGE;
-      main_tile(blk, t_end, qc, qsum, c_q, pv_exact, &parts[1 + j - j0],
-                dqk ? dqk + PAGE * j : NULL, dpc ? dpc + PAGE * j : NULL,
-                dpv ? dpv + (size_t)j * HD : NULL);
+/* Re-prefill (chunked-prefill) attention over the cache: sequence s's chunk of
+ * n_s = cu[s+1] - cu[s] query tokens at positions start[s] .. start[s]+n_s-1,
+ * whose K/V the cache already holds (the cache ends at E = start[s] + n_s);
+ * query token i attends [0, start[s] + i] with the protected set of that cache
+ * state.  q, out: [T][Hq][128] with T = cu[nseq]; dbg indexed by token. */
+int kv4ref_prefill_attention(const kv4ref_cache *c, const uint16_t *q, const int32_t *cu_seqlens,
+                             const int32_t *start_pos, const int32_t *slot,
+                             const int32_t *page_table, int32_t pt_stride, int32_t nseq, int32_t Hq,
+                             float softmax_scale, int32_t pv_exact, double *out, double *lse,
+                             const kv4ref_debug *dbg, int32_t nthreads) {
+  exp2_init();
+  const int Hkv = c->num_kv_heads;
+  if (Hkv <= 0 || Hq % Hkv != 0 || !budget_ok(c)) return -1;
+  const int G = Hq / Hkv;
+  const float scale_log2 = kv4ref_scale_log2(softmax_scale);
+  const int32_t T = cu_seqlens[nseq];
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int64_t th = 0; th < (int64_t)T * Hq; th++) {
+    const int32_t t = (int32_t)(th / Hq), h = (int32_t)(th % Hq), g = h / G;
+    int sq = 0;
+    while (cu_seqlens[sq + 1] <= t) sq++;
+    const int32_t L = start_pos[sq] + (t - cu_seqlens[sq]) + 1;
+    const int32_t E = start_pos[sq] + (cu_seqlens[sq + 1] - cu_seqlens[sq]);
+    if ((E + PAGE - 1) / PAGE > pt_stride) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
     }
-    merge(parts, ntiles + 1, out + (size_t)bh * HD, lse + bh);
-    free(parts);
+    decode_one_query(c, q + (size_t)th * HD, L, E, slot ? slot[sq] : sq, g,
+                     page_table + (size_t)sq * pt_stride, scale_log2, pv_exact, out + (size_t)th * HD,
+                     lse + th, (dbg && dbg->qcodes) ? dbg->qcodes + (size_t)th * HD : NULL,
+                     (dbg && dbg->qsum) ? dbg->qsum + th : NULL,
+                     (dbg && dbg->qk) ? dbg->qk + (size_t)th * dbg->max_ctx : NULL,
+                     (dbg && dbg->pcode) ? dbg->pcode + (size_t)th * dbg->max_ctx : NULL,
+                     (dbg && dbg->pv) ? dbg->pv + (size_t)th * dbg->max_pages * HD : NULL);
   }
   return bad ? -2 : 0;
 }
@@ -947,7 +998,7 @@ int mxref_decode(const kv4ref_cache *c, const uint16_t *q, const int32_t *ctx_le
     quant_query(qr, qc, &s_q, &qsum);
     for (int i = 0; i < HD; i++) qb[i] = kv4ref_bf16_to_f32(kv4ref_f32_to_bf16(qr[i]));
     partial_t parts[2];
-    protected_region(c, slot ? slot[b] : b, g, L, qc, s_q * scale_log2, &parts[0], NULL);
+    protected_region(c, slot ? slot[b] : b, g, L, L, qc, s_q * scale_log2, &parts[0], NULL);
     const int32_t main_end = L - c->window;
     mx_main(c, page_table + (size_t)b * pt_stride, g, c->sink, main_end > c->sink ? main_end : c->sink,
             qb, scale_log2, &parts[1]);

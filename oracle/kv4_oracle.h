@@ -82,6 +82,16 @@ int kv4ref_decode(const kv4ref_cache *c, const uint16_t *q, const int32_t *ctx_l
                   int32_t Hq, float softmax_scale, int32_t pv_exact, double *out, double *lse,
                   const kv4ref_debug *dbg, int32_t nthreads);
 
+/* Re-prefill attention: the chunk of query tokens of sequence s at positions
+ * start[s] .. start[s]+n_s-1 (n_s = cu[s+1]-cu[s]), after their K/V were written;
+ * token i attends [0, start[s]+i] under the protected set of the cache ending at
+ * start[s]+n_s.  q, out [T][Hq][128], lse [T][Hq]; dbg indexed by token. */
+int kv4ref_prefill_attention(const kv4ref_cache *c, const uint16_t *q, const int32_t *cu_seqlens,
+                             const int32_t *start_pos, const int32_t *slot,
+                             const int32_t *page_table, int32_t pt_stride, int32_t nseq, int32_t Hq,
+                             float softmax_scale, int32_t pv_exact, double *out, double *lse,
+                             const kv4ref_debug *dbg, int32_t nthreads);
+
 /* KV8 everywhere (INT8 comparison variant): paged pool
  * uint8 [num_pages][num_kv_heads][4160] = K codes int8 [16][128] (rotated) |
  * V codes int8 [128][16] | s_k FP16 [16] | s_v FP16 [16]. */
