@@ -598,7 +598,22 @@ def main():
         pbytes = nseq * n * wl.Hkv * (512 + 136)
         extra.update(prefill_ms_per_layer=round(t_pre * 1e3, 3),
                      prefill_gbps=round(pbytes / t_pre / 1e9, 1))
-        del pk, pv, pcache
+        del pk, pv
+        # the attention half: every token of each 16384-token chunk attends its prefix
+        log("timing the re-prefill attention of the 8 x 16384 tokens")
+        pq = draw_values(wl.seed, 1001, 1, nseq * n, wl.Hq, wl.Hkv, device=dev)[2]
+        pws = torch.empty(kv4.prefill_attention_workspace_bytes(pcache, nseq * n, wl.Hq, n),
+                          dtype=torch.uint8, device=dev)
+        pout = torch.empty((nseq * n, wl.Hq, 128), dtype=torch.float32, device=dev)
+        plse = torch.empty((nseq * n, wl.Hq), dtype=torch.float32, device=dev)
+        t_att = timed(lambda: kv4.prefill_attention(pcache, pq, pcu, pstart, pslot, ptable, n, scale, pout,
+                                                    plse, pws), 2, 1)
+        pos = np.arange(n, dtype=np.int64)
+        per_seq = (np.maximum(pos + 1 - 144, 0) * 136 + np.minimum(pos + 1, 144) * 260).sum()
+        extra.update(prefill_attention_ms_per_layer=round(t_att * 1e3, 3),
+                     prefill_attention_kv_bytes_per_s=round(per_seq * nseq * wl.Hkv / t_att / 1e9, 1),
+                     prefill_attention_finite=bool(torch.isfinite(pout).all()))
+        del pq, pws, pout, plse, pcache
 
     if not args.no_copy:
         # plain device-to-device copy of a known size: the box's practical HBM

@@ -160,6 +160,36 @@ int kv4_decode_attention_debug(const kv4_cache_desc *cache, const void *q,
                                float *lse, void *workspace, size_t workspace_bytes,
                                const kv4_decode_debug *dbg, void *stream);
 
+/* ---- re-prefill (chunked-prefill) attention ----------------------------------
+ * The attention half of carried-prefix re-prefill (step 1 of the pages), over
+ * the KV4-RL cache after kv4_prefill_quantize wrote the chunk: sequence s has
+ * n_s = cu_seqlens[s+1] - cu_seqlens[s] query tokens at positions start_pos[s]
+ * .. start_pos[s] + n_s - 1, and its cache now ends at E_s = start_pos[s] + n_s.
+ * Token i attends [0, start_pos[s] + i]: the sinks and the positions of the
+ * cache's recent window [max(s, E_s - w), E_s) it can see from the INT8 side
+ * rows, the rest of [s, min(p + 1, E_s - w)) from the INT4 pages, with the
+ * rules of kv4_decode_attention (a one-token chunk is a decode step).
+ *   q          bf16 [total_q][Hq][128] (total_q = cu_seqlens[nseq])
+ *   slot, page_table, pt_stride: per sequence, as for kv4_prefill_quantize
+ *   max_ctx    host upper bound of E_s
+ *   out, lse   fp32 [total_q][Hq][128], [total_q][Hq]
+ * The tokens are decoded as one batch: each re-reads its prefix, served mostly
+ * from the caches since the tokens of a chunk share their pages. */
+size_t kv4_prefill_attention_workspace_bytes(const kv4_cache_desc *cache, int32_t total_q,
+                                             int32_t Hq, int32_t max_ctx);
+int kv4_prefill_attention(const kv4_cache_desc *cache, const void *q, const int32_t *cu_seqlens,
+                          const int32_t *start_pos, const int32_t *slot, const int32_t *page_table,
+                          int32_t pt_stride, int32_t nseq, int32_t total_q, int32_t Hq,
+                          int32_t max_ctx, float softmax_scale, float *out, float *lse,
+                          void *workspace, size_t workspace_bytes, void *stream);
+/* With the debug stores of kv4_decode_attention_debug, indexed by token. */
+int kv4_prefill_attention_debug(const kv4_cache_desc *cache, const void *q,
+                                const int32_t *cu_seqlens, const int32_t *start_pos,
+                                const int32_t *slot, const int32_t *page_table, int32_t pt_stride,
+                                int32_t nseq, int32_t total_q, int32_t Hq, int32_t max_ctx,
+                                float softmax_scale, float *out, float *lse, void *workspace,
+                                size_t workspace_bytes, const kv4_decode_debug *dbg, void *stream);
+
 /* Static message for a status code (for KV4_ERR_HIP: the last HIP error seen
  * by this thread). */
 const char *kv4_strerror(int status);

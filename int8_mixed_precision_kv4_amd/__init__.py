@@ -23,7 +23,9 @@ EXPORTS = ("kv4_append", "kv4_prefill_quantize", "kv4_decode_workspace_bytes",
            "kv4bench_bf16_workspace_bytes", "kv4bench_bf16_paged_decode",
            "kv4bench_decode_attention_timed", "kv8_append", "kv8_prefill_quantize",
            "kv8_decode_workspace_bytes", "kv8_decode_attention", "kv8_decode_attention_debug",
-           "kv4mx_append", "kv4mx_prefill_quantize", "kv4mx_decode_attention")
+           "kv4mx_append", "kv4mx_prefill_quantize", "kv4mx_decode_attention",
+           "kv4_prefill_attention_workspace_bytes", "kv4_prefill_attention",
+           "kv4_prefill_attention_debug")
 KV8_BLOCK_BYTES = 4160
 
 _lib = None
@@ -75,6 +77,11 @@ def lib():
         L.kv4bench_bf16_paged_decode.argtypes = [P, I, I, P, P, P, I, I, I, I, F, P, P, P, Z, P]
         L.kv4bench_decode_attention_timed.argtypes = [D, P, P, P, P, I, I, I, I, F, P, P, P, Z,
                                                       P, P, P]
+        L.kv4_prefill_attention_workspace_bytes.argtypes = [D, I, I, I]
+        L.kv4_prefill_attention_workspace_bytes.restype = Z
+        L.kv4_prefill_attention.argtypes = [D, P, P, P, P, P, I, I, I, I, I, F, P, P, P, Z, P]
+        L.kv4_prefill_attention_debug.argtypes = [D, P, P, P, P, P, I, I, I, I, I, F, P, P, P, Z,
+                                                  C.POINTER(_Debug), P]
         L.kv4mx_append.argtypes = [D, P, P, P, P, P, I, I, P]
         L.kv4mx_prefill_quantize.argtypes = [D, P, P, P, P, P, P, I, I, I, P]
         L.kv4mx_decode_attention.argtypes = [D, P, P, P, P, I, I, I, I, F, P, P, P, Z, P]
@@ -347,3 +354,53 @@ def mx_decode_attention(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ctx: 
                                         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                         workspace.numel(), _stream()))
     return out, lse
+
+
+# ------------------------------------------------- re-prefill attention --
+
+def prefill_attention_workspace_bytes(cache: Kv4Cache, total_q: int, Hq: int, max_ctx: int) -> int:
+    return int(lib().kv4_prefill_attention_workspace_bytes(cache.desc(), total_q, Hq, max_ctx))
+
+
+def prefill_attention(cache: Kv4Cache, q, cu_seqlens, start_pos, slot, page_table, max_ctx: int,
+                      softmax_scale: float, out=None, lse=None, workspace=None):
+    """kv4_prefill_attention: q bf16 [T][Hq][128] of the chunks (cu_seqlens, start_pos as for
+    prefill_quantize) -> (out fp32 [T][Hq][128], lse fp32 [T][Hq])."""
+    T, Hq = int(q.shape[0]), int(q.shape[1])
+    if out is None:
+        out = torch.empty((T, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(prefill_attention_workspace_bytes(cache, T, Hq, max_ctx),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib().kv4_prefill_attention(cache.desc(), _ptr(q), _ptr(cu_seqlens), _ptr(start_pos),
+                                       _ptr(slot), _ptr(page_table), page_table.shape[1],
+                                       start_pos.shape[0], T, Hq, int(max_ctx), float(softmax_scale),
+                                       _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                       _stream()))
+    return out, lse
+
+
+def prefill_attention_debug(cache: Kv4Cache, q, cu_seqlens, start_pos, slot, page_table,
+                            max_ctx: int, softmax_scale: float):
+    """kv4_prefill_attention_debug: also the integer intermediates, indexed by token."""
+    T, Hq = int(q.shape[0]), int(q.shape[1])
+    W = int(page_table.shape[1])
+    dev = q.device
+    dbg = dict(qcodes=torch.zeros((T, Hq, HEAD_DIM), dtype=torch.int8, device=dev),
+               qsum=torch.zeros((T, Hq), dtype=torch.int32, device=dev),
+               qk=torch.zeros((T, Hq, W * PAGE), dtype=torch.int32, device=dev),
+               pcode=torch.zeros((T, Hq, W * PAGE), dtype=torch.uint8, device=dev),
+               pv=torch.zeros((T, Hq, W, HEAD_DIM), dtype=torch.int32, device=dev))
+    d = _Debug(dbg["qcodes"].data_ptr(), dbg["qsum"].data_ptr(), dbg["qk"].data_ptr(),
+               dbg["pcode"].data_ptr(), dbg["pv"].data_ptr(), W * PAGE, W)
+    out = torch.empty((T, Hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(prefill_attention_workspace_bytes(cache, T, Hq, max_ctx), dtype=torch.uint8,
+                     device=dev)
+    _check(lib().kv4_prefill_attention_debug(cache.desc(), _ptr(q), _ptr(cu_seqlens), _ptr(start_pos),
+                                             _ptr(slot), _ptr(page_table), W, start_pos.shape[0], T, Hq,
+                                             int(max_ctx), float(softmax_scale), _ptr(out), _ptr(lse),
+                                             _ptr(ws), ws.numel(), C.byref(d), _stream()))
+    return out, lse, dbg

@@ -217,6 +217,64 @@ int kv4bench_bf16_paged_decode(const void* pages, int32_t num_pages, int32_t Hkv
   return e == hipSuccess ? KV4_OK : hip_fail(e);
 }
 
+// ---- re-prefill attention ------------------------------------------------------
+
+size_t kv4_prefill_attention_workspace_bytes(const kv4_cache_desc* cache, int32_t total_q,
+                                             int32_t Hq, int32_t max_ctx) {
+  if (check_cache(cache) != KV4_OK || total_q <= 0 || Hq <= 0 || max_ctx <= 0) return 0;
+  return kv4::chunk_workspace_bytes(total_q, Hq, cache->num_kv_heads, kv4::main_region_waves());
+}
+
+static int chunk_common(const kv4_cache_desc* cache, const void* q, const int32_t* cu_seqlens,
+                        const int32_t* start_pos, const int32_t* slot, const int32_t* page_table,
+                        int32_t pt_stride, int32_t nseq, int32_t total_q, int32_t Hq, int32_t max_ctx,
+                        float softmax_scale, float* out, float* lse, void* workspace,
+                        size_t workspace_bytes, const kv4_decode_debug* dbg, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != KV4_OK) return rc;
+  if (!q || !cu_seqlens || !start_pos || !page_table || !out || !lse) return KV4_ERR_NULLPTR;
+  const int Hkv = cache->num_kv_heads;
+  if (Hq <= 0 || Hq % Hkv != 0 || Hq / Hkv != kv4::GQA) return KV4_ERR_UNSUPPORTED;
+  if (nseq <= 0 || total_q <= 0 || pt_stride <= 0 || max_ctx <= 0 ||
+      static_cast<int64_t>(max_ctx) > static_cast<int64_t>(pt_stride) * 16)
+    return KV4_ERR_SHAPE;
+  if (static_cast<int64_t>(total_q) * Hkv * (max_ctx / 16 + 1) > INT32_MAX) return KV4_ERR_SHAPE;
+  const int nw = kv4::main_region_waves();
+  if (!workspace || workspace_bytes < kv4::chunk_workspace_bytes(total_q, Hq, Hkv, nw))
+    return KV4_ERR_WORKSPACE;
+  kv4::DecodeDebug d{};
+  if (dbg) {
+    if (dbg->max_ctx < max_ctx || dbg->max_pages < pt_stride) return KV4_ERR_SHAPE;
+    d = kv4::DecodeDebug{dbg->qcodes, dbg->qsum, dbg->qk, dbg->pcode, dbg->pv, dbg->max_ctx,
+                         dbg->max_pages};
+  }
+  hipError_t e = kv4::launch_chunk_attention(view(cache), static_cast<const uint16_t*>(q), cu_seqlens,
+                                             start_pos, nseq, total_q, slot, page_table, pt_stride, Hq,
+                                             scale_log2(softmax_scale), out, lse, workspace, nw,
+                                             dbg ? &d : nullptr, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KV4_OK : hip_fail(e);
+}
+
+int kv4_prefill_attention(const kv4_cache_desc* cache, const void* q, const int32_t* cu_seqlens,
+                          const int32_t* start_pos, const int32_t* slot, const int32_t* page_table,
+                          int32_t pt_stride, int32_t nseq, int32_t total_q, int32_t Hq,
+                          int32_t max_ctx, float softmax_scale, float* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_common(cache, q, cu_seqlens, start_pos, slot, page_table, pt_stride, nseq, total_q,
+                      Hq, max_ctx, softmax_scale, out, lse, workspace, workspace_bytes, nullptr, stream);
+}
+
+int kv4_prefill_attention_debug(const kv4_cache_desc* cache, const void* q,
+                                const int32_t* cu_seqlens, const int32_t* start_pos,
+                                const int32_t* slot, const int32_t* page_table, int32_t pt_stride,
+                                int32_t nseq, int32_t total_q, int32_t Hq, int32_t max_ctx,
+                                float softmax_scale, float* out, float* lse, void* workspace,
+                                size_t workspace_bytes, const kv4_decode_debug* dbg, void* stream) {
+  if (!dbg) return KV4_ERR_NULLPTR;
+  return chunk_common(cache, q, cu_seqlens, start_pos, slot, page_table, pt_stride, nseq, total_q,
+                      Hq, max_ctx, softmax_scale, out, lse, workspace, workspace_bytes, dbg, stream);
+}
+
 // ---- MXFP4 variant -----------------------------------------------------------
 
 int kv4mx_append(const kv4_cache_desc* cache, const void* k, const void* v, const int32_t* pos,

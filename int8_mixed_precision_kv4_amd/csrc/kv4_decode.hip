@@ -36,6 +36,12 @@ struct DecArgs {
   const int32_t* slot;
   const int32_t* page_table;
   int pt_stride;
+  // Chunk attention (re-prefill): entry b of the batch is one query token of
+  // sequence seq_of[b] (its slot and page-table row) whose cache ends at
+  // cache_end[b]; ctx[b] is that token's position + 1.  Both NULL for a decode
+  // step (seq_of = b, cache_end = ctx).
+  const int32_t* seq_of;
+  const int32_t* cache_end;
   int sink, window;  // protection budget s, w
   float scale_log2;
   float* out;
@@ -44,10 +50,17 @@ struct DecArgs {
   DecodeDebug dbg;
 };
 
-// Main region M = [s, L-w) covers logical pages s/16 .. (L-w-1)/16 (s is a
-// multiple of 16, so the first page starts at s).
-__device__ __forceinline__ int main_pages(int L, int s, int w) {
-  return L - w > s ? (L - w - 1) / PAGE - s / PAGE + 1 : 0;
+// Main region of a query attending [0, L) of a cache that ends at E (E = L
+// for a decode step): M = [s, min(L, E-w)), logical pages s/16 .. (end-1)/16
+// (s is a multiple of 16, so the first page starts at s).
+__device__ __forceinline__ int main_end_of(int L, int E, int w) { return min(L, E - w); }
+__device__ __forceinline__ int main_pages(int L, int E, int s, int w) {
+  const int me = main_end_of(L, E, w);
+  return me > s ? (me - 1) / PAGE - s / PAGE + 1 : 0;
+}
+__device__ __forceinline__ int seq_of(const DecArgs& a, int b) { return a.seq_of ? ld_const(a.seq_of + b) : b; }
+__device__ __forceinline__ int end_of(const DecArgs& a, int b, int L) {
+  return a.cache_end ? ld_const(a.cache_end + b) : L;
 }
 
 // plan[b] = sum over earlier sequences of main_pages * Hkv (one workgroup).
@@ -61,7 +74,8 @@ __device__ void build_plan(const DecArgs& a) {
   __syncthreads();
   for (int base = 0; base < a.B; base += 256) {
     const int b = base + threadIdx.x;
-    scan[threadIdx.x] = (b < a.B) ? main_pages(a.ctx[b], a.sink, a.window) * a.Hkv : 0;
+    scan[threadIdx.x] = (b < a.B) ? main_pages(a.ctx[b], a.cache_end ? a.cache_end[b] : a.ctx[b], a.sink,
+                                               a.window) * a.Hkv : 0;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
       const int t = (threadIdx.x >= off) ? scan[threadIdx.x - off] : 0;
@@ -169,12 +183,13 @@ __device__ __forceinline__ int qk_rows(v4i d) {
 
 // ------------------------------------------------------------ protected --
 
-// Position held by side row r when the context is L, for sinks [0, s) and a
-// ring of w recent positions in rows [s, s+w) (-1: row not in use).
-__device__ __forceinline__ int side_position(int r, int L, int s, int w) {
+// Position held by side row r of a cache ending at E, for sinks [0, s) and a
+// ring of w recent positions in rows [s, s+w), if a query attending [0, L)
+// sees it (-1 otherwise).
+__device__ __forceinline__ int side_position(int r, int L, int E, int s, int w) {
   if (r < s) return r < L ? r : -1;
   if (r >= s + w) return -1;
-  const int base = max(s, L - w);
+  const int base = max(s, E - w);
   const int p = base + ((r - s - base) % w + w) % w;
   return p < L ? p : -1;
 }
@@ -212,8 +227,10 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   float* cqs = reinterpret_cast<float*>(qn + GQA * HD);                                                    // [4]
 
   const int L = ld_const(a.ctx + b);
+  const int E = end_of(a, b, L);
   const int nrows = a.sink + a.window;  // rows [0, s+w) can hold the region
-  const int slot = a.slot ? ld_const(a.slot + b) : b;
+  const int sq = seq_of(a, b);
+  const int slot = a.slot ? ld_const(a.slot + sq) : sq;
   const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
   const gptr side = (gptr)a.side_codes + row0 * 2 * HD;
   typedef const __attribute__((address_space(1))) uint16_t* gptr16;
@@ -245,7 +262,7 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
     vop[i] = r < nrows ? *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(side + (2 * r + 1) * HD + 4 * cg) : 0u;
   }
   if (tid < SIDE_ROWS)
-    ssv[tid] = side_position(tid, L, a.sink, a.window) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
+    ssv[tid] = side_position(tid, L, E, a.sink, a.window) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
   // Query of head `wave`: rotate like the keys, then symmetric INT8 with an
   // FP32 scale (lane l holds channels 2l, 2l+1); codes in natural order to LDS.
   {
@@ -288,7 +305,7 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
       d = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], kop[k][1], d, 0, 0, 0);
       const int D8 = qk_rows(d);
       const int r = 16 * rg + r16;
-      const int p = side_position(r, L, a.sink, a.window);
+      const int p = side_position(r, L, E, a.sink, a.window);
       se[r][grp] = (p >= 0) ? (static_cast<float>(D8) * sk[k]) * c_q : -INFINITY;
       if (DEBUG && a.dbg.qk && p >= 0) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + p] = D8;
     }
@@ -990,7 +1007,8 @@ __device__ __forceinline__ PlanView plan_view(const DecArgs& a, int lane) {
   for (int k = 0; k < 4; ++k) {
     const int i = 4 * lane + k;
     const int L = a.ctx[min(i, a.B - 1)];
-    m[k] = i < a.B ? main_pages(L, a.sink, a.window) * a.Hkv : 0;
+    const int E = a.cache_end ? a.cache_end[min(i, a.B - 1)] : L;
+    m[k] = i < a.B ? main_pages(L, E, a.sink, a.window) * a.Hkv : 0;
   }
   m[1] += m[0];
   m[2] += m[1];
@@ -1147,7 +1165,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
     d.last = ip + d.np >= stop;
     d.opens = ip == seg0;
     d.closes = stop == seg_end;
-    const int32_t* ptrow = a.page_table + static_cast<size_t>(ib) * a.pt_stride;
+    const int32_t* ptrow = a.page_table + static_cast<size_t>(seq_of(a, ib)) * a.pt_stride;
     pt = ptrow[d.j0 + min(lane & 3, d.np - 1)];
     if (d.first)  // BF16 query of head grp, channels 8 r16 .. 8 r16 + 7
       raw2 = reinterpret_cast<const uint4*>(a.q + ((static_cast<size_t>(ib) * a.Hq + seg_g * GQA + grp) * HD) / 2)[r16];
@@ -1162,7 +1180,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
     for (int t = 0; t < F::kUnit; ++t)
       blk[t] = gbase + static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(pt, t))) * pstride;
     F::to_lds(slot, blk, lane, r16, grp);
-    if (d.first) d.main_end = ld_const(a.ctx + d.b) - a.window;
+    if (d.first) {
+      const int L = ld_const(a.ctx + d.b);
+      d.main_end = main_end_of(L, end_of(a, d.b, L), a.window);
+    }
   };
 
   // Pipeline: quad i is computed while quad i+1 streams into the LDS slot
@@ -1244,7 +1265,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
 // the main partials of each head, one workgroup per (kv-head g, sequence b),
 // wave h for head h, lane l for channels 2l, 2l+1.  Writes out and lse.
 __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
-  const int g = blockIdx.x, b = blockIdx.y;
+  const int g = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.Hkv));
+  const int b = static_cast<int>(blockIdx.x / static_cast<unsigned>(a.Hkv));
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const size_t bh = static_cast<size_t>(b) * a.Hq + g * GQA + wave;
   float2 Am = make_float2(0.0f, 0.0f);
@@ -1258,7 +1280,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
   // main partials: chunks c_lo..c_hi (recorded by the main kernel) at slots c + b*Hkv + g
   const int bg = b * a.Hkv + g;
   const int2 cr = a.ws.mrange[bg];  // written by the main kernel when the segment has pages
-  const int c_lo = cr.x, n_parts = main_pages(ld_const(a.ctx + b), a.sink, a.window) > 0 ? cr.y - cr.x + 1 : 0;
+  const int Lb = ld_const(a.ctx + b);
+  const int c_lo = cr.x, n_parts = main_pages(Lb, end_of(a, b, Lb), a.sink, a.window) > 0 ? cr.y - cr.x + 1 : 0;
   constexpr int kBatch = 4;
   for (int k0 = 0; k0 < n_parts; k0 += kBatch) {
     float2 Ac[kBatch];
@@ -1285,6 +1308,26 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
   }
   reinterpret_cast<float2*>(a.out + bh * HD)[lane] = make_float2(Am.x / lm, Am.y / lm);
   if (lane == 0) a.lse[bh] = 0.69314718055994531f * (Zm + log2f(lm));
+}
+
+// Per-token entries of a chunk-attention call: token t of the packed chunks
+// (sequence s: tokens cu[s] .. cu[s+1]-1 at positions start[s] ..) attends
+// [0, start[s] + t - cu[s]] of a cache ending at start[s] + cu[s+1] - cu[s].
+__global__ __launch_bounds__(256) void chunk_tokens_kernel(const int32_t* __restrict__ cu,
+                                                           const int32_t* __restrict__ start, int nseq,
+                                                           int T, int32_t* ctx_v, int32_t* seq_v,
+                                                           int32_t* end_v) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int lo = 0, hi = nseq;  // cu[lo] <= t < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  ctx_v[t] = start[lo] + (t - cu[lo]) + 1;
+  seq_v[t] = lo;
+  end_v[t] = start[lo] + (cu[lo + 1] - cu[lo]);
 }
 
 }  // namespace
@@ -1322,7 +1365,8 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
                          const int32_t* slot, const int32_t* page_table, int pt_stride, int B,
                          int Hq, float scale_log2, float* out, float* lse,
                          const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
-                         hipEvent_t ev_main_begin, hipEvent_t ev_main_end, bool mx) {
+                         hipEvent_t ev_main_begin, hipEvent_t ev_main_end, bool mx,
+                         const int32_t* seq_of, const int32_t* cache_end) {
   if (ws.n_waves <= 0 || ws.n_waves % 4 != 0) return hipErrorInvalidValue;
   if (mx && dbg) return hipErrorInvalidValue;  // no debug instantiation of the MXFP4 variant
   DecArgs a{};
@@ -1337,6 +1381,8 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   a.slot = slot;
   a.page_table = page_table;
   a.pt_stride = pt_stride;
+  a.seq_of = seq_of;
+  a.cache_end = cache_end;
   a.sink = c.sink;
   a.window = c.window;
   a.scale_log2 = scale_log2;
@@ -1346,7 +1392,7 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   if (dbg) a.dbg = *dbg;
   // main-region workgroups, then one protected-region workgroup per (b, g)
   const int prot_groups = c.sink + c.window > 0 ? B * c.Hkv : 0;
-  const dim3 block(256), groups(c.Hkv, B), grid(ws.n_waves / 4 + prot_groups);
+  const dim3 block(256), groups(c.Hkv * B), grid(ws.n_waves / 4 + prot_groups);
   if (B > 256) hipLaunchKernelGGL(plan_kernel, dim3(1), block, 0, s, a);
   if (dbg) {
     hipLaunchKernelGGL((main_kernel<Kv4Format, true>), grid, block, 0, s, a);
@@ -1365,6 +1411,28 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
     hipLaunchKernelGGL(merge_kernel, groups, block, 0, s, a);
   }
   return hipGetLastError();
+}
+
+size_t chunk_workspace_bytes(int T, int Hq, int Hkv, int n_waves) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  return decode_workspace_bytes(T, Hq, Hkv, n_waves) + 3 * up(static_cast<size_t>(T) * 4);
+}
+
+hipError_t launch_chunk_attention(const CacheView& c, const uint16_t* q, const int32_t* cu,
+                                  const int32_t* start, int nseq, int T, const int32_t* slot,
+                                  const int32_t* page_table, int pt_stride, int Hq, float scale_log2,
+                                  float* out, float* lse, void* ws_base, int n_waves,
+                                  const DecodeDebug* dbg, hipStream_t s) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  char* tok = static_cast<char*>(ws_base) + decode_workspace_bytes(T, Hq, c.Hkv, n_waves);
+  int32_t* ctx_v = reinterpret_cast<int32_t*>(tok);
+  int32_t* seq_v = reinterpret_cast<int32_t*>(tok + up(static_cast<size_t>(T) * 4));
+  int32_t* end_v = reinterpret_cast<int32_t*>(tok + 2 * up(static_cast<size_t>(T) * 4));
+  hipLaunchKernelGGL(chunk_tokens_kernel, dim3((T + 255) / 256), dim3(256), 0, s, cu, start, nseq, T,
+                     ctx_v, seq_v, end_v);
+  const DecodeWorkspace ws = carve_workspace(ws_base, T, Hq, c.Hkv, n_waves);
+  return launch_decode(c, q, ctx_v, slot, page_table, pt_stride, T, Hq, scale_log2, out, lse, ws, dbg,
+                       s, nullptr, nullptr, false, seq_v, end_v);
 }
 
 hipError_t launch_kv8_decode(const uint8_t* pages, int Hkv, const uint16_t* q, const int32_t* ctx,
@@ -1388,7 +1456,7 @@ hipError_t launch_kv8_decode(const uint8_t* pages, int Hkv, const uint16_t* q, c
   a.lse = lse;
   a.ws = ws;
   if (dbg) a.dbg = *dbg;
-  const dim3 block(256), groups(Hkv, B), grid(ws.n_waves / 4);
+  const dim3 block(256), groups(Hkv * B), grid(ws.n_waves / 4);
   if (B > 256) hipLaunchKernelGGL(plan_kernel, dim3(1), block, 0, s, a);
   if (dbg) hipLaunchKernelGGL((main_kernel<Kv8Format, true>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((main_kernel<Kv8Format, false>), grid, block, 0, s, a);

@@ -76,7 +76,17 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
                          int Hq, float scale_log2, float* out, float* lse,
                          const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
                          hipEvent_t ev_main_begin = nullptr, hipEvent_t ev_main_end = nullptr,
-                         bool mx = false);
+                         bool mx = false, const int32_t* seq_of = nullptr,
+                         const int32_t* cache_end = nullptr);
+// Re-prefill (chunked-prefill) attention: every query token of the packed
+// chunks is one entry of a decode batch (its context = position + 1, its cache
+// end = the chunk's end); the per-token arrays live after the decode workspace.
+size_t chunk_workspace_bytes(int T, int Hq, int Hkv, int n_waves);
+hipError_t launch_chunk_attention(const CacheView& c, const uint16_t* q, const int32_t* cu,
+                                  const int32_t* start, int nseq, int T, const int32_t* slot,
+                                  const int32_t* page_table, int pt_stride, int Hq, float scale_log2,
+                                  float* out, float* lse, void* ws_base, int n_waves,
+                                  const DecodeDebug* dbg, hipStream_t s);
 hipError_t launch_bf16_decode(const uint16_t* pages, int num_pages, int Hkv, const uint16_t* q,
                               const int32_t* ctx, const int32_t* page_table, int pt_stride, int B,
                               int Hq, float scale_log2, float* out, float* lse, void* ws,
