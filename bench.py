@@ -4,8 +4,8 @@
 Workload (qwen8b-shaped decode step): B=256 sequences, Hq/Hkv = 32/8, head_dim
 128, page 16, 36 layers, contexts = U[128,512] prompt + a length-biased
 lognormal(mean 3000, sd 2250) response position (+ this step's token).  One
-step = for each of the 36 layers: kv4_append of one token per sequence, then
-kv4_decode_attention.  Every layer has its own cache, so the step streams
+step = for each of the 36 layers: the append of one token per sequence and
+the decode attention, in one launch (kv4_append_decode_attention).  Every layer has its own cache, so the step streams
 ~28 GB of INT4 pages and never hits the 256 MB last-level cache.
 
 Prints one JSON line: decode-attention tokens/s (whole step), achieved HBM
@@ -65,10 +65,13 @@ def main_kernel_bytes(ctx, Hkv):
     """Algorithmic bytes of the main kernel per launch: 136 B (64 B K codes +
     64 B V codes + 4 B + 4 B FP16 metadata) per main (position, kv-head), plus
     the protected region its last workgroups read: 260 B (2 x 128 B INT8
-    codes + 2 x 2 B FP16 scales) per side (position, kv-head)."""
+    codes + 2 x 2 B FP16 scales) per side (position, kv-head), plus this
+    step's append done by those workgroups: 512 B of BF16 K and V read, 136 B
+    of page entry and 260 B of side row written per (sequence, kv-head)."""
     import numpy as np
     ctx = np.asarray(ctx, dtype=np.int64)
-    return int((np.maximum(ctx - 144, 0) * Hkv * 136).sum() + (np.minimum(ctx, 144) * Hkv * 260).sum())
+    return int((np.maximum(ctx - 144, 0) * Hkv * 136).sum() + (np.minimum(ctx, 144) * Hkv * 260).sum()
+               + len(ctx) * Hkv * (512 + 136 + 260))
 
 
 class HipEvents:
@@ -498,10 +501,12 @@ def main():
 
     def step(decode_only=False):
         for L in layers:
-            if not decode_only:
-                kv4.append(L["cache"], L["k_app"], L["v_app"], pos, slots, table)
-            kv4.decode_attention(L["cache"], L["q"], ctx, slots, table, wl.max_ctx, scale,
-                                 out, lse, ws)
+            if decode_only:
+                kv4.decode_attention(L["cache"], L["q"], ctx, slots, table, wl.max_ctx, scale,
+                                     out, lse, ws)
+            else:  # this step's append and the decode in one launch
+                kv4.append_decode_attention(L["cache"], L["k_app"], L["v_app"], pos, L["q"], ctx, slots,
+                                            table, wl.max_ctx, scale, out, lse, ws)
 
     def timed(fn, steps, warmup):
         for _ in range(warmup):
@@ -546,7 +551,7 @@ def main():
         for li, L in enumerate(layers):
             e0, e1 = evs.pair(r * LAYERS + li)
             kv4.decode_attention_timed(L["cache"], L["q"], ctx, slots, table, wl.max_ctx, scale,
-                                       out, lse, ws, e0, e1)
+                                       out, lse, ws, e0, e1, k=L["k_app"], v=L["v_app"], pos=pos)
     torch.cuda.synchronize()
     main_ms = float(np.mean([evs.elapsed_ms(i) for i in range(LAYERS * args.steps)]))
     evs.close()
@@ -654,7 +659,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": ("qwen8b decode step: B=256, Hq/Hkv=32/8, head_dim 128, page 16, "
                                 "36 layers, ctx = U[128,512] + length-biased lognormal(3000, 2250) "
-                                "position + 1; per layer kv4_append then kv4_decode_attention"
+                                "position + 1; per layer kv4_append_decode_attention (this step's "
+                                "append and the decode in one launch)"
                                 + ("; contexts replayed from one steady-state step of a simulated "
                                    "continuous-refill run" if args.workload == "refill" else "")),
                    "B": B, "layers": LAYERS, "mean_ctx": round(float(wl.ctx.mean()), 1),
@@ -665,7 +671,8 @@ def main():
         "hbm_gbps": round(mb * LAYERS / t_decode / 1e9, 1),
         "hbm_frac_of_peak": round(mb * LAYERS / t_decode / 1e9 / PEAK_GBS, 4),
         "metric_bytes_per_layer": mb,
-        "roofline": {"bound": "hbm", "kernel": "main_kernel (INT4 main region + INT8 protected region)",
+        "roofline": {"bound": "hbm", "kernel": ("main_kernel (INT4 main region + INT8 protected region "
+                                                "+ this step's append)"),
                      "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(main_ms * 1e3, 2), "alg_bytes_per_launch": main_bytes},

@@ -132,6 +132,20 @@ int kv4_decode_attention(const kv4_cache_desc *cache, const void *q, const int32
                          int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale, float *out,
                          float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
+/* One whole decode step in one launch: kv4_append(k, v, pos) followed by
+ * kv4_decode_attention, with identical results.  Requires pos[b] = ctx_len[b]
+ * - 1 (this step's token; not checked on the device).  When w > 0 the token
+ * lies in its sequence's recent window, so the protected-region workgroup of
+ * (b, kv-head) quantizes and writes it (page entry and side row) before it
+ * attends, and no other work of the step reads it; with w = 0 the append runs
+ * as its own launch first.  Arguments as for the two calls. */
+int kv4_append_decode_attention(const kv4_cache_desc *cache, const void *k, const void *v,
+                                const int32_t *pos, const void *q, const int32_t *ctx_len,
+                                const int32_t *slot, const int32_t *page_table, int32_t pt_stride,
+                                int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale,
+                                float *out, float *lse, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* Integer intermediates of a decode step, for bit-exact checking (device
  * pointers; any may be NULL).  Same layouts as the arguments of
  * kv4_decode_attention plus:
@@ -206,16 +220,18 @@ int kv4bench_bf16_paged_decode(const void *pages, int32_t num_pages, int32_t Hkv
                                float softmax_scale, float *out, float *lse, void *workspace,
                                size_t workspace_bytes, void *stream);
 
-/* Benchmark hook: kv4_decode_attention that also records two caller-created
+/* Benchmark hook: kv4_append_decode_attention (k, v, pos given) or
+ * kv4_decode_attention (all three NULL) that also records two caller-created
  * HIP events (hipEvent_t passed as void*) on `stream`, immediately before and
- * after the main-region kernel, so the dominant kernel can be timed on the
- * stream it runs on.  Either event may be NULL. */
-int kv4bench_decode_attention_timed(const kv4_cache_desc *cache, const void *q,
-                                    const int32_t *ctx_len, const int32_t *slot,
-                                    const int32_t *page_table, int32_t pt_stride, int32_t B,
-                                    int32_t Hq, int32_t max_ctx, float softmax_scale, float *out,
-                                    float *lse, void *workspace, size_t workspace_bytes,
-                                    void *ev_main_begin, void *ev_main_end, void *stream);
+ * after the main kernel, so the dominant kernel can be timed on the stream it
+ * runs on.  Either event may be NULL. */
+int kv4bench_decode_attention_timed(const kv4_cache_desc *cache, const void *k, const void *v,
+                                    const int32_t *pos, const void *q, const int32_t *ctx_len,
+                                    const int32_t *slot, const int32_t *page_table,
+                                    int32_t pt_stride, int32_t B, int32_t Hq, int32_t max_ctx,
+                                    float softmax_scale, float *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *ev_main_begin, void *ev_main_end,
+                                    void *stream);
 
 /* ---- variant: MXFP4 main region ----------------------------------------------
  * The 4-bit format comparison of the pages (KV4-RL, appendix D.4: NVFP4 and

@@ -25,7 +25,7 @@ EXPORTS = ("kv4_append", "kv4_prefill_quantize", "kv4_decode_workspace_bytes",
            "kv8_decode_workspace_bytes", "kv8_decode_attention", "kv8_decode_attention_debug",
            "kv4mx_append", "kv4mx_prefill_quantize", "kv4mx_decode_attention",
            "kv4_prefill_attention_workspace_bytes", "kv4_prefill_attention",
-           "kv4_prefill_attention_debug")
+           "kv4_prefill_attention_debug", "kv4_append_decode_attention")
 KV8_BLOCK_BYTES = 4160
 
 _lib = None
@@ -75,8 +75,9 @@ def lib():
         L.kv4bench_bf16_workspace_bytes.argtypes = [I, I, I, I]
         L.kv4bench_bf16_workspace_bytes.restype = Z
         L.kv4bench_bf16_paged_decode.argtypes = [P, I, I, P, P, P, I, I, I, I, F, P, P, P, Z, P]
-        L.kv4bench_decode_attention_timed.argtypes = [D, P, P, P, P, I, I, I, I, F, P, P, P, Z,
-                                                      P, P, P]
+        L.kv4bench_decode_attention_timed.argtypes = [D, P, P, P, P, P, P, P, I, I, I, I, F, P, P,
+                                                      P, Z, P, P, P]
+        L.kv4_append_decode_attention.argtypes = [D, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P, Z, P]
         L.kv4_prefill_attention_workspace_bytes.argtypes = [D, I, I, I]
         L.kv4_prefill_attention_workspace_bytes.restype = Z
         L.kv4_prefill_attention.argtypes = [D, P, P, P, P, P, I, I, I, I, I, F, P, P, P, Z, P]
@@ -231,15 +232,35 @@ def bf16_paged_decode(pages, q, ctx_len, page_table, max_ctx: int, softmax_scale
 
 
 def decode_attention_timed(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ctx: int,
-                           softmax_scale: float, out, lse, workspace, ev_begin, ev_end):
-    """kv4bench_decode_attention_timed: as decode_attention, recording the two
-    raw hipEvent_t handles (ctypes.c_void_p) around the main-region kernel."""
+                           softmax_scale: float, out, lse, workspace, ev_begin, ev_end,
+                           k=None, v=None, pos=None):
+    """kv4bench_decode_attention_timed: as decode_attention (or, with k, v, pos,
+    append_decode_attention), recording the two raw hipEvent_t handles
+    (ctypes.c_void_p) around the main kernel."""
     B, Hq = int(q.shape[0]), int(q.shape[1])
     _check(lib().kv4bench_decode_attention_timed(
-        cache.desc(), _ptr(q), _ptr(ctx_len), _ptr(slot), _ptr(page_table), page_table.shape[1],
-        B, Hq, int(max_ctx), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
-        workspace.numel(), ev_begin, ev_end,
-        _stream()))
+        cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(q), _ptr(ctx_len), _ptr(slot),
+        _ptr(page_table), page_table.shape[1], B, Hq, int(max_ctx), float(softmax_scale), _ptr(out),
+        _ptr(lse), _ptr(workspace), workspace.numel(), ev_begin, ev_end, _stream()))
+
+
+def append_decode_attention(cache: Kv4Cache, k, v, pos, q, ctx_len, slot, page_table, max_ctx: int,
+                            softmax_scale: float, out=None, lse=None, workspace=None):
+    """kv4_append_decode_attention: append(k, v, pos) then decode_attention in one launch
+    (pos = ctx_len - 1)."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(cache, B, Hq, max_ctx), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().kv4_append_decode_attention(
+        cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(q), _ptr(ctx_len), _ptr(slot),
+        _ptr(page_table), page_table.shape[1], B, Hq, int(max_ctx), float(softmax_scale), _ptr(out),
+        _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse
 
 
 # ------------------------------------------------------------ KV8 variant --

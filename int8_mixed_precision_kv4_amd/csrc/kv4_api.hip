@@ -138,7 +138,8 @@ static int decode_common(const kv4_cache_desc* cache, const void* q, const int32
                          int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale, float* out,
                          float* lse, void* workspace, size_t workspace_bytes,
                          const kv4_decode_debug* dbg, void* stream, void* ev0 = nullptr,
-                         void* ev1 = nullptr, bool mx = false) {
+                         void* ev1 = nullptr, bool mx = false, const void* k_new = nullptr,
+                         const void* v_new = nullptr, const int32_t* pos_new = nullptr) {
   int rc = check_decode(cache, q, ctx_len, page_table, pt_stride, B, Hq, max_ctx, out, lse);
   if (rc != KV4_OK) return rc;
   if (B > 65535) return KV4_ERR_SHAPE;
@@ -153,11 +154,22 @@ static int decode_common(const kv4_cache_desc* cache, const void* q, const int32
   }
   const kv4::DecodeWorkspace ws =
       kv4::carve_workspace(workspace, B, Hq, cache->num_kv_heads, nw);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (k_new && cache->window <= 0) {
+    // no protected workgroup owns the new token: append first, then decode
+    hipError_t e = kv4::launch_append(view(cache), static_cast<const uint16_t*>(k_new),
+                                      static_cast<const uint16_t*>(v_new), pos_new, slot, page_table,
+                                      pt_stride, B, st);
+    if (e != hipSuccess) return hip_fail(e);
+    k_new = v_new = nullptr;
+    pos_new = nullptr;
+  }
   hipError_t e = kv4::launch_decode(view(cache), static_cast<const uint16_t*>(q), ctx_len, slot,
                                     page_table, pt_stride, B, Hq, scale_log2(softmax_scale), out,
-                                    lse, ws, dbg ? &d : nullptr,
-                                    static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev0),
-                                    static_cast<hipEvent_t>(ev1), mx);
+                                    lse, ws, dbg ? &d : nullptr, st, static_cast<hipEvent_t>(ev0),
+                                    static_cast<hipEvent_t>(ev1), mx, nullptr, nullptr,
+                                    static_cast<const uint16_t*>(k_new),
+                                    static_cast<const uint16_t*>(v_new), pos_new);
   return e == hipSuccess ? KV4_OK : hip_fail(e);
 }
 
@@ -180,15 +192,29 @@ int kv4_decode_attention_debug(const kv4_cache_desc* cache, const void* q,
                        softmax_scale, out, lse, workspace, workspace_bytes, dbg, stream);
 }
 
-int kv4bench_decode_attention_timed(const kv4_cache_desc* cache, const void* q,
-                                    const int32_t* ctx_len, const int32_t* slot,
-                                    const int32_t* page_table, int32_t pt_stride, int32_t B,
-                                    int32_t Hq, int32_t max_ctx, float softmax_scale, float* out,
-                                    float* lse, void* workspace, size_t workspace_bytes,
-                                    void* ev_main_begin, void* ev_main_end, void* stream) {
+int kv4_append_decode_attention(const kv4_cache_desc* cache, const void* k, const void* v,
+                                const int32_t* pos, const void* q, const int32_t* ctx_len,
+                                const int32_t* slot, const int32_t* page_table, int32_t pt_stride,
+                                int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale,
+                                float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!k || !v || !pos) return KV4_ERR_NULLPTR;
+  return decode_common(cache, q, ctx_len, slot, page_table, pt_stride, B, Hq, max_ctx,
+                       softmax_scale, out, lse, workspace, workspace_bytes, nullptr, stream, nullptr,
+                       nullptr, false, k, v, pos);
+}
+
+int kv4bench_decode_attention_timed(const kv4_cache_desc* cache, const void* k, const void* v,
+                                    const int32_t* pos, const void* q, const int32_t* ctx_len,
+                                    const int32_t* slot, const int32_t* page_table,
+                                    int32_t pt_stride, int32_t B, int32_t Hq, int32_t max_ctx,
+                                    float softmax_scale, float* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* ev_main_begin, void* ev_main_end,
+                                    void* stream) {
+  if ((k == nullptr) != (v == nullptr) || (k == nullptr) != (pos == nullptr)) return KV4_ERR_NULLPTR;
   return decode_common(cache, q, ctx_len, slot, page_table, pt_stride, B, Hq, max_ctx,
                        softmax_scale, out, lse, workspace, workspace_bytes, nullptr, stream,
-                       ev_main_begin, ev_main_end);
+                       ev_main_begin, ev_main_end, false, k, v, pos);
 }
 
 size_t kv4bench_bf16_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx) {

@@ -42,6 +42,13 @@ struct DecArgs {
   // step (seq_of = b, cache_end = ctx).
   const int32_t* seq_of;
   const int32_t* cache_end;
+  // Fused append (decode step only): this step's token of sequence b at
+  // position pos_new[b] (= ctx[b] - 1), bf16 pairs [B][Hkv][64]; NULL: none.
+  // Its protected workgroup writes the token's page entry and side row before
+  // attending (the token is in the recent window, so nothing else reads it).
+  const uint32_t* k_new;
+  const uint32_t* v_new;
+  const int32_t* pos_new;
   int sink, window;  // protection budget s, w
   float scale_log2;
   float* out;
@@ -214,6 +221,7 @@ __device__ __forceinline__ void round_bf16x2(float& x, float& y) {
 // with a permlane swap and the 4 waves through LDS.  Wave h writes the
 // partial (A[128], Z, l) of head h to the workspace.
 constexpr int kProtLds = SIDE_ROWS * GQA * 4 + SIDE_ROWS * 4 + 4 * GQA * HD * 4 + GQA * HD + GQA * 4;  // 11600 B
+constexpr int kProtLdsFused = kProtLds + 2 * HD + 8;  // plus this step's INT8 row and its scales
 
 template <bool DEBUG>
 __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b, uint8_t* lds_raw) {
@@ -237,7 +245,25 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   const gptr16 scales = (gptr16)(a.side_scales + row0 * 2);
   const size_t qb = static_cast<size_t>(b) * a.Hq + g * GQA;
 
-  // ---- every load first
+  // ---- every load first: this step's token (fused append) with the side
+  // rows, so that the append overlaps their arrival.  Wave 0 makes the INT8
+  // row, wave 1 the INT4 K half of the page entry, wave 2 its V half.
+  int r_new = -1, new_pos = 0;
+  uint32_t kw = 0, vw = 0;
+  uint8_t* new_blk = nullptr;
+  VBytes new_vb{0, 0};
+  if (a.k_new) {
+    new_pos = ld_const(a.pos_new + b);
+    r_new = new_pos < a.sink ? new_pos : a.sink + new_pos % a.window;  // w > 0 on this path
+    const size_t vec = static_cast<size_t>(b) * a.Hkv + g;
+    if (wave == 0 || wave == 1) kw = a.k_new[vec * 64 + lane];
+    if (wave == 0 || wave == 2) vw = a.v_new[vec * 64 + lane];
+    if (wave == 1 || wave == 2) {
+      const int phys = ld_const(a.page_table + static_cast<size_t>(sq) * a.pt_stride + (new_pos >> 4));
+      new_blk = const_cast<uint8_t*>(a.pages) + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
+      if (wave == 2) new_vb = v_bytes_of(new_blk, new_pos & (PAGE - 1), lane);
+    }
+  }
   // K operands and scales of this wave's row groups (rg = wave + 4k)
   v4i kop[3][2];
   float sk[3];
@@ -263,6 +289,32 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   }
   if (tid < SIDE_ROWS)
     ssv[tid] = side_position(tid, L, E, a.sink, a.window) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
+  // Fused append: this step's token goes to its page slot and its side row,
+  // and the INT8 row also to LDS; after the barrier below every wave replaces
+  // what it loaded for that row (the loads above may have seen the old row).
+  int8_t* nrow = reinterpret_cast<int8_t*>(lds_raw + kProtLds);   // [2][128] K, V codes
+  float* nscale = reinterpret_cast<float*>(lds_raw + kProtLds + 2 * HD);  // s_k, s_v
+  if (r_new >= 0 && wave < 3) {
+    const int t = new_pos & (PAGE - 1);
+    float k0 = bf16_lo(kw), k1 = bf16_hi(kw);
+    const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
+    if (wave != 2) fwht128_wave(k0, k1);
+    if (wave == 0) {
+      const size_t rr = row0 + r_new;
+      const Int8Row nr = write_int8_row(const_cast<int8_t*>(a.side_codes) + rr * 2 * HD,
+                                        const_cast<uint16_t*>(a.side_scales) + rr * 2, k0, k1, v0, v1, lane);
+      reinterpret_cast<uint16_t*>(nrow)[lane] = static_cast<uint16_t>(nr.kp);
+      reinterpret_cast<uint16_t*>(nrow)[64 + lane] = static_cast<uint16_t>(nr.vp);
+      if (lane == 0) {
+        nscale[0] = f16_value(nr.ks16);
+        nscale[1] = f16_value(nr.vs16);
+      }
+    } else if (wave == 1) {
+      write_int4_k(new_blk, t, k0, k1, lane);
+    } else {
+      write_int4_v(new_blk, t, v0, v1, lane, new_vb);
+    }
+  }
   // Query of head `wave`: rotate like the keys, then symmetric INT8 with an
   // FP32 scale (lane l holds channels 2l, 2l+1); codes in natural order to LDS.
   {
@@ -289,6 +341,25 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
     }
   }
   __syncthreads();
+  if (r_new >= 0) {  // this step's row from LDS, one read per lane, selected in place
+    {
+      const v4i kn0 = *reinterpret_cast<const v4i*>(nrow + 16 * grp);
+      const v4i kn1 = *reinterpret_cast<const v4i*>(nrow + 64 + 16 * grp);
+      const float skn = nscale[0];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const bool hit = 16 * (wave + 4 * k) + r16 == r_new;
+        kop[k][0] = hit ? kn0 : kop[k][0];
+        kop[k][1] = hit ? kn1 : kop[k][1];
+        sk[k] = hit ? skn : sk[k];
+      }
+    }
+    const uint32_t vn = *reinterpret_cast<const uint32_t*>(nrow + HD + 4 * cg);
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave / 2; ++i)
+      vop[i] = kRowsPerWave * wave + rp + 2 * i == r_new ? vn : vop[i];
+    if (tid == r_new) ssv[tid] = nscale[1];  // read by the PV phase, after two more barriers
+  }
   v4i qa[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
   if (r16 < GQA) {
     qa[0] = *reinterpret_cast<const v4i*>(qn + r16 * HD + 16 * grp);
@@ -1062,7 +1133,7 @@ struct QuadDesc {
 template <class F, bool DEBUG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPerSimd, F::kWavesPerSimd))) void main_kernel(DecArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kSlotBytes];
-  static_assert(kProtLds <= 4 * kSlotBytes, "the protected role reuses the main role's LDS");
+  static_assert(kProtLdsFused <= 4 * kSlotBytes, "the protected role reuses the main role's LDS");
   const int nw = a.ws.n_waves;
   if constexpr (F::kProtected) {
     if (blockIdx.x >= nw / 4) {  // protected-region workgroups fill the tail of the grid
@@ -1366,7 +1437,10 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
                          int Hq, float scale_log2, float* out, float* lse,
                          const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
                          hipEvent_t ev_main_begin, hipEvent_t ev_main_end, bool mx,
-                         const int32_t* seq_of, const int32_t* cache_end) {
+                         const int32_t* seq_of, const int32_t* cache_end, const uint16_t* k_new,
+                         const uint16_t* v_new, const int32_t* pos_new) {
+  // the fused append needs protected workgroups that own the new token
+  if (k_new && (mx || c.window <= 0 || seq_of)) return hipErrorInvalidValue;
   if (ws.n_waves <= 0 || ws.n_waves % 4 != 0) return hipErrorInvalidValue;
   if (mx && dbg) return hipErrorInvalidValue;  // no debug instantiation of the MXFP4 variant
   DecArgs a{};
@@ -1383,6 +1457,9 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   a.pt_stride = pt_stride;
   a.seq_of = seq_of;
   a.cache_end = cache_end;
+  a.k_new = reinterpret_cast<const uint32_t*>(k_new);
+  a.v_new = reinterpret_cast<const uint32_t*>(v_new);
+  a.pos_new = pos_new;
   a.sink = c.sink;
   a.window = c.window;
   a.scale_log2 = scale_log2;

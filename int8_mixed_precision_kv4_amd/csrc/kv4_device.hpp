@@ -198,6 +198,66 @@ __device__ __forceinline__ int32_t int8_code(float x, const Int8Meta& q) {
   return static_cast<int32_t>(fminf(fmaxf(t, -127.0f), 127.0f));
 }
 
+// ------------------------------------------------------ cache entries --
+// One token of one kv-head, held by one wave (lane l: channels 2l, 2l+1; K
+// already rotated).
+
+// INT4 entry in slot t of its page block: K token-major (channel 2l in the low
+// nibble of byte l), V channel-major (this position's nibble of bytes 8c + t/2
+// for channels 2l, 2l+1; the neighbouring position's nibble is kept), and the
+// FP16 (delta, m) pairs.  The K half and the V half are independent (two
+// waves may write them); the two V bytes this lane rewrites are read first
+// (v_bytes_of), which a caller may issue early, next to its other loads.
+struct VBytes {
+  uint8_t b0, b1;
+};
+__device__ __forceinline__ VBytes v_bytes_of(const uint8_t* blk, int t, int lane) {
+  const uint8_t* vb0 = blk + OFF_VCODE + 8 * (2 * lane) + (t >> 1);
+  return VBytes{vb0[0], vb0[8]};
+}
+__device__ __forceinline__ void write_int4_k(uint8_t* blk, int t, float k0, float k1, int lane) {
+  const Int4Meta kq = int4_meta(wave_min(fminf(k0, k1)), wave_max(fmaxf(k0, k1)));
+  blk[64 * t + lane] = static_cast<uint8_t>(int4_code(k0, kq) | (int4_code(k1, kq) << 4));
+  if (lane == 0) *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
+}
+__device__ __forceinline__ void write_int4_v(uint8_t* blk, int t, float v0, float v1, int lane, VBytes old) {
+  const Int4Meta vq = int4_meta(wave_min(fminf(v0, v1)), wave_max(fmaxf(v0, v1)));
+  const int sh = (t & 1) * 4;
+  const uint32_t keep = (t & 1) ? 0x0Fu : 0xF0u;
+  uint8_t* vb0 = blk + OFF_VCODE + 8 * (2 * lane) + (t >> 1);
+  vb0[0] = static_cast<uint8_t>((old.b0 & keep) | (int4_code(v0, vq) << sh));
+  vb0[8] = static_cast<uint8_t>((old.b1 & keep) | (int4_code(v1, vq) << sh));
+  if (lane == 0) *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
+}
+__device__ __forceinline__ void write_int4_entry(uint8_t* blk, int t, float k0, float k1, float v0,
+                                                 float v1, int lane) {
+  write_int4_k(blk, t, k0, k1, lane);
+  write_int4_v(blk, t, v0, v1, lane, v_bytes_of(blk, t, lane));
+}
+
+// INT8 side row: codes [2][128] (K then V), scales [2] FP16.  Returns this
+// lane's two K and two V codes (byte pairs) and the scale bit patterns.
+struct Int8Row {
+  uint32_t kp, vp, ks16, vs16;
+};
+__device__ __forceinline__ Int8Row write_int8_row(int8_t* codes, uint16_t* scales, float k0, float k1,
+                                                  float v0, float v1, int lane) {
+  const Int8Meta ks = int8_meta(wave_max(fmaxf(fabsf(k0), fabsf(k1))));
+  const Int8Meta vs = int8_meta(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
+  Int8Row r;
+  r.kp = (static_cast<uint32_t>(int8_code(k0, ks)) & 0xFFu) | ((static_cast<uint32_t>(int8_code(k1, ks)) & 0xFFu) << 8);
+  r.vp = (static_cast<uint32_t>(int8_code(v0, vs)) & 0xFFu) | ((static_cast<uint32_t>(int8_code(v1, vs)) & 0xFFu) << 8);
+  r.ks16 = ks.s16;
+  r.vs16 = vs.s16;
+  reinterpret_cast<uint16_t*>(codes)[lane] = static_cast<uint16_t>(r.kp);
+  reinterpret_cast<uint16_t*>(codes)[64 + lane] = static_cast<uint16_t>(r.vp);
+  if (lane == 0) {
+    scales[0] = static_cast<uint16_t>(ks.s16);
+    scales[1] = static_cast<uint16_t>(vs.s16);
+  }
+  return r;
+}
+
 // ----------------------------------------------------------------- exp2 --
 // Softmax weights: 2^y for y <= 0 evaluated the same way on every device so
 // that P-operand codes are reproducible: y < -125 gives 0; otherwise

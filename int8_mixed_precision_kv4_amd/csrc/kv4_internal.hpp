@@ -77,7 +77,8 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
                          const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
                          hipEvent_t ev_main_begin = nullptr, hipEvent_t ev_main_end = nullptr,
                          bool mx = false, const int32_t* seq_of = nullptr,
-                         const int32_t* cache_end = nullptr);
+                         const int32_t* cache_end = nullptr, const uint16_t* k_new = nullptr,
+                         const uint16_t* v_new = nullptr, const int32_t* pos_new = nullptr);
 // Re-prefill (chunked-prefill) attention: every query token of the packed
 // chunks is one entry of a decode batch (its context = position + 1, its cache
 // end = the chunk's end); the per-token arrays live after the decode workspace.

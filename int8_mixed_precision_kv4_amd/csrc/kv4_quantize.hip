@@ -36,19 +36,7 @@ __device__ __forceinline__ int side_row(const QuantArgs& a, int p) {
 __device__ __forceinline__ void write_side_row(const QuantArgs& a, int slot, int g, int pos,
                                                float k0, float k1, float v0, float v1, int lane) {
   const size_t r = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS + side_row(a, pos);
-  const Int8Meta ks = int8_meta(wave_max(fmaxf(fabsf(k0), fabsf(k1))));
-  const Int8Meta vs = int8_meta(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
-  const uint32_t kp = (static_cast<uint32_t>(int8_code(k0, ks)) & 0xFFu) |
-                      ((static_cast<uint32_t>(int8_code(k1, ks)) & 0xFFu) << 8);
-  const uint32_t vp = (static_cast<uint32_t>(int8_code(v0, vs)) & 0xFFu) |
-                      ((static_cast<uint32_t>(int8_code(v1, vs)) & 0xFFu) << 8);
-  uint16_t* codes = reinterpret_cast<uint16_t*>(a.side_codes + r * 2 * HD);
-  codes[lane] = static_cast<uint16_t>(kp);
-  codes[64 + lane] = static_cast<uint16_t>(vp);
-  if (lane == 0) {
-    a.side_scales[r * 2 + 0] = static_cast<uint16_t>(ks.s16);
-    a.side_scales[r * 2 + 1] = static_cast<uint16_t>(vs.s16);
-  }
+  write_int8_row(a.side_codes + r * 2 * HD, a.side_scales + r * 2, k0, k1, v0, v1, lane);
 }
 
 // MXFP4 variant of the main-region entry (KV4-RL pages, comparison of 4-bit
@@ -101,37 +89,26 @@ __global__ __launch_bounds__(64) void append_kernel(QuantArgs a, const int32_t* 
   const int t = pos & (PAGE - 1);
   uint8_t* blk = a.pages + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
 
-  uint32_t kbyte, vc0, vc1;
   if constexpr (MX) {
     const MxCodes mc = mx_codes(k0, k1, v0, v1);
-    kbyte = mc.kbyte;
-    vc0 = mc.v0;
-    vc1 = mc.v1;
+    const uint32_t kbyte = mc.kbyte, vc0 = mc.v0, vc1 = mc.v1;
     if ((lane & 15) == 0) {
       blk[MX_OFF_KS + 4 * t + (lane >> 4)] = static_cast<uint8_t>(mc.ke8);
       blk[MX_OFF_VS + 4 * t + (lane >> 4)] = static_cast<uint8_t>(mc.ve8);
     }
+    // K: token-major, channel 2l in the low nibble of byte l
+    blk[64 * t + lane] = static_cast<uint8_t>(kbyte);
+    // V: channel-major, this position's nibble in bytes 8c + t/2 of channels 2l, 2l+1;
+    // the other nibble belongs to the neighbouring position and is kept.
+    const int sh = (t & 1) * 4;
+    const uint32_t keep = (t & 1) ? 0x0Fu : 0xF0u;
+    uint8_t* vb0 = blk + OFF_VCODE + 8 * (2 * lane) + (t >> 1);
+    uint8_t* vb1 = vb0 + 8;
+    *vb0 = static_cast<uint8_t>((*vb0 & keep) | (vc0 << sh));
+    *vb1 = static_cast<uint8_t>((*vb1 & keep) | (vc1 << sh));
   } else {
-    const Int4Meta kq = int4_meta(wave_min(fminf(k0, k1)), wave_max(fmaxf(k0, k1)));
-    const Int4Meta vq = int4_meta(wave_min(fminf(v0, v1)), wave_max(fmaxf(v0, v1)));
-    kbyte = static_cast<uint32_t>(int4_code(k0, kq) | (int4_code(k1, kq) << 4));
-    vc0 = static_cast<uint32_t>(int4_code(v0, vq));
-    vc1 = static_cast<uint32_t>(int4_code(v1, vq));
-    if (lane == 0) {
-      *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
-      *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
-    }
+    write_int4_entry(blk, t, k0, k1, v0, v1, lane);
   }
-  // K: token-major, channel 2l in the low nibble of byte l
-  blk[64 * t + lane] = static_cast<uint8_t>(kbyte);
-  // V: channel-major, this position's nibble in bytes 8c + t/2 of channels 2l, 2l+1;
-  // the other nibble belongs to the neighbouring position and is kept.
-  const int sh = (t & 1) * 4;
-  const uint32_t keep = (t & 1) ? 0x0Fu : 0xF0u;
-  uint8_t* vb0 = blk + OFF_VCODE + 8 * (2 * lane) + (t >> 1);
-  uint8_t* vb1 = vb0 + 8;
-  *vb0 = static_cast<uint8_t>((*vb0 & keep) | (vc0 << sh));
-  *vb1 = static_cast<uint8_t>((*vb1 & keep) | (vc1 << sh));
   if (pos < a.sink || a.window > 0) write_side_row(a, slot, g, pos, k0, k1, v0, v1, lane);
 }
 
