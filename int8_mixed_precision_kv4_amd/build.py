@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkv4.so")
-SOURCES = ["kv4_api.hip", "kv4_quantize.hip", "kv4_decode.hip", "kv4_bf16.hip"]
+SOURCES = ["kv4_api.hip", "kv4_quantize.hip", "kv4_decode.hip", "kv4_prefill_attn.hip", "kv4_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 

@@ -1491,8 +1491,48 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
 }
 
 size_t chunk_workspace_bytes(int T, int Hq, int Hkv, int n_waves) {
+  (void)Hkv;
+  (void)n_waves;
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  return decode_workspace_bytes(T, Hq, Hkv, n_waves) + 3 * up(static_cast<size_t>(T) * 4);
+  // protected partials [T][Hq][kPart], per-token context / sequence / cache
+  // end, block bases [nseq + 1] (nseq <= T)
+  return up(static_cast<size_t>(T) * Hq * kPart * 4) + 3 * up(static_cast<size_t>(T) * 4) +
+         up(static_cast<size_t>(T + 1) * 4);
+}
+
+// The protected-region workgroups of the decode kernel alone, one per (entry,
+// kv-head), writing their partials to prot.
+static hipError_t launch_protected_only(const CacheView& c, const uint16_t* q, const int32_t* ctx,
+                                        const int32_t* slot, const int32_t* page_table, int pt_stride,
+                                        int B, int Hq, float scale_log2, float* prot,
+                                        const DecodeDebug* dbg, hipStream_t s, const int32_t* seq_of,
+                                        const int32_t* cache_end) {
+  DecArgs a{};
+  a.pages = c.pages;
+  a.side_codes = c.side_codes;
+  a.side_scales = c.side_scales;
+  a.Hkv = c.Hkv;
+  a.Hq = Hq;
+  a.B = B;
+  a.q = reinterpret_cast<const uint32_t*>(q);
+  a.ctx = ctx;
+  a.slot = slot;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.seq_of = seq_of;
+  a.cache_end = cache_end;
+  a.sink = c.sink;
+  a.window = c.window;
+  a.scale_log2 = scale_log2;
+  a.ws.prot = prot;
+  a.ws.n_waves = 0;  // every workgroup of the grid takes the protected role
+  if (dbg) a.dbg = *dbg;
+  const long long groups = static_cast<long long>(B) * c.Hkv;
+  if (groups > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(groups)), block(256);
+  if (dbg) hipLaunchKernelGGL((main_kernel<Kv4Format, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((main_kernel<Kv4Format, false>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_chunk_attention(const CacheView& c, const uint16_t* q, const int32_t* cu,
@@ -1500,16 +1540,27 @@ hipError_t launch_chunk_attention(const CacheView& c, const uint16_t* q, const i
                                   const int32_t* page_table, int pt_stride, int Hq, float scale_log2,
                                   float* out, float* lse, void* ws_base, int n_waves,
                                   const DecodeDebug* dbg, hipStream_t s) {
+  (void)n_waves;
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  char* tok = static_cast<char*>(ws_base) + decode_workspace_bytes(T, Hq, c.Hkv, n_waves);
-  int32_t* ctx_v = reinterpret_cast<int32_t*>(tok);
-  int32_t* seq_v = reinterpret_cast<int32_t*>(tok + up(static_cast<size_t>(T) * 4));
-  int32_t* end_v = reinterpret_cast<int32_t*>(tok + 2 * up(static_cast<size_t>(T) * 4));
-  hipLaunchKernelGGL(chunk_tokens_kernel, dim3((T + 255) / 256), dim3(256), 0, s, cu, start, nseq, T,
-                     ctx_v, seq_v, end_v);
-  const DecodeWorkspace ws = carve_workspace(ws_base, T, Hq, c.Hkv, n_waves);
-  return launch_decode(c, q, ctx_v, slot, page_table, pt_stride, T, Hq, scale_log2, out, lse, ws, dbg,
-                       s, nullptr, nullptr, false, seq_v, end_v);
+  char* p = static_cast<char*>(ws_base);
+  float* prot = reinterpret_cast<float*>(p);
+  p += up(static_cast<size_t>(T) * Hq * kPart * 4);
+  int32_t* ctx_v = reinterpret_cast<int32_t*>(p);
+  int32_t* seq_v = reinterpret_cast<int32_t*>(p + up(static_cast<size_t>(T) * 4));
+  int32_t* end_v = reinterpret_cast<int32_t*>(p + 2 * up(static_cast<size_t>(T) * 4));
+  int32_t* blk_base = reinterpret_cast<int32_t*>(p + 3 * up(static_cast<size_t>(T) * 4));
+  if (nseq > T) return hipErrorInvalidValue;
+  const bool protected_set = c.sink + c.window > 0;
+  if (protected_set) {
+    // token t: context = its position + 1, its sequence, the chunk's end
+    hipLaunchKernelGGL(chunk_tokens_kernel, dim3((T + 255) / 256), dim3(256), 0, s, cu, start, nseq, T,
+                       ctx_v, seq_v, end_v);
+    const hipError_t e = launch_protected_only(c, q, ctx_v, slot, page_table, pt_stride, T, Hq, scale_log2,
+                                               prot, dbg, s, seq_v, end_v);
+    if (e != hipSuccess) return e;
+  }
+  return launch_prefill_blocked(c, q, cu, start, nseq, T, page_table, pt_stride, Hq, scale_log2,
+                                protected_set ? prot : nullptr, out, lse, blk_base, dbg, s);
 }
 
 hipError_t launch_kv8_decode(const uint8_t* pages, int Hkv, const uint16_t* q, const int32_t* ctx,

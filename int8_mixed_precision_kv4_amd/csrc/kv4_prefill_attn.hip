@@ -1,0 +1,457 @@
+// Re-prefill attention, query-blocked: the main region of a chunk's query
+// tokens computed a block of 8 tokens at a time, so that every INT4 tile a
+// workgroup loads serves 8 tokens x 4 heads.
+//
+// KV4-RL pages ("KV4-RL" method summary, step 1: carried prefixes are
+// re-prefilled after a weight update; step 4: hybrid attention with integer
+// QK and integer PV over the INT4 region).  Token p of a chunk attends [0, p]
+// under the protected set of the cache as it stands (cache end E): the main
+// region is [s, min(p + 1, E - w)) and every one of its 16-position tiles is
+// processed by the same per-tile rule as the decode step (integer QK, Delta/m
+// after the dot, tile softmax with exp2s, P-operand codes with the V step
+// folded in, integer PV, FP32 running merge).  The protected partials come
+// from the decode kernel's protected workgroups (one per token and kv-head);
+// this kernel merges them with its main partials and writes out and lse.
+//
+// Layout of one workgroup: (block of 8 tokens, kv-head g), 4 waves splitting
+// the block's main tiles.  Every MFMA is v_mfma_i32_32x32x16_i8 with the 32
+// rows n = 4 * token + head as its N dimension, computed transposed:
+//   QK:  D^T[32 positions][32 rows] = K[positions][16 channels] q^T
+//   PV:  O^T[32 channels][32 rows]  = V^T[channels][16 positions] P^T
+// so that lane (n, kg) (n = lane % 32, kg = lane / 32) owns row n: it holds
+// D of positions 8 (r / 4) + 4 kg + r % 4 (register r) of the two tiles of a
+// pair, reduces a tile's max over its own 8 values and its partner lane's,
+// and its 8 P codes of a tile are already the B operand of the PV product.
+#include <hip/hip_runtime.h>
+
+#include "kv4_device.hpp"
+#include "kv4_internal.hpp"
+
+namespace kv4 {
+namespace {
+
+constexpr int QB = 8;             // query tokens per block
+constexpr int NR = QB * GQA;      // 32 rows
+constexpr int kQRowBytes = HD;    // query codes of a row in LDS: even channels, then odd
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+
+struct PaArgs {
+  const uint8_t* pages;
+  int Hkv, Hq, sink, window;
+  const uint32_t* q;  // BF16 pairs [T][Hq][64]
+  const int32_t* cu;
+  const int32_t* start;
+  const int32_t* page_table;
+  int pt_stride, nseq;
+  const int32_t* blk_base;  // [nseq + 1] first block of each sequence
+  float scale_log2;
+  const float* prot;  // [T][Hq][kPart] protected partials, or null (s = w = 0)
+  float* out;
+  float* lse;
+  DecodeDebug dbg;
+};
+
+template <typename T>
+__device__ __forceinline__ T ldc(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
+// Block base of each sequence: blk_base[s] = sum over earlier sequences of
+// ceil(n / 8) (one workgroup).
+__global__ __launch_bounds__(256) void block_base_kernel(const int32_t* __restrict__ cu, int nseq,
+                                                         int32_t* blk_base) {
+  __shared__ int32_t scan[256];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < nseq; base += 256) {
+    const int s = base + threadIdx.x;
+    scan[threadIdx.x] = s < nseq ? (cu[s + 1] - cu[s] + QB - 1) / QB : 0;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int t = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += t;
+      __syncthreads();
+    }
+    if (s < nseq) blk_base[s + 1] = carry + scan[threadIdx.x];
+    __syncthreads();
+    if (threadIdx.x == 255) carry += scan[255];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) blk_base[0] = 0;
+}
+
+__device__ __forceinline__ long lo_nib64(long x) { return x & 0x0F0F0F0F0F0F0F0FL; }
+__device__ __forceinline__ long hi_nib64(long x) {
+  return static_cast<long>((static_cast<unsigned long>(x) >> 4) & 0x0F0F0F0F0F0F0F0FUL);
+}
+
+// The swap of lanes l and l + 32 leaves, in every lane, its own value in one
+// result and its partner's in the other.
+__device__ __forceinline__ float partner_max(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Max of the 8 values of one tile held by this lane (registers 8 t' .. 8 t' + 7)
+// and those of the partner lane (same row, other kg).
+__device__ __forceinline__ float tile_max8(const float* v) {
+  float m = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+  return partner_max(m);
+}
+__device__ __forceinline__ float partner_sum(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+constexpr int kLdsQ = 0;                                // [32 rows][128] query codes (even | odd)
+constexpr int kLdsQi = kLdsQ + NR * kQRowBytes;         // [32] c_q, [32] S_q
+constexpr int kPartRow = HD + 4;                        // padded row of a partial in LDS (floats)
+constexpr int kLdsPart = kLdsQi + 2 * NR * 4;           // [4 waves][32 rows][kPartRow] A
+constexpr int kLdsZL = kLdsPart + 4 * NR * kPartRow * 4;  // [4 waves][32 rows] Z, then l
+constexpr int kLdsBytes = kLdsZL + 2 * 4 * NR * 4;
+
+template <bool DEBUG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(PaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  const int g = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.Hkv));
+  const int total = ldc(a.blk_base + a.nseq);
+  const int rev = static_cast<int>(blockIdx.x / static_cast<unsigned>(a.Hkv));
+  if (rev >= total) return;
+  const int bq = total - 1 - rev;  // later (longer) blocks first
+  int lo = 0, hi = a.nseq;         // blk_base[lo] <= bq < blk_base[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ldc(a.blk_base + mid) <= bq) lo = mid;
+    else hi = mid;
+  }
+  const int sq = lo;
+  const int lb = bq - ldc(a.blk_base + sq);
+  const int cu0 = ldc(a.cu + sq), n_s = ldc(a.cu + sq + 1) - cu0;
+  const int st0 = ldc(a.start + sq);
+  const int tok0 = cu0 + QB * lb;
+  const int ntok = min(QB, n_s - QB * lb);
+  const int p0 = st0 + QB * lb;  // position of the block's first token
+  const int E = st0 + n_s;       // cache end
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31, kg = lane >> 5;  // row n = 4 * token + head
+  int8_t* qlds = reinterpret_cast<int8_t*>(lds + kLdsQ);
+  float* cq_l = reinterpret_cast<float*>(lds + kLdsQi);
+  float* sq_l = cq_l + NR;
+
+  // ---- queries: rotate, symmetric INT8 (rows 8 wave .. 8 wave + 7; lane l
+  // holds channels 2l, 2l+1), codes to LDS as even channels then odd
+#pragma unroll 1
+  for (int k = 0; k < QB; ++k) {
+    const int row = QB * wave + k;
+    const int ti = row >> 2, h = row & 3;
+    int c0 = 0, c1 = 0;
+    float s_q = 0.0f;
+    if (ti < ntok) {
+      const size_t bh = static_cast<size_t>(tok0 + ti) * a.Hq + g * GQA + h;
+      const uint32_t qw = a.q[bh * 64 + lane];
+      float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
+      fwht128_wave(x0, x1);
+      const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+      s_q = amax / 127.0f;
+      if (s_q != 0.0f) {
+        c0 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x0 / s_q), -127.0f), 127.0f));
+        c1 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x1 / s_q), -127.0f), 127.0f));
+      }
+      if (DEBUG && a.dbg.qcodes) {
+        a.dbg.qcodes[bh * HD + 2 * lane] = static_cast<int8_t>(c0);
+        a.dbg.qcodes[bh * HD + 2 * lane + 1] = static_cast<int8_t>(c1);
+      }
+    }
+    const int S = wave_sum_i(c0 + c1);
+    if (DEBUG && a.dbg.qsum && lane == 0 && ti < ntok)
+      a.dbg.qsum[static_cast<size_t>(tok0 + ti) * a.Hq + g * GQA + h] = S;
+    qlds[row * kQRowBytes + lane] = static_cast<int8_t>(c0);
+    qlds[row * kQRowBytes + 64 + lane] = static_cast<int8_t>(c1);
+    if (lane == 0) {
+      cq_l[row] = s_q * a.scale_log2;
+      sq_l[row] = static_cast<float>(S);
+    }
+  }
+  __syncthreads();
+  // B operands of QK: MFMA (c, parity) takes channels 32 c + 16 kg + 2 i + parity
+  long qb[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      qb[c][par] = *reinterpret_cast<const long*>(qlds + n * kQRowBytes + 64 * par + 16 * c + 8 * kg);
+  const float c_q = cq_l[n], S_q = sq_l[n];
+  const int tn = n >> 2;  // token of this lane's row
+  const bool row_live = tn < ntok;
+  const int me_row = row_live ? min(p0 + tn + 1, E - a.window) : 0;  // main region end of the row
+
+  // ---- main tiles of the block: [s / 16, (me_max - 1) / 16], in pairs
+  const int me_max = min(p0 + ntok, E - a.window);
+  const int j_lo = a.sink / PAGE;
+  const int n_tiles = me_max > a.sink ? (me_max - 1) / PAGE - j_lo + 1 : 0;
+  const int n_pairs = (n_tiles + 1) >> 1;
+  const int pr0 = n_pairs * wave / 4, pr1 = n_pairs * (wave + 1) / 4;
+  const int32_t* ptrow = a.page_table + static_cast<size_t>(sq) * a.pt_stride;
+  const size_t pstride = static_cast<size_t>(a.Hkv) * BLOCK_BYTES;
+  const gbytes gbase = (gbytes)a.pages + static_cast<size_t>(g) * BLOCK_BYTES;
+
+  float O[4][16];
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[s2][r] = 0.0f;
+  float Zr = -INFINITY, Ls = 0.0f, Ms = 0.0f;
+
+#pragma unroll 1
+  for (int pr = pr0; pr < pr1; ++pr) {
+    const int ja = j_lo + 2 * pr;
+    const bool has_b = 2 * pr + 1 < n_tiles;
+    const int pta = ldc(ptrow + ja);
+    const int ptb = has_b ? ldc(ptrow + ja + 1) : pta;
+    const gbytes blk[2] = {gbase + static_cast<size_t>(static_cast<uint32_t>(pta)) * pstride,
+                           gbase + static_cast<size_t>(static_cast<uint32_t>(ptb)) * pstride};
+    // A operands of QK: position m = n of the pair (tile m / 16, slot m % 16),
+    // K code bytes 16 c + 8 kg .. + 7
+    const gbytes kb = blk[n >> 4] + 64 * (n & 15);
+    long ka[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ka[c] = *reinterpret_cast<const __attribute__((address_space(1))) long*>(kb + 16 * c + 8 * kg);
+    // A operands of PV (per tile t and channel block s2): channel 32 s2 + n,
+    // bytes holding positions 4 kg .. 4 kg + 3 and 8 + 4 kg .. 8 + 4 kg + 3
+    uint32_t vw[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const u2v w = *reinterpret_cast<const __attribute__((address_space(1))) u2v*>(
+            blk[t] + OFF_VCODE + 8 * (32 * s2 + n));
+        // bytes {2kg, 2kg+1} of w[0] and of w[1]
+        vw[t][s2] = __builtin_amdgcn_perm(w[1], w[0], kg ? 0x07060302u : 0x05040100u);
+      }
+    // (delta, m) of the lane's positions: registers 4 j4 .. 4 j4 + 3 hold
+    // positions 8 j4 + 4 kg .. + 3 of the pair, i.e. tile j4 / 2, slots
+    // 8 (j4 % 2) + 4 kg .. + 3
+    u4v kmeta[4], vmeta[4];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const gbytes mb = blk[j4 >> 1] + 4 * (8 * (j4 & 1) + 4 * kg);
+      kmeta[j4] = *reinterpret_cast<const __attribute__((address_space(1))) u4v*>(mb + OFF_KMETA);
+      vmeta[j4] = *reinterpret_cast<const __attribute__((address_space(1))) u4v*>(mb + OFF_VMETA);
+    }
+    // integer QK^T of the pair
+    v16i d = {};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      d = __builtin_amdgcn_mfma_i32_32x32x16_i8(lo_nib64(ka[c]), qb[c][0], d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_i32_32x32x16_i8(hi_nib64(ka[c]), qb[c][1], d, 0, 0, 0);
+    }
+    float z[16], e[16], u[16];
+    float emv_t[2] = {0.0f, 0.0f}, e_t[2] = {0.0f, 0.0f};
+    bool valid[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j4 = r >> 2, i = r & 3;
+      const int t = j4 >> 1;
+      const int slot16 = 8 * (j4 & 1) + 4 * kg + i;
+      const int pos = PAGE * (ja + t) + slot16;
+      valid[r] = row_live && (t == 0 || has_b) && pos < me_row;
+      const uint32_t km = kmeta[j4][i];
+      const float dk = f16_value(km & 0xFFFFu), mk = f16_value(km >> 16);
+      z[r] = valid[r] ? __builtin_fmaf(dk, static_cast<float>(d[r]), mk * S_q) * c_q : -INFINITY;
+      if (DEBUG && valid[r] && a.dbg.qk) {
+        const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + g * GQA + (n & 3);
+        a.dbg.qk[bh * a.dbg.max_ctx + pos] = d[r];
+      }
+    }
+    const float zmax[2] = {tile_max8(&z[0]), tile_max8(&z[8])};
+    float umax[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float um = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 8 * t + k;
+        const int j4 = r >> 2, i = r & 3;
+        e[r] = exp2s(z[r] - zmax[t]);
+        const uint32_t vm = vmeta[j4][i];
+        const float dv = f16_value(vm & 0xFFFFu), mv = f16_value(vm >> 16);
+        u[r] = valid[r] ? e[r] * dv : 0.0f;
+        e_t[t] += valid[r] ? e[r] : 0.0f;
+        emv_t[t] += valid[r] ? e[r] * mv : 0.0f;
+        um = fmaxf(um, u[r]);
+      }
+      umax[t] = partner_max(um);
+    }
+    // P codes; B operand of PV per tile: bytes in the order of the V operand's
+    // nibble split (registers 0, 2, 4, 6 then 1, 3, 5, 7 of the tile)
+    long pb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float qx = 127.0f / umax[t];
+      const float inv = umax[t] == 0.0f ? 0.0f : qx;
+      uint32_t uc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(u[8 * t + k] * inv), 0.0f, 127.0f);
+        uc[k] = static_cast<uint32_t>(r);
+        if (DEBUG && valid[8 * t + k] && a.dbg.pcode) {
+          const int j4 = (8 * t + k) >> 2, i = k & 3;
+          const int pos = PAGE * (ja + t) + 8 * (j4 & 1) + 4 * kg + i;
+          const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + g * GQA + (n & 3);
+          a.dbg.pcode[bh * a.dbg.max_ctx + pos] = static_cast<uint8_t>(uc[k]);
+        }
+      }
+      const uint32_t w0 = uc[0] | (uc[2] << 8) | (uc[4] << 16) | (uc[6] << 24);
+      const uint32_t w1 = uc[1] | (uc[3] << 8) | (uc[5] << 16) | (uc[7] << 24);
+      pb[t] = static_cast<long>(w0) | (static_cast<long>(w1) << 32);
+    }
+    // running reference max of the row; rescale what is accumulated
+    // (rows with no valid position yet keep Z = -inf and a scale of 1)
+    const float Zn = fmaxf(Zr, fmaxf(zmax[0], zmax[1]));
+    const float al = Zr == Zn ? 1.0f : __builtin_amdgcn_exp2f(Zr - Zn);
+    Zr = Zn;
+    if (__builtin_amdgcn_ballot_w64(al != 1.0f)) {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[s2][r] *= al;
+    }
+    Ls *= al;
+    Ms *= al;
+    float wsu[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float wt = zmax[t] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(zmax[t] - Zn);
+      Ls = __builtin_fmaf(wt, e_t[t], Ls);
+      Ms = __builtin_fmaf(wt, emv_t[t], Ms);
+      wsu[t] = wt * (umax[t] * (1.0f / 127.0f));
+    }
+    // integer PV^T per tile and channel block
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const uint32_t x = vw[t][s2];
+        const long va = static_cast<long>(x & 0x0F0F0F0Fu) | (static_cast<long>((x >> 4) & 0x0F0F0F0Fu) << 32);
+        const v16i acc = __builtin_amdgcn_mfma_i32_32x32x16_i8(va, pb[t], v16i{}, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[s2][r] = __builtin_fmaf(wsu[t], static_cast<float>(acc[r]), O[s2][r]);
+        if (DEBUG && a.dbg.pv && row_live && (t == 0 || has_b)) {
+          const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + g * GQA + (n & 3);
+          // a tile outside this row's main region leaves its accumulators unwritten
+          if (PAGE * (ja + t) < me_row) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int ch = 32 * s2 + 8 * (r >> 2) + 4 * kg + (r & 3);
+              a.dbg.pv[(bh * a.dbg.max_pages + (ja + t)) * HD + ch] = acc[r];
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- this wave's partial: A = O + sum(w e m_v), Z, l (rows n; both lanes
+  // of a row hold half of the sums)
+  const float Lrow = partner_sum(Ls), Mrow = partner_sum(Ms);
+  float* part = reinterpret_cast<float*>(lds + kLdsPart) + (wave * NR + n) * kPartRow;
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[32 * s2 + 8 * (r >> 2) + 4 * kg + (r & 3)] = O[s2][r] + Mrow;
+  float* zl = reinterpret_cast<float*>(lds + kLdsZL);
+  if (kg == 0) {
+    zl[wave * NR + n] = Zr;
+    zl[4 * NR + wave * NR + n] = Lrow;
+  }
+  __syncthreads();
+
+  // ---- exact merge of the 4 main partials and the protected partial of each
+  // row (wave w: rows 8 w .. 8 w + 7; lane l: channels 2l, 2l+1)
+  const float* partr = reinterpret_cast<const float*>(lds + kLdsPart);
+#pragma unroll 1
+  for (int k = 0; k < QB; ++k) {
+    const int row = QB * wave + k;
+    const int ti = row >> 2, h = row & 3;
+    if (ti >= ntok) continue;
+    const size_t bh = static_cast<size_t>(tok0 + ti) * a.Hq + g * GQA + h;
+    float Zs[5], Lv[5];
+    float2 Av[5];
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      Zs[w2] = zl[w2 * NR + row];
+      Lv[w2] = zl[4 * NR + w2 * NR + row];
+      Av[w2] = *reinterpret_cast<const float2*>(partr + (w2 * NR + row) * kPartRow + 2 * lane);
+    }
+    if (a.prot) {
+      const float* P = a.prot + bh * kPart;
+      Zs[4] = P[128];
+      Lv[4] = P[129];
+      Av[4] = reinterpret_cast<const float2*>(P)[lane];
+    } else {
+      Zs[4] = -INFINITY;
+      Lv[4] = 0.0f;
+      Av[4] = make_float2(0.0f, 0.0f);
+    }
+    float Z = Zs[0];
+#pragma unroll
+    for (int i = 1; i < 5; ++i) Z = fmaxf(Z, Zs[i]);
+    float l = 0.0f;
+    float2 A = make_float2(0.0f, 0.0f);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const float w = Zs[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Zs[i] - Z);
+      l = __builtin_fmaf(w, Lv[i], l);
+      A.x = __builtin_fmaf(w, Av[i].x, A.x);
+      A.y = __builtin_fmaf(w, Av[i].y, A.y);
+    }
+    reinterpret_cast<float2*>(a.out + bh * HD)[lane] = make_float2(A.x / l, A.y / l);
+    if (lane == 0) a.lse[bh] = 0.69314718055994531f * (Z + __builtin_log2f(l));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_blocked(const CacheView& c, const uint16_t* q, const int32_t* cu,
+                                  const int32_t* start, int nseq, int T, const int32_t* page_table,
+                                  int pt_stride, int Hq, float scale_log2, const float* prot,
+                                  float* out, float* lse, int32_t* blk_base, const DecodeDebug* dbg,
+                                  hipStream_t s) {
+  if (nseq <= 0 || T <= 0) return hipErrorInvalidValue;
+  PaArgs a{};
+  a.pages = c.pages;
+  a.Hkv = c.Hkv;
+  a.Hq = Hq;
+  a.sink = c.sink;
+  a.window = c.window;
+  a.q = reinterpret_cast<const uint32_t*>(q);
+  a.cu = cu;
+  a.start = start;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.nseq = nseq;
+  a.blk_base = blk_base;
+  a.scale_log2 = scale_log2;
+  a.prot = prot;
+  a.out = out;
+  a.lse = lse;
+  if (dbg) a.dbg = *dbg;
+  hipLaunchKernelGGL(block_base_kernel, dim3(1), dim3(256), 0, s, cu, nseq, blk_base);
+  // blocks: sum of ceil(n / 8) <= (T + 7 nseq) / 8
+  const long long nblk = (static_cast<long long>(T) + 7LL * nseq) / QB;
+  const long long groups = nblk * c.Hkv;
+  if (groups > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(groups)), block(256);
+  if (dbg) hipLaunchKernelGGL((prefill_attn_kernel<true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((prefill_attn_kernel<false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kv4
