@@ -236,7 +236,10 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
 
   const int L = ld_const(a.ctx + b);
   const int E = end_of(a, b, L);
-  const int nrows = a.sink + a.window;  // rows [0, s+w) can hold the region
+  // rows that can hold a position of the region: the sinks below L, and the
+  // ring only when the window [max(s, E - w), E) starts below L (a token of a
+  // re-prefilled chunk before the window sees sinks alone)
+  const int nrows = L > max(a.sink, E - a.window) ? a.sink + a.window : min(a.sink, L);
   const int sq = seq_of(a, b);
   const int slot = a.slot ? ld_const(a.slot + sq) : sq;
   const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;

@@ -24,6 +24,8 @@
 // and its 8 P codes of a tile are already the B operand of the PV product.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kv4_device.hpp"
 #include "kv4_internal.hpp"
 
@@ -209,8 +211,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int r = 0; r < 16; ++r) O[s2][r] = 0.0f;
   float Zr = -INFINITY, Ls = 0.0f, Ms = 0.0f;
 
-#pragma unroll 1
-  for (int pr = pr0; pr < pr1; ++pr) {
+  // A pair every row sees whole (all 8 tokens live, both tiles below the
+  // first token's main end) skips the masks.
+  const int me_min = min(p0 + 1, E - a.window);
+  auto pair_step = [&](int pr, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int ja = j_lo + 2 * pr;
     const bool has_b = 2 * pr + 1 < n_tiles;
     const int pta = ldc(ptrow + ja);
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int t = j4 >> 1;
       const int slot16 = 8 * (j4 & 1) + 4 * kg + i;
       const int pos = PAGE * (ja + t) + slot16;
-      valid[r] = row_live && (t == 0 || has_b) && pos < me_row;
+      valid[r] = FULL || (row_live && (t == 0 || has_b) && pos < me_row);
       const uint32_t km = kmeta[j4][i];
       const float dk = f16_value(km & 0xFFFFu), mk = f16_value(km >> 16);
       z[r] = valid[r] ? __builtin_fmaf(dk, static_cast<float>(d[r]), mk * S_q) * c_q : -INFINITY;
@@ -356,6 +361,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
+    };
+#pragma unroll 1
+  for (int pr = pr0; pr < pr1; ++pr) {
+    const int ja = j_lo + 2 * pr;
+    if (ntok == QB && 2 * pr + 1 < n_tiles && PAGE * (ja + 2) <= me_min) pair_step(pr, std::true_type{});
+    else pair_step(pr, std::false_type{});
   }
 
   // ---- this wave's partial: A = O + sum(w e m_v), Z, l (rows n; both lanes
