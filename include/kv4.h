@@ -187,13 +187,13 @@ int kv4_decode_attention_debug(const kv4_cache_desc *cache, const void *q,
  *   slot, page_table, pt_stride: per sequence, as for kv4_prefill_quantize
  *   max_ctx    host upper bound of E_s
  *   out, lse   fp32 [total_q][Hq][128], [total_q][Hq]
- * The main region runs a block of 8 consecutive tokens of a chunk per
- * (block, kv-head) workgroup, so every INT4 tile is read once per 8 tokens;
- * the integer intermediates (query codes, QK, P codes, PV accumulators) are
- * those of the decode step, and out / lse equal it up to the FP32 order of
- * the exact partial merges.  The workspace holds the protected partials
- * (total_q x Hq x 528 B) and per-token and per-sequence indices; nseq must not
- * exceed total_q (KV4_ERR_HIP otherwise). */
+ * One workgroup per (block of 8 consecutive tokens of a chunk, kv-head) covers
+ * the block's protected rows and main tiles, so every INT4 tile and side row
+ * is read once per 8 tokens; the integer intermediates (query codes, QK, P
+ * codes, PV accumulators) are those of the decode step, and out / lse equal it
+ * up to the FP32 order of the exact region and tile merges.  The workspace
+ * holds (total_q + 1) int32 block bases; nseq must not exceed total_q
+ * (KV4_ERR_HIP otherwise). */
 size_t kv4_prefill_attention_workspace_bytes(const kv4_cache_desc *cache, int32_t total_q,
                                              int32_t Hq, int32_t max_ctx);
 int kv4_prefill_attention(const kv4_cache_desc *cache, const void *q, const int32_t *cu_seqlens,

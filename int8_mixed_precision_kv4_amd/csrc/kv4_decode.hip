@@ -190,17 +190,6 @@ __device__ __forceinline__ int qk_rows(v4i d) {
 
 // ------------------------------------------------------------ protected --
 
-// Position held by side row r of a cache ending at E, for sinks [0, s) and a
-// ring of w recent positions in rows [s, s+w), if a query attending [0, L)
-// sees it (-1 otherwise).
-__device__ __forceinline__ int side_position(int r, int L, int E, int s, int w) {
-  if (r < s) return r < L ? r : -1;
-  if (r >= s + w) return -1;
-  const int base = max(s, E - w);
-  const int p = base + ((r - s - base) % w + w) % w;
-  return p < L ? p : -1;
-}
-
 // Round two FP32 values to BF16 (nearest even) with one v_cvt_pk_bf16_f32;
 // results kept in FP32.
 __device__ __forceinline__ void round_bf16x2(float& x, float& y) {
@@ -1384,25 +1373,6 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
   if (lane == 0) a.lse[bh] = 0.69314718055994531f * (Zm + log2f(lm));
 }
 
-// Per-token entries of a chunk-attention call: token t of the packed chunks
-// (sequence s: tokens cu[s] .. cu[s+1]-1 at positions start[s] ..) attends
-// [0, start[s] + t - cu[s]] of a cache ending at start[s] + cu[s+1] - cu[s].
-__global__ __launch_bounds__(256) void chunk_tokens_kernel(const int32_t* __restrict__ cu,
-                                                           const int32_t* __restrict__ start, int nseq,
-                                                           int T, int32_t* ctx_v, int32_t* seq_v,
-                                                           int32_t* end_v) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
-  int lo = 0, hi = nseq;  // cu[lo] <= t < cu[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= t) lo = mid;
-    else hi = mid;
-  }
-  ctx_v[t] = start[lo] + (t - cu[lo]) + 1;
-  seq_v[t] = lo;
-  end_v[t] = start[lo] + (cu[lo + 1] - cu[lo]);
-}
 
 }  // namespace
 
@@ -1494,48 +1464,11 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
 }
 
 size_t chunk_workspace_bytes(int T, int Hq, int Hkv, int n_waves) {
+  (void)Hq;
   (void)Hkv;
   (void)n_waves;
-  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  // protected partials [T][Hq][kPart], per-token context / sequence / cache
-  // end, block bases [nseq + 1] (nseq <= T)
-  return up(static_cast<size_t>(T) * Hq * kPart * 4) + 3 * up(static_cast<size_t>(T) * 4) +
-         up(static_cast<size_t>(T + 1) * 4);
-}
-
-// The protected-region workgroups of the decode kernel alone, one per (entry,
-// kv-head), writing their partials to prot.
-static hipError_t launch_protected_only(const CacheView& c, const uint16_t* q, const int32_t* ctx,
-                                        const int32_t* slot, const int32_t* page_table, int pt_stride,
-                                        int B, int Hq, float scale_log2, float* prot,
-                                        const DecodeDebug* dbg, hipStream_t s, const int32_t* seq_of,
-                                        const int32_t* cache_end) {
-  DecArgs a{};
-  a.pages = c.pages;
-  a.side_codes = c.side_codes;
-  a.side_scales = c.side_scales;
-  a.Hkv = c.Hkv;
-  a.Hq = Hq;
-  a.B = B;
-  a.q = reinterpret_cast<const uint32_t*>(q);
-  a.ctx = ctx;
-  a.slot = slot;
-  a.page_table = page_table;
-  a.pt_stride = pt_stride;
-  a.seq_of = seq_of;
-  a.cache_end = cache_end;
-  a.sink = c.sink;
-  a.window = c.window;
-  a.scale_log2 = scale_log2;
-  a.ws.prot = prot;
-  a.ws.n_waves = 0;  // every workgroup of the grid takes the protected role
-  if (dbg) a.dbg = *dbg;
-  const long long groups = static_cast<long long>(B) * c.Hkv;
-  if (groups > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(groups)), block(256);
-  if (dbg) hipLaunchKernelGGL((main_kernel<Kv4Format, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((main_kernel<Kv4Format, false>), grid, block, 0, s, a);
-  return hipGetLastError();
+  // block bases [nseq + 1] (nseq <= T)
+  return (static_cast<size_t>(T + 1) * 4 + 255) & ~static_cast<size_t>(255);
 }
 
 hipError_t launch_chunk_attention(const CacheView& c, const uint16_t* q, const int32_t* cu,
@@ -1544,26 +1477,9 @@ hipError_t launch_chunk_attention(const CacheView& c, const uint16_t* q, const i
                                   float* out, float* lse, void* ws_base, int n_waves,
                                   const DecodeDebug* dbg, hipStream_t s) {
   (void)n_waves;
-  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  char* p = static_cast<char*>(ws_base);
-  float* prot = reinterpret_cast<float*>(p);
-  p += up(static_cast<size_t>(T) * Hq * kPart * 4);
-  int32_t* ctx_v = reinterpret_cast<int32_t*>(p);
-  int32_t* seq_v = reinterpret_cast<int32_t*>(p + up(static_cast<size_t>(T) * 4));
-  int32_t* end_v = reinterpret_cast<int32_t*>(p + 2 * up(static_cast<size_t>(T) * 4));
-  int32_t* blk_base = reinterpret_cast<int32_t*>(p + 3 * up(static_cast<size_t>(T) * 4));
   if (nseq > T) return hipErrorInvalidValue;
-  const bool protected_set = c.sink + c.window > 0;
-  if (protected_set) {
-    // token t: context = its position + 1, its sequence, the chunk's end
-    hipLaunchKernelGGL(chunk_tokens_kernel, dim3((T + 255) / 256), dim3(256), 0, s, cu, start, nseq, T,
-                       ctx_v, seq_v, end_v);
-    const hipError_t e = launch_protected_only(c, q, ctx_v, slot, page_table, pt_stride, T, Hq, scale_log2,
-                                               prot, dbg, s, seq_v, end_v);
-    if (e != hipSuccess) return e;
-  }
-  return launch_prefill_blocked(c, q, cu, start, nseq, T, page_table, pt_stride, Hq, scale_log2,
-                                protected_set ? prot : nullptr, out, lse, blk_base, dbg, s);
+  return launch_prefill_blocked(c, q, cu, start, nseq, T, slot, page_table, pt_stride, Hq, scale_log2, out,
+                                lse, static_cast<int32_t*>(ws_base), dbg, s);
 }
 
 hipError_t launch_kv8_decode(const uint8_t* pages, int Hkv, const uint16_t* q, const int32_t* ctx,

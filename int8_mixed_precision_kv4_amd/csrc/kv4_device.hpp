@@ -24,6 +24,17 @@ constexpr int KV8_OFF_V = 2048;
 constexpr int KV8_OFF_SK = 4096;
 constexpr int KV8_OFF_SV = 4128;
 
+// Position held by side row r of a cache ending at E, for sinks [0, s) and a
+// ring of w recent positions in rows [s, s+w), if a query attending [0, L)
+// sees it (-1 otherwise).
+__device__ __forceinline__ int side_position(int r, int L, int E, int s, int w) {
+  if (r < s) return r < L ? r : -1;
+  if (r >= s + w) return -1;
+  const int base = max(s, E - w);
+  const int p = base + ((r - s - base) % w + w) % w;
+  return p < L ? p : -1;
+}
+
 // ---------------------------------------------------------------- formats --
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -79,23 +79,20 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
                          bool mx = false, const int32_t* seq_of = nullptr,
                          const int32_t* cache_end = nullptr, const uint16_t* k_new = nullptr,
                          const uint16_t* v_new = nullptr, const int32_t* pos_new = nullptr);
-// Re-prefill (chunked-prefill) attention: the protected partial of every
-// query token comes from the decode kernel's protected workgroups (each token
-// one entry of a batch: context = position + 1, cache end = the chunk's end);
-// the main region and the merge run query-blocked (launch_prefill_blocked).
+// Re-prefill (chunked-prefill) attention: query-blocked (blocks of 8 tokens
+// per kv-head workgroup) over the protected rows and the main region, merged
+// in the kernel; the workspace holds the block bases.
 size_t chunk_workspace_bytes(int T, int Hq, int Hkv, int n_waves);
-// Main region of blocks of 8 query tokens per kv-head, merged with the
-// protected partials prot [T][Hq][kPart] (null when s = w = 0) into out, lse.
-hipError_t launch_prefill_blocked(const CacheView& c, const uint16_t* q, const int32_t* cu,
-                                  const int32_t* start, int nseq, int T, const int32_t* page_table,
-                                  int pt_stride, int Hq, float scale_log2, const float* prot,
-                                  float* out, float* lse, int32_t* blk_base, const DecodeDebug* dbg,
-                                  hipStream_t s);
 hipError_t launch_chunk_attention(const CacheView& c, const uint16_t* q, const int32_t* cu,
                                   const int32_t* start, int nseq, int T, const int32_t* slot,
                                   const int32_t* page_table, int pt_stride, int Hq, float scale_log2,
                                   float* out, float* lse, void* ws_base, int n_waves,
                                   const DecodeDebug* dbg, hipStream_t s);
+hipError_t launch_prefill_blocked(const CacheView& c, const uint16_t* q, const int32_t* cu,
+                                  const int32_t* start, int nseq, int T, const int32_t* slot,
+                                  const int32_t* page_table, int pt_stride, int Hq, float scale_log2,
+                                  float* out, float* lse, int32_t* blk_base, const DecodeDebug* dbg,
+                                  hipStream_t s);
 hipError_t launch_bf16_decode(const uint16_t* pages, int num_pages, int Hkv, const uint16_t* q,
                               const int32_t* ctx, const int32_t* page_table, int pt_stride, int B,
                               int Hq, float scale_log2, float* out, float* lse, void* ws,

@@ -36,21 +36,25 @@ constexpr int QB = 8;             // query tokens per block
 constexpr int NR = QB * GQA;      // 32 rows
 constexpr int kQRowBytes = HD;    // query codes of a row in LDS: even channels, then odd
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(1))) uint8_t* gbytes;
 
 struct PaArgs {
   const uint8_t* pages;
+  const int8_t* side_codes;
+  const uint16_t* side_scales;
   int Hkv, Hq, sink, window;
   const uint32_t* q;  // BF16 pairs [T][Hq][64]
   const int32_t* cu;
   const int32_t* start;
+  const int32_t* slot;  // [nseq] side-buffer slot of each sequence (null: the sequence index)
   const int32_t* page_table;
   int pt_stride, nseq;
   const int32_t* blk_base;  // [nseq + 1] first block of each sequence
   float scale_log2;
-  const float* prot;  // [T][Hq][kPart] protected partials, or null (s = w = 0)
   float* out;
   float* lse;
   DecodeDebug dbg;
@@ -204,12 +208,121 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const size_t pstride = static_cast<size_t>(a.Hkv) * BLOCK_BYTES;
   const gbytes gbase = (gbytes)a.pages + static_cast<size_t>(g) * BLOCK_BYTES;
 
-  float O[4][16];
+  v16f O[4];
 #pragma unroll
-  for (int s2 = 0; s2 < 4; ++s2)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) O[s2][r] = 0.0f;
+  for (int s2 = 0; s2 < 4; ++s2) O[s2] = v16f{};
   float Zr = -INFINITY, Ls = 0.0f, Ms = 0.0f;
+
+  // ---- protected region: side rows [0, n_side) in groups of 32 (group k on
+  // wave k % 4), INT8 QK^T on the same query operands (side K bytes split into
+  // even and odd channels), FP32 weights, v^ = bf16(s_v c) and PV^T on the
+  // BF16 MFMA with each weight as the sum of two BF16 parts (hi = bf16(e),
+  // lo = bf16(e - hi): 16 significant bits), accumulated into the same
+  // running state as the main tiles (an exact log-sum-exp merge of the two
+  // regions)
+  const int p_last = p0 + ntok - 1;
+  const bool any_window = a.window > 0 && p_last >= max(a.sink, E - a.window);
+  const int n_side = any_window ? a.sink + a.window : min(a.sink, p_last + 1);
+  const int slot = a.slot ? ldc(a.slot + sq) : sq;
+  const size_t srow0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
+#pragma unroll 1
+  for (int kgp = wave; 32 * kgp < n_side; kgp += 4) {
+    const int r0 = 32 * kgp;
+    // A operands of QK^T: side row r0 + n (loads clamped to the buffer)
+    const gbytes krow = (gbytes)a.side_codes + (srow0 + min(r0 + n, SIDE_ROWS - 1)) * 2 * HD;
+    long sa[4][2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u4v x = *reinterpret_cast<const __attribute__((address_space(1))) u4v*>(krow + 32 * c + 16 * kg);
+      const uint32_t e0 = __builtin_amdgcn_perm(x[1], x[0], 0x06040200u), e1 = __builtin_amdgcn_perm(x[3], x[2], 0x06040200u);
+      const uint32_t o0 = __builtin_amdgcn_perm(x[1], x[0], 0x07050301u), o1 = __builtin_amdgcn_perm(x[3], x[2], 0x07050301u);
+      sa[c][0] = static_cast<long>(e0) | (static_cast<long>(e1) << 32);
+      sa[c][1] = static_cast<long>(o0) | (static_cast<long>(o1) << 32);
+    }
+    // (s_k, s_v) of the lane's side rows r0 + 8 j4 + 4 kg .. + 3
+    u4v sc[4];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4)
+      sc[j4] = *reinterpret_cast<const __attribute__((address_space(1))) u4v*>(
+          (gbytes)a.side_scales + (srow0 + min(r0 + 8 * j4 + 4 * kg, SIDE_ROWS - 4)) * 4);
+    v16i d = {};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      d = __builtin_amdgcn_mfma_i32_32x32x16_i8(sa[c][0], qb[c][0], d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_i32_32x32x16_i8(sa[c][1], qb[c][1], d, 0, 0, 0);
+    }
+    float z[16];
+    float zm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rs = r0 + 8 * (r >> 2) + 4 * kg + (r & 3);
+      const int pos = row_live ? side_position(rs, p0 + tn + 1, E, a.sink, a.window) : -1;
+      const float sk = f16_value(sc[r >> 2][r & 3] & 0xFFFFu);
+      z[r] = pos >= 0 ? (static_cast<float>(d[r]) * sk) * c_q : -INFINITY;
+      zm = fmaxf(zm, z[r]);
+      if (DEBUG && pos >= 0 && a.dbg.qk) {
+        const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + g * GQA + (n & 3);
+        a.dbg.qk[bh * a.dbg.max_ctx + pos] = d[r];
+      }
+    }
+    const float Zn = fmaxf(Zr, partner_max(zm));
+    const float al = Zr == Zn ? 1.0f : __builtin_amdgcn_exp2f(Zr - Zn);
+    Zr = Zn;
+    if (__builtin_amdgcn_ballot_w64(al != 1.0f)) {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) O[s2] *= al;
+    }
+    Ls *= al;
+    Ms *= al;
+    // weights as BF16 hi / lo parts, B operands of PV^T per chunk j4
+    v4s ehi[4], elo[4];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      float hv[4], lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = exp2s(z[4 * j4 + i] - Zn);
+        Ls += e;
+        hv[i] = round_bf16(e);
+        lv[i] = e - hv[i];
+      }
+      ehi[j4] = v4s{static_cast<short>(__float_as_uint(hv[0]) >> 16), static_cast<short>(__float_as_uint(hv[1]) >> 16),
+                    static_cast<short>(__float_as_uint(hv[2]) >> 16), static_cast<short>(__float_as_uint(hv[3]) >> 16)};
+      elo[j4] = v4s{static_cast<short>(__float_as_uint(round_bf16(lv[0])) >> 16),
+                    static_cast<short>(__float_as_uint(round_bf16(lv[1])) >> 16),
+                    static_cast<short>(__float_as_uint(round_bf16(lv[2])) >> 16),
+                    static_cast<short>(__float_as_uint(round_bf16(lv[3])) >> 16)};
+    }
+    // A operands of PV^T: v^ of channel 32 s2 + n for side rows r0 + 8 j4 +
+    // 4 kg .. + 3; rows no token of the block sees are zero (their bytes may
+    // be stale)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      float sv[4];
+      int rr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rs = r0 + 8 * j4 + 4 * kg + i;
+        const bool seen = side_position(rs, p_last + 1, E, a.sink, a.window) >= 0;
+        sv[i] = seen ? f16_value(sc[j4][i] >> 16) : 0.0f;
+        rr[i] = min(rs, SIDE_ROWS - 1);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int8_t cv = *reinterpret_cast<const __attribute__((address_space(1))) int8_t*>(
+              (gbytes)a.side_codes + ((srow0 + rr[i]) * 2 + 1) * HD + 32 * s2 + n);
+          x[i] = round_bf16(sv[i] * static_cast<float>(cv));  // s_v c is exact in FP32
+        }
+        const v4s va = v4s{static_cast<short>(__float_as_uint(x[0]) >> 16), static_cast<short>(__float_as_uint(x[1]) >> 16),
+                           static_cast<short>(__float_as_uint(x[2]) >> 16), static_cast<short>(__float_as_uint(x[3]) >> 16)};
+        O[s2] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(va, ehi[j4], O[s2], 0, 0, 0);
+        O[s2] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(va, elo[j4], O[s2], 0, 0, 0);
+      }
+    }
+  }
 
   // A pair every row sees whole (all 8 tokens live, both tiles below the
   // first token's main end) skips the masks.
@@ -324,9 +437,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     Zr = Zn;
     if (__builtin_amdgcn_ballot_w64(al != 1.0f)) {
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[s2][r] *= al;
+      for (int s2 = 0; s2 < 4; ++s2) O[s2] *= al;
     }
     Ls *= al;
     Ms *= al;
@@ -393,31 +504,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int ti = row >> 2, h = row & 3;
     if (ti >= ntok) continue;
     const size_t bh = static_cast<size_t>(tok0 + ti) * a.Hq + g * GQA + h;
-    float Zs[5], Lv[5];
-    float2 Av[5];
+    float Zs[4], Lv[4];
+    float2 Av[4];
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       Zs[w2] = zl[w2 * NR + row];
       Lv[w2] = zl[4 * NR + w2 * NR + row];
       Av[w2] = *reinterpret_cast<const float2*>(partr + (w2 * NR + row) * kPartRow + 2 * lane);
     }
-    if (a.prot) {
-      const float* P = a.prot + bh * kPart;
-      Zs[4] = P[128];
-      Lv[4] = P[129];
-      Av[4] = reinterpret_cast<const float2*>(P)[lane];
-    } else {
-      Zs[4] = -INFINITY;
-      Lv[4] = 0.0f;
-      Av[4] = make_float2(0.0f, 0.0f);
-    }
     float Z = Zs[0];
 #pragma unroll
-    for (int i = 1; i < 5; ++i) Z = fmaxf(Z, Zs[i]);
+    for (int i = 1; i < 4; ++i) Z = fmaxf(Z, Zs[i]);
     float l = 0.0f;
     float2 A = make_float2(0.0f, 0.0f);
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const float w = Zs[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Zs[i] - Z);
       l = __builtin_fmaf(w, Lv[i], l);
       A.x = __builtin_fmaf(w, Av[i].x, A.x);
@@ -431,13 +532,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }  // namespace
 
 hipError_t launch_prefill_blocked(const CacheView& c, const uint16_t* q, const int32_t* cu,
-                                  const int32_t* start, int nseq, int T, const int32_t* page_table,
-                                  int pt_stride, int Hq, float scale_log2, const float* prot,
+                                  const int32_t* start, int nseq, int T, const int32_t* slot,
+                                  const int32_t* page_table, int pt_stride, int Hq, float scale_log2,
                                   float* out, float* lse, int32_t* blk_base, const DecodeDebug* dbg,
                                   hipStream_t s) {
   if (nseq <= 0 || T <= 0) return hipErrorInvalidValue;
   PaArgs a{};
   a.pages = c.pages;
+  a.side_codes = c.side_codes;
+  a.side_scales = c.side_scales;
   a.Hkv = c.Hkv;
   a.Hq = Hq;
   a.sink = c.sink;
@@ -445,12 +548,12 @@ hipError_t launch_prefill_blocked(const CacheView& c, const uint16_t* q, const i
   a.q = reinterpret_cast<const uint32_t*>(q);
   a.cu = cu;
   a.start = start;
+  a.slot = slot;
   a.page_table = page_table;
   a.pt_stride = pt_stride;
   a.nseq = nseq;
   a.blk_base = blk_base;
   a.scale_log2 = scale_log2;
-  a.prot = prot;
   a.out = out;
   a.lse = lse;
   if (dbg) a.dbg = *dbg;
