@@ -167,7 +167,7 @@ static int decode_common(const kv4_cache_desc* cache, const void* q, const int32
   hipError_t e = kv4::launch_decode(view(cache), static_cast<const uint16_t*>(q), ctx_len, slot,
                                     page_table, pt_stride, B, Hq, scale_log2(softmax_scale), out,
                                     lse, ws, dbg ? &d : nullptr, st, static_cast<hipEvent_t>(ev0),
-                                    static_cast<hipEvent_t>(ev1), mx, nullptr, nullptr,
+                                    static_cast<hipEvent_t>(ev1), mx,
                                     static_cast<const uint16_t*>(k_new),
                                     static_cast<const uint16_t*>(v_new), pos_new);
   return e == hipSuccess ? KV4_OK : hip_fail(e);

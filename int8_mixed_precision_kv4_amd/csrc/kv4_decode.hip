@@ -36,12 +36,6 @@ struct DecArgs {
   const int32_t* slot;
   const int32_t* page_table;
   int pt_stride;
-  // Chunk attention (re-prefill): entry b of the batch is one query token of
-  // sequence seq_of[b] (its slot and page-table row) whose cache ends at
-  // cache_end[b]; ctx[b] is that token's position + 1.  Both NULL for a decode
-  // step (seq_of = b, cache_end = ctx).
-  const int32_t* seq_of;
-  const int32_t* cache_end;
   // Fused append (decode step only): this step's token of sequence b at
   // position pos_new[b] (= ctx[b] - 1), bf16 pairs [B][Hkv][64]; NULL: none.
   // Its protected workgroup writes the token's page entry and side row before
@@ -65,10 +59,6 @@ __device__ __forceinline__ int main_pages(int L, int E, int s, int w) {
   const int me = main_end_of(L, E, w);
   return me > s ? (me - 1) / PAGE - s / PAGE + 1 : 0;
 }
-__device__ __forceinline__ int seq_of(const DecArgs& a, int b) { return a.seq_of ? ld_const(a.seq_of + b) : b; }
-__device__ __forceinline__ int end_of(const DecArgs& a, int b, int L) {
-  return a.cache_end ? ld_const(a.cache_end + b) : L;
-}
 
 // plan[b] = sum over earlier sequences of main_pages * Hkv (one workgroup).
 __device__ void build_plan(const DecArgs& a) {
@@ -81,7 +71,7 @@ __device__ void build_plan(const DecArgs& a) {
   __syncthreads();
   for (int base = 0; base < a.B; base += 256) {
     const int b = base + threadIdx.x;
-    scan[threadIdx.x] = (b < a.B) ? main_pages(a.ctx[b], a.cache_end ? a.cache_end[b] : a.ctx[b], a.sink,
+    scan[threadIdx.x] = (b < a.B) ? main_pages(a.ctx[b], a.ctx[b], a.sink,
                                                a.window) * a.Hkv : 0;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
@@ -224,12 +214,11 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   float* cqs = reinterpret_cast<float*>(qn + GQA * HD);                                                    // [4]
 
   const int L = ld_const(a.ctx + b);
-  const int E = end_of(a, b, L);
+  const int E = L;  // the cache ends at this step's token
   // rows that can hold a position of the region: the sinks below L, and the
-  // ring only when the window [max(s, E - w), E) starts below L (a token of a
-  // re-prefilled chunk before the window sees sinks alone)
+  // ring when the window [max(s, L - w), L) is not empty
   const int nrows = L > max(a.sink, E - a.window) ? a.sink + a.window : min(a.sink, L);
-  const int sq = seq_of(a, b);
+  const int sq = b;
   const int slot = a.slot ? ld_const(a.slot + sq) : sq;
   const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
   const gptr side = (gptr)a.side_codes + row0 * 2 * HD;
@@ -1070,7 +1059,7 @@ __device__ __forceinline__ PlanView plan_view(const DecArgs& a, int lane) {
   for (int k = 0; k < 4; ++k) {
     const int i = 4 * lane + k;
     const int L = a.ctx[min(i, a.B - 1)];
-    const int E = a.cache_end ? a.cache_end[min(i, a.B - 1)] : L;
+    const int E = L;
     m[k] = i < a.B ? main_pages(L, E, a.sink, a.window) * a.Hkv : 0;
   }
   m[1] += m[0];
@@ -1228,7 +1217,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
     d.last = ip + d.np >= stop;
     d.opens = ip == seg0;
     d.closes = stop == seg_end;
-    const int32_t* ptrow = a.page_table + static_cast<size_t>(seq_of(a, ib)) * a.pt_stride;
+    const int32_t* ptrow = a.page_table + static_cast<size_t>(ib) * a.pt_stride;
     pt = ptrow[d.j0 + min(lane & 3, d.np - 1)];
     if (d.first)  // BF16 query of head grp, channels 8 r16 .. 8 r16 + 7
       raw2 = reinterpret_cast<const uint4*>(a.q + ((static_cast<size_t>(ib) * a.Hq + seg_g * GQA + grp) * HD) / 2)[r16];
@@ -1245,7 +1234,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
     F::to_lds(slot, blk, lane, r16, grp);
     if (d.first) {
       const int L = ld_const(a.ctx + d.b);
-      d.main_end = main_end_of(L, end_of(a, d.b, L), a.window);
+      d.main_end = main_end_of(L, L, a.window);
     }
   };
 
@@ -1344,7 +1333,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
   const int bg = b * a.Hkv + g;
   const int2 cr = a.ws.mrange[bg];  // written by the main kernel when the segment has pages
   const int Lb = ld_const(a.ctx + b);
-  const int c_lo = cr.x, n_parts = main_pages(Lb, end_of(a, b, Lb), a.sink, a.window) > 0 ? cr.y - cr.x + 1 : 0;
+  const int c_lo = cr.x, n_parts = main_pages(Lb, Lb, a.sink, a.window) > 0 ? cr.y - cr.x + 1 : 0;
   constexpr int kBatch = 4;
   for (int k0 = 0; k0 < n_parts; k0 += kBatch) {
     float2 Ac[kBatch];
@@ -1410,10 +1399,10 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
                          int Hq, float scale_log2, float* out, float* lse,
                          const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
                          hipEvent_t ev_main_begin, hipEvent_t ev_main_end, bool mx,
-                         const int32_t* seq_of, const int32_t* cache_end, const uint16_t* k_new,
+                         const uint16_t* k_new,
                          const uint16_t* v_new, const int32_t* pos_new) {
   // the fused append needs protected workgroups that own the new token
-  if (k_new && (mx || c.window <= 0 || seq_of)) return hipErrorInvalidValue;
+  if (k_new && (mx || c.window <= 0)) return hipErrorInvalidValue;
   if (ws.n_waves <= 0 || ws.n_waves % 4 != 0) return hipErrorInvalidValue;
   if (mx && dbg) return hipErrorInvalidValue;  // no debug instantiation of the MXFP4 variant
   DecArgs a{};
@@ -1428,8 +1417,6 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   a.slot = slot;
   a.page_table = page_table;
   a.pt_stride = pt_stride;
-  a.seq_of = seq_of;
-  a.cache_end = cache_end;
   a.k_new = reinterpret_cast<const uint32_t*>(k_new);
   a.v_new = reinterpret_cast<const uint32_t*>(v_new);
   a.pos_new = pos_new;

@@ -76,8 +76,7 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
                          int Hq, float scale_log2, float* out, float* lse,
                          const DecodeWorkspace& ws, const DecodeDebug* dbg, hipStream_t s,
                          hipEvent_t ev_main_begin = nullptr, hipEvent_t ev_main_end = nullptr,
-                         bool mx = false, const int32_t* seq_of = nullptr,
-                         const int32_t* cache_end = nullptr, const uint16_t* k_new = nullptr,
+                         bool mx = false, const uint16_t* k_new = nullptr,
                          const uint16_t* v_new = nullptr, const int32_t* pos_new = nullptr);
 // Re-prefill (chunked-prefill) attention: query-blocked (blocks of 8 tokens
 // per kv-head workgroup) over the protected rows and the main region, merged

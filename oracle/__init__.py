@@ -64,6 +64,9 @@ def lib():
         _lib.kv4ref_prefill_attention.argtypes = ([KC] + [C.c_void_p] * 5 + [C.c_int32] * 3
                                                   + [C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
                                                      C.POINTER(_Debug), C.c_int32])
+        _lib.kv4ref_prefill_attention_sampled.argtypes = ([KC] + [C.c_void_p] * 5 + [C.c_int32] * 3
+                                                          + [C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
+                                                             C.c_void_p, C.c_int32])
         _lib.mxref_append.argtypes = [KC] + [C.c_void_p] * 5 + [C.c_int32] * 2
         _lib.mxref_prefill.argtypes = [KC] + [C.c_void_p] * 6 + [C.c_int32] * 3
         _lib.mxref_decode.argtypes = ([KC] + [C.c_void_p] * 4 + [C.c_int32] * 3 + [C.c_float]
@@ -412,3 +415,25 @@ def prefill_attention(cache: Cache, q, cu_seqlens, start_pos, slot, page_table, 
     if rc != 0:
         raise ValueError(f"kv4ref_prefill_attention failed ({rc})")
     return out, lse, dbg
+
+
+def prefill_attention_sampled(cache: Cache, q, cu_seqlens, start_pos, slot, page_table, Hq: int,
+                              softmax_scale: float, tokens, heads, nthreads=None):
+    """prefill_attention for the listed (token, q-head) pairs only; returns
+    out [n][128], lse [n] (FP64)."""
+    q = _c(q, np.uint16)
+    cu, start, table = (_c(cu_seqlens, np.int32), _c(start_pos, np.int32), _c(page_table, np.int32))
+    slot = None if slot is None else _c(slot, np.int32)
+    th = _c(np.asarray(tokens, np.int64) * Hq + np.asarray(heads, np.int64), np.int64)
+    n = th.shape[0]
+    assert q.shape == (int(cu[-1]), Hq, HD)
+    out = np.zeros((n, HD), np.float64)
+    lse = np.zeros(n, np.float64)
+    st = cache._struct()
+    rc = lib().kv4ref_prefill_attention_sampled(C.byref(st), _p(q), _p(cu), _p(start),
+                                                None if slot is None else _p(slot), _p(table),
+                                                table.shape[1], start.shape[0], Hq, softmax_scale, n, _p(th),
+                                                _p(out), _p(lse), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"kv4ref_prefill_attention_sampled failed ({rc})")
+    return out, lse

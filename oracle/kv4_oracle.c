@@ -705,6 +705,45 @@ int kv4ref_prefill_attention(const kv4ref_cache *c, const uint16_t *q, const int
   return bad ? -2 : 0;
 }
 
+/* The same attention for a chosen list of (token, q-head) pairs only,
+ * th[i] = token * Hq + head; out [n][128], lse [n].  For checking samples of
+ * chunks too long to attend in full on the CPU. */
+int kv4ref_prefill_attention_sampled(const kv4ref_cache *c, const uint16_t *q, const int32_t *cu_seqlens,
+                                     const int32_t *start_pos, const int32_t *slot,
+                                     const int32_t *page_table, int32_t pt_stride, int32_t nseq,
+                                     int32_t Hq, float softmax_scale, int32_t n, const int64_t *th,
+                                     double *out, double *lse, int32_t nthreads) {
+  exp2_init();
+  const int Hkv = c->num_kv_heads;
+  if (Hkv <= 0 || Hq % Hkv != 0 || !budget_ok(c)) return -1;
+  const int G = Hq / Hkv;
+  const float scale_log2 = kv4ref_scale_log2(softmax_scale);
+  const int64_t T = cu_seqlens[nseq];
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int32_t i = 0; i < n; i++) {
+    if (th[i] < 0 || th[i] >= T * Hq) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    const int32_t t = (int32_t)(th[i] / Hq), h = (int32_t)(th[i] % Hq), g = h / G;
+    int sq = 0;
+    while (cu_seqlens[sq + 1] <= t) sq++;
+    const int32_t L = start_pos[sq] + (t - cu_seqlens[sq]) + 1;
+    const int32_t E = start_pos[sq] + (cu_seqlens[sq + 1] - cu_seqlens[sq]);
+    if ((E + PAGE - 1) / PAGE > pt_stride) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    decode_one_query(c, q + (size_t)th[i] * HD, L, E, slot ? slot[sq] : sq, g,
+                     page_table + (size_t)sq * pt_stride, scale_log2, 0, out + (size_t)i * HD, lse + i,
+                     NULL, NULL, NULL, NULL, NULL);
+  }
+  return bad ? -2 : 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* KV8 everywhere: the INT8 comparison variant of the quantization-target     */
 /* comparisons (KV4-RL pages, quantization-target comparison, figure 3).     */

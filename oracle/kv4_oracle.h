@@ -91,6 +91,13 @@ int kv4ref_prefill_attention(const kv4ref_cache *c, const uint16_t *q, const int
                              const int32_t *page_table, int32_t pt_stride, int32_t nseq, int32_t Hq,
                              float softmax_scale, int32_t pv_exact, double *out, double *lse,
                              const kv4ref_debug *dbg, int32_t nthreads);
+/* The same for the (token, q-head) pairs th[i] = token * Hq + head only:
+ * out [n][128], lse [n] (FP64). */
+int kv4ref_prefill_attention_sampled(const kv4ref_cache *c, const uint16_t *q, const int32_t *cu_seqlens,
+                                     const int32_t *start_pos, const int32_t *slot,
+                                     const int32_t *page_table, int32_t pt_stride, int32_t nseq,
+                                     int32_t Hq, float softmax_scale, int32_t n, const int64_t *th,
+                                     double *out, double *lse, int32_t nthreads);
 
 /* KV8 everywhere (INT8 comparison variant): paged pool
  * uint8 [num_pages][num_kv_heads][4160] = K codes int8 [16][128] (rotated) |

@@ -119,3 +119,44 @@ def test_chunk_blocks_and_budgets():
         lerr = float(np.abs(lse.cpu().numpy() - r_lse).max())
         _say(f"[chunk] budget {sw}: out {err:.2e} lse {lerr:.2e}")
         assert err <= OUT_TOL and lerr <= LSE_TOL, (sw, err, lerr)
+
+
+def test_benchmark_reprefill_sampled():
+    """The benchmark's re-prefill attention (8 chunks of 16,384 tokens, 32/8
+    heads, the same values and launch), sampled: tokens around every region
+    boundary of each chunk against the oracle's per-token attention."""
+    from synth import draw_values
+    wl = make_workload(4)
+    nseq, n = wl.prefill_nseq, wl.prefill_len
+    dev = torch.device("cuda")
+    _say(f"[chunk] benchmark re-prefill {nseq} x {n}")
+    pk, pv, _ = draw_values(wl.seed, 1000, nseq * n, 1, 4, wl.Hkv, device=dev)
+    pq = draw_values(wl.seed, 1001, 1, nseq * n, wl.Hq, wl.Hkv, device=dev)[2]
+    ppages = nseq * n // 16
+    cache = kv4.Kv4Cache.zeros(ppages, wl.Hkv, nseq, dev)
+    table = torch.arange(ppages, dtype=torch.int32, device=dev).view(nseq, n // 16)
+    cu = torch.arange(0, nseq * n + 1, n, dtype=torch.int32, device=dev)
+    start = torch.zeros(nseq, dtype=torch.int32, device=dev)
+    slot = torch.arange(nseq, dtype=torch.int32, device=dev)
+    kv4.prefill_quantize(cache, pk, pv, cu, start, slot, table, n)
+    out, lse = kv4.prefill_attention(cache, pq, cu, start, slot, table, n, SCALE)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    hk = pk.view(torch.int16).cpu().numpy().view(np.uint16)
+    hv = pv.view(torch.int16).cpu().numpy().view(np.uint16)
+    hq = pq.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.Cache(ppages, wl.Hkv, nseq)
+    oracle.prefill(ref, hk, hv, cu.cpu().numpy(), start.cpu().numpy(), slot.cpu().numpy(), table.cpu().numpy())
+    rng = np.random.default_rng(7)
+    pos = [0, 15, 16, 31, 143, 144, 4095, n // 2 + 3, n - 129, n - 128, n - 127, n - 2, n - 1]
+    tokens = np.array([s * n + p for s in (0, 3, 7) for p in pos], np.int64)
+    heads = rng.integers(0, wl.Hq, len(tokens))
+    r_out, r_lse = oracle.prefill_attention_sampled(ref, hq, cu.cpu().numpy(), start.cpu().numpy(),
+                                                    slot.cpu().numpy(), table.cpu().numpy(), wl.Hq, SCALE,
+                                                    tokens, heads)
+    got_o = out.cpu().numpy()[tokens, heads]
+    got_l = lse.cpu().numpy()[tokens, heads]
+    err = float(np.abs(got_o - r_out).max())
+    lerr = float(np.abs(got_l - r_lse).max())
+    _say(f"[chunk] benchmark sample of {len(tokens)}: out {err:.2e} lse {lerr:.2e}")
+    assert err <= OUT_TOL and lerr <= LSE_TOL, (err, lerr)

@@ -150,3 +150,15 @@ def test_prefill_attention_exact_pv_is_causal_softmax(chunk):
                 e = np.exp2(z - z.max())
                 assert np.abs(out[t, h] - (e[:, None] * vals).sum(0) / e.sum()).max() < 1e-4
                 assert abs(lse[t, h] - math.log(2) * (z.max() + math.log2(e.sum()))) < 1e-4
+
+
+def test_sampled_entry_equals_full(chunk):
+    """The sampled entry point returns the full call's rows for the listed
+    (token, head) pairs (the same arithmetic, the rest skipped)."""
+    wl, hi, cache, n, start, cu, q = chunk
+    out, lse, _ = oracle.prefill_attention(cache, q, cu, start, wl.slots, wl.page_table, wl.Hq, SCALE)
+    tokens = np.array([0, 5, 39, 40, 62], np.int64)
+    heads = np.array([0, 3, 1, 2, 3], np.int64)
+    o2, l2 = oracle.prefill_attention_sampled(cache, q, cu, start, wl.slots, wl.page_table, wl.Hq, SCALE,
+                                              tokens, heads)
+    assert np.array_equal(o2, out[tokens, heads]) and np.array_equal(l2, lse[tokens, heads])
