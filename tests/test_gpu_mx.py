@@ -93,3 +93,57 @@ def test_mx_appends_equal_prefill():
     torch.cuda.synchronize()
     assert torch.equal(a.cache.pages, b.cache.pages)
     assert torch.equal(a.cache.side_codes, b.cache.side_codes)
+
+
+def test_mx_fullsize_sampled():
+    """The 256-sequence benchmark workload written and decoded in the MXFP4
+    variant on the GPU in the benchmark's launch configuration; a sample of
+    sequences rebuilt (prefill of the prefix, append of the last token) and
+    decoded by the oracle."""
+    from synth import draw_values
+    from tests.wl import bf16_bits
+    dev = torch.device("cuda")
+    wl = make_workload(4)
+    _say(f"[mx] full size B={wl.B} mean ctx {wl.ctx.mean():.0f}")
+    n_tok = int(wl.ctx.sum())
+    k, v, q = draw_values(wl.seed, 0, n_tok, wl.B, wl.Hq, wl.Hkv, device=dev)
+    off = np.zeros(wl.B + 1, np.int64)
+    off[1:] = np.cumsum(wl.ctx)
+    lead = wl.ctx - 1
+    rows = torch.from_numpy(np.concatenate([np.arange(off[b], off[b] + lead[b]) for b in range(wl.B)])).to(dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lead)]).astype(np.int32)).to(dev)
+    table, slots = i32(wl.page_table, dev), i32(wl.slots, dev)
+    cache = kv4.Kv4Cache.zeros(wl.num_pages, wl.Hkv, wl.max_slots, dev)
+    kv4.mx_prefill_quantize(cache, k[rows].contiguous(), v[rows].contiguous(), cu,
+                            torch.zeros(wl.B, dtype=torch.int32, device=dev), slots, table, int(lead.max()))
+    last = torch.from_numpy(off[:-1] + lead).to(dev)
+    kv4.mx_append(cache, k[last].contiguous(), v[last].contiguous(), i32(lead, dev), slots, table)
+    out, lse = kv4.mx_decode_attention(cache, q, i32(wl.ctx, dev), slots, table, wl.max_ctx, SCALE)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    order = np.argsort(wl.ctx, kind="stable")
+    sample = np.unique([order[0], order[len(order) // 2], order[-1], 11])
+    _say(f"[mx] oracle on sequences {sample.tolist()} (ctx {wl.ctx[sample].tolist()})")
+    ctx_s = wl.ctx[sample]
+    need = (ctx_s + 15) // 16
+    rtable = np.zeros((len(sample), int(need.max())), np.int32)
+    o = 0
+    for i, n in enumerate(need):
+        rtable[i, :n] = np.arange(o, o + n)
+        o += n
+    ref = oracle.Cache(int(need.sum()), wl.Hkv, len(sample))
+    lead_s = ctx_s - 1
+    prow = np.concatenate([np.arange(off[b], off[b] + lead[b]) for b in sample])
+    cu_s = np.concatenate([[0], np.cumsum(lead_s)]).astype(np.int32)
+    oracle.mx_prefill(ref, bf16_bits(k[torch.from_numpy(prow).to(dev)]), bf16_bits(v[torch.from_numpy(prow).to(dev)]),
+                      cu_s, np.zeros(len(sample), np.int32), np.arange(len(sample), dtype=np.int32), rtable)
+    lrow = torch.from_numpy(off[sample] + lead_s).to(dev)
+    oracle.mx_append(ref, bf16_bits(k[lrow]), bf16_bits(v[lrow]), lead_s.astype(np.int32),
+                     np.arange(len(sample), dtype=np.int32), rtable)
+    r_out, r_lse = oracle.mx_decode(ref, bf16_bits(q[torch.from_numpy(sample).to(dev)]), ctx_s.astype(np.int32),
+                                    np.arange(len(sample), dtype=np.int32), rtable, wl.Hq, SCALE)
+    sel = torch.from_numpy(sample).to(dev)
+    err = float(np.abs(out[sel].cpu().numpy() - r_out).max())
+    lerr = float(np.abs(lse[sel].cpu().numpy() - r_lse).max())
+    _say(f"[mx] full size: out {err:.2e} lse {lerr:.2e}")
+    assert err <= OUT_TOL and lerr <= LSE_TOL, (err, lerr)
