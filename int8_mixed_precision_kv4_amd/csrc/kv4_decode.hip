@@ -20,6 +20,8 @@
 //   2. merge_kernel, one workgroup per (kv-head, sequence): exact
 //      log-sum-exp merge of the protected partial with the main partials,
 //      written as out and lse.
+#include <type_traits>
+
 #include "kv4_device.hpp"
 #include "kv4_internal.hpp"
 
@@ -104,9 +106,10 @@ __global__ __launch_bounds__(256) void plan_kernel(DecArgs a) { build_plan(a); }
 
 // Row-of-16 reductions of an int (lanes 16r .. 16r+15).
 __device__ __forceinline__ int row16_sum_i(int v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
-  return v;
+  v += xor_lane_i<1>(v);
+  v += xor_lane_i<2>(v);
+  v += xor_lane_i<4>(v);
+  return v + xor_lane_i<8>(v);
 }
 
 // Rotated INT8 query of the 4 heads of a group, computed by one wave: lane
@@ -126,26 +129,7 @@ __device__ __forceinline__ void rotate_group_query(uint4 raw, int r16, float x[8
     x[2 * i] = bf16_lo(w[i]);
     x[2 * i + 1] = bf16_hi(w[i]);
   }
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if ((j & h) == 0) {
-        const float u = x[j], v = x[j + h];
-        x[j] = u + v;
-        x[j + h] = u - v;
-      }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    const bool upper = (r16 & m) != 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = __shfl_xor(x[j], m);
-      x[j] = upper ? (p - x[j]) : (x[j] + p);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) x[j] = x[j] * kInvSqrt128;
+  fwht128_row16(x, r16);
 }
 __device__ __forceinline__ GroupQuery quantize_group_query(uint4 raw, float scale_log2, int r16) {
   float x[8];
@@ -374,8 +358,7 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
     se[i][wave] = e;
     ls += e;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+  ls = wave_sum(ls);
   __syncthreads();
 
   // ---- PV with v^ = bf16(s_v c) and FP32 weights

@@ -4,6 +4,7 @@
 // silent the rule is stated where it is implemented.
 #pragma once
 
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -74,6 +75,13 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_f32<0x140>(v));
   return v;
 }
+__device__ __forceinline__ float row16_min(float v) {
+  v = fminf(v, dpp_f32<0xB1>(v));
+  v = fminf(v, dpp_f32<0x4E>(v));
+  v = fminf(v, dpp_f32<0x141>(v));
+  v = fminf(v, dpp_f32<0x140>(v));
+  return v;
+}
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);
@@ -110,20 +118,71 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 }
 
+// Value of lane l ^ H in every lane l (H = 1, 2, 4, 8, 16, 32) without LDS
+// traffic: DPP quad permutations for 1 and 2, the swizzle crossbar for 4, a
+// DPP rotation of the 16-lane row by 8 for 8, and the row-pair and half swaps
+// (which leave every lane's own value in one result and its partner's in the
+// other) for 16 and 32.
+template <int H>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  static_assert(H == 1 || H == 2 || H == 4 || H == 8 || H == 16 || H == 32, "lane distance");
+  if constexpr (H == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true));
+  } else if constexpr (H == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true));
+  } else if constexpr (H == 4) {
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x101F));  // xor 4 in 32 lanes
+  } else if constexpr (H == 8) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, true));
+  } else if constexpr (H == 16) {
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? s[0] : s[1];
+  } else {
+    const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? s[0] : s[1];
+  }
+}
+template <int H>
+__device__ __forceinline__ float xor_lane_f(float v) {
+  return __uint_as_float(xor_lane<H>(__float_as_uint(v)));
+}
+template <int H>
+__device__ __forceinline__ int xor_lane_i(int v) {
+  return static_cast<int>(xor_lane<H>(static_cast<uint32_t>(v)));
+}
+
+// Wave-wide all-reductions, partners at lane distances 32, 16, ..., 1.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, xor_lane_f<32>(v));
+  v = fmaxf(v, xor_lane_f<16>(v));
+  v = fmaxf(v, xor_lane_f<8>(v));
+  v = fmaxf(v, xor_lane_f<4>(v));
+  v = fmaxf(v, xor_lane_f<2>(v));
+  return fmaxf(v, xor_lane_f<1>(v));
 }
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-  return v;
+  v = fminf(v, xor_lane_f<32>(v));
+  v = fminf(v, xor_lane_f<16>(v));
+  v = fminf(v, xor_lane_f<8>(v));
+  v = fminf(v, xor_lane_f<4>(v));
+  v = fminf(v, xor_lane_f<2>(v));
+  return fminf(v, xor_lane_f<1>(v));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += xor_lane_f<32>(v);
+  v += xor_lane_f<16>(v);
+  v += xor_lane_f<8>(v);
+  v += xor_lane_f<4>(v);
+  v += xor_lane_f<2>(v);
+  return v + xor_lane_f<1>(v);
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += xor_lane_i<32>(v);
+  v += xor_lane_i<16>(v);
+  v += xor_lane_i<8>(v);
+  v += xor_lane_i<4>(v);
+  v += xor_lane_i<2>(v);
+  return v + xor_lane_i<1>(v);
 }
 
 // ------------------------------------------------------------- rotation --
@@ -134,20 +193,56 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 // The stride order fixes the FP32 sum tree of every output.
 constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;
 
+template <int H>
+__device__ __forceinline__ void fwht_lane_stage(float& x0, float& x1) {
+  const float p0 = xor_lane_f<H>(x0), p1 = xor_lane_f<H>(x1);
+  const bool upper = (threadIdx.x & H) != 0;
+  x0 = upper ? (p0 - x0) : (x0 + p0);
+  x1 = upper ? (p1 - x1) : (x1 + p1);
+}
 __device__ __forceinline__ void fwht128_wave(float& x0, float& x1) {
   const float a = x0 + x1, b = x0 - x1;
   x0 = a;
   x1 = b;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {  // element stride 2h lives h lanes away
-    const float p0 = __shfl_xor(x0, h), p1 = __shfl_xor(x1, h);
-    const bool upper = (lane & h) != 0;
-    x0 = upper ? (p0 - x0) : (x0 + p0);
-    x1 = upper ? (p1 - x1) : (x1 + p1);
-  }
+  fwht_lane_stage<1>(x0, x1);  // element stride 2h lives h lanes away
+  fwht_lane_stage<2>(x0, x1);
+  fwht_lane_stage<4>(x0, x1);
+  fwht_lane_stage<8>(x0, x1);
+  fwht_lane_stage<16>(x0, x1);
+  fwht_lane_stage<32>(x0, x1);
   x0 = x0 * kInvSqrt128;
   x1 = x1 * kInvSqrt128;
+}
+
+// The same rotation with a row of 16 lanes per vector: lane r16 of the row
+// holds elements 8 r16 .. 8 r16 + 7 in x[0..7]; strides 1, 2, 4 inside the
+// lane, then 8, 16, 32, 64 across lanes (lane distances 1, 2, 4, 8), in that
+// order, then the 2^-3.5 scale (the same sum tree as fwht128_wave).
+__device__ __forceinline__ void fwht128_row16(float x[8], int r16) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((j & h) == 0) {
+        const float u = x[j], v = x[j + h];
+        x[j] = u + v;
+        x[j + h] = u - v;
+      }
+  auto stage = [&](auto m_tag) {
+    constexpr int M = decltype(m_tag)::value;
+    const bool upper = (r16 & M) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = xor_lane_f<M>(x[j]);
+      x[j] = upper ? (p - x[j]) : (x[j] + p);
+    }
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 8>{});
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = x[j] * kInvSqrt128;
 }
 
 // ----------------------------------------------------------- quantizers --

@@ -134,10 +134,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(QuantArgs a, const int32_t
 
   __shared__ uint8_t vcodes[PAGE][HD];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int t = t0 + wave; t < t1; t += 4) {
+  // the wave's positions t = t0 + wave + 4i: every load first, so that the
+  // four tokens' K and V are in flight together
+  uint32_t kwv[4], vwv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + wave + 4 * i;
+    kwv[i] = vwv[i] = 0u;
+    if (t < t1) {
+      const size_t vec = (static_cast<size_t>(cu[s]) + (page * PAGE + t - start)) * a.Hkv + g;
+      kwv[i] = a.k[vec * 64 + lane];
+      vwv[i] = a.v[vec * 64 + lane];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + wave + 4 * i;
+    if (t >= t1) break;
     const int p = page * PAGE + t;
-    const size_t vec = (static_cast<size_t>(cu[s]) + (p - start)) * a.Hkv + g;
-    const uint32_t kw = a.k[vec * 64 + lane], vw = a.v[vec * 64 + lane];
+    const uint32_t kw = kwv[i], vw = vwv[i];
     float k0 = bf16_lo(kw), k1 = bf16_hi(kw);
     const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
     fwht128_wave(k0, k1);
@@ -174,6 +189,126 @@ __global__ __launch_bounds__(256) void prefill_kernel(QuantArgs a, const int32_t
   for (int i = 0; i < 8; ++i) {
     const int t = 8 * half + i;
     if (t >= t0 && t < t1) w = (w & ~(0xFu << (4 * i))) | (static_cast<uint32_t>(vcodes[t][j]) << (4 * i));
+  }
+  *vw = w;
+}
+
+// KV4-RL re-prefill with a row of 16 lanes per token (lane r16: channels
+// 8 r16 .. 8 r16 + 7), so that one wave quantizes 4 tokens at once and the
+// per-vector work (reductions, metadata) is shared by four times more data
+// per instruction.  Workgroup (page, kv-head, sequence): the 16 slots of one
+// page, wave w holding slots 4w .. 4w+3.  Same arithmetic as prefill_kernel:
+// the same rotation sum tree, exact min / max, the same quantizer calls.
+__device__ __forceinline__ void unpack_bf16x8(uint4 r, float x[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(w[i]);
+    x[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+// Nibble codes of 8 channels: channel 8 r16 + j in bits 4j .. 4j+3 (byte i
+// = channels 2i (low nibble) and 2i+1 of the lane's 8).
+__device__ __forceinline__ uint32_t int4_codes8(const float x[8], const Int4Meta& q) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w |= int4_code(x[j], q) << (4 * j);
+  return w;
+}
+__device__ __forceinline__ Int4Meta int4_meta_row16(const float x[8]) {
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) {
+    mn = fminf(mn, x[j]);
+    mx = fmaxf(mx, x[j]);
+  }
+  return int4_meta(row16_min(mn), row16_max(mx));
+}
+__device__ __forceinline__ uint2 int8_codes8(const float x[8], const Int8Meta& q) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j >> 2] |= (static_cast<uint32_t>(int8_code(x[j], q)) & 0xFFu) << (8 * (j & 3));
+  return make_uint2(w[0], w[1]);
+}
+__device__ __forceinline__ Int8Meta int8_meta_row16(const float x[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  return int8_meta(row16_max(amax));
+}
+
+__global__ __launch_bounds__(256) void prefill16_kernel(QuantArgs a, const int32_t* __restrict__ cu,
+                                                        const int32_t* __restrict__ start_pos) {
+  const int lp = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int n = cu[s + 1] - cu[s];
+  if (n <= 0) return;
+  const int start = start_pos[s], end = start + n;
+  const int page = (start >> 4) + lp;
+  if (page > ((end - 1) >> 4)) return;
+  const int t0 = max(start - page * PAGE, 0), t1 = min(end - page * PAGE, PAGE);
+  const int slot = a.slot ? a.slot[s] : s;
+  const int phys = a.page_table[static_cast<size_t>(s) * a.pt_stride + page];
+  uint8_t* blk = a.pages + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
+  const int keep_from = max(a.sink, end - a.window);  // == end when w = 0
+
+  __shared__ __attribute__((aligned(16))) uint8_t vcodes[PAGE][HD];
+  const int r16 = threadIdx.x & 15;
+  const int t = threadIdx.x >> 4;  // page slot of this row
+  const bool live = t >= t0 && t < t1;
+  const int p = page * PAGE + t;
+  float kx[8], vx[8];
+  {
+    uint4 kr = make_uint4(0u, 0u, 0u, 0u), vr = kr;
+    if (live) {
+      const size_t vec = (static_cast<size_t>(cu[s]) + (p - start)) * a.Hkv + g;
+      kr = reinterpret_cast<const uint4*>(a.k + vec * 64)[r16];
+      vr = reinterpret_cast<const uint4*>(a.v + vec * 64)[r16];
+    }
+    unpack_bf16x8(kr, kx);
+    unpack_bf16x8(vr, vx);
+  }
+  fwht128_row16(kx, r16);  // every row takes part in the cross-lane stages
+  const Int4Meta kq = int4_meta_row16(kx);
+  const Int4Meta vq = int4_meta_row16(vx);
+  const uint32_t kc = int4_codes8(kx, kq), vc = int4_codes8(vx, vq);
+  if (live) {
+    *reinterpret_cast<uint32_t*>(blk + 64 * t + 4 * r16) = kc;
+    // V codes of the slot, one byte per channel, for the channel-major pass
+    uint2 vb;
+    vb.x = (vc & 0xFu) | (((vc >> 4) & 0xFu) << 8) | (((vc >> 8) & 0xFu) << 16) | (((vc >> 12) & 0xFu) << 24);
+    vb.y = ((vc >> 16) & 0xFu) | (((vc >> 20) & 0xFu) << 8) | (((vc >> 24) & 0xFu) << 16) | ((vc >> 28) << 24);
+    *reinterpret_cast<uint2*>(&vcodes[t][8 * r16]) = vb;
+    if (r16 == 0) {
+      *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
+      *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
+    }
+  }
+  // INT8 side row: final sinks and the last w positions of the sequence
+  const bool side = live && (p < a.sink || p >= keep_from);
+  if (__builtin_amdgcn_ballot_w64(side)) {  // rows of 16 lanes agree; the reductions need all of them
+    const Int8Meta ks = int8_meta_row16(kx), vs = int8_meta_row16(vx);
+    if (side) {
+      const size_t r = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS + side_row(a, p);
+      int8_t* codes = a.side_codes + r * 2 * HD;
+      *reinterpret_cast<uint2*>(codes + 8 * r16) = int8_codes8(kx, ks);
+      *reinterpret_cast<uint2*>(codes + HD + 8 * r16) = int8_codes8(vx, vs);
+      if (r16 == 0) {
+        a.side_scales[r * 2] = static_cast<uint16_t>(ks.s16);
+        a.side_scales[r * 2 + 1] = static_cast<uint16_t>(vs.s16);
+      }
+    }
+  }
+  __syncthreads();
+  // V codes, channel-major: thread -> channel j, positions 8*half .. 8*half+7
+  // (one dword); nibbles of positions outside [t0, t1) are kept.
+  const int j = threadIdx.x >> 1, half = threadIdx.x & 1;
+  uint32_t* vw = reinterpret_cast<uint32_t*>(blk + OFF_VCODE + 8 * j + 4 * half);
+  const bool whole = (t0 <= 8 * half) && (t1 >= 8 * half + 8);
+  uint32_t w = whole ? 0u : *vw;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tt = 8 * half + i;
+    if (tt >= t0 && tt < t1) w = (w & ~(0xFu << (4 * i))) | (static_cast<uint32_t>(vcodes[tt][j]) << (4 * i));
   }
   *vw = w;
 }
@@ -277,7 +412,7 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t*
               slot, page_table, pt_stride, c.sink, c.window};
   const int pages = (max_seqlen + PAGE - 1) / PAGE + 1;
   if (mx) hipLaunchKernelGGL(prefill_kernel<true>, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
-  else hipLaunchKernelGGL(prefill_kernel<false>, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
+  else hipLaunchKernelGGL(prefill16_kernel, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
   return hipGetLastError();
 }
 
