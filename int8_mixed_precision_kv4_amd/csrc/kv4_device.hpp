@@ -281,9 +281,9 @@ __device__ __forceinline__ Int4Meta int4_meta(float mn, float mx) {
 }
 // c = clamp(rint((x - m) / delta), 0, 15); a zero delta gives code 0.
 __device__ __forceinline__ uint32_t int4_code(float x, const Int4Meta& q) {
-  if (q.d == 0.0f) return 0u;
   const float t = __builtin_rintf(div_short_divisor(x - q.m, q.d, q.dinv));
-  return static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), 15.0f));
+  const uint32_t c = static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), 15.0f));
+  return q.d == 0.0f ? 0u : c;  // a select, not a branch per element
 }
 
 // Symmetric INT8 side copy: s = fp16(max|x| / 127), c = clamp(rint(x / s), -127, 127).
@@ -299,9 +299,9 @@ __device__ __forceinline__ Int8Meta int8_meta(float amax) {
   return r;
 }
 __device__ __forceinline__ int32_t int8_code(float x, const Int8Meta& q) {
-  if (q.s == 0.0f) return 0;
   const float t = __builtin_rintf(div_short_divisor(x, q.s, q.sinv));
-  return static_cast<int32_t>(fminf(fmaxf(t, -127.0f), 127.0f));
+  const int32_t c = static_cast<int32_t>(fminf(fmaxf(t, -127.0f), 127.0f));
+  return q.s == 0.0f ? 0 : c;
 }
 
 // ------------------------------------------------------ cache entries --

@@ -237,9 +237,13 @@ __device__ __forceinline__ Int8Meta int8_meta_row16(const float x[8]) {
   return int8_meta(row16_max(amax));
 }
 
-__global__ __launch_bounds__(256) void prefill16_kernel(QuantArgs a, const int32_t* __restrict__ cu,
+// 128 threads: row r (lanes 16r .. 16r+15) quantizes page slots r and r + 8,
+// both tokens' K and V loaded before either is processed.
+__global__ __launch_bounds__(128) void prefill16_kernel(QuantArgs a, const int32_t* __restrict__ cu,
                                                         const int32_t* __restrict__ start_pos) {
-  const int lp = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  // the kv-heads of a page side by side in the grid
+  const int g = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.Hkv));
+  const int lp = static_cast<int>(blockIdx.x / static_cast<unsigned>(a.Hkv)), s = blockIdx.y;
   const int n = cu[s + 1] - cu[s];
   if (n <= 0) return;
   const int start = start_pos[s], end = start + n;
@@ -253,64 +257,75 @@ __global__ __launch_bounds__(256) void prefill16_kernel(QuantArgs a, const int32
 
   __shared__ __attribute__((aligned(16))) uint8_t vcodes[PAGE][HD];
   const int r16 = threadIdx.x & 15;
-  const int t = threadIdx.x >> 4;  // page slot of this row
-  const bool live = t >= t0 && t < t1;
-  const int p = page * PAGE + t;
-  float kx[8], vx[8];
-  {
-    uint4 kr = make_uint4(0u, 0u, 0u, 0u), vr = kr;
+  const int row = threadIdx.x >> 4;  // 0..7
+  uint4 kr[2], vr[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = row + 8 * u;
+    kr[u] = vr[u] = make_uint4(0u, 0u, 0u, 0u);
+    if (t >= t0 && t < t1) {
+      const size_t vec = (static_cast<size_t>(cu[s]) + (page * PAGE + t - start)) * a.Hkv + g;
+      kr[u] = reinterpret_cast<const uint4*>(a.k + vec * 64)[r16];
+      vr[u] = reinterpret_cast<const uint4*>(a.v + vec * 64)[r16];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = row + 8 * u;  // page slot of this row
+    const bool live = t >= t0 && t < t1;
+    const int p = page * PAGE + t;
+    float kx[8], vx[8];
+    unpack_bf16x8(kr[u], kx);
+    unpack_bf16x8(vr[u], vx);
+    fwht128_row16(kx, r16);  // every row takes part in the cross-lane stages
+    const Int4Meta kq = int4_meta_row16(kx);
+    const Int4Meta vq = int4_meta_row16(vx);
+    const uint32_t kc = int4_codes8(kx, kq), vc = int4_codes8(vx, vq);
     if (live) {
-      const size_t vec = (static_cast<size_t>(cu[s]) + (p - start)) * a.Hkv + g;
-      kr = reinterpret_cast<const uint4*>(a.k + vec * 64)[r16];
-      vr = reinterpret_cast<const uint4*>(a.v + vec * 64)[r16];
-    }
-    unpack_bf16x8(kr, kx);
-    unpack_bf16x8(vr, vx);
-  }
-  fwht128_row16(kx, r16);  // every row takes part in the cross-lane stages
-  const Int4Meta kq = int4_meta_row16(kx);
-  const Int4Meta vq = int4_meta_row16(vx);
-  const uint32_t kc = int4_codes8(kx, kq), vc = int4_codes8(vx, vq);
-  if (live) {
-    *reinterpret_cast<uint32_t*>(blk + 64 * t + 4 * r16) = kc;
-    // V codes of the slot, one byte per channel, for the channel-major pass
-    uint2 vb;
-    vb.x = (vc & 0xFu) | (((vc >> 4) & 0xFu) << 8) | (((vc >> 8) & 0xFu) << 16) | (((vc >> 12) & 0xFu) << 24);
-    vb.y = ((vc >> 16) & 0xFu) | (((vc >> 20) & 0xFu) << 8) | (((vc >> 24) & 0xFu) << 16) | ((vc >> 28) << 24);
-    *reinterpret_cast<uint2*>(&vcodes[t][8 * r16]) = vb;
-    if (r16 == 0) {
-      *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
-      *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
-    }
-  }
-  // INT8 side row: final sinks and the last w positions of the sequence
-  const bool side = live && (p < a.sink || p >= keep_from);
-  if (__builtin_amdgcn_ballot_w64(side)) {  // rows of 16 lanes agree; the reductions need all of them
-    const Int8Meta ks = int8_meta_row16(kx), vs = int8_meta_row16(vx);
-    if (side) {
-      const size_t r = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS + side_row(a, p);
-      int8_t* codes = a.side_codes + r * 2 * HD;
-      *reinterpret_cast<uint2*>(codes + 8 * r16) = int8_codes8(kx, ks);
-      *reinterpret_cast<uint2*>(codes + HD + 8 * r16) = int8_codes8(vx, vs);
+      *reinterpret_cast<uint32_t*>(blk + 64 * t + 4 * r16) = kc;
+      // V codes of the slot, one byte per channel, for the channel-major pass
+      uint2 vb;
+      vb.x = (vc & 0xFu) | (((vc >> 4) & 0xFu) << 8) | (((vc >> 8) & 0xFu) << 16) | (((vc >> 12) & 0xFu) << 24);
+      vb.y = ((vc >> 16) & 0xFu) | (((vc >> 20) & 0xFu) << 8) | (((vc >> 24) & 0xFu) << 16) | ((vc >> 28) << 24);
+      *reinterpret_cast<uint2*>(&vcodes[t][8 * r16]) = vb;
       if (r16 == 0) {
-        a.side_scales[r * 2] = static_cast<uint16_t>(ks.s16);
-        a.side_scales[r * 2 + 1] = static_cast<uint16_t>(vs.s16);
+        *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
+        *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
+      }
+    }
+    // INT8 side row: final sinks and the last w positions of the sequence
+    const bool side = live && (p < a.sink || p >= keep_from);
+    if (__builtin_amdgcn_ballot_w64(side)) {  // the row reductions need every lane of a row
+      const Int8Meta ks = int8_meta_row16(kx), vs = int8_meta_row16(vx);
+      if (side) {
+        const size_t r = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS + side_row(a, p);
+        int8_t* codes = a.side_codes + r * 2 * HD;
+        *reinterpret_cast<uint2*>(codes + 8 * r16) = int8_codes8(kx, ks);
+        *reinterpret_cast<uint2*>(codes + HD + 8 * r16) = int8_codes8(vx, vs);
+        if (r16 == 0) {
+          a.side_scales[r * 2] = static_cast<uint16_t>(ks.s16);
+          a.side_scales[r * 2 + 1] = static_cast<uint16_t>(vs.s16);
+        }
       }
     }
   }
   __syncthreads();
-  // V codes, channel-major: thread -> channel j, positions 8*half .. 8*half+7
-  // (one dword); nibbles of positions outside [t0, t1) are kept.
-  const int j = threadIdx.x >> 1, half = threadIdx.x & 1;
-  uint32_t* vw = reinterpret_cast<uint32_t*>(blk + OFF_VCODE + 8 * j + 4 * half);
-  const bool whole = (t0 <= 8 * half) && (t1 >= 8 * half + 8);
-  uint32_t w = whole ? 0u : *vw;
+  // V codes, channel-major: per pass, thread -> channel j, positions 8*half ..
+  // 8*half+7 (one dword); nibbles of positions outside [t0, t1) are kept.
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int tt = 8 * half + i;
-    if (tt >= t0 && tt < t1) w = (w & ~(0xFu << (4 * i))) | (static_cast<uint32_t>(vcodes[tt][j]) << (4 * i));
+  for (int pass = 0; pass < 2; ++pass) {
+    const int idx = threadIdx.x + 128 * pass;
+    const int j = idx >> 1, half = idx & 1;
+    uint32_t* vw = reinterpret_cast<uint32_t*>(blk + OFF_VCODE + 8 * j + 4 * half);
+    const bool whole = (t0 <= 8 * half) && (t1 >= 8 * half + 8);
+    uint32_t w = whole ? 0u : *vw;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tt = 8 * half + i;
+      if (tt >= t0 && tt < t1) w = (w & ~(0xFu << (4 * i))) | (static_cast<uint32_t>(vcodes[tt][j]) << (4 * i));
+    }
+    *vw = w;
   }
-  *vw = w;
 }
 
 // ------------------------------------------------------------ KV8 pool --
@@ -412,7 +427,7 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t*
               slot, page_table, pt_stride, c.sink, c.window};
   const int pages = (max_seqlen + PAGE - 1) / PAGE + 1;
   if (mx) hipLaunchKernelGGL(prefill_kernel<true>, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
-  else hipLaunchKernelGGL(prefill16_kernel, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
+  else hipLaunchKernelGGL(prefill16_kernel, dim3(pages * c.Hkv, nseq), dim3(128), 0, s, a, cu, start);
   return hipGetLastError();
 }
 
