@@ -1,27 +1,27 @@
-// Re-prefill attention, query-blocked: the main region of a chunk's query
-// tokens computed a block of 8 tokens at a time, so that every INT4 tile a
-// workgroup loads serves 8 tokens x 4 heads.
+// Re-prefill attention, query-blocked (paper.rainbus.top summary, "方法步骤详情"
+// step 1: carried prefixes are re-prefilled after a weight update; step 4:
+// the hybrid attention).  Token p of a chunk attends [0, p] under the
+// protected set of the cache as it stands (cache end E = the chunk's end):
+// the sinks below p + 1 and the window positions [max(s, E - w), p] from the
+// INT8 side rows, and the main region [s, min(p + 1, E - w)) from the INT4
+// pages, every 16-position tile of it processed by the decode step's per-tile
+// rule (integer QK, Delta/m after the dot, tile softmax with exp2s, P-operand
+// codes with the V step folded in, integer PV, FP32 running merge).
 //
-// KV4-RL pages ("KV4-RL" method summary, step 1: carried prefixes are
-// re-prefilled after a weight update; step 4: hybrid attention with integer
-// QK and integer PV over the INT4 region).  Token p of a chunk attends [0, p]
-// under the protected set of the cache as it stands (cache end E): the main
-// region is [s, min(p + 1, E - w)) and every one of its 16-position tiles is
-// processed by the same per-tile rule as the decode step (integer QK, Delta/m
-// after the dot, tile softmax with exp2s, P-operand codes with the V step
-// folded in, integer PV, FP32 running merge).  The protected partials come
-// from the decode kernel's protected workgroups (one per token and kv-head);
-// this kernel merges them with its main partials and writes out and lse.
-//
-// Layout of one workgroup: (block of 8 tokens, kv-head g), 4 waves splitting
-// the block's main tiles.  Every MFMA is v_mfma_i32_32x32x16_i8 with the 32
-// rows n = 4 * token + head as its N dimension, computed transposed:
-//   QK:  D^T[32 positions][32 rows] = K[positions][16 channels] q^T
-//   PV:  O^T[32 channels][32 rows]  = V^T[channels][16 positions] P^T
+// One workgroup per (block of 8 consecutive tokens of a chunk, kv-head), its
+// 4 waves splitting the block's side-row groups and main tiles, each tile and
+// side row read once for 8 tokens x 4 heads.  Every product takes the 32 rows
+// n = 4 * token + head as its N dimension and is computed transposed:
+//   QK:  D^T[32 positions][32 rows] = K[positions][16 channels] q^T   (i8)
+//   PV:  O^T[32 channels][32 rows]  = V^T[channels][16 positions] P^T (i8 for
+//        the main tiles; BF16 hi / lo parts of the FP32 weights for the
+//        protected rows)
 // so that lane (n, kg) (n = lane % 32, kg = lane / 32) owns row n: it holds
 // D of positions 8 (r / 4) + 4 kg + r % 4 (register r) of the two tiles of a
 // pair, reduces a tile's max over its own 8 values and its partner lane's,
 // and its 8 P codes of a tile are already the B operand of the PV product.
+// Both regions accumulate into one running state per row (an exact
+// log-sum-exp merge); the 4 waves' states merge through LDS into out, lse.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
