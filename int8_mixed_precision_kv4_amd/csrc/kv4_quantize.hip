@@ -116,89 +116,12 @@ __global__ __launch_bounds__(64) void append_kernel(QuantArgs a, const int32_t* 
 // nibble bytes shared by neighbouring positions have a single writer.  Side
 // rows are written only where appends would leave them in the final state:
 // sinks, and the last w positions of the range (earlier ring rows would be
-// overwritten within the same range anyway; none when w = 0).
-template <bool MX>
-__global__ __launch_bounds__(256) void prefill_kernel(QuantArgs a, const int32_t* __restrict__ cu,
-                                                      const int32_t* __restrict__ start_pos) {
-  const int lp = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int n = cu[s + 1] - cu[s];
-  if (n <= 0) return;
-  const int start = start_pos[s], end = start + n;
-  const int page = (start >> 4) + lp;
-  if (page > ((end - 1) >> 4)) return;
-  const int t0 = max(start - page * PAGE, 0), t1 = min(end - page * PAGE, PAGE);
-  const int slot = a.slot ? a.slot[s] : s;
-  const int phys = a.page_table[static_cast<size_t>(s) * a.pt_stride + page];
-  uint8_t* blk = a.pages + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
-  const int keep_from = max(a.sink, end - a.window);  // == end when w = 0
-
-  __shared__ uint8_t vcodes[PAGE][HD];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // the wave's positions t = t0 + wave + 4i: every load first, so that the
-  // four tokens' K and V are in flight together
-  uint32_t kwv[4], vwv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + wave + 4 * i;
-    kwv[i] = vwv[i] = 0u;
-    if (t < t1) {
-      const size_t vec = (static_cast<size_t>(cu[s]) + (page * PAGE + t - start)) * a.Hkv + g;
-      kwv[i] = a.k[vec * 64 + lane];
-      vwv[i] = a.v[vec * 64 + lane];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + wave + 4 * i;
-    if (t >= t1) break;
-    const int p = page * PAGE + t;
-    const uint32_t kw = kwv[i], vw = vwv[i];
-    float k0 = bf16_lo(kw), k1 = bf16_hi(kw);
-    const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
-    fwht128_wave(k0, k1);
-    if constexpr (MX) {
-      const MxCodes mc = mx_codes(k0, k1, v0, v1);
-      blk[64 * t + lane] = static_cast<uint8_t>(mc.kbyte);
-      vcodes[t][2 * lane] = static_cast<uint8_t>(mc.v0);
-      vcodes[t][2 * lane + 1] = static_cast<uint8_t>(mc.v1);
-      if ((lane & 15) == 0) {
-        blk[MX_OFF_KS + 4 * t + (lane >> 4)] = static_cast<uint8_t>(mc.ke8);
-        blk[MX_OFF_VS + 4 * t + (lane >> 4)] = static_cast<uint8_t>(mc.ve8);
-      }
-    } else {
-      const Int4Meta kq = int4_meta(wave_min(fminf(k0, k1)), wave_max(fmaxf(k0, k1)));
-      const Int4Meta vq = int4_meta(wave_min(fminf(v0, v1)), wave_max(fmaxf(v0, v1)));
-      blk[64 * t + lane] = static_cast<uint8_t>(int4_code(k0, kq) | (int4_code(k1, kq) << 4));
-      vcodes[t][2 * lane] = static_cast<uint8_t>(int4_code(v0, vq));
-      vcodes[t][2 * lane + 1] = static_cast<uint8_t>(int4_code(v1, vq));
-      if (lane == 0) {
-        *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
-        *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
-      }
-    }
-    if (p < a.sink || p >= keep_from) write_side_row(a, slot, g, p, k0, k1, v0, v1, lane);
-  }
-  __syncthreads();
-  // V codes, channel-major: thread -> channel j, positions 8*half .. 8*half+7
-  // (one dword); nibbles of positions outside [t0, t1) are kept.
-  const int j = threadIdx.x >> 1, half = threadIdx.x & 1;
-  uint32_t* vw = reinterpret_cast<uint32_t*>(blk + OFF_VCODE + 8 * j + 4 * half);
-  const bool whole = (t0 <= 8 * half) && (t1 >= 8 * half + 8);
-  uint32_t w = whole ? 0u : *vw;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = 8 * half + i;
-    if (t >= t0 && t < t1) w = (w & ~(0xFu << (4 * i))) | (static_cast<uint32_t>(vcodes[t][j]) << (4 * i));
-  }
-  *vw = w;
-}
-
-// KV4-RL re-prefill with a row of 16 lanes per token (lane r16: channels
-// 8 r16 .. 8 r16 + 7), so that one wave quantizes 4 tokens at once and the
-// per-vector work (reductions, metadata) is shared by four times more data
-// per instruction.  Workgroup (page, kv-head, sequence): the 16 slots of one
-// page, wave w holding slots 4w .. 4w+3.  Same arithmetic as prefill_kernel:
-// the same rotation sum tree, exact min / max, the same quantizer calls.
+// overwritten within the same range anyway; none when w = 0).  A row of 16
+// lanes quantizes one token (lane r16: channels 8 r16 .. 8 r16 + 7), so that
+// one wave takes 4 tokens at once and the per-vector work (reductions,
+// metadata) is shared by four times more data per instruction.  Same
+// arithmetic as the append kernel: the same rotation sum tree, exact min /
+// max, the same quantizer calls, hence the same bytes.
 __device__ __forceinline__ void unpack_bf16x8(uint4 r, float x[8]) {
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
@@ -237,8 +160,27 @@ __device__ __forceinline__ Int8Meta int8_meta_row16(const float x[8]) {
   return int8_meta(row16_max(amax));
 }
 
+// MXFP4 with 8 channels per lane: the block's max |x| over its 4 lanes (the
+// quad of the DPP quad permutations), and the E2M1 codes of the lane's 8
+// channels at unit scale after the exact ldexp by -E (low nibble first).
+__device__ __forceinline__ float quad_max_abs8(const float x[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
+  m = fmaxf(m, dpp_f32<0xB1>(m));
+  return fmaxf(m, dpp_f32<0x4E>(m));
+}
+__device__ __forceinline__ uint32_t mx_codes8(const float x[8], int E) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w |= mx_pair(x[2 * i], x[2 * i + 1], E) << (8 * i);
+  return w;
+}
+
 // 128 threads: row r (lanes 16r .. 16r+15) quantizes page slots r and r + 8,
-// both tokens' K and V loaded before either is processed.
+// both tokens' K and V loaded before either is processed; MX selects the
+// MXFP4 main-region entry instead of INT4.
+template <bool MX>
 __global__ __launch_bounds__(128) void prefill16_kernel(QuantArgs a, const int32_t* __restrict__ cu,
                                                         const int32_t* __restrict__ start_pos) {
   // the kv-heads of a page side by side in the grid
@@ -278,9 +220,26 @@ __global__ __launch_bounds__(128) void prefill16_kernel(QuantArgs a, const int32
     unpack_bf16x8(kr[u], kx);
     unpack_bf16x8(vr[u], vx);
     fwht128_row16(kx, r16);  // every row takes part in the cross-lane stages
-    const Int4Meta kq = int4_meta_row16(kx);
-    const Int4Meta vq = int4_meta_row16(vx);
-    const uint32_t kc = int4_codes8(kx, kq), vc = int4_codes8(vx, vq);
+    uint32_t kc, vc;  // nibble codes of the lane's 8 channels
+    if constexpr (MX) {
+      // MXFP4: 32-channel blocks = 4 lanes (block r16 / 4)
+      const int ek = mx_exponent(quad_max_abs8(kx)), ev = mx_exponent(quad_max_abs8(vx));
+      kc = mx_codes8(kx, ek);
+      vc = mx_codes8(vx, ev);
+      if (live && (r16 & 3) == 0) {
+        blk[MX_OFF_KS + 4 * t + (r16 >> 2)] = static_cast<uint8_t>(ek + 127);
+        blk[MX_OFF_VS + 4 * t + (r16 >> 2)] = static_cast<uint8_t>(ev + 127);
+      }
+    } else {
+      const Int4Meta kq = int4_meta_row16(kx);
+      const Int4Meta vq = int4_meta_row16(vx);
+      kc = int4_codes8(kx, kq);
+      vc = int4_codes8(vx, vq);
+      if (live && r16 == 0) {
+        *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
+        *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
+      }
+    }
     if (live) {
       *reinterpret_cast<uint32_t*>(blk + 64 * t + 4 * r16) = kc;
       // V codes of the slot, one byte per channel, for the channel-major pass
@@ -288,10 +247,6 @@ __global__ __launch_bounds__(128) void prefill16_kernel(QuantArgs a, const int32
       vb.x = (vc & 0xFu) | (((vc >> 4) & 0xFu) << 8) | (((vc >> 8) & 0xFu) << 16) | (((vc >> 12) & 0xFu) << 24);
       vb.y = ((vc >> 16) & 0xFu) | (((vc >> 20) & 0xFu) << 8) | (((vc >> 24) & 0xFu) << 16) | ((vc >> 28) << 24);
       *reinterpret_cast<uint2*>(&vcodes[t][8 * r16]) = vb;
-      if (r16 == 0) {
-        *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
-        *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
-      }
     }
     // INT8 side row: final sinks and the last w positions of the sequence
     const bool side = live && (p < a.sink || p >= keep_from);
@@ -426,8 +381,8 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t*
               reinterpret_cast<const uint32_t*>(k), reinterpret_cast<const uint32_t*>(v),
               slot, page_table, pt_stride, c.sink, c.window};
   const int pages = (max_seqlen + PAGE - 1) / PAGE + 1;
-  if (mx) hipLaunchKernelGGL(prefill_kernel<true>, dim3(pages, c.Hkv, nseq), dim3(256), 0, s, a, cu, start);
-  else hipLaunchKernelGGL(prefill16_kernel, dim3(pages * c.Hkv, nseq), dim3(128), 0, s, a, cu, start);
+  if (mx) hipLaunchKernelGGL(prefill16_kernel<true>, dim3(pages * c.Hkv, nseq), dim3(128), 0, s, a, cu, start);
+  else hipLaunchKernelGGL(prefill16_kernel<false>, dim3(pages * c.Hkv, nseq), dim3(128), 0, s, a, cu, start);
   return hipGetLastError();
 }
 
