@@ -506,14 +506,14 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
     const int D = qk_rows(d[t]);
     const int pos = PAGE * (j0 + t) + r16;
     const bool valid = (t < np) && (pos < main_end);
-    const float dk = f16_value(q.km[t] & 0xFFFFu), mk = f16_value(q.km[t] >> 16);
-    const float dv = f16_value(q.vm[t] & 0xFFFFu), mv = f16_value(q.vm[t] >> 16);
+    const float dk = f16_value(q.km[t] & 0xFFFFu);
     // q.k^ = s_q (delta * sum(qc*c) + m * sum(qc)); c_q carries s_q, the scale and log2(e)
-    const float z = valid ? __builtin_fmaf(dk, static_cast<float>(D), mk * S_q) * c_q : -INFINITY;
+    const float z = valid ? __builtin_fmaf(dk, static_cast<float>(D), mul_f16(S_q, q.km[t] >> 16)) * c_q : -INFINITY;
     zmax[t] = row16_max(z);
+    // (metadata of positions outside the region may be any bits: selected away)
     e[t] = valid ? exp2s(z - zmax[t]) : 0.0f;
-    u[t] = valid ? e[t] * dv : 0.0f;    // V scale folded into P
-    emv[t] = valid ? e[t] * mv : 0.0f;  // V offset applied after the dot
+    u[t] = valid ? mul_f16(e[t], q.vm[t] & 0xFFFFu) : 0.0f;  // V scale folded into P
+    emv[t] = valid ? mul_f16(e[t], q.vm[t] >> 16) : 0.0f;    // V offset applied after the dot
     umax[t] = __uint_as_float(row16_max_u32(__float_as_uint(u[t])));
     if (DEBUG && valid && a.dbg.qk) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + pos] = D;
   }

@@ -51,6 +51,13 @@ __device__ __forceinline__ float f16_value(uint32_t bits) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
 }
 
+// x times the FP16 value with bits h, rounded once (the FP32 product of x and
+// the exactly widened h), as an FMA with a +0 addend so that the compiler
+// folds the widening into one v_fma_mix_f32 (with -0 it would become a plain
+// multiply after a separate conversion).  The addend only turns a -0 product
+// into +0; every caller's result is the same for either zero.
+__device__ __forceinline__ float mul_f16(float x, uint32_t h) { return __builtin_fmaf(x, f16_value(h), 0.0f); }
+
 // Round a finite binary32 to bfloat16 (nearest, ties to even); value kept in FP32.
 __device__ __forceinline__ float round_bf16(float x) {
   uint32_t u = __float_as_uint(x);
@@ -383,10 +390,11 @@ constexpr float kC7 = static_cast<float>(kLn2 * kLn2 * kLn2 * kLn2 * kLn2 * kLn2
 
 __device__ __forceinline__ float exp2s(float y) {
   using namespace detail;
+  // below -125 (and for -inf) the polynomial runs on whatever y gives and
+  // the select returns 0
   const bool live = (y >= -125.0f);
-  const float yc = live ? y : 0.0f;
-  const float n = __builtin_rintf(yc);
-  const float f = yc - n;
+  const float n = __builtin_rintf(y);
+  const float f = y - n;
   float p = kC7;
   p = __builtin_fmaf(p, f, kC6);
   p = __builtin_fmaf(p, f, kC5);

@@ -381,8 +381,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int pos = PAGE * (ja + t) + slot16;
       valid[r] = FULL || (row_live && (t == 0 || has_b) && pos < me_row);
       const uint32_t km = kmeta[j4][i];
-      const float dk = f16_value(km & 0xFFFFu), mk = f16_value(km >> 16);
-      z[r] = valid[r] ? __builtin_fmaf(dk, static_cast<float>(d[r]), mk * S_q) * c_q : -INFINITY;
+      const float dk = f16_value(km & 0xFFFFu);
+      z[r] = valid[r] ? __builtin_fmaf(dk, static_cast<float>(d[r]), mul_f16(S_q, km >> 16)) * c_q : -INFINITY;
       if (DEBUG && valid[r] && a.dbg.qk) {
         const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + g * GQA + (n & 3);
         a.dbg.qk[bh * a.dbg.max_ctx + pos] = d[r];
@@ -399,10 +399,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int j4 = r >> 2, i = r & 3;
         e[r] = exp2s(z[r] - zmax[t]);
         const uint32_t vm = vmeta[j4][i];
-        const float dv = f16_value(vm & 0xFFFFu), mv = f16_value(vm >> 16);
-        u[r] = valid[r] ? e[r] * dv : 0.0f;
+        // (metadata of positions outside the region may be any bits: selected away)
+        u[r] = valid[r] ? mul_f16(e[r], vm & 0xFFFFu) : 0.0f;
         e_t[t] += valid[r] ? e[r] : 0.0f;
-        emv_t[t] += valid[r] ? e[r] * mv : 0.0f;
+        emv_t[t] = valid[r] ? __builtin_fmaf(e[r], f16_value(vm >> 16), emv_t[t]) : emv_t[t];
         um = fmaxf(um, u[r]);
       }
       umax[t] = partner_max(um);
