@@ -502,8 +502,10 @@ static void main_tile(const uint8_t *blk, int t_end, const int8_t qc[HD], int32_
     if (umax == 0.0f) {
       uc[t] = 0;
     } else {
+      /* a u_max below 127 / FLT_MAX makes inv infinite: a zero weight then
+       * gives 0 * inf = NaN, read as code 0, and every nonzero one 127 */
       float r = rintf(u[t] * inv);
-      if (r < 0.0f) r = 0.0f;
+      if (!(r >= 0.0f)) r = 0.0f;
       if (r > 127.0f) r = 127.0f;
       uc[t] = (int32_t)r;
     }

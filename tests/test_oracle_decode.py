@@ -8,6 +8,7 @@ import pytest
 import oracle
 from oracle import brute
 from synth import make_workload
+from tests import crafted
 from tests.wl import host_inputs, oracle_cache
 
 SCALE = 1.0 / math.sqrt(128)
@@ -201,3 +202,32 @@ def test_integer_accumulators_equal_fp64_sums(small):
                 want = float(dbg["qcodes"][b, h].astype(np.float64) @ kc[p % 16].astype(np.float64))
                 assert dbg["qk"][b, h, p] == want
                 assert abs(want) <= 128 * 127 * 15
+
+
+def test_p_codes_when_127_over_u_max_overflows():
+    """P-operand rule at its overflow corner: a tile whose heaviest position
+    has delta_v = 0 and whose other weights are near 2^-115 has u_max FP32
+    subnormal, so 127 / u_max is infinite.  Nonzero u saturate at 127, and
+    the zero weight's 0 * inf is read as code 0.  Position 0 carries all
+    but 2^-111 of the weight, so out is its dequantized value m_v = 1.5 and
+    lse its logit times ln 2."""
+    cache = oracle.Cache(2, 1, 1, sink=0, window=0)
+    cache.pages[0, 0] = crafted.tiny_weight_page()
+    q = crafted.unit_query(1, 4)
+    table = np.array([[0, 1]], np.int32)
+    out, lse, dbg = oracle.decode(cache, q, np.array([16], np.int32), np.array([0], np.int32), table, 4,
+                                  SCALE, debug=True)
+    assert (dbg["qsum"] == 127 * 128).all()
+    assert (dbg["pcode"][0, :, 0] == 0).all() and (dbg["pcode"][0, :, 1:16] == 127).all()
+    assert (dbg["pv"][0, :, 0] == 15 * 127 * crafted.TINY_PAGE_V[2]).all()
+    assert np.abs(out - crafted.TINY_PAGE_V[0]).max() < 1e-9
+    # z_0 = (0 * D + m_k * S_q) * c_q in FP32, c_q = s_q * scale_log2 (s_q = 2^-3.5 / 127)
+    s_q = np.float32(np.float32(2.0 ** -3.5) / np.float32(127.0))
+    c_q = np.float32(s_q * np.float32(SCALE * LOG2E))
+    z0 = np.float32(np.float32(crafted.TINY_PAGE_Z_GAP_M[0] * 127 * 128) * c_q)
+    assert np.abs(lse - math.log(2.0) * float(z0)).max() < 1e-5
+    # the one-token chunk at the last position sees the same tile
+    out2, lse2, dbg2 = oracle.prefill_attention(cache, q, np.array([0, 1], np.int32), np.array([15], np.int32),
+                                                np.array([0], np.int32), table, 4, SCALE, debug=True)
+    assert np.array_equal(dbg2["pcode"], dbg["pcode"]) and np.array_equal(dbg2["pv"], dbg["pv"])
+    assert np.abs(out2 - crafted.TINY_PAGE_V[0]).max() < 1e-9
