@@ -33,19 +33,21 @@ def _compare(tag, out, lse, dbg, r_out, r_lse, r_dbg):
     assert err <= OUT_TOL and lerr <= LSE_TOL, (tag, err, lerr)
 
 
-def test_p_codes_when_127_over_u_max_overflows():
-    """A tile whose heaviest position has delta_v = 0 and whose other weights
-    are near 2^-115: u_max is FP32-subnormal and 127 / u_max infinite, so the
-    nonzero u saturate at 127 and the zero weight gives code 0 (needs FP32
-    subnormals kept through the weights, the products and the division)."""
+@pytest.mark.parametrize("name", sorted(crafted.CASES))
+def test_crafted_page(name):
+    """u_max_subnormal: u_max FP32-subnormal and 127 / u_max infinite, so the
+    nonzero u saturate at 127 and the zero weight gives code 0 (FP32
+    subnormals kept through the weights, the products and the division);
+    weights_cut_off: weights below the exp2s cutoff are exactly 0;
+    u_max_zero: constant V vectors, every code 0."""
     dev = torch.device("cuda")
     ref = oracle.Cache(2, 1, 1, sink=0, window=0)
-    ref.pages[0, 0] = crafted.tiny_weight_page()
+    ref.pages[0, 0] = crafted.page(name)
     cache = kv4.Kv4Cache.zeros(2, 1, 1, dev, 0, 0)
     cache.pages.copy_(torch.from_numpy(ref.pages))
     q = crafted.unit_query(1, 4)
     table, ctx, slot = np.array([[0, 1]], np.int32), np.array([16], np.int32), np.array([0], np.int32)
-    print("[crafted] decode, one page, s = w = 0", flush=True)
+    print(f"[crafted] {name}: decode, one page, s = w = 0", flush=True)
     out, lse, dbg = kv4.decode_attention_debug(cache, bf(q, dev), i32(ctx, dev), i32(slot, dev),
                                                i32(table, dev), 32, SCALE)
     out2, lse2 = kv4.decode_attention(cache, bf(q, dev), i32(ctx, dev), i32(slot, dev), i32(table, dev), 32,
@@ -53,12 +55,11 @@ def test_p_codes_when_127_over_u_max_overflows():
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
     r_out, r_lse, r_dbg = oracle.decode(ref, q, ctx, slot, table, 4, SCALE, debug=True)
-    assert (r_dbg["pcode"][0, :, 0] == 0).all() and (r_dbg["pcode"][0, :, 1:16] == 127).all()
-    _compare("decode", out, lse, dbg, r_out, r_lse, r_dbg)
-    print("[crafted] re-prefill attention, one-token chunk at position 15", flush=True)
+    _compare(f"{name} decode", out, lse, dbg, r_out, r_lse, r_dbg)
+    print(f"[crafted] {name}: re-prefill attention, one-token chunk at position 15", flush=True)
     cu, start = np.array([0, 1], np.int32), np.array([15], np.int32)
     out, lse, dbg = kv4.prefill_attention_debug(cache, bf(q, dev), i32(cu, dev), i32(start, dev),
                                                 i32(slot, dev), i32(table, dev), 32, SCALE)
     torch.cuda.synchronize()
     r_out, r_lse, r_dbg = oracle.prefill_attention(ref, q, cu, start, slot, table, 4, SCALE, debug=True)
-    _compare("re-prefill", out, lse, dbg, r_out, r_lse, r_dbg)
+    _compare(f"{name} re-prefill", out, lse, dbg, r_out, r_lse, r_dbg)

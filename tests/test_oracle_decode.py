@@ -204,30 +204,69 @@ def test_integer_accumulators_equal_fp64_sums(small):
                 assert abs(want) <= 128 * 127 * 15
 
 
-def test_p_codes_when_127_over_u_max_overflows():
-    """P-operand rule at its overflow corner: a tile whose heaviest position
-    has delta_v = 0 and whose other weights are near 2^-115 has u_max FP32
-    subnormal, so 127 / u_max is infinite.  Nonzero u saturate at 127, and
-    the zero weight's 0 * inf is read as code 0.  Position 0 carries all
-    but 2^-111 of the weight, so out is its dequantized value m_v = 1.5 and
-    lse its logit times ln 2."""
+
+def _crafted_run(name):
     cache = oracle.Cache(2, 1, 1, sink=0, window=0)
-    cache.pages[0, 0] = crafted.tiny_weight_page()
+    cache.pages[0, 0] = crafted.page(name)
     q = crafted.unit_query(1, 4)
     table = np.array([[0, 1]], np.int32)
-    out, lse, dbg = oracle.decode(cache, q, np.array([16], np.int32), np.array([0], np.int32), table, 4,
-                                  SCALE, debug=True)
+    dec = oracle.decode(cache, q, np.array([16], np.int32), np.array([0], np.int32), table, 4, SCALE, debug=True)
+    # the one-token chunk at the last position sees the same tile
+    pre = oracle.prefill_attention(cache, q, np.array([0, 1], np.int32), np.array([15], np.int32),
+                                   np.array([0], np.int32), table, 4, SCALE, debug=True)
+    for key in ("qcodes", "qsum", "qk", "pcode", "pv"):
+        assert np.array_equal(dec[2][key], pre[2][key]), key
+    assert np.array_equal(dec[0], pre[0]) or np.abs(dec[0] - pre[0]).max() < 1e-12
+    return dec
+
+
+def _logit_units():
+    """Base-2 logit of one unit of m_k for the unit query: S_q * c_q, with
+    c_q = s_q * scale_log2 in FP32 (s_q = 2^-3.5 / 127)."""
+    s_q = np.float32(np.float32(2.0 ** -3.5) / np.float32(127.0))
+    return np.float32(s_q * np.float32(SCALE * LOG2E)), 127 * 128
+
+
+def test_p_codes_when_127_over_u_max_overflows():
+    """P-operand rule at its overflow corner: u_max FP32-subnormal, so
+    127 / u_max is infinite; the nonzero u saturate at 127 and the zero
+    weight's 0 * inf is read as code 0.  Position 0 carries all but 2^-111 of
+    the weight, so out is its dequantized value m_v and lse its logit times
+    ln 2."""
+    mk0, _, _, _, mv0, _, code = crafted.CASES["u_max_subnormal"]
+    out, lse, dbg = _crafted_run("u_max_subnormal")
     assert (dbg["qsum"] == 127 * 128).all()
     assert (dbg["pcode"][0, :, 0] == 0).all() and (dbg["pcode"][0, :, 1:16] == 127).all()
-    assert (dbg["pv"][0, :, 0] == 15 * 127 * crafted.TINY_PAGE_V[2]).all()
-    assert np.abs(out - crafted.TINY_PAGE_V[0]).max() < 1e-9
-    # z_0 = (0 * D + m_k * S_q) * c_q in FP32, c_q = s_q * scale_log2 (s_q = 2^-3.5 / 127)
-    s_q = np.float32(np.float32(2.0 ** -3.5) / np.float32(127.0))
-    c_q = np.float32(s_q * np.float32(SCALE * LOG2E))
-    z0 = np.float32(np.float32(crafted.TINY_PAGE_Z_GAP_M[0] * 127 * 128) * c_q)
+    assert (dbg["pv"][0, :, 0] == 15 * 127 * code).all()
+    assert np.abs(out - mv0).max() < 1e-9
+    c_q, S = _logit_units()
+    z0 = np.float32(np.float32(mk0 * S) * c_q)
     assert np.abs(lse - math.log(2.0) * float(z0)).max() < 1e-5
-    # the one-token chunk at the last position sees the same tile
-    out2, lse2, dbg2 = oracle.prefill_attention(cache, q, np.array([0, 1], np.int32), np.array([15], np.int32),
-                                                np.array([0], np.int32), table, 4, SCALE, debug=True)
-    assert np.array_equal(dbg2["pcode"], dbg["pcode"]) and np.array_equal(dbg2["pv"], dbg["pv"])
-    assert np.abs(out2 - crafted.TINY_PAGE_V[0]).max() < 1e-9
+
+
+def test_p_codes_when_weights_fall_below_the_exp2s_cutoff():
+    """Positions 144 base-2 units below the maximum get e = 0 exactly (exp2s
+    returns 0 below -125): codes 127 at position 0 and 0 elsewhere, and out
+    is position 0's dequantized value delta_v * code + m_v."""
+    mk0, _, dv0, _, mv0, _, code = crafted.CASES["weights_cut_off"]
+    out, lse, dbg = _crafted_run("weights_cut_off")
+    assert (dbg["pcode"][0, :, 0] == 127).all() and (dbg["pcode"][0, :, 1:16] == 0).all()
+    assert (dbg["pv"][0, :, 0] == 127 * code).all()
+    assert np.abs(out - (dv0 * code + mv0)).max() < 1e-9
+    c_q, S = _logit_units()
+    assert np.abs(lse - math.log(2.0) * float(np.float32(np.float32(mk0 * S) * c_q))).max() < 1e-5
+
+
+def test_p_codes_when_every_v_vector_is_constant():
+    """delta_v = 0 at every position: u_max = 0, every code 0, PV = 0, and
+    out is the softmax-weighted mean of the offsets m_v (weights 2^(z - z_max)
+    from the hand-computed logits)."""
+    mk0, mk1, _, _, mv0, mv1, _ = crafted.CASES["u_max_zero"]
+    out, lse, dbg = _crafted_run("u_max_zero")
+    assert (dbg["pcode"][0, :, :16] == 0).all() and (dbg["pv"][0, :, 0] == 0).all()
+    c_q, S = _logit_units()
+    z0, z1 = (float(np.float32(np.float32(m * S) * c_q)) for m in (mk0, mk1))
+    w = 2.0 ** (z1 - z0)
+    want = (mv0 + 15 * w * mv1) / (1 + 15 * w)
+    assert np.abs(out - want).max() < 1e-6
+    assert np.abs(lse - math.log(2.0) * (z0 + math.log2(1 + 15 * w))).max() < 1e-5
