@@ -438,7 +438,8 @@ __device__ __forceinline__ int pcode_slot(int t) { return 8 * (t >> 3) + 4 * (t 
 
 // Per-wave LDS staging slot of one quad (4 pages of one segment):
 //   [0, 4096)     K codes, tile t at 1024 t + 16 lane
-//   [4096, 8192)  V codes, channel block s2 at 4096 + 1024 s2 + 16 lane
+//   [4096, 8192)  V codes, tile t at 4096 + 1024 t + 16 lane (lane (r16, g):
+//                 the channel pair 4 r16 + g, i.e. channels 8 r16 + 2 g, + 1)
 //   [8192, 8704)  metadata, page t at 8192 + 128 t: 16 x {delta, m} K, then V
 // followed by 256 B where the P operand is assembled and 512 B where the
 // query codes of a group are rearranged into the MFMA operand order.
@@ -450,19 +451,17 @@ struct QuadRegs {
 };
 
 // Issue the direct-to-LDS loads of one quad.  Tile t reads physical page
-// blk[t]; lane (r16, grp) fetches K bytes 64 r16 + 16 grp of every tile, and V
-// bytes 1024 + 16(16 s2 + r16) of tile grp (the k-group of the PV MFMA).
+// blk[t]; lane (r16, grp) fetches bytes 64 r16 + 16 grp of the tile's K codes
+// and of its V codes (1 KB contiguous per instruction for both).
 __device__ __forceinline__ void quad_to_lds(uint8_t* slot, const gptr blk[4], int lane, int r16,
                                             int grp) {
   const int koff = 64 * r16 + 16 * grp;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
     __builtin_amdgcn_global_load_lds(blk[t] + koff, (lptr)(slot + kSlotK + 1024 * t), 16, 0, 0);
-  const gptr vb = grp == 0 ? blk[0] : grp == 1 ? blk[1] : grp == 2 ? blk[2] : blk[3];
 #pragma unroll
-  for (int s2 = 0; s2 < 4; ++s2)
-    __builtin_amdgcn_global_load_lds(vb + OFF_VCODE + 16 * (16 * s2 + r16),
-                                     (lptr)(slot + kSlotV + 1024 * s2), 16, 0, 0);
+  for (int t = 0; t < 4; ++t)
+    __builtin_amdgcn_global_load_lds(blk[t] + OFF_VCODE + koff, (lptr)(slot + kSlotV + 1024 * t), 16, 0, 0);
   if (lane < 32) {  // 4 pages x 128 B of metadata
     const int t = lane >> 3;
     const gptr mb = t == 0 ? blk[0] : t == 1 ? blk[1] : t == 2 ? blk[2] : blk[3];
@@ -474,7 +473,8 @@ __device__ __forceinline__ void quad_from_lds(QuadRegs& q, const uint8_t* slot, 
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     q.kq[t] = *reinterpret_cast<const uint4*>(slot + kSlotK + 1024 * t + 16 * lane);
-    q.vq[t] = *reinterpret_cast<const uint4*>(slot + kSlotV + 1024 * t + 16 * lane);
+    // channel pair 4 r16 + t of tile grp (the k-group of the PV MFMA): channels 8 r16 + 2 t, + 1
+    q.vq[t] = *reinterpret_cast<const uint4*>(slot + kSlotV + 1024 * (lane >> 4) + 256 * t + 16 * r16);
     q.km[t] = *reinterpret_cast<const uint32_t*>(slot + kSlotMeta + 128 * t + 4 * r16);
     q.vm[t] = *reinterpret_cast<const uint32_t*>(slot + kSlotMeta + 128 * t + 64 + 4 * r16);
   }
@@ -563,7 +563,7 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
     for (int e2 = 0; e2 < 2; ++e2) {
       const v4i bv = e2 == 0 ? nib_positions(q.vq[s2].x, q.vq[s2].y) : nib_positions(q.vq[s2].z, q.vq[s2].w);
       const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, bv, v4i{0, 0, 0, 0}, 0, 0, 0);
-      // lane: head grp, channel 2(16 s2 + r16) + e2, tile v in register v
+      // lane: head grp, channel 8 r16 + 2 s2 + e2, tile v in register v
       const int o = 2 * s2 + e2;
       float x = st.O[o];
       x = __builtin_fmaf(wsu[0], static_cast<float>(acc[0]), x);
@@ -572,7 +572,7 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
       x = __builtin_fmaf(wsu[3], static_cast<float>(acc[3]), x);
       st.O[o] = x;
       if (DEBUG && a.dbg.pv) {
-        const int ch = 2 * (16 * s2 + r16) + e2;
+        const int ch = 8 * r16 + 2 * s2 + e2;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           if (t < np) a.dbg.pv[((qb + grp) * a.dbg.max_pages + (j0 + t)) * HD + ch] = acc[t];
@@ -622,7 +622,7 @@ struct Kv4Format {
     compute_quad<DEBUG>(a, st, q, np, qa0, qa1, c_q, S_q, j0, main_end, qb, slot + kSlotP, r16, grp,
                         pslot);
   }
-  // A = O + sum(w e m_v); lane (head grp, r16) holds channels 2(16 s2 + r16) + e2 in A[2 s2 + e2]
+  // A = O + sum(w e m_v); lane (head grp, r16) holds channels 8 r16 .. 8 r16 + 7 in A[0..7]
   __device__ static void finish(const State& st, float A[8], float& Z, float& L) {
     const float Mh = row16_sum(st.Ms);
     L = row16_sum(st.Ls);
@@ -632,10 +632,9 @@ struct Kv4Format {
   }
   // P0: the 4 heads' partials of the slot, kPart floats apart; this lane's head is grp
   __device__ static void store(float* P0, const float A[8], int r16, int grp) {
-    float* P = P0 + grp * kPart;
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
-      *reinterpret_cast<float2*>(P + 2 * (16 * s2 + r16)) = make_float2(A[2 * s2], A[2 * s2 + 1]);
+    float* P = P0 + grp * kPart + 8 * r16;  // 16-byte aligned: kPart * 4 = 528 = 16 * 33
+    *reinterpret_cast<float4*>(P) = make_float4(A[0], A[1], A[2], A[3]);
+    *reinterpret_cast<float4*>(P + 4) = make_float4(A[4], A[5], A[6], A[7]);
   }
 };
 
