@@ -3,6 +3,7 @@
 // same work decomposition as the KV4 main region so the two are timed on equal
 // terms: a plan of page prefix sums, equal contiguous page chunks per wave,
 // QK and PV on BF16 MFMA with FP32 accumulation, and an exact log-sum-exp merge.
+// Its page loads are non-temporal like the KV4 kernel's (each page is read once).
 //
 // Pool layout bf16 [num_pages][Hkv][2][16][128]: per (page, kv-head) the K
 // block is token-major [16 positions][128 channels] and the V block is
@@ -121,13 +122,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          kb[t][m] = *reinterpret_cast<const v8bf*>(blk[t] + r16 * HD + 32 * m + 8 * grp);
+          kb[t][m] = __builtin_nontemporal_load(reinterpret_cast<const v8bf*>(blk[t] + r16 * HD + 32 * m + 8 * grp));
       // V: lane group grp covers positions 8grp..8grp+7 of the page pair
       const uint16_t* vblk = (grp < 2 ? blk[0] : blk[1]) + PAGE * HD + 8 * (grp & 1);
       v8bf vb[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        vb[s] = *reinterpret_cast<const v8bf*>(vblk + (16 * s + r16) * PAGE);
+        vb[s] = __builtin_nontemporal_load(reinterpret_cast<const v8bf*>(vblk + (16 * s + r16) * PAGE));
 
       float z[2];
 #pragma unroll

@@ -239,9 +239,9 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
     sk[k] = 0.0f;
     if (rg < SIDE_ROWS / 16 && 16 * rg < nrows) {
       const gptr krow = side + (16 * rg + r16) * 2 * HD;
-      kop[k][0] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 16 * grp);
-      kop[k][1] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 64 + 16 * grp);
-      sk[k] = f16_value(scales[2 * (16 * rg + r16)]);
+      kop[k][0] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 16 * grp));
+      kop[k][1] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 64 + 16 * grp));
+      sk[k] = f16_value(__builtin_nontemporal_load(scales + 2 * (16 * rg + r16)));
     }
   }
   // V codes of this wave's PV rows
@@ -250,7 +250,7 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
 #pragma unroll
   for (int i = 0; i < kRowsPerWave / 2; ++i) {
     const int r = kRowsPerWave * wave + rp + 2 * i;
-    vop[i] = r < nrows ? *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(side + (2 * r + 1) * HD + 4 * cg) : 0u;
+    vop[i] = r < nrows ? __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(side + (2 * r + 1) * HD + 4 * cg)) : 0u;
   }
   if (tid < SIDE_ROWS)
     ssv[tid] = side_position(tid, L, E, a.sink, a.window) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
@@ -444,6 +444,10 @@ __device__ __forceinline__ int pcode_slot(int t) { return 8 * (t >> 3) + 4 * (t 
 // followed by 256 B where the P operand is assembled and 512 B where the
 // query codes of a group are rearranged into the MFMA operand order.
 constexpr int kSlotK = 0, kSlotV = 4096, kSlotMeta = 8192, kSlotP = 8704, kSlotQ = 8960, kSlotBytes = 9472;
+// Cache policy of the page loads: non-temporal.  Every page block of a step is
+// read once, so the loads stream past the caches instead of allocating in
+// them (about 10% faster for the whole main kernel than default loads).
+constexpr int kNT = 2;
 
 struct QuadRegs {
   uint4 kq[4], vq[4];
@@ -458,14 +462,14 @@ __device__ __forceinline__ void quad_to_lds(uint8_t* slot, const gptr blk[4], in
   const int koff = 64 * r16 + 16 * grp;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    __builtin_amdgcn_global_load_lds(blk[t] + koff, (lptr)(slot + kSlotK + 1024 * t), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(blk[t] + koff, (lptr)(slot + kSlotK + 1024 * t), 16, 0, kNT);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    __builtin_amdgcn_global_load_lds(blk[t] + OFF_VCODE + koff, (lptr)(slot + kSlotV + 1024 * t), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(blk[t] + OFF_VCODE + koff, (lptr)(slot + kSlotV + 1024 * t), 16, 0, kNT);
   if (lane < 32) {  // 4 pages x 128 B of metadata
     const int t = lane >> 3;
     const gptr mb = t == 0 ? blk[0] : t == 1 ? blk[1] : t == 2 ? blk[2] : blk[3];
-    __builtin_amdgcn_global_load_lds(mb + OFF_KMETA + 16 * (lane & 7), (lptr)(slot + kSlotMeta), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(mb + OFF_KMETA + 16 * (lane & 7), (lptr)(slot + kSlotMeta), 16, 0, kNT);
   }
 }
 
@@ -781,16 +785,16 @@ struct Kv8Format {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         __builtin_amdgcn_global_load_lds(blk[t] + HD * r16 + 64 * h + 16 * grp,
-                                         (lptr)(slot + k8K + 2048 * t + 1024 * h), 16, 0, 0);
+                                         (lptr)(slot + k8K + 2048 * t + 1024 * h), 16, 0, kNT);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         __builtin_amdgcn_global_load_lds(blk[t] + KV8_OFF_V + 1024 * i + 16 * lane,
-                                         (lptr)(slot + k8V + 2048 * t + 1024 * i), 16, 0, 0);
+                                         (lptr)(slot + k8V + 2048 * t + 1024 * i), 16, 0, kNT);
     if (lane < 8)  // 2 pages x 64 B of scales
       __builtin_amdgcn_global_load_lds((lane < 4 ? blk[0] : blk[1]) + KV8_OFF_SK + 16 * (lane & 3),
-                                       (lptr)(slot + k8S), 16, 0, 0);
+                                       (lptr)(slot + k8S), 16, 0, kNT);
   }
   __device__ static void from_lds(Regs& r, const uint8_t* slot, int lane, int r16, int grp) {
 #pragma unroll
@@ -964,12 +968,12 @@ struct MxFormat {
   __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      __builtin_amdgcn_global_load_lds(blk[t] + 64 * r16 + 16 * grp, (lptr)(slot + kmxK + 1024 * t), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(blk[t] + OFF_VCODE + 16 * lane, (lptr)(slot + kmxV + 1024 * t), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(blk[t] + 64 * r16 + 16 * grp, (lptr)(slot + kmxK + 1024 * t), 16, 0, kNT);
+      __builtin_amdgcn_global_load_lds(blk[t] + OFF_VCODE + 16 * lane, (lptr)(slot + kmxV + 1024 * t), 16, 0, kNT);
     }
     if (lane < 16)  // 2 pages x 128 B of scales
       __builtin_amdgcn_global_load_lds((lane < 8 ? blk[0] : blk[1]) + OFF_KMETA + 16 * (lane & 7),
-                                       (lptr)(slot + kmxS), 16, 0, 0);
+                                       (lptr)(slot + kmxS), 16, 0, kNT);
   }
   __device__ static void from_lds(Regs& r, const uint8_t* slot, int lane, int r16, int grp) {
     (void)lane;
