@@ -513,7 +513,7 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
     const float dk = f16_value(q.km[t] & 0xFFFFu);
     // q.k^ = s_q (delta * sum(qc*c) + m * sum(qc)); c_q carries s_q, the scale and log2(e)
     const float z = valid ? __builtin_fmaf(dk, static_cast<float>(D), mul_f16(S_q, q.km[t] >> 16)) * c_q : -INFINITY;
-    zmax[t] = row16_max(z);
+    zmax[t] = row16_max_ord(z);
     // (metadata of positions outside the region may be any bits: selected away)
     e[t] = valid ? exp2s(z - zmax[t]) : 0.0f;
     u[t] = valid ? mul_f16(e[t], q.vm[t] & 0xFFFFu) : 0.0f;  // V scale folded into P

@@ -99,6 +99,20 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 // Same all-reduce for non-negative floats, on their bit patterns (which order
 // like unsigned integers), so each step is one fused DPP v_max_u32.
+// row16_max for finite or -inf values on order-preserving integer keys (the
+// bits for x >= +0, the bits with the low 31 flipped below, compared as
+// signed), so that each stage is one DPP max; the same result except that a
+// zero maximum is always +0.
+__device__ __forceinline__ float row16_max_ord(float v) {
+  int k = __float_as_int(v);
+  k ^= (k >> 31) & 0x7FFFFFFF;
+  k = max(k, __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, true));
+  k = max(k, __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, true));
+  k = max(k, __builtin_amdgcn_mov_dpp(k, 0x141, 0xF, 0xF, true));
+  k = max(k, __builtin_amdgcn_mov_dpp(k, 0x140, 0xF, 0xF, true));
+  k ^= (k >> 31) & 0x7FFFFFFF;
+  return __int_as_float(k);
+}
 __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true)));
   v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true)));
