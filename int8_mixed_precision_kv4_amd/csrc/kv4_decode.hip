@@ -417,20 +417,24 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
 // ------------------------------------------------------------------ main --
 
 __device__ __forceinline__ uint32_t lo_nibbles(uint32_t x) { return x & 0x0F0F0F0Fu; }
-__device__ __forceinline__ uint32_t hi_nibbles(uint32_t x) { return (x >> 4) & 0x0F0F0F0Fu; }
 __device__ __forceinline__ v4i nib_lo(uint4 x) {
   return v4i{static_cast<int>(lo_nibbles(x.x)), static_cast<int>(lo_nibbles(x.y)),
              static_cast<int>(lo_nibbles(x.z)), static_cast<int>(lo_nibbles(x.w))};
 }
+// high nibbles of two dwords with one 64-bit shift
+__device__ __forceinline__ uint64_t hi_nibbles64(uint32_t a, uint32_t b) {
+  return ((static_cast<uint64_t>(b) << 32 | a) >> 4) & 0x0F0F0F0F0F0F0F0Full;
+}
 __device__ __forceinline__ v4i nib_hi(uint4 x) {
-  return v4i{static_cast<int>(hi_nibbles(x.x)), static_cast<int>(hi_nibbles(x.y)),
-             static_cast<int>(hi_nibbles(x.z)), static_cast<int>(hi_nibbles(x.w))};
+  const uint64_t h0 = hi_nibbles64(x.x, x.y), h1 = hi_nibbles64(x.z, x.w);
+  return v4i{static_cast<int>(h0), static_cast<int>(h0 >> 32), static_cast<int>(h1), static_cast<int>(h1 >> 32)};
 }
 // 16 positions of one channel (8 nibble bytes) -> 16 INT8 operand bytes; byte
 // i of the result holds position 8(i/8) + 2(i%4) + (i/4)%2.
 __device__ __forceinline__ v4i nib_positions(uint32_t lo8, uint32_t hi8) {
-  return v4i{static_cast<int>(lo_nibbles(lo8)), static_cast<int>(hi_nibbles(lo8)),
-             static_cast<int>(lo_nibbles(hi8)), static_cast<int>(hi_nibbles(hi8))};
+  const uint64_t h = hi_nibbles64(lo8, hi8);
+  return v4i{static_cast<int>(lo_nibbles(lo8)), static_cast<int>(h), static_cast<int>(lo_nibbles(hi8)),
+             static_cast<int>(h >> 32)};
 }
 // inverse of that byte order
 __device__ __forceinline__ int pcode_slot(int t) { return 8 * (t >> 3) + 4 * (t & 1) + ((t & 7) >> 1); }
