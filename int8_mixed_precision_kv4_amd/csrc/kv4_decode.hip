@@ -1095,6 +1095,10 @@ __device__ __forceinline__ int find_seq(const PlanView& r, int p, int lo, int la
 }
 
 // One quad of the wave's page stream.
+struct PageIds {  // physical pages of a unit's tiles (wave-uniform)
+  int id[4];
+};
+
 struct QuadDesc {
   int b, g, j0, np, slot, main_end;
   bool first, last;    // first / last quad of its piece
@@ -1185,9 +1189,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
   };
 
   // Stage 1: describe the next quad of the chunk and fetch its page-table
-  // entries (lanes 0..3, one per tile) into pt; false when the chunk is done.
-  // Runs two quads ahead of the compute.
-  auto plan_quad = [&](QuadDesc& d, int& pt) -> bool {
+  // entries (scalar loads, so that they do not count with the page loads in
+  // vmcnt) into pt; false when the chunk is done.  Runs two quads ahead of the
+  // compute.
+  auto plan_quad = [&](QuadDesc& d, PageIds& pt) -> bool {
     if (ip >= iend) return false;
     if (ip >= seg_end || ip == chunk0) {  // entering a segment: locate it once
       while (plan_at(pv, ib + 1) <= ip) ++ib;
@@ -1208,19 +1213,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
     d.opens = ip == seg0;
     d.closes = stop == seg_end;
     const int32_t* ptrow = a.page_table + static_cast<size_t>(ib) * a.pt_stride;
-    pt = ptrow[d.j0 + min(lane & 3, d.np - 1)];
+#pragma unroll
+    for (int t = 0; t < F::kUnit; ++t) pt.id[t] = ld_const(ptrow + d.j0 + min(t, d.np - 1));
     if (d.first)  // BF16 query of head grp, channels 8 r16 .. 8 r16 + 7
       raw2 = reinterpret_cast<const uint4*>(a.q + ((static_cast<size_t>(ib) * a.Hq + seg_g * GQA + grp) * HD) / 2)[r16];
     ip += d.np;
     return true;
   };
   // Stage 2: start the page loads of a described quad into the LDS slot.
-  auto issue_quad = [&](QuadDesc& d, int pt) {
+  auto issue_quad = [&](QuadDesc& d, const PageIds& pt) {
     const gptr gbase = (gptr)a.pages + static_cast<size_t>(d.g) * F::kBlock;
     gptr blk[F::kUnit];
 #pragma unroll
     for (int t = 0; t < F::kUnit; ++t)
-      blk[t] = gbase + static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(pt, t))) * pstride;
+      blk[t] = gbase + static_cast<size_t>(static_cast<uint32_t>(pt.id[t])) * pstride;
     F::to_lds(slot, blk, lane, r16, grp);
     if (d.first) {
       const int L = ld_const(a.ctx + d.b);
@@ -1232,7 +1238,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
   // and the page-table entries of quad i+2 are fetched; pieces and ranges
   // follow one another without a gap.
   QuadDesc d1, d2;  // quads i+1 (in flight) and i+2 (described)
-  int pt1 = 0, pt2 = 0;
+  PageIds pt1{}, pt2{};
   bool have1 = plan_quad(d1, pt1);
   raw1 = raw2;
   if (have1) {
