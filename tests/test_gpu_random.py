@@ -57,7 +57,7 @@ def _compare(tag, out, lse, dbg, r_out, r_lse, r_dbg):
     assert err <= OUT_TOL and lerr <= LSE_TOL, (tag, err, lerr)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", list(range(8)) + list(range(22, 34)))
 def test_random_decode(seed):
     wl, sink, window = _random_workload(seed)
     tag = f"decode seed {seed} B={wl.B} Hkv={wl.Hkv} s={sink} w={window} ctx max {int(wl.ctx.max())}"
@@ -73,7 +73,7 @@ def test_random_decode(seed):
     _compare(tag, out, lse, dbg, r_out, r_lse, r_dbg)
 
 
-@pytest.mark.parametrize("seed", range(8, 14))
+@pytest.mark.parametrize("seed", list(range(8, 14)) + list(range(34, 42)))
 def test_random_fused_step(seed):
     """This step's append inside the decode launch, from a cache holding
     [0, ctx - 1): pages, side rows, out and lse against the oracle's append
@@ -105,7 +105,7 @@ def test_random_fused_step(seed):
     assert err <= OUT_TOL and lerr <= LSE_TOL, (tag, err, lerr)
 
 
-@pytest.mark.parametrize("seed", range(14, 22))
+@pytest.mark.parametrize("seed", list(range(14, 22)) + list(range(42, 50)))
 def test_random_prefill_attention(seed):
     """Chunks of random length at the end of random prefixes (several per
     call), random budget and slots."""
