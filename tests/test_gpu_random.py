@@ -1,8 +1,8 @@
 """Seeded random cases on the GPU against the oracle: random batch sizes, head
 counts, context lengths (many on a region boundary), protection budgets, slot
 permutations and page pools with free pages, for the decode step (plain, and
-with this step's append in the same launch) and for re-prefill attention.
-Bar: page blocks and side rows, query codes and sums, int32 QK, P codes and
+with this step's append in the same launch), for re-prefill attention, and
+for the MXFP4 and KV8 formats.  Bar: page blocks and side rows, query codes and sums, int32 QK, P codes and
 int32 PV bit-exact; out within 2e-3 max-abs, lse within 1e-4."""
 import numpy as np
 import pytest
@@ -134,3 +134,38 @@ def test_random_prefill_attention(seed):
     r_out, r_lse, r_dbg = oracle.prefill_attention(ref, q, cu, start, wl.slots, wl.page_table, wl.Hq, SCALE,
                                                    debug=True)
     _compare(tag, out, lse, dbg, r_out, r_lse, r_dbg)
+
+
+@pytest.mark.parametrize("seed", range(50, 58))
+def test_random_mx(seed):
+    """MXFP4 main region with the random budget: page blocks and side rows
+    bit-exact, out and lse within the bar."""
+    from tests.test_gpu_mx import _Case, _oracle_mx
+    wl, sink, window = _random_workload(seed)
+    tag = f"mxfp4 seed {seed} B={wl.B} Hkv={wl.Hkv} s={sink} w={window}"
+    _say(f"[random] {tag}")
+    dev = torch.device("cuda")
+    hi = host_inputs(wl)
+    ref = _oracle_mx(wl, hi, sink, window)
+    case = _Case(wl, hi, sink, window, dev)
+    out, lse = kv4.mx_decode_attention(case.cache, bf(hi.q, dev), i32(wl.ctx, dev), case.slots, case.table,
+                                       wl.max_ctx, SCALE)
+    torch.cuda.synchronize()
+    assert_cache_equal(case, ref)
+    r_out, r_lse = oracle.mx_decode(ref, hi.q, wl.ctx.astype(np.int32), wl.slots, wl.page_table, wl.Hq, SCALE)
+    err = float(np.abs(out.cpu().numpy() - r_out).max())
+    lerr = float(np.abs(lse.cpu().numpy() - r_lse).max())
+    _say(f"[random] {tag}: out {err:.2e} lse {lerr:.2e}")
+    assert err <= OUT_TOL and lerr <= LSE_TOL, (tag, err, lerr)
+
+
+@pytest.mark.parametrize("seed", range(58, 66))
+def test_random_kv8(seed):
+    """KV8 everywhere on the random shapes (no budget): pool bytes, query
+    codes and QK bit-exact, out and lse within the bar."""
+    from tests.test_gpu_kv8 import _check
+    wl, _, _ = _random_workload(seed)
+    tag = f"kv8 seed {seed} B={wl.B} Hkv={wl.Hkv} ctx max {int(wl.ctx.max())}"
+    _say(f"[random] {tag}")
+    err, lerr = _check(wl, host_inputs(wl), torch.device("cuda"))
+    _say(f"[random] {tag}: out {err:.2e} lse {lerr:.2e}")
