@@ -469,8 +469,8 @@ def main():
                     help="skip the protection-budget variants (run last; they rebuild the side rows)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sequences and kv-heads shard with no exchange; see DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the path has no multi-GPU part "
+              "(sequences and kv-heads shard with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
