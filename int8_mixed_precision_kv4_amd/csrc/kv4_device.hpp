@@ -214,12 +214,14 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 // The stride order fixes the FP32 sum tree of every output.
 constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;
 
+// One butterfly stage across lanes: the lower lane of a pair keeps x + p, the
+// upper one p - x, both written as p + (+-x) with the sign flipped by an xor
+// (exact), so that the partner's value can enter the add as a DPP operand.
 template <int H>
 __device__ __forceinline__ void fwht_lane_stage(float& x0, float& x1) {
-  const float p0 = xor_lane_f<H>(x0), p1 = xor_lane_f<H>(x1);
-  const bool upper = (threadIdx.x & H) != 0;
-  x0 = upper ? (p0 - x0) : (x0 + p0);
-  x1 = upper ? (p1 - x1) : (x1 + p1);
+  const uint32_t flip = (threadIdx.x & H) ? 0x80000000u : 0u;
+  x0 = xor_lane_f<H>(x0) + __uint_as_float(__float_as_uint(x0) ^ flip);
+  x1 = xor_lane_f<H>(x1) + __uint_as_float(__float_as_uint(x1) ^ flip);
 }
 __device__ __forceinline__ void fwht128_wave(float& x0, float& x1) {
   const float a = x0 + x1, b = x0 - x1;
@@ -249,14 +251,11 @@ __device__ __forceinline__ void fwht128_row16(float x[8], int r16) {
         x[j] = u + v;
         x[j + h] = u - v;
       }
-  auto stage = [&](auto m_tag) {
+  auto stage = [&](auto m_tag) {  // p + (+-x), as in fwht_lane_stage
     constexpr int M = decltype(m_tag)::value;
-    const bool upper = (r16 & M) != 0;
+    const uint32_t flip = (r16 & M) ? 0x80000000u : 0u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = xor_lane_f<M>(x[j]);
-      x[j] = upper ? (p - x[j]) : (x[j] + p);
-    }
+    for (int j = 0; j < 8; ++j) x[j] = xor_lane_f<M>(x[j]) + __uint_as_float(__float_as_uint(x[j]) ^ flip);
   };
   stage(std::integral_constant<int, 1>{});
   stage(std::integral_constant<int, 2>{});
