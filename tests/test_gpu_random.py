@@ -169,3 +169,42 @@ def test_random_kv8(seed):
     _say(f"[random] {tag}")
     err, lerr = _check(wl, host_inputs(wl), torch.device("cuda"))
     _say(f"[random] {tag}: out {err:.2e} lse {lerr:.2e}")
+
+
+def test_large_batch_short_contexts():
+    """Many sequences (3000, above the 256 the in-kernel plan covers, so the
+    plan kernel runs) with contexts drawn half from the region edges and half
+    from [1, 400]: the decode and the one-launch step against the oracle."""
+    rng = np.random.default_rng(4242)
+    B = 3000
+    ctx = np.where(rng.random(B) < 0.5, rng.choice(EDGES, B), rng.integers(1, 400, B))
+    wl = make_workload(0, seed=4243, ctx=ctx, Hq=4, Hkv=1, pool_slack=8)
+    tag = f"large batch B={wl.B} ctx max {int(wl.ctx.max())}"
+    _say(f"[random] {tag}")
+    hi = host_inputs(wl)
+    ref = oracle_cache(wl, hi)
+    case = GpuCase(wl, hi)
+    out, lse, dbg = case.decode(debug=True)
+    torch.cuda.synchronize()
+    assert_cache_equal(case, ref)
+    r_out, r_lse, r_dbg = oracle.decode(ref, hi.q, wl.ctx.astype(np.int32), wl.slots, wl.page_table, wl.Hq,
+                                        SCALE, debug=True)
+    _compare(tag, out, lse, dbg, r_out, r_lse, r_dbg)
+    # the one-launch step from a cache holding [0, ctx - 1)
+    dev = torch.device("cuda")
+    cache = kv4.Kv4Cache.zeros(wl.num_pages, wl.Hkv, wl.max_slots, dev)
+    table, slots = i32(wl.page_table, dev), i32(wl.slots, dev)
+    lead = wl.ctx - 1
+    k, v, cu = hi.prefix(lead)
+    if len(k):
+        kv4.prefill_quantize(cache, bf(k, dev), bf(v, dev), i32(cu, dev), i32(np.zeros(wl.B), dev), slots, table,
+                             int(max(1, lead.max())))
+    ka, va = hi.at(lead)
+    out2, lse2 = kv4.append_decode_attention(cache, bf(ka, dev), bf(va, dev), i32(lead, dev), bf(hi.q, dev),
+                                             i32(wl.ctx, dev), slots, table, wl.max_ctx, SCALE)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.pages.cpu().numpy(), ref.pages)
+    err = float(np.abs(out2.cpu().numpy() - r_out).max())
+    lerr = float(np.abs(lse2.cpu().numpy() - r_lse).max())
+    _say(f"[random] {tag} one launch: out {err:.2e} lse {lerr:.2e}")
+    assert err <= OUT_TOL and lerr <= LSE_TOL
