@@ -19,7 +19,8 @@
  *   - All array pointers are DEVICE pointers (HIP global memory) unless a
  *     comment says otherwise; descriptors and debug structs live on the host.
  *   - The caller owns all memory.  The library never allocates, frees or
- *     synchronizes, keeps no state between calls, and enqueues its work on the
+ *     synchronizes, keeps no state between calls (apart from the fixed scratch
+ *     array of kv4_append_decode_attention_noalloc), and enqueues its work on the
  *     given HIP stream (`hipStream_t` passed as void*; NULL = default stream).
  *     Calls are stream-ordered: an append followed by a decode on the same
  *     stream sees the appended token.
@@ -52,7 +53,8 @@ enum {
                                mismatch */
   KV4_ERR_SHAPE = -3,       /* a size is out of range (B <= 0, max_ctx > pt_stride*16,
                                B * num_kv_heads * (max_ctx/16 + 1) > INT32_MAX, ...) */
-  KV4_ERR_WORKSPACE = -4,   /* workspace missing or smaller than kv4_decode_workspace_bytes */
+  KV4_ERR_WORKSPACE = -4,   /* workspace missing or smaller than kv4_decode_workspace_bytes
+                               (no-allocation entry point: more than its fixed scratch) */
   KV4_ERR_HIP = -5          /* a HIP call failed; kv4_strerror gives the HIP message */
 };
 
@@ -145,6 +147,27 @@ int kv4_append_decode_attention(const kv4_cache_desc *cache, const void *k, cons
                                 int32_t B, int32_t Hq, int32_t max_ctx, float softmax_scale,
                                 float *out, float *lse, void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * kv4_append_decode_attention with the workspace taken from a fixed scratch
+ * array inside the library instead of a caller buffer; the same kernels, the
+ * same results bit for bit.  No allocation or free of any kind happens in the
+ * call.  The array holds KV4_NOALLOC_SCRATCH_BYTES on every GPU the library
+ * runs on, from the first call on that GPU until the process ends; a call
+ * whose kv4_decode_workspace_bytes exceeds it returns KV4_ERR_WORKSPACE before
+ * anything is enqueued (32 MiB covers B = 512 sequences at Hq/Hkv = 32/8 on a
+ * 256-CU device).  Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (different streams, or host threads racing on one
+ * stream) race on it: serialize them.  Nothing in the array has to start at
+ * zero, so what an earlier call left there does not matter.  Arguments,
+ * layouts and other errors as for kv4_append_decode_attention. */
+#define KV4_NOALLOC_SCRATCH_BYTES (32u << 20)
+int kv4_append_decode_attention_noalloc(const kv4_cache_desc *cache, const void *k, const void *v,
+                                        const int32_t *pos, const void *q, const int32_t *ctx_len,
+                                        const int32_t *slot, const int32_t *page_table,
+                                        int32_t pt_stride, int32_t B, int32_t Hq, int32_t max_ctx,
+                                        float softmax_scale, float *out, float *lse, void *stream);
 
 /* Integer intermediates of a decode step, for bit-exact checking (device
  * pointers; any may be NULL).  Same layouts as the arguments of

@@ -25,7 +25,9 @@ EXPORTS = ("kv4_append", "kv4_prefill_quantize", "kv4_decode_workspace_bytes",
            "kv8_decode_workspace_bytes", "kv8_decode_attention", "kv8_decode_attention_debug",
            "kv4mx_append", "kv4mx_prefill_quantize", "kv4mx_decode_attention",
            "kv4_prefill_attention_workspace_bytes", "kv4_prefill_attention",
-           "kv4_prefill_attention_debug", "kv4_append_decode_attention")
+           "kv4_prefill_attention_debug", "kv4_append_decode_attention",
+           "kv4_append_decode_attention_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # KV4_NOALLOC_SCRATCH_BYTES
 KV8_BLOCK_BYTES = 4160
 
 _lib = None
@@ -78,6 +80,7 @@ def lib():
         L.kv4bench_decode_attention_timed.argtypes = [D, P, P, P, P, P, P, P, I, I, I, I, F, P, P,
                                                       P, Z, P, P, P]
         L.kv4_append_decode_attention.argtypes = [D, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P, Z, P]
+        L.kv4_append_decode_attention_noalloc.argtypes = [D, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P]
         L.kv4_prefill_attention_workspace_bytes.argtypes = [D, I, I, I]
         L.kv4_prefill_attention_workspace_bytes.restype = Z
         L.kv4_prefill_attention.argtypes = [D, P, P, P, P, P, I, I, I, I, I, F, P, P, P, Z, P]
@@ -260,6 +263,19 @@ def append_decode_attention(cache: Kv4Cache, k, v, pos, q, ctx_len, slot, page_t
         cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(q), _ptr(ctx_len), _ptr(slot),
         _ptr(page_table), page_table.shape[1], B, Hq, int(max_ctx), float(softmax_scale), _ptr(out),
         _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse
+
+
+def append_decode_attention_noalloc(cache: Kv4Cache, k, v, pos, q, ctx_len, slot, page_table,
+                                    max_ctx: int, softmax_scale: float, out, lse):
+    """kv4_append_decode_attention_noalloc: append_decode_attention with the
+    workspace in the library's fixed per-device scratch; out fp32 [B][Hq][128]
+    and lse fp32 [B][Hq] are the caller's (nothing is allocated here)."""
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    _check(lib().kv4_append_decode_attention_noalloc(
+        cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(q), _ptr(ctx_len), _ptr(slot),
+        _ptr(page_table), page_table.shape[1], B, Hq, int(max_ctx), float(softmax_scale), _ptr(out),
+        _ptr(lse), _stream()))
     return out, lse
 
 

@@ -1,7 +1,8 @@
 // kv4_api.hip -- extern "C" entry points of libkv4 (declared in include/kv4.h):
 // argument validation on the host, then stream-ordered kernel launches.  No
 // allocation, no synchronization, no state kept between calls (apart from a
-// per-device cache of the compute-unit count and a thread-local error text).
+// per-device cache of the compute-unit count, a thread-local error text and
+// the per-device address of the no-allocation entry point's fixed scratch).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -60,6 +61,44 @@ int check_decode(const kv4_cache_desc* c, const void* q, const int32_t* ctx,
   return KV4_OK;
 }
 
+// ---- fixed scratch of the no-allocation entry point ------------------------
+// The decode workspace of kv4_append_decode_attention_noalloc lives in this
+// array: every GPU the library runs on holds its own copy for the life of the
+// process.  Host code never passes the array's name to a kernel (on the host
+// it is only a stand-in symbol); the device address is looked up once per
+// device with hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[KV4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (nullptr and a recorded HIP
+// error if the lookup fails).
+void* scratch_for_current_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    hip_fail(e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    hip_fail(hipErrorInvalidDevice);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 namespace kv4 {
@@ -93,7 +132,10 @@ const char* kv4_strerror(int status) {
       return "unsupported configuration (needs abi_version 1, page 16, head_dim 128, "
              "sink a multiple of 16, sink + window <= 144, Hq/Hkv = 4)";
     case KV4_ERR_SHAPE: return "a size argument is out of range";
-    case KV4_ERR_WORKSPACE: return "workspace missing or smaller than kv4_decode_workspace_bytes";
+    case KV4_ERR_WORKSPACE:
+      return "workspace missing or smaller than kv4_decode_workspace_bytes (for "
+             "kv4_append_decode_attention_noalloc: the batch needs more than its fixed "
+             "KV4_NOALLOC_SCRATCH_BYTES of scratch)";
     case KV4_ERR_HIP: return g_hip_error;
     default: return "unknown status";
   }
@@ -202,6 +244,27 @@ int kv4_append_decode_attention(const kv4_cache_desc* cache, const void* k, cons
   return decode_common(cache, q, ctx_len, slot, page_table, pt_stride, B, Hq, max_ctx,
                        softmax_scale, out, lse, workspace, workspace_bytes, nullptr, stream, nullptr,
                        nullptr, false, k, v, pos);
+}
+
+int kv4_append_decode_attention_noalloc(const kv4_cache_desc* cache, const void* k, const void* v,
+                                        const int32_t* pos, const void* q, const int32_t* ctx_len,
+                                        const int32_t* slot, const int32_t* page_table,
+                                        int32_t pt_stride, int32_t B, int32_t Hq, int32_t max_ctx,
+                                        float softmax_scale, float* out, float* lse, void* stream) {
+  if (!k || !v || !pos) return KV4_ERR_NULLPTR;
+  // host-checkable errors first, so that a refused call touches no device state
+  int rc = check_decode(cache, q, ctx_len, page_table, pt_stride, B, Hq, max_ctx, out, lse);
+  if (rc != KV4_OK) return rc;
+  if (B > 65535) return KV4_ERR_SHAPE;
+  const size_t need = kv4::decode_workspace_bytes(B, Hq, cache->num_kv_heads, kv4::main_region_waves());
+  if (need > KV4_NOALLOC_SCRATCH_BYTES) return KV4_ERR_WORKSPACE;
+  void* ws = scratch_for_current_device();
+  if (!ws) return KV4_ERR_HIP;
+  // Nothing in the workspace has to start at zero: every partial, chunk range
+  // and plan entry the merge reads is written earlier in the same step.
+  return decode_common(cache, q, ctx_len, slot, page_table, pt_stride, B, Hq, max_ctx,
+                       softmax_scale, out, lse, ws, KV4_NOALLOC_SCRATCH_BYTES, nullptr, stream,
+                       nullptr, nullptr, false, k, v, pos);
 }
 
 int kv4bench_decode_attention_timed(const kv4_cache_desc* cache, const void* k, const void* v,

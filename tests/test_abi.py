@@ -73,3 +73,22 @@ def test_host_validation_of_the_protection_budget(sink, window, ok):
     assert L.kv4_prefill_quantize(ctypes.byref(d), None, 1, 1, 1, None, 1, 1, 1, 1, None) == want
     assert L.kv4_decode_attention(ctypes.byref(d), None, 1, None, 1, 1, 1, 4, 16, 1.0, 1, 1, 1, 1,
                                   None) == want
+
+
+def test_noalloc_entry_point_refuses_beyond_its_scratch_without_gpu():
+    """kv4_append_decode_attention_noalloc: a batch whose workspace exceeds the
+    fixed scratch is refused with KV4_ERR_WORKSPACE before any launch (the
+    pointers are dummies and never touched); NULL inputs give KV4_ERR_NULLPTR."""
+    import int8_mixed_precision_kv4_amd as kv4
+    if not os.path.exists(kv4.LIB_PATH):
+        pytest.skip("libkv4.so not built")
+    L = kv4.lib()
+    d = kv4._Desc(1, 4, 16, 8, 128, 16, 128, 1, 1, 1, 1)
+    big = L.kv4_decode_workspace_bytes(ctypes.byref(d), 65535, 32, 16)
+    assert big > kv4.NOALLOC_SCRATCH_BYTES
+    assert L.kv4_append_decode_attention_noalloc(ctypes.byref(d), 1, 1, 1, 1, 1, 1, 1, 1, 65535, 32, 16,
+                                                 0.1, 1, 1, None) == -4
+    assert L.kv4_append_decode_attention_noalloc(ctypes.byref(d), None, 1, 1, 1, 1, 1, 1, 1, 4, 32, 16,
+                                                 0.1, 1, 1, None) == -1
+    # the benchmark's batch (256 sequences, 32/8 heads) fits with room to spare
+    assert L.kv4_decode_workspace_bytes(ctypes.byref(d), 256, 32, 16384) <= kv4.NOALLOC_SCRATCH_BYTES
