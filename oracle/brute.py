@@ -100,6 +100,32 @@ def exp2s(y: float) -> float:
     return float(Fraction(p) * Fraction(2) ** n)
 
 
+# ------------------------------------------------------------ quantizers --
+
+def quant_int4_exact(x):
+    """Group-affine INT4 of one vector of binary32 values by exact rational
+    steps: delta = rn16(rn32((max - min) / 15)) from the FP32 difference,
+    m = rn16(min), code = clamp(rint_even(rn32(rn32(x - m) / delta)), 0, 15),
+    all zero when delta is 0.  Returns (codes, delta, m) as Python values."""
+    xs = [float(v) for v in x]
+    mn, mx = min(xs), max(xs)
+    d = rn16(Fraction(f32_div(f32_sub(mx, mn), 15.0)))
+    m = rn16(Fraction(mn))
+    if d == 0.0:
+        return [0] * len(xs), d, m
+    return [min(15, max(0, rint_even(f32_div(f32_sub(v, m), d)))) for v in xs], d, m
+
+
+def quant_int8_exact(x):
+    """Symmetric INT8 of one vector: s = rn16(rn32(max|x| / 127)),
+    code = clamp(rint_even(rn32(x / s)), -127, 127), all zero when s is 0."""
+    xs = [float(v) for v in x]
+    s = rn16(Fraction(f32_div(max(abs(v) for v in xs), 127.0)))
+    if s == 0.0:
+        return [0] * len(xs), s
+    return [min(127, max(-127, rint_even(f32_div(v, s)))) for v in xs], s
+
+
 # --------------------------------------------------------------- rotation --
 
 def sylvester(n: int) -> np.ndarray:

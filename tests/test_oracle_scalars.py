@@ -117,15 +117,17 @@ def test_int4_codes_are_nearest_grid_points():
     mn, mx = x.min(1), x.max(1)
     assert np.array_equal(d16, ((mx - mn).astype(np.float32) / np.float32(15)).astype(np.float16).view(np.uint16))
     assert np.array_equal(m16, mn.astype(np.float16).view(np.uint16))
+    # every code, ties included, equals the exact-rational rule
+    # (rn32(x - m), rn32(/ delta), round half to even, clamp)
+    want = np.array([brute.quant_int4_exact(row)[0] for row in x], np.uint8)
+    assert np.array_equal(codes, want)
+    # and it is a nearest grid point: its distance exceeds the best one by at
+    # most the FP32 rounding of x - m and of the quotient
     grid = d * np.arange(16)[None, :] + m                    # [n, 16]
     dist = np.abs(xs[:, :, None] - grid[:, None, :])        # [n, 128, 16]
-    best = dist.argmin(-1)
-    # exclude near-ties where FP32 rounding of (x-m)/delta may legitimately decide
-    srt = np.sort(dist, -1)
-    near_tie = (srt[..., 1] - srt[..., 0]) < 1e-5 * np.maximum(np.abs(xs), d)
-    ok = (codes == best) | near_tie
-    assert ok.all()
-    assert (~near_tie).mean() > 0.99
+    mine = np.take_along_axis(dist, codes[..., None].astype(np.int64), -1)[..., 0]
+    slack = 2.0 ** -22 * (np.abs(xs) + np.abs(m) + 16 * d)
+    assert (mine <= dist.min(-1) + slack).all()
     # dequantization error bound for elements inside the grid
     xhat = d * codes + m
     inside = (xs >= m) & (xs <= m + 15 * d)
@@ -159,9 +161,12 @@ def test_int8_symmetric_nearest_and_odd():
     a = np.abs(x).max(1)
     assert np.array_equal(s16, (a / np.float32(127)).astype(np.float16).view(np.uint16))
     q = x.astype(np.float64) / s
-    near_tie = np.abs(np.abs(q - np.floor(q)) - 0.5) < 1e-4
-    best = np.clip(np.rint(q), -127, 127)
-    assert ((codes == best) | near_tie).all()
+    # every code, ties included, equals the exact-rational rule
+    want = np.array([brute.quant_int8_exact(row)[0] for row in x], np.int8)
+    assert np.array_equal(codes, want)
+    # and it is the nearest integer of the FP64 quotient, a tie (exactly
+    # representable there) going to the even code
+    assert np.array_equal(codes, np.clip(np.rint(q), -127, 127).astype(np.int8))
     err = np.abs(x - s * codes)
     inside = np.abs(q) <= 127
     assert (err[inside] <= (np.broadcast_to(s, err.shape)[inside] / 2) * (1 + 1e-6)).all()
