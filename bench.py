@@ -345,6 +345,64 @@ def variant_leg(wl, layers, sh, ctx, scale, steps, t_bf16):
                 budgets=res)
 
 
+def prefill_leg(wl, dev, scale, steps):
+    """The benchmark's re-prefill of 8 sequences x 16384 tokens (one layer,
+    Hkv = 8): the quantize kernel (kv4_prefill_quantize) timed over several
+    calls, then the attention half (kv4_prefill_attention) of the same chunks."""
+    import numpy as np
+    import torch
+
+    import int8_mixed_precision_kv4_amd as kv4
+    from synth import draw_values
+
+    log("timing the 8 x 16384-token re-prefill")
+    nseq, n = wl.prefill_nseq, wl.prefill_len
+    pk, pv, _ = draw_values(wl.seed, 1000, nseq * n, 1, 4, wl.Hkv, device=dev)
+    ppages = nseq * n // 16
+    pcache = kv4.Kv4Cache.zeros(ppages, wl.Hkv, nseq, dev)
+    ptable = torch.arange(ppages, dtype=torch.int32, device=dev).view(nseq, n // 16)
+    pcu = torch.arange(0, nseq * n + 1, n, dtype=torch.int32, device=dev)
+    pstart = torch.zeros(nseq, dtype=torch.int32, device=dev)
+    pslot = torch.arange(nseq, dtype=torch.int32, device=dev)
+    t_pre = _timed(lambda: kv4.prefill_quantize(pcache, pk, pv, pcu, pstart, pslot, ptable, n),
+                   max(3, steps // 2), 2)
+    pbytes = nseq * n * wl.Hkv * (512 + 136)
+    res = dict(prefill_ms_per_layer=round(t_pre * 1e3, 3), prefill_gbps=round(pbytes / t_pre / 1e9, 1),
+               prefill_frac_of_peak=round(pbytes / t_pre / 1e9 / PEAK_GBS, 4))
+    del pk, pv
+    # the attention half: every token of each 16384-token chunk attends its prefix
+    log("timing the re-prefill attention of the 8 x 16384 tokens")
+    pq = draw_values(wl.seed, 1001, 1, nseq * n, wl.Hq, wl.Hkv, device=dev)[2]
+    pws = torch.empty(kv4.prefill_attention_workspace_bytes(pcache, nseq * n, wl.Hq, n),
+                      dtype=torch.uint8, device=dev)
+    pout = torch.empty((nseq * n, wl.Hq, 128), dtype=torch.float32, device=dev)
+    plse = torch.empty((nseq * n, wl.Hq), dtype=torch.float32, device=dev)
+    t_att = _timed(lambda: kv4.prefill_attention(pcache, pq, pcu, pstart, pslot, ptable, n, scale, pout,
+                                                 plse, pws), 2, 1)
+    pos = np.arange(n, dtype=np.int64)
+    per_seq = (np.maximum(pos + 1 - 144, 0) * 136 + np.minimum(pos + 1, 144) * 260).sum()
+    # bytes of cache the tokens attend (each tile is served to 8 tokens from
+    # one load, so this is attended bytes per second, not HBM traffic)
+    res.update(prefill_attention_ms_per_layer=round(t_att * 1e3, 3),
+               prefill_attention_attended_gb_per_s=round(per_seq * nseq * wl.Hkv / t_att / 1e9, 1),
+               prefill_attention_finite=bool(torch.isfinite(pout).all()))
+    del pq, pws, pout, plse, pcache
+    torch.cuda.empty_cache()
+    return res
+
+
+def _timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
 def cpu_baseline(wl, layer0, shared, budget_s):
     """The oracle as it stands, on the host cores, on layer 0 of the step (all
     256 sequences): one append + one 32-head decode, repeated until about
@@ -399,7 +457,7 @@ def cpu_baseline(wl, layer0, shared, budget_s):
     return dict(value=round(wl.B / t_step, 3), unit="tokens/s", cores=threads, kind="oracle",
                 sample=(f"layer 0 of 36 (all {len(sample)} sequences, mean ctx {ctx.mean():.0f}): "
                         f"append + 32-head decode, {reps} reps in {t_total:.1f}s; x36 layers"),
-                cpu=cpu, single_thread_layer_s=round(t_single, 3)), (sample, out, lse)
+                cpu=cpu, single_thread_layer_s=round(t_single, 3)), (sample, out, lse, cache, table, need)
 
 
 def traffic_from_counters(fetch_db, write_db, command):
@@ -460,6 +518,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the 8 x 16384-token re-prefill leg (quantize + attention) and "
+                         "print its figures (for profiling those kernels)")
     ap.add_argument("--no-copy", action="store_true", help="skip the 2 GiB device copy probe")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
     ap.add_argument("--workload", choices=("qwen8b", "refill"), default="qwen8b",
@@ -483,6 +544,10 @@ def main():
     dev = torch.device("cuda:0")
     kv4.lib()
     wl = make_workload(WORKLOAD)
+    if args.prefill_only:
+        print(json.dumps(dict(workload="re-prefill of 8 x 16384 tokens, one layer, Hq/Hkv = 32/8",
+                              **prefill_leg(wl, dev, 1.0 / math.sqrt(128), args.steps))), flush=True)
+        return
     if args.workload == "refill":
         from synth.concentration import LengthLaw, refill_snapshot
         wl = make_workload(WORKLOAD, ctx=refill_snapshot(LengthLaw.lognormal(3000, 2250), wl.B, wl.seed))
@@ -588,37 +653,7 @@ def main():
                      speedup_decode_vs_bf16=round(t_bf16 / t_decode, 3),
                      kv4_vs_bf16_out_maxabs=float((out - bout).abs().max()))
     if not args.no_prefill:
-        log("timing the 8 x 16384-token re-prefill")
-        from synth import draw_values
-        nseq, n = wl.prefill_nseq, wl.prefill_len
-        pk, pv, _ = draw_values(wl.seed, 1000, nseq * n, 1, 4, wl.Hkv, device=dev)
-        ppages = nseq * n // 16
-        pcache = kv4.Kv4Cache.zeros(ppages, wl.Hkv, nseq, dev)
-        ptable = torch.arange(ppages, dtype=torch.int32, device=dev).view(nseq, n // 16)
-        pcu = torch.arange(0, nseq * n + 1, n, dtype=torch.int32, device=dev)
-        pstart = torch.zeros(nseq, dtype=torch.int32, device=dev)
-        pslot = torch.arange(nseq, dtype=torch.int32, device=dev)
-        t_pre = timed(lambda: kv4.prefill_quantize(pcache, pk, pv, pcu, pstart, pslot, ptable, n),
-                      max(3, args.steps // 2), 2)
-        pbytes = nseq * n * wl.Hkv * (512 + 136)
-        extra.update(prefill_ms_per_layer=round(t_pre * 1e3, 3),
-                     prefill_gbps=round(pbytes / t_pre / 1e9, 1))
-        del pk, pv
-        # the attention half: every token of each 16384-token chunk attends its prefix
-        log("timing the re-prefill attention of the 8 x 16384 tokens")
-        pq = draw_values(wl.seed, 1001, 1, nseq * n, wl.Hq, wl.Hkv, device=dev)[2]
-        pws = torch.empty(kv4.prefill_attention_workspace_bytes(pcache, nseq * n, wl.Hq, n),
-                          dtype=torch.uint8, device=dev)
-        pout = torch.empty((nseq * n, wl.Hq, 128), dtype=torch.float32, device=dev)
-        plse = torch.empty((nseq * n, wl.Hq), dtype=torch.float32, device=dev)
-        t_att = timed(lambda: kv4.prefill_attention(pcache, pq, pcu, pstart, pslot, ptable, n, scale, pout,
-                                                    plse, pws), 2, 1)
-        pos = np.arange(n, dtype=np.int64)
-        per_seq = (np.maximum(pos + 1 - 144, 0) * 136 + np.minimum(pos + 1, 144) * 260).sum()
-        extra.update(prefill_attention_ms_per_layer=round(t_att * 1e3, 3),
-                     prefill_attention_kv_bytes_per_s=round(per_seq * nseq * wl.Hkv / t_att / 1e9, 1),
-                     prefill_attention_finite=bool(torch.isfinite(pout).all()))
-        del pq, pws, pout, plse, pcache
+        extra.update(prefill_leg(wl, dev, scale, args.steps))
 
     if not args.no_copy:
         # plain device-to-device copy of a known size: the box's practical HBM
@@ -632,13 +667,27 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("oracle CPU baseline")
-        cpu, (sample, ref_out, ref_lse) = cpu_baseline(wl, layers[0], sh, args.cpu_budget)
-        kv4.decode_attention(layers[0]["cache"], layers[0]["q"], ctx, slots, table, wl.max_ctx,
-                             scale, out, lse, ws)
+        cpu, (sample, ref_out, ref_lse, ref_cache, ref_table, need) = cpu_baseline(wl, layers[0], sh,
+                                                                                   args.cpu_budget)
+        # parity of the timed launch itself (the one-launch step; re-appending
+        # this step's token rewrites the same bytes) on layer 0, every sequence
+        L0 = layers[0]
+        kv4.append_decode_attention(L0["cache"], L0["k_app"], L0["v_app"], pos, L0["q"], ctx, slots, table,
+                                    wl.max_ctx, scale, out, lse, ws)
         torch.cuda.synchronize()
-        got = out[torch.from_numpy(sample).to(dev)].cpu().numpy()
-        extra["sample_parity_out_maxabs"] = float(np.abs(got - ref_out).max())
-        extra["sample_parity_lse_maxabs"] = float(np.abs(lse[torch.from_numpy(sample).to(dev)].cpu().numpy() - ref_lse).max())
+        sel = torch.from_numpy(sample).to(dev)
+        extra["sample_parity_out_maxabs"] = float(np.abs(out[sel].cpu().numpy() - ref_out).max())
+        extra["sample_parity_lse_maxabs"] = float(np.abs(lse[sel].cpu().numpy() - ref_lse).max())
+        gpu_ids = np.concatenate([wl.page_table[b, :need[i]] for i, b in enumerate(sample)]).astype(np.int64)
+        ref_ids = np.concatenate([ref_table[i, :need[i]] for i in range(len(sample))]).astype(np.int64)
+        slot_ids = torch.from_numpy(wl.slots[sample].astype(np.int64)).to(dev)
+        extra["sample_parity_pages_equal"] = bool(
+            np.array_equal(L0["cache"].pages[torch.from_numpy(gpu_ids).to(dev)].cpu().numpy(),
+                           ref_cache.pages[ref_ids])
+            and np.array_equal(L0["cache"].side_codes[slot_ids].cpu().numpy(), ref_cache.side_codes)
+            and np.array_equal(L0["cache"].side_scales[slot_ids].cpu().numpy().view(np.uint16),
+                               ref_cache.side_scales))
+        extra["sample_parity_launch"] = "kv4_append_decode_attention (the timed launch), layer 0, all sequences"
 
     if not args.no_variants:
         extra["variants"] = variant_leg(wl, layers, sh, ctx, scale, max(3, args.steps // 2), t_bf16)
@@ -668,8 +717,12 @@ def main():
         "decode_tokens_per_s": round(B / t_decode, 1),
         "decode_ms_per_step": round(t_decode * 1e3, 4),
         "append_ms_per_step": round((t_step - t_decode) * 1e3, 4),
+        # the metric's byte formula over the decode-only step, and over the
+        # timed step (this step's appends included, same bytes)
         "hbm_gbps": round(mb * LAYERS / t_decode / 1e9, 1),
         "hbm_frac_of_peak": round(mb * LAYERS / t_decode / 1e9 / PEAK_GBS, 4),
+        "hbm_gbps_with_append": round(mb * LAYERS / t_step / 1e9, 1),
+        "hbm_frac_of_peak_with_append": round(mb * LAYERS / t_step / 1e9 / PEAK_GBS, 4),
         "metric_bytes_per_layer": mb,
         "roofline": {"bound": "hbm", "kernel": ("main_kernel (INT4 main region + INT8 protected region "
                                                 "+ this step's append)"),

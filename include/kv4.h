@@ -49,8 +49,10 @@ enum {
   KV4_ERR_NULLPTR = -1,     /* a required pointer is NULL */
   KV4_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_size != 16, sink < 0,
                                window < 0, sink % 16 != 0, sink + window > 144,
-                               Hq % Hkv != 0 or Hq / Hkv != 4, or abi_version
-                               mismatch */
+                               Hq % Hkv != 0 or Hq / Hkv != 4 (the kernels are
+                               built for groups of 4 query heads per kv-head,
+                               the GQA shape of the pages' Qwen3 models and of
+                               their TP shards), or abi_version mismatch */
   KV4_ERR_SHAPE = -3,       /* a size is out of range (B <= 0, max_ctx > pt_stride*16,
                                B * num_kv_heads * (max_ctx/16 + 1) > INT32_MAX, ...) */
   KV4_ERR_WORKSPACE = -4,   /* workspace missing or smaller than kv4_decode_workspace_bytes

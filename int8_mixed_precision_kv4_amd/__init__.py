@@ -109,8 +109,55 @@ def _check(rc: int):
 def _ptr(t):
     if t is None:
         return None
-    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA tensors"
+    if not (t.is_cuda and t.is_contiguous()):
+        raise Kv4Error("device tensors must be contiguous CUDA tensors")
     return C.c_void_p(t.data_ptr())
+
+
+def _want(t, dtype, what, rows=None, ndim=None, optional=False):
+    """Host-side check of one argument before it reaches the library, which
+    reads it on the device with the given element type: dtype, and (when
+    given) the number of dimensions and at least `rows` leading rows."""
+    if t is None:
+        if optional:
+            return
+        raise Kv4Error(f"{what} is required")
+    if t.dtype != dtype:
+        raise Kv4Error(f"{what} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise Kv4Error(f"{what} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if rows is not None and (t.dim() == 0 or t.shape[0] < rows):
+        raise Kv4Error(f"{what} needs at least {rows} rows, got shape {tuple(t.shape)}")
+
+
+def _step_args(B, q=None, k=None, v=None, pos=None, slot=None, ctx_len=None, page_table=None):
+    """Checks of the per-sequence arguments of an append / decode call."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is not None:
+            _want(t, torch.bfloat16, name, rows=B, ndim=3)
+            if t.shape[0] != B or t.shape[2] != HEAD_DIM:
+                raise Kv4Error(f"{name} must be [B={B}][heads][{HEAD_DIM}], got {tuple(t.shape)}")
+    for name, t in (("pos", pos), ("ctx_len", ctx_len)):
+        if t is not None:
+            _want(t, torch.int32, name, ndim=1)
+            if t.shape[0] != B:
+                raise Kv4Error(f"{name} must hold B={B} entries, got {t.shape[0]}")
+    _want(slot, torch.int32, "slot", rows=B, ndim=1, optional=True)
+    _want(page_table, torch.int32, "page_table", rows=B, ndim=2)
+
+
+def _chunk_args(nseq, T=None, k=None, v=None, q=None, cu_seqlens=None, start_pos=None, slot=None,
+                page_table=None):
+    """Checks of the arguments of a re-prefill call over nseq sequences."""
+    for name, t in (("k", k), ("v", v), ("q", q)):
+        if t is not None:
+            _want(t, torch.bfloat16, name, ndim=3)
+            if T is not None and t.shape[0] != T:
+                raise Kv4Error(f"{name} must hold {T} tokens, got {t.shape[0]}")
+    _want(cu_seqlens, torch.int32, "cu_seqlens", rows=nseq + 1, ndim=1)
+    _want(start_pos, torch.int32, "start_pos", rows=nseq, ndim=1)
+    _want(slot, torch.int32, "slot", rows=nseq, ndim=1, optional=True)
+    _want(page_table, torch.int32, "page_table", rows=nseq, ndim=2)
 
 
 def _stream():
@@ -150,6 +197,7 @@ class Kv4Cache:
 
 def append(cache: Kv4Cache, k, v, pos, slot, page_table):
     """kv4_append: k, v bf16 [B][Hkv][128]; pos, slot int32 [B]; page_table int32 [B][W]."""
+    _step_args(int(pos.shape[0]), k=k, v=v, pos=pos, slot=slot, page_table=page_table)
     _check(lib().kv4_append(cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(slot),
                             _ptr(page_table), page_table.shape[1], pos.shape[0], _stream()))
 
@@ -157,6 +205,8 @@ def append(cache: Kv4Cache, k, v, pos, slot, page_table):
 def prefill_quantize(cache: Kv4Cache, k, v, cu_seqlens, start_pos, slot, page_table,
                      max_seqlen: int):
     """kv4_prefill_quantize: k, v bf16 [T][Hkv][128]; cu_seqlens int32 [nseq+1]."""
+    _chunk_args(int(start_pos.shape[0]), k=k, v=v, cu_seqlens=cu_seqlens, start_pos=start_pos, slot=slot,
+                page_table=page_table)
     _check(lib().kv4_prefill_quantize(cache.desc(), _ptr(k), _ptr(v), _ptr(cu_seqlens),
                                       _ptr(start_pos), _ptr(slot), _ptr(page_table),
                                       page_table.shape[1], start_pos.shape[0], int(max_seqlen),
@@ -171,6 +221,7 @@ def decode_attention(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ctx: int
                      softmax_scale: float, out=None, lse=None, workspace=None):
     """kv4_decode_attention: q bf16 [B][Hq][128] -> (out fp32 [B][Hq][128], lse fp32 [B][Hq])."""
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    _step_args(B, q=q, slot=slot, ctx_len=ctx_len, page_table=page_table)
     if out is None:
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -190,6 +241,7 @@ def decode_attention_debug(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ct
     """kv4_decode_attention_debug: also returns the integer intermediates
     (qcodes, qsum, qk, pcode, pv) as device tensors."""
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    _step_args(B, q=q, slot=slot, ctx_len=ctx_len, page_table=page_table)
     W = int(page_table.shape[1])
     dev = q.device
     dbg = dict(qcodes=torch.zeros((B, Hq, HEAD_DIM), dtype=torch.int8, device=dev),
@@ -218,6 +270,8 @@ def bf16_paged_decode(pages, q, ctx_len, page_table, max_ctx: int, softmax_scale
     """kv4bench_bf16_paged_decode (comparator): pages bf16 [P][Hkv][2][16][128]
     with K token-major and V channel-major."""
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    _want(pages, torch.bfloat16, "pages", ndim=5)
+    _step_args(B, q=q, ctx_len=ctx_len, page_table=page_table)
     Hkv = int(pages.shape[1])
     if out is None:
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
@@ -241,6 +295,7 @@ def decode_attention_timed(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ct
     append_decode_attention), recording the two raw hipEvent_t handles
     (ctypes.c_void_p) around the main kernel."""
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    _step_args(B, q=q, k=k, v=v, pos=pos, slot=slot, ctx_len=ctx_len, page_table=page_table)
     _check(lib().kv4bench_decode_attention_timed(
         cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(q), _ptr(ctx_len), _ptr(slot),
         _ptr(page_table), page_table.shape[1], B, Hq, int(max_ctx), float(softmax_scale), _ptr(out),
@@ -252,6 +307,7 @@ def append_decode_attention(cache: Kv4Cache, k, v, pos, q, ctx_len, slot, page_t
     """kv4_append_decode_attention: append(k, v, pos) then decode_attention in one launch
     (pos = ctx_len - 1)."""
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    _step_args(B, q=q, k=k, v=v, pos=pos, slot=slot, ctx_len=ctx_len, page_table=page_table)
     if out is None:
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -272,6 +328,9 @@ def append_decode_attention_noalloc(cache: Kv4Cache, k, v, pos, q, ctx_len, slot
     workspace in the library's fixed per-device scratch; out fp32 [B][Hq][128]
     and lse fp32 [B][Hq] are the caller's (nothing is allocated here)."""
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    _step_args(B, q=q, k=k, v=v, pos=pos, slot=slot, ctx_len=ctx_len, page_table=page_table)
+    _want(out, torch.float32, "out", rows=B)
+    _want(lse, torch.float32, "lse", rows=B)
     _check(lib().kv4_append_decode_attention_noalloc(
         cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(q), _ptr(ctx_len), _ptr(slot),
         _ptr(page_table), page_table.shape[1], B, Hq, int(max_ctx), float(softmax_scale), _ptr(out),
@@ -304,12 +363,15 @@ class Kv8Cache:
 
 def kv8_append(cache: Kv8Cache, k, v, pos, page_table):
     """kv8_append: k, v bf16 [B][Hkv][128]; pos int32 [B]; page_table int32 [B][W]."""
+    _step_args(int(pos.shape[0]), k=k, v=v, pos=pos, page_table=page_table)
     _check(lib().kv8_append(cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(page_table),
                             page_table.shape[1], pos.shape[0], _stream()))
 
 
 def kv8_prefill_quantize(cache: Kv8Cache, k, v, cu_seqlens, start_pos, page_table, max_seqlen: int):
     """kv8_prefill_quantize: k, v bf16 [T][Hkv][128]; cu_seqlens int32 [nseq+1]."""
+    _chunk_args(int(start_pos.shape[0]), k=k, v=v, cu_seqlens=cu_seqlens, start_pos=start_pos,
+                page_table=page_table)
     _check(lib().kv8_prefill_quantize(cache.desc(), _ptr(k), _ptr(v), _ptr(cu_seqlens),
                                       _ptr(start_pos), _ptr(page_table), page_table.shape[1],
                                       start_pos.shape[0], int(max_seqlen), _stream()))
@@ -323,6 +385,7 @@ def kv8_decode_attention(cache: Kv8Cache, q, ctx_len, page_table, max_ctx: int,
                          softmax_scale: float, out=None, lse=None, workspace=None):
     """kv8_decode_attention: q bf16 [B][Hq][128] -> (out fp32 [B][Hq][128], lse fp32 [B][Hq])."""
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    _step_args(B, q=q, ctx_len=ctx_len, page_table=page_table)
     if out is None:
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -341,6 +404,7 @@ def kv8_decode_attention_debug(cache: Kv8Cache, q, ctx_len, page_table, max_ctx:
                                softmax_scale: float):
     """kv8_decode_attention_debug: also returns qcodes, qsum and qk as device tensors."""
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    _step_args(B, q=q, ctx_len=ctx_len, page_table=page_table)
     W = int(page_table.shape[1])
     dev = q.device
     dbg = dict(qcodes=torch.zeros((B, Hq, HEAD_DIM), dtype=torch.int8, device=dev),
@@ -363,12 +427,15 @@ def kv8_decode_attention_debug(cache: Kv8Cache, q, ctx_len, page_table, max_ctx:
 
 def mx_append(cache: Kv4Cache, k, v, pos, slot, page_table):
     """kv4mx_append: as append, main-region entry in MXFP4."""
+    _step_args(int(pos.shape[0]), k=k, v=v, pos=pos, slot=slot, page_table=page_table)
     _check(lib().kv4mx_append(cache.desc(), _ptr(k), _ptr(v), _ptr(pos), _ptr(slot),
                               _ptr(page_table), page_table.shape[1], pos.shape[0], _stream()))
 
 
 def mx_prefill_quantize(cache: Kv4Cache, k, v, cu_seqlens, start_pos, slot, page_table,
                         max_seqlen: int):
+    _chunk_args(int(start_pos.shape[0]), k=k, v=v, cu_seqlens=cu_seqlens, start_pos=start_pos, slot=slot,
+                page_table=page_table)
     _check(lib().kv4mx_prefill_quantize(cache.desc(), _ptr(k), _ptr(v), _ptr(cu_seqlens),
                                         _ptr(start_pos), _ptr(slot), _ptr(page_table),
                                         page_table.shape[1], start_pos.shape[0], int(max_seqlen),
@@ -379,6 +446,7 @@ def mx_decode_attention(cache: Kv4Cache, q, ctx_len, slot, page_table, max_ctx: 
                         softmax_scale: float, out=None, lse=None, workspace=None):
     """kv4mx_decode_attention: q bf16 [B][Hq][128] -> (out fp32 [B][Hq][128], lse fp32 [B][Hq])."""
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    _step_args(B, q=q, slot=slot, ctx_len=ctx_len, page_table=page_table)
     if out is None:
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -404,6 +472,8 @@ def prefill_attention(cache: Kv4Cache, q, cu_seqlens, start_pos, slot, page_tabl
     """kv4_prefill_attention: q bf16 [T][Hq][128] of the chunks (cu_seqlens, start_pos as for
     prefill_quantize) -> (out fp32 [T][Hq][128], lse fp32 [T][Hq])."""
     T, Hq = int(q.shape[0]), int(q.shape[1])
+    _chunk_args(int(start_pos.shape[0]), T=T, q=q, cu_seqlens=cu_seqlens, start_pos=start_pos, slot=slot,
+                page_table=page_table)
     if out is None:
         out = torch.empty((T, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -423,6 +493,8 @@ def prefill_attention_debug(cache: Kv4Cache, q, cu_seqlens, start_pos, slot, pag
                             max_ctx: int, softmax_scale: float):
     """kv4_prefill_attention_debug: also the integer intermediates, indexed by token."""
     T, Hq = int(q.shape[0]), int(q.shape[1])
+    _chunk_args(int(start_pos.shape[0]), T=T, q=q, cu_seqlens=cu_seqlens, start_pos=start_pos, slot=slot,
+                page_table=page_table)
     W = int(page_table.shape[1])
     dev = q.device
     dbg = dict(qcodes=torch.zeros((T, Hq, HEAD_DIM), dtype=torch.int8, device=dev),

@@ -12,14 +12,22 @@ CFLAGS = ["-std=gnu11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp"
           "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = ["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"]
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source (for
+# the sanitized run of the oracle's pins; a process loading it needs libasan
+# preloaded).  Host code only: the oracle has no GPU part.
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+            "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str | None = None) -> str:
+    lib = out or LIB
+    tmp = lib + f".tmp{os.getpid()}"
+    cmd = ["gcc", *CFLAGS, *(SANITIZE if sanitize else []), "-o", tmp, SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

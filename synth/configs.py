@@ -2,7 +2,8 @@
 
 Every workload is GQA decode with head_dim 128 and 16-position pages; the
 KV4-RL pages fix sink s=16 and recent window w=128 (paper.rainbus.top summary,
-"核心方法"), which the kernels take as constants.
+"核心方法"), the default protection budget of the cache descriptor (other
+budgets are descriptor fields too).
 
   tiny     B=4,   Hq/Hkv=4/1,  ctx {100,144,400,700}, 128-page pool (width 64)
   short    B=64,  32/8, prompt U[128,512] + length-biased lognormal(1450, 1087.5)

@@ -92,3 +92,56 @@ def test_noalloc_entry_point_refuses_beyond_its_scratch_without_gpu():
                                                  0.1, 1, 1, None) == -1
     # the benchmark's batch (256 sequences, 32/8 heads) fits with room to spare
     assert L.kv4_decode_workspace_bytes(ctypes.byref(d), 256, 32, 16384) <= kv4.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (64, 8), (6, 2), (5, 1)])
+def test_gqa_groups_other_than_four_are_refused_without_gpu(Hq, Hkv):
+    """The kernels take exactly 4 query heads per kv-head (the pages' GQA
+    models have 32/8 heads); any other group is refused as unsupported on the
+    host, before any launch, by every decode-side entry point."""
+    import int8_mixed_precision_kv4_amd as kv4
+    if not os.path.exists(kv4.LIB_PATH):
+        pytest.skip("libkv4.so not built")
+    L = kv4.lib()
+    d = kv4._Desc(1, 4, 16, Hkv, 128, 16, 128, 1, 1, 1, 1)
+    assert L.kv4_decode_attention(ctypes.byref(d), 1, 1, None, 1, 1, 1, Hq, 16, 1.0, 1, 1, 1, 1 << 30,
+                                  None) == -2
+    assert L.kv4_append_decode_attention(ctypes.byref(d), 1, 1, 1, 1, 1, None, 1, 1, 1, Hq, 16, 1.0, 1, 1,
+                                         1, 1 << 30, None) == -2
+    assert L.kv4_append_decode_attention_noalloc(ctypes.byref(d), 1, 1, 1, 1, 1, None, 1, 1, 1, Hq, 16,
+                                                 1.0, 1, 1, None) == -2
+    assert L.kv4_prefill_attention(ctypes.byref(d), 1, 1, 1, None, 1, 1, 1, 1, Hq, 16, 1.0, 1, 1, 1,
+                                   1 << 30, None) == -2
+    assert L.kv4mx_decode_attention(ctypes.byref(d), 1, 1, None, 1, 1, 1, Hq, 16, 1.0, 1, 1, 1, 1 << 30,
+                                    None) == -2
+    d8 = kv4._Kv8Desc(1, 4, 16, Hkv, 128, 1)
+    assert L.kv8_decode_attention(ctypes.byref(d8), 1, 1, 1, 1, 1, Hq, 16, 1.0, 1, 1, 1, 1 << 30, None) == -2
+    assert L.kv4bench_bf16_paged_decode(1, 4, Hkv, 1, 1, 1, 1, 1, Hq, 16, 1.0, 1, 1, 1, 1 << 30, None) == -2
+
+
+def test_binding_checks_dtypes_and_shapes_without_gpu():
+    """The Python binding refuses, on the host, arguments whose element type
+    or leading dimension the library would misread on the device."""
+    import torch
+
+    import int8_mixed_precision_kv4_amd as kv4
+    cache = kv4.Kv4Cache.zeros(4, 1, 2, device="cpu")
+    B = 2
+    q = torch.zeros((B, 4, 128), dtype=torch.bfloat16)
+    ctx = torch.ones(B, dtype=torch.int32)
+    table = torch.zeros((B, 1), dtype=torch.int32)
+    bad = [dict(q=q.float()), dict(ctx_len=ctx.long()), dict(page_table=table.long()),
+           dict(ctx_len=torch.ones(B + 1, dtype=torch.int32)), dict(page_table=table[:1]),
+           dict(slot=torch.zeros(B, dtype=torch.int64))]
+    for change in bad:
+        args = dict(q=q, ctx_len=ctx, slot=None, page_table=table)
+        args.update(change)
+        with pytest.raises(kv4.Kv4Error):
+            kv4.decode_attention(cache, args["q"], args["ctx_len"], args["slot"], args["page_table"], 16, 0.1)
+    with pytest.raises(kv4.Kv4Error):  # int64 positions for an append
+        kv4.append(cache, q[:, :1].contiguous(), q[:, :1].contiguous(), torch.zeros(B, dtype=torch.int64), None,
+                   table)
+    with pytest.raises(kv4.Kv4Error):  # float32 keys for a re-prefill
+        kv4.prefill_quantize(cache, torch.zeros((3, 1, 128)), torch.zeros((3, 1, 128)),
+                             torch.tensor([0, 3], dtype=torch.int32), torch.zeros(1, dtype=torch.int32), None,
+                             table[:1], 3)

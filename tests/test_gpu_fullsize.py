@@ -3,10 +3,13 @@
 The whole batch is built and decoded on the GPU exactly as bench.py does it
 (values drawn on the device, re-prefill of the leading positions, this
 step's append, one decode launch over all B sequences in the timed launch
-configuration).  A sample of sequences is then rebuilt by the CPU oracle
-from the same values, and compared: page blocks and side rows bit-exact,
-query codes / int32 QK / P-operand codes / int32 PV accumulators bit-exact,
-out within 2e-3 and lse within 1e-4."""
+configuration).  The CPU oracle rebuilds the whole batch from the same values
+in the same page table: every page block and side row bit-exact, out within
+2e-3 and lse within 1e-4 for every sequence and head.  A sample of sequences
+is also decoded by the oracle with its integer intermediates: query codes /
+int32 QK / P-operand codes / int32 PV accumulators bit-exact.  The
+benchmark's own launch, the one-launch step (this step's append inside the
+decode), is checked the same way on the 256-sequence workload."""
 import math
 
 import numpy as np
@@ -43,7 +46,7 @@ def _sample(ctx, n_random, seed):
     return np.array(sorted(pick))
 
 
-def _build_gpu(wl, layer, dev):
+def _build_gpu(wl, layer, dev, append=True):
     n_tok = int(wl.ctx.sum())
     k, v, q = draw_values(wl.seed, layer, n_tok, wl.B, wl.Hq, wl.Hkv, device=dev)
     off = np.zeros(wl.B + 1, np.int64)
@@ -56,11 +59,42 @@ def _build_gpu(wl, layer, dev):
     cache = kv4.Kv4Cache.zeros(wl.num_pages, wl.Hkv, wl.max_slots, dev)
     kv4.prefill_quantize(cache, k[rows].contiguous(), v[rows].contiguous(), cu,
                          torch.zeros(wl.B, dtype=torch.int32, device=dev), slots, table, int(lead.max()))
-    if wl.append_step:
+    if wl.append_step and append:
         last = torch.from_numpy(off[:-1] + lead).to(dev)
         kv4.append(cache, k[last].contiguous(), v[last].contiguous(),
                    torch.from_numpy((wl.ctx - 1).astype(np.int32)).to(dev), slots, table)
     return cache, k, v, q, off, table, slots
+
+
+def _oracle_full(wl, k, v, q, off):
+    """The oracle's cache of the whole batch in the workload's own page table
+    and slots (re-prefill of the leading positions, then this step's token),
+    and its decode of every sequence and head (out, lse)."""
+    lead = wl.ctx - 1 if wl.append_step else wl.ctx
+    kh, vh = bf16_bits(k), bf16_bits(v)
+    rows = np.concatenate([np.arange(off[b], off[b] + lead[b]) for b in range(wl.B)])
+    cu = np.concatenate([[0], np.cumsum(lead)]).astype(np.int32)
+    cache = oracle.Cache(wl.num_pages, wl.Hkv, wl.max_slots)
+    oracle.prefill(cache, kh[rows], vh[rows], cu, np.zeros(wl.B, np.int32), wl.slots, wl.page_table)
+    del rows
+    if wl.append_step:
+        last = off[:-1] + lead
+        oracle.append(cache, kh[last], vh[last], lead.astype(np.int32), wl.slots, wl.page_table)
+    del kh, vh
+    out, lse, _ = oracle.decode(cache, bf16_bits(q), wl.ctx.astype(np.int32), wl.slots, wl.page_table,
+                                wl.Hq, SCALE)
+    return cache, out, lse
+
+
+def _compare_full(cache, out, lse, ref, ref_out, ref_lse, what):
+    assert np.array_equal(cache.pages.cpu().numpy(), ref.pages), f"{what}: page bytes differ"
+    assert np.array_equal(cache.side_codes.cpu().numpy(), ref.side_codes), f"{what}: side codes differ"
+    assert np.array_equal(cache.side_scales.cpu().numpy().view(np.uint16), ref.side_scales), \
+        f"{what}: side scales differ"
+    err = float(np.abs(out.cpu().numpy() - ref_out).max())
+    lerr = float(np.abs(lse.cpu().numpy() - ref_lse).max())
+    _say(f"{what}: every sequence and head: out {err:.2e} lse {lerr:.2e}; pages and side rows equal")
+    assert err <= OUT_TOL and lerr <= LSE_TOL, (what, err, lerr)
 
 
 def _oracle_for(wl, sample, k, v, q, off):
@@ -103,6 +137,10 @@ def test_fullsize_sampled_parity(index, layer):
     out_d, lse_d, dbg = kv4.decode_attention_debug(cache, q, ctx_d, slots, table, max_ctx, SCALE)
     torch.cuda.synchronize()
     assert torch.equal(out, out_d) and torch.equal(lse, lse_d)
+    _say("[fullsize] oracle on the whole batch")
+    ref_all, out_all, lse_all = _oracle_full(wl, k, v, q, off)
+    _compare_full(cache, out, lse, ref_all, out_all, lse_all, f"[fullsize] {wl.name} layer {layer}")
+    del ref_all, out_all, lse_all
     sample = _sample(wl.ctx, 5, 100 + index + layer)
     _say(f"[fullsize] oracle on sequences {sample.tolist()} (ctx {wl.ctx[sample].tolist()})")
     ref, rtable, ref_out, ref_lse, ref_dbg = _oracle_for(wl, sample, k, v, q, off)
@@ -133,6 +171,26 @@ def test_fullsize_sampled_parity(index, layer):
     assert err <= OUT_TOL and lerr <= LSE_TOL, (err, lerr)
     # every output is finite and every lse at least the largest logit seen by any region
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("layer", [0, 35])
+def test_fullsize_one_launch_step(layer):
+    """The launch bench.py times: kv4_append_decode_attention on the
+    256-sequence workload (re-prefill of [0, ctx-1), then this step's append
+    inside the decode), against the oracle's append + decode of the whole
+    batch: every page block and side row bit-exact, every out and lse within
+    the bar."""
+    dev = torch.device("cuda")
+    wl = make_workload(4)
+    _say(f"[fullsize] one-launch step, workload {wl.name} layer {layer}")
+    cache, k, v, q, off, table, slots = _build_gpu(wl, layer, dev, append=False)
+    last = torch.from_numpy(off[:-1] + wl.ctx - 1).to(dev)
+    ctx_d = torch.from_numpy(wl.ctx.astype(np.int32)).to(dev)
+    out, lse = kv4.append_decode_attention(cache, k[last].contiguous(), v[last].contiguous(), ctx_d - 1, q,
+                                           ctx_d, slots, table, int(wl.ctx.max()), SCALE)
+    torch.cuda.synchronize()
+    ref, ref_out, ref_lse = _oracle_full(wl, k, v, q, off)
+    _compare_full(cache, out, lse, ref, ref_out, ref_lse, f"[fullsize] one-launch step layer {layer}")
 
 
 @pytest.mark.parametrize("first", [0, 9, 18, 27])

@@ -36,6 +36,9 @@ def _clone(cache, sink, window):
     ("split_budget", dict(ctx=EDGE, Hq=4, Hkv=1, seed=102), (32, 64)),
     ("all_sink_fallback", dict(ctx=EDGE, Hq=4, Hkv=1, seed=103), (144, 0)),
     ("all_recent", dict(ctx=EDGE, Hq=4, Hkv=1, seed=104), (0, 144)),
+    ("window_100", dict(ctx=EDGE, Hq=8, Hkv=2, seed=105), (16, 100)),
+    ("window_7", dict(ctx=EDGE + [8, 23, 24, 25, 151, 152, 153], Hq=4, Hkv=1, seed=106), (0, 7)),
+    ("window_1", dict(ctx=EDGE + [18, 33], Hq=4, Hkv=1, seed=107), (32, 1)),
 ])
 def test_fused_step_equals_append_then_decode(name, kw, sw):
     _say(f"[fused] {name} s={sw[0]} w={sw[1]}")

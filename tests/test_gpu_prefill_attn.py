@@ -122,9 +122,11 @@ def test_chunk_blocks_and_budgets():
 
 
 def test_benchmark_reprefill_sampled():
-    """The benchmark's re-prefill attention (8 chunks of 16,384 tokens, 32/8
-    heads, the same values and launch), sampled: tokens around every region
-    boundary of each chunk against the oracle's per-token attention."""
+    """The benchmark's re-prefill (8 chunks of 16,384 tokens, 32/8 heads, the
+    same values and launches): the whole quantized cache (all 8 x 16,384
+    tokens' page entries, side rows and scales) byte for byte against the
+    oracle's re-prefill, then the attention sampled at tokens around every
+    region boundary of each chunk against the oracle's per-token attention."""
     from synth import draw_values
     wl = make_workload(4)
     nseq, n = wl.prefill_nseq, wl.prefill_len
@@ -147,6 +149,11 @@ def test_benchmark_reprefill_sampled():
     hq = pq.view(torch.int16).cpu().numpy().view(np.uint16)
     ref = oracle.Cache(ppages, wl.Hkv, nseq)
     oracle.prefill(ref, hk, hv, cu.cpu().numpy(), start.cpu().numpy(), slot.cpu().numpy(), table.cpu().numpy())
+    assert np.array_equal(cache.pages.cpu().numpy(), ref.pages), "re-prefill page bytes differ"
+    assert np.array_equal(cache.side_codes.cpu().numpy(), ref.side_codes), "re-prefill side codes differ"
+    assert np.array_equal(cache.side_scales.cpu().numpy().view(np.uint16), ref.side_scales), \
+        "re-prefill side scales differ"
+    _say(f"[chunk] benchmark re-prefill: {ref.pages.nbytes >> 20} MiB of pages and all side rows equal")
     rng = np.random.default_rng(7)
     pos = [0, 15, 16, 31, 143, 144, 4095, n // 2 + 3, n - 129, n - 128, n - 127, n - 2, n - 1]
     tokens = np.array([s * n + p for s in (0, 3, 7) for p in pos], np.int64)

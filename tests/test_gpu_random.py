@@ -19,6 +19,10 @@ pytestmark = pytest.mark.gpu
 
 OUT_TOL, LSE_TOL = 2e-3, 1e-4
 BUDGETS = [(16, 128), (0, 0), (144, 0), (0, 144), (32, 64), (48, 96), (16, 0), (0, 16)]
+# windows that are not a multiple of the page size: the boundary between the
+# INT4 and the INT8 regions falls inside a page (seeds from 100 on); with
+# w < 16 this step's token can share a page with the last main positions
+ODD_BUDGETS = [(16, 100), (0, 7), (32, 1), (0, 15), (16, 113), (48, 17)]
 EDGES = [1, 2, 15, 16, 17, 31, 32, 33, 127, 128, 129, 143, 144, 145, 160, 161, 176, 177]
 
 
@@ -42,7 +46,8 @@ def _random_workload(seed):
     extra = int(rng.integers(0, 5))
     wl.slots = rng.permutation(B + extra)[:B].astype(np.int32)
     wl.max_slots = B + extra
-    sink, window = BUDGETS[int(rng.integers(0, len(BUDGETS)))]
+    pool = ODD_BUDGETS if seed >= 100 else BUDGETS
+    sink, window = pool[int(rng.integers(0, len(pool)))] if seed < 100 else pool[seed % len(pool)]
     return wl, sink, window
 
 
@@ -57,7 +62,7 @@ def _compare(tag, out, lse, dbg, r_out, r_lse, r_dbg):
     assert err <= OUT_TOL and lerr <= LSE_TOL, (tag, err, lerr)
 
 
-@pytest.mark.parametrize("seed", list(range(8)) + list(range(22, 34)))
+@pytest.mark.parametrize("seed", list(range(8)) + list(range(22, 34)) + list(range(100, 106)))
 def test_random_decode(seed):
     wl, sink, window = _random_workload(seed)
     tag = f"decode seed {seed} B={wl.B} Hkv={wl.Hkv} s={sink} w={window} ctx max {int(wl.ctx.max())}"
@@ -73,7 +78,7 @@ def test_random_decode(seed):
     _compare(tag, out, lse, dbg, r_out, r_lse, r_dbg)
 
 
-@pytest.mark.parametrize("seed", list(range(8, 14)) + list(range(34, 42)))
+@pytest.mark.parametrize("seed", list(range(8, 14)) + list(range(34, 42)) + list(range(106, 118)))
 def test_random_fused_step(seed):
     """This step's append inside the decode launch, from a cache holding
     [0, ctx - 1): pages, side rows, out and lse against the oracle's append
@@ -105,7 +110,7 @@ def test_random_fused_step(seed):
     assert err <= OUT_TOL and lerr <= LSE_TOL, (tag, err, lerr)
 
 
-@pytest.mark.parametrize("seed", list(range(14, 22)) + list(range(42, 50)))
+@pytest.mark.parametrize("seed", list(range(14, 22)) + list(range(42, 50)) + list(range(118, 124)))
 def test_random_prefill_attention(seed):
     """Chunks of random length at the end of random prefixes (several per
     call), random budget and slots."""
