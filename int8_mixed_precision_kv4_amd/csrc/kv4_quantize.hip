@@ -283,6 +283,223 @@ __global__ __launch_bounds__(128) void prefill16_kernel(QuantArgs a, const int32
   }
 }
 
+// ---------------------------------------------- re-prefill, page per wave --
+// One wave quantizes the 16 page slots of one (page, kv-head) block: lane
+// (t = lane / 4, cg = lane % 4) holds token t's channels 32 i + 8 cg + k
+// (chunk i = 0..3, k = 0..7) of K and of V, so the per-vector work (the
+// min / max reductions, two of them across the lane quad, and the FP16
+// metadata) is shared by 16 tokens per instruction, and the V codes of the
+// whole page can be turned channel-major inside the wave.  Rotation: FWHT
+// strides 1, 2, 4 over k, 8 and 16 across the quad (lane distances 1 and 2),
+// 32 and 64 over i, in that order, then the 2^-3.5 scale: the sum tree of
+// fwht128_wave.  Codes come from the same division and rounding as
+// int4_code; a zero delta has a zero reciprocal, so the quotient is 0 and
+// the codes are 0 with no select.  Side rows as in prefill16_kernel.
+
+// FP32 in-lane butterflies over the chunk index bits (h = 8 for stride 32,
+// 16 for stride 64) or over k (h = 1, 2, 4): element j pairs with j + h.
+template <int H>
+__device__ __forceinline__ void fwht_inlane(float x[32]) {
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+    if ((j & H) == 0) {
+      const float u = x[j], v = x[j + H];
+      x[j] = u + v;
+      x[j + H] = u - v;
+    }
+}
+__device__ __forceinline__ void fwht128_quad(float x[32]) {
+  fwht_inlane<1>(x);
+  fwht_inlane<2>(x);
+  fwht_inlane<4>(x);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {  // strides 8 and 16: partner lanes lane ^ 1, lane ^ 2
+    const uint32_t flip = (threadIdx.x & 1) ? 0x80000000u : 0u;
+    x[j] = xor_lane_f<1>(x[j]) + __uint_as_float(__float_as_uint(x[j]) ^ flip);
+  }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t flip = (threadIdx.x & 2) ? 0x80000000u : 0u;
+    x[j] = xor_lane_f<2>(x[j]) + __uint_as_float(__float_as_uint(x[j]) ^ flip);
+  }
+  fwht_inlane<8>(x);
+  fwht_inlane<16>(x);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) x[j] = x[j] * kInvSqrt128;
+}
+
+// min / max over the 128 channels of the lane quad's token
+__device__ __forceinline__ Int4Meta int4_meta_quad(const float x[32]) {
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int j = 1; j < 32; ++j) {
+    mn = fminf(mn, x[j]);
+    mx = fmaxf(mx, x[j]);
+  }
+  mn = fminf(mn, dpp_f32<0xB1>(mn));
+  mn = fminf(mn, dpp_f32<0x4E>(mn));
+  mx = fmaxf(mx, dpp_f32<0xB1>(mx));
+  mx = fmaxf(mx, dpp_f32<0x4E>(mx));
+  return int4_meta(mn, mx);
+}
+__device__ __forceinline__ Int8Meta int8_meta_quad(const float x[32]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) a = fmaxf(a, fabsf(x[j]));
+  a = fmaxf(a, dpp_f32<0xB1>(a));
+  a = fmaxf(a, dpp_f32<0x4E>(a));
+  return int8_meta(a);
+}
+
+// INT4 code of x as a float in {0, ..., 15}: rint((x - m) / delta) clamped.
+__device__ __forceinline__ float int4_code_f(float x, const Int4Meta& q) {
+  return __builtin_amdgcn_fmed3f(__builtin_rintf(div_short_divisor(x - q.m, q.d, q.dinv)), 0.0f, 15.0f);
+}
+// Chunk of 8 channels -> 8 nibbles (channel k of the chunk in bits 4k..4k+3):
+// four codes at a time are combined as c0 + 16 c1 + 256 c2 + 4096 c3, exact
+// in FP32, before one conversion.
+__device__ __forceinline__ uint32_t int4_chunk(const float* x, const Int4Meta& q) {
+  float c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c[k] = int4_code_f(x[k], q);
+  const float lo = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c[3], 16.0f, c[2]), 16.0f, c[1]), 16.0f, c[0]);
+  const float hi = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c[7], 16.0f, c[6]), 16.0f, c[5]), 16.0f, c[4]);
+  return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+}
+__device__ __forceinline__ uint2 int8_chunk(const float* x, const Int8Meta& q) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k >> 2] |= (static_cast<uint32_t>(int8_code(x[k], q)) & 0xFFu) << (8 * (k & 3));
+  return make_uint2(w[0], w[1]);
+}
+
+// 256 threads = 4 waves, wave w takes kv-head 4 blockIdx.x % hq4 + w of page
+// blockIdx.x / hq4 of sequence blockIdx.y (hq4 = ceil(Hkv / 4)).
+__global__ __launch_bounds__(256) void prefill_page_kernel(QuantArgs a, const int32_t* __restrict__ cu,
+                                                           const int32_t* __restrict__ start_pos) {
+  const int hq4 = (a.Hkv + 3) >> 2;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int g = 4 * static_cast<int>(blockIdx.x % static_cast<unsigned>(hq4)) + wave;
+  const int lp = static_cast<int>(blockIdx.x / static_cast<unsigned>(hq4)), s = blockIdx.y;
+  if (g >= a.Hkv) return;  // wave-uniform; the kernel has no workgroup barrier
+  const int n = cu[s + 1] - cu[s];
+  if (n <= 0) return;
+  const int start = start_pos[s], end = start + n;
+  const int page = (start >> 4) + lp;
+  if (page > ((end - 1) >> 4)) return;
+  const int t0 = max(start - page * PAGE, 0), t1 = min(end - page * PAGE, PAGE);
+  const int t = lane >> 2, cg = lane & 3;
+  const bool live = t >= t0 && t < t1;
+  const int slot = a.slot ? a.slot[s] : s;
+  const int phys = a.page_table[static_cast<size_t>(s) * a.pt_stride + page];
+  uint8_t* blk = a.pages + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
+  const int keep_from = max(a.sink, end - a.window);  // == end when w = 0
+
+  // token t's K and V: 16-byte chunk 4 i + cg holds channels 32 i + 8 cg ..
+  // (lanes of slots outside [t0, t1) point at slot t0 and load nothing)
+  uint4 kr[4], vr[4];
+  {
+    const int tl = live ? t : t0;
+    const size_t vec = (static_cast<size_t>(cu[s]) + (page * PAGE + tl - start)) * a.Hkv + g;
+    const uint4* kp = reinterpret_cast<const uint4*>(a.k + vec * 64);
+    const uint4* vp = reinterpret_cast<const uint4*>(a.v + vec * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = live ? kp[4 * i + cg] : make_uint4(0u, 0u, 0u, 0u);
+      vr[i] = live ? vp[4 * i + cg] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  float kx[32], vx[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unpack_bf16x8(kr[i], kx + 8 * i);
+    unpack_bf16x8(vr[i], vx + 8 * i);
+  }
+  fwht128_quad(kx);  // keys are stored in the rotated basis
+
+  const Int4Meta kq = int4_meta_quad(kx);
+  const Int4Meta vq = int4_meta_quad(vx);
+  uint32_t kc[4], vc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kc[i] = int4_chunk(kx + 8 * i, kq);
+    vc[i] = int4_chunk(vx + 8 * i, vq);
+  }
+  if (live) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(blk + 64 * t + 16 * i + 4 * cg) = kc[i];
+    if (cg == 0) {
+      *reinterpret_cast<uint32_t*>(blk + OFF_KMETA + 4 * t) = kq.d16 | (kq.m16 << 16);
+      *reinterpret_cast<uint32_t*>(blk + OFF_VMETA + 4 * t) = vq.d16 | (vq.m16 << 16);
+    }
+  }
+  // INT8 side row: final sinks and the last w positions of the sequence
+  const int p = page * PAGE + t;
+  const bool side = live && (p < a.sink || p >= keep_from);
+  if (__builtin_amdgcn_ballot_w64(side)) {  // the quad reductions need every lane of a quad
+    const Int8Meta ks = int8_meta_quad(kx), vs = int8_meta_quad(vx);
+    if (side) {
+      const size_t r = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS + side_row(a, p);
+      int8_t* codes = a.side_codes + r * 2 * HD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<uint2*>(codes + 32 * i + 8 * cg) = int8_chunk(kx + 8 * i, ks);
+        *reinterpret_cast<uint2*>(codes + HD + 32 * i + 8 * cg) = int8_chunk(vx + 8 * i, vs);
+      }
+      if (cg == 0) {
+        a.side_scales[r * 2] = static_cast<uint16_t>(ks.s16);
+        a.side_scales[r * 2 + 1] = static_cast<uint16_t>(vs.s16);
+      }
+    }
+  }
+
+  // V codes channel-major through the wave's 1 KB of LDS: written token-major
+  // (row t = 64 bytes, channel 2b in the low nibble of byte b), then lane L
+  // gathers byte L of the 16 rows (channels 2L, 2L+1 of every slot) and
+  // splits the nibbles into the two channels' 8-byte runs.
+  __shared__ __attribute__((aligned(16))) uint8_t vt[4][PAGE * 64];
+  uint8_t* tl = vt[wave];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(tl + 64 * t + 16 * i + 4 * cg) = vc[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint32_t lo[4], hi[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    // bytes of slots 4m .. 4m+3, then the low nibbles of slot pairs (2k, 2k+1)
+    // into bytes 0 and 2, and the high nibbles likewise
+    const uint32_t d = static_cast<uint32_t>(tl[64 * (4 * m) + lane]) |
+                       (static_cast<uint32_t>(tl[64 * (4 * m + 1) + lane]) << 8) |
+                       (static_cast<uint32_t>(tl[64 * (4 * m + 2) + lane]) << 16) |
+                       (static_cast<uint32_t>(tl[64 * (4 * m + 3) + lane]) << 24);
+    const uint32_t x = d & 0x0F0F0F0Fu, z = d & 0xF0F0F0F0u;
+    lo[m] = x | (x >> 4);
+    hi[m] = (z >> 4) | (z >> 8);
+  }
+  // channel 2L: bytes 0 and 2 of lo[0..3]; channel 2L + 1: the same of hi
+  uint4 out;
+  out.x = __builtin_amdgcn_perm(lo[1], lo[0], 0x06040200u);
+  out.y = __builtin_amdgcn_perm(lo[3], lo[2], 0x06040200u);
+  out.z = __builtin_amdgcn_perm(hi[1], hi[0], 0x06040200u);
+  out.w = __builtin_amdgcn_perm(hi[3], hi[2], 0x06040200u);
+  uint4* dst = reinterpret_cast<uint4*>(blk + OFF_VCODE + 16 * lane);
+  if (t0 > 0 || t1 < PAGE) {  // a partial page keeps the other slots' nibbles
+    uint32_t keep0 = 0u, keep1 = 0u;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      keep0 |= (tt >= t0 && tt < t1) ? 0u : (0xFu << (4 * tt));
+      keep1 |= (tt + 8 >= t0 && tt + 8 < t1) ? 0u : (0xFu << (4 * tt));
+    }
+    const uint4 old = *dst;
+    out.x = (out.x & ~keep0) | (old.x & keep0);
+    out.y = (out.y & ~keep1) | (old.y & keep1);
+    out.z = (out.z & ~keep0) | (old.z & keep0);
+    out.w = (out.w & ~keep1) | (old.w & keep1);
+  }
+  *dst = out;
+}
+
 // ------------------------------------------------------------ KV8 pool --
 // KV8 everywhere (the INT8 comparison variant): every position in the side
 // rows' representation (rotated key, symmetric INT8 per 128-dim vector, FP16
@@ -382,7 +599,8 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* k, const uint16_t*
               slot, page_table, pt_stride, c.sink, c.window};
   const int pages = (max_seqlen + PAGE - 1) / PAGE + 1;
   if (mx) hipLaunchKernelGGL(prefill16_kernel<true>, dim3(pages * c.Hkv, nseq), dim3(128), 0, s, a, cu, start);
-  else hipLaunchKernelGGL(prefill16_kernel<false>, dim3(pages * c.Hkv, nseq), dim3(128), 0, s, a, cu, start);
+  else hipLaunchKernelGGL(prefill_page_kernel, dim3(pages * ((c.Hkv + 3) / 4), nseq), dim3(256), 0, s, a, cu,
+                          start);
   return hipGetLastError();
 }
 
