@@ -59,14 +59,9 @@ __global__ __launch_bounds__(256) void bf16_plan_kernel(BfArgs a) {
   }
 }
 
-__device__ __forceinline__ float qk_rows_f(v4f d) {
-  const auto r01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[0]), __float_as_uint(d[1]),
-                                                    false, false);
-  const auto r23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[2]), __float_as_uint(d[3]),
-                                                    false, false);
-  const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
-  return __uint_as_float(r[0]);
-}
+// QK output with each head's query in four A rows (row r = head r / 4): lane
+// l holds head l / 16 at position l % 16 in every register.
+__device__ __forceinline__ float qk_rows_f(v4f d) { return d[0]; }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void bf16_main_kernel(BfArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 pstage[4][GQA][2 * PAGE];
@@ -96,12 +91,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const size_t qb = static_cast<size_t>(b) * a.Hq + g * GQA;
     v8bf qa[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (r16 < GQA)
-        qa[m] = *reinterpret_cast<const v8bf*>(a.q + (qb + r16) * HD + 32 * m + 8 * grp);
-      else
-        qa[m] = v8bf{};
-    }
+    for (int m = 0; m < 4; ++m)
+      qa[m] = *reinterpret_cast<const v8bf*>(a.q + (qb + (r16 >> 2)) * HD + 32 * m + 8 * grp);
     float Zr = -INFINITY, Ls = 0.0f;
     v4f O[8];
 #pragma unroll

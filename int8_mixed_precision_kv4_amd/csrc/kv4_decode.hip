@@ -100,6 +100,11 @@ typedef __attribute__((address_space(3))) void* lptr;
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitLgkm0 = 0xC07F;
 
+// Cache policy of the page loads: non-temporal.  Every page block of a step is
+// read once, so the loads stream past the caches instead of allocating in
+// them (about 10% faster for the whole main kernel than default loads).
+constexpr int kNT = 2;
+
 // Plan for batches of more than 256 sequences (smaller batches build it in
 // registers in every main-kernel wave): one workgroup.
 __global__ __launch_bounds__(256) void plan_kernel(DecArgs a) { build_plan(a); }
@@ -151,51 +156,58 @@ __device__ __forceinline__ GroupQuery quantize_group_query(uint4 raw, float scal
   return g;
 }
 
-// QK MFMA output has head v of position l%16 in register v of lanes 0..15;
-// move head h to row h (lanes 16h..16h+15).
-__device__ __forceinline__ int qk_rows(v4i d) {
-  const auto r01 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(d[0]),
-                                                    static_cast<uint32_t>(d[1]), false, false);
-  const auto r23 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(d[2]),
-                                                    static_cast<uint32_t>(d[3]), false, false);
-  const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
-  return static_cast<int>(r[0]);
-}
+// QK on a 16x16 MFMA with the 4 heads' query rows each repeated 4 times
+// (A row r = head r / 4): lane l then receives rows 4 (l / 16) .. + 3 of
+// column l % 16, all four the dot product of head l / 16 with position
+// l % 16, which is the (head, position) layout of the softmax work; no lane
+// moves are needed.
+__device__ __forceinline__ int qk_rows(v4i d) { return d[0]; }
 
 // ------------------------------------------------------------ protected --
 
-// Round two FP32 values to BF16 (nearest even) with one v_cvt_pk_bf16_f32;
-// results kept in FP32.
-__device__ __forceinline__ void round_bf16x2(float& x, float& y) {
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Two FP32 values as packed BF16 (nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   typedef float f2 __attribute__((ext_vector_type(2)));
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-  const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{x, y}), b2));
-  x = __uint_as_float(u << 16);
-  y = __uint_as_float(u & 0xFFFF0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{x, y}), b2));
 }
 
 // Protected-region partial of one (kv-head g, sequence b), computed by one
 // workgroup of the main kernel (the last B*Hkv workgroups of its grid, which
 // the dispatcher starts as main-region workgroups retire; none when s = w = 0).
-// Only rows [0, s+w) are read.  QK: up to 9
-// MFMA row groups of 16 side rows spread over the 4 waves.  Softmax: wave h for head h.
-// PV: wave w takes rows [36w, 36w+36), lane (rp, cg) rows 36w + rp + 2i and
-// channels 4cg..4cg+3 for all 4 heads; the 2 row phases of a wave are reduced
-// with a permlane swap and the 4 waves through LDS.  Wave h writes the
-// partial (A[128], Z, l) of head h to the workspace.
-constexpr int kProtLds = SIDE_ROWS * GQA * 4 + SIDE_ROWS * 4 + 4 * GQA * HD * 4 + GQA * HD + GQA * 4;  // 11600 B
-constexpr int kProtLdsFused = kProtLds + 2 * HD + 8;  // plus this step's INT8 row and its scales
+// Only rows [0, s+w) are read.  QK: up to 9 MFMA row groups of 16 side rows
+// spread over the 4 waves.  Softmax: wave h for head h, its FP32 weights
+// written to LDS as two BF16 parts, hi = bf16(e) and lo = bf16(e - hi), 16
+// significant bits.  PV on BF16 MFMAs over the V rows staged in LDS (v^ =
+// bf16(s_v c)): wave w owns channels 32 w .. 32 w + 31 for all rows and heads,
+// so each wave stores its share of the partial directly; wave h adds Z and l
+// of head h.
+constexpr int kPvRows = 160;  // 144 side rows padded to 5 MFMA k-steps of 32
+constexpr int kPrSe = 0;                                 // float [144][4] logits
+constexpr int kPrSv = kPrSe + SIDE_ROWS * GQA * 4;       // float [160] V scales (0: row unused)
+constexpr int kPrP = kPrSv + kPvRows * 4;                // bf16 [2][4][160] weights, hi then lo
+constexpr int kPrV = kPrP + 2 * GQA * kPvRows * 2;       // int8 [144][128] V codes of the side rows
+constexpr int kPrQ = kPrV + SIDE_ROWS * HD;              // int8 [4][128] query codes
+constexpr int kPrC = kPrQ + GQA * HD;                    // float [4] c_q per head
+constexpr int kProtLds = kPrC + GQA * 4;                 // 24192 B
+constexpr int kProtLdsFused = kProtLds + 2 * HD + 8;     // plus this step's INT8 row and its scales
+// The PV reads of rows 144 .. 159 land in the bytes after the V rows (finite
+// int8 values, weighted by a zero scale): they must stay inside the role's LDS.
+static_assert(kPrV + kPvRows * HD <= kProtLdsFused + 2048, "padded V rows inside the protected LDS");
 
 template <bool DEBUG>
 __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b, uint8_t* lds_raw) {
-  constexpr int kRowsPerWave = SIDE_ROWS / 4;  // 36
   const int wave = wave_id(), lane = threadIdx.x & 63, tid = threadIdx.x;
   const int r16 = lane & 15, grp = lane >> 4;
-  auto se = reinterpret_cast<float (*)[GQA]>(lds_raw);                                  // [144][4] logits, then weights
-  float* ssv = reinterpret_cast<float*>(lds_raw + SIDE_ROWS * GQA * 4);                   // [144] V scales (0: row unused)
-  auto red = reinterpret_cast<float (*)[GQA][HD]>(lds_raw + SIDE_ROWS * GQA * 4 + SIDE_ROWS * 4);  // [4][4][128]
-  int8_t* qn = reinterpret_cast<int8_t*>(lds_raw + SIDE_ROWS * GQA * 4 + SIDE_ROWS * 4 + 4 * GQA * HD * 4);  // [4][128]
-  float* cqs = reinterpret_cast<float*>(qn + GQA * HD);                                                    // [4]
+  auto se = reinterpret_cast<float (*)[GQA]>(lds_raw + kPrSe);
+  float* ssv = reinterpret_cast<float*>(lds_raw + kPrSv);
+  uint16_t* pw = reinterpret_cast<uint16_t*>(lds_raw + kPrP);  // [hi, lo][head][160]
+  uint8_t* vst = lds_raw + kPrV;
+  int8_t* qn = reinterpret_cast<int8_t*>(lds_raw + kPrQ);
+  float* cqs = reinterpret_cast<float*>(lds_raw + kPrC);
 
   const int L = ld_const(a.ctx + b);
   const int E = L;  // the cache ends at this step's token
@@ -244,16 +256,16 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
       sk[k] = f16_value(__builtin_nontemporal_load(scales + 2 * (16 * rg + r16)));
     }
   }
-  // V codes of this wave's PV rows
-  const int rp = lane >> 5, cg = lane & 31;
-  uint32_t vop[kRowsPerWave / 2];
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave / 2; ++i) {
-    const int r = kRowsPerWave * wave + rp + 2 * i;
-    vop[i] = r < nrows ? __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(side + (2 * r + 1) * HD + 4 * cg)) : 0u;
+  // V codes of the used rows into LDS, 8 rows (1 KB) per instruction: lane l
+  // moves bytes 16 (l % 8) .. of row 8 j + l / 8 (blocks j = wave, wave + 4, ..)
+  for (int j = wave; 8 * j < nrows; j += 4) {
+    const int r = 8 * j + (lane >> 3);
+    __builtin_amdgcn_global_load_lds(side + (2 * r + 1) * HD + 16 * (lane & 7), (lptr)(vst + 1024 * j), 16, 0,
+                                     kNT);
   }
-  if (tid < SIDE_ROWS)
-    ssv[tid] = side_position(tid, L, E, a.sink, a.window) >= 0 ? f16_value(scales[2 * tid + 1]) : 0.0f;
+  if (tid < kPvRows)
+    ssv[tid] = tid < SIDE_ROWS && side_position(tid, L, E, a.sink, a.window) >= 0 ? f16_value(scales[2 * tid + 1])
+                                                                                 : 0.0f;
   // Fused append: this step's token goes to its page slot and its side row,
   // and the INT8 row also to LDS; after the barrier below every wave replaces
   // what it loaded for that row (the loads above may have seen the old row).
@@ -305,31 +317,27 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the staged V rows have landed
   __syncthreads();
   if (r_new >= 0) {  // this step's row from LDS, one read per lane, selected in place
-    {
-      const v4i kn0 = *reinterpret_cast<const v4i*>(nrow + 16 * grp);
-      const v4i kn1 = *reinterpret_cast<const v4i*>(nrow + 64 + 16 * grp);
-      const float skn = nscale[0];
+    const v4i kn0 = *reinterpret_cast<const v4i*>(nrow + 16 * grp);
+    const v4i kn1 = *reinterpret_cast<const v4i*>(nrow + 64 + 16 * grp);
+    const float skn = nscale[0];
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const bool hit = 16 * (wave + 4 * k) + r16 == r_new;
-        kop[k][0] = hit ? kn0 : kop[k][0];
-        kop[k][1] = hit ? kn1 : kop[k][1];
-        sk[k] = hit ? skn : sk[k];
-      }
+    for (int k = 0; k < 3; ++k) {
+      const bool hit = 16 * (wave + 4 * k) + r16 == r_new;
+      kop[k][0] = hit ? kn0 : kop[k][0];
+      kop[k][1] = hit ? kn1 : kop[k][1];
+      sk[k] = hit ? skn : sk[k];
     }
-    const uint32_t vn = *reinterpret_cast<const uint32_t*>(nrow + HD + 4 * cg);
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave / 2; ++i)
-      vop[i] = kRowsPerWave * wave + rp + 2 * i == r_new ? vn : vop[i];
-    if (tid == r_new) ssv[tid] = nscale[1];  // read by the PV phase, after two more barriers
+    // the staged V row: read by the PV phase, after two more barriers
+    if (wave == 0) reinterpret_cast<uint16_t*>(vst + r_new * HD)[lane] = reinterpret_cast<const uint16_t*>(nrow + HD)[lane];
+    if (tid == r_new) ssv[tid] = nscale[1];
   }
-  v4i qa[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  if (r16 < GQA) {
-    qa[0] = *reinterpret_cast<const v4i*>(qn + r16 * HD + 16 * grp);
-    qa[1] = *reinterpret_cast<const v4i*>(qn + r16 * HD + 64 + 16 * grp);
-  }
+  // A operand: row r16 = head r16 / 4 (each head's codes in four rows)
+  v4i qa[2];
+  qa[0] = *reinterpret_cast<const v4i*>(qn + (r16 >> 2) * HD + 16 * grp);
+  qa[1] = *reinterpret_cast<const v4i*>(qn + (r16 >> 2) * HD + 64 + 16 * grp);
   const float c_q = cqs[grp];
 
   // ---- INT8 QK: lane (head grp, row 16 rg + r16)
@@ -348,67 +356,61 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   }
   __syncthreads();
 
-  // ---- FP32 softmax of head `wave` over the region (rows not in use: 0)
+  // ---- FP32 softmax of head `wave` over the region (rows not in use: 0); the
+  // weights go to LDS as hi + lo BF16 parts, zero past row 144
   float zl = -INFINITY;
   for (int i = lane; i < SIDE_ROWS; i += 64) zl = fmaxf(zl, se[i][wave]);
   const float Z = wave_max(zl);
   float ls = 0.0f;
-  for (int i = lane; i < SIDE_ROWS; i += 64) {
-    const float e = exp2s(se[i][wave] - Z);
-    se[i][wave] = e;
+  for (int i = lane; i < kPvRows; i += 64) {
+    const float e = i < SIDE_ROWS ? exp2s(se[i][wave] - Z) : 0.0f;
     ls += e;
+    const uint32_t hi = pack_bf16x2(e, 0.0f) & 0xFFFFu;
+    const uint32_t lo = pack_bf16x2(e - __uint_as_float(hi << 16), 0.0f) & 0xFFFFu;
+    pw[wave * kPvRows + i] = static_cast<uint16_t>(hi);
+    pw[(GQA + wave) * kPvRows + i] = static_cast<uint16_t>(lo);
   }
   ls = wave_sum(ls);
   __syncthreads();
 
-  // ---- PV with v^ = bf16(s_v c) and FP32 weights
-  float acc[GQA][4];
+  // ---- PV with v^ = bf16(s_v c): wave w, channels 32 w + 16 cb + n (column
+  // blocks cb = 0, 1).  MFMA rows 4 cb + h carry head h's weights (A zero in
+  // the other rows), so one accumulator gathers both blocks: lane (n, rg)
+  // ends with rows 4 rg .. 4 rg + 3 = heads 0..3 of channel 32 w + 16 rg + n.
+  // k = 32 rows per step, lane group grp holding rows 8 grp .. 8 grp + 7.
+  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const u4 zero4 = u4{0u, 0u, 0u, 0u};
+  const int hrow = r16 & 3, blk = r16 >> 2;
 #pragma unroll
-  for (int h = 0; h < GQA; ++h)
+  for (int st = 0; st < kPvRows / 32; ++st) {
+    const int p0 = 32 * st + 8 * grp;
+    const u4 ph = *reinterpret_cast<const u4*>(pw + hrow * kPvRows + p0);
+    const u4 pl = *reinterpret_cast<const u4*>(pw + (GQA + hrow) * kPvRows + p0);
+    const float4 sv0 = *reinterpret_cast<const float4*>(ssv + p0);
+    const float4 sv1 = *reinterpret_cast<const float4*>(ssv + p0 + 4);
+    const float sv[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[h][j] = 0.0f;
+    for (int cb = 0; cb < 2; ++cb) {
+      const int ch = 32 * wave + 16 * cb + r16;
+      float x[8];
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave / 2; ++i) {
-    const int r = kRowsPerWave * wave + rp + 2 * i;
-    const float4 e4 = *reinterpret_cast<const float4*>(&se[r][0]);
-    const float sv = ssv[r];
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = sv * static_cast<float>(static_cast<int8_t>((vop[i] >> (8 * j)) & 0xFF));
-    round_bf16x2(v[0], v[1]);
-    round_bf16x2(v[2], v[3]);
-    const float ev[GQA] = {e4.x, e4.y, e4.z, e4.w};
-#pragma unroll
-    for (int h = 0; h < GQA; ++h)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[h][j] = __builtin_fmaf(ev[h], v[j], acc[h][j]);
-  }
-  // reduce over the two row phases: lanes 0-31 keep heads 0, 1, lanes 32-63
-  // heads 2, 3
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    float hs[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[k][j]),
-                                                        __float_as_uint(acc[k + 2][j]), false, false);
-      hs[j] = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+      for (int i = 0; i < 8; ++i) x[i] = sv[i] * static_cast<float>(reinterpret_cast<const int8_t*>(vst)[(p0 + i) * HD + ch]);
+      const u4 pk = u4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                       pack_bf16x2(x[6], x[7])};
+      const v8bf vb = __builtin_bit_cast(v8bf, pk);
+      const bool mine = blk == cb;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, mine ? ph : zero4), vb, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, mine ? pl : zero4), vb, acc, 0, 0, 0);
     }
-    *reinterpret_cast<float4*>(&red[wave][k + 2 * rp][4 * cg]) = make_float4(hs[0], hs[1], hs[2], hs[3]);
   }
-  __syncthreads();
-
-  // ---- partial of head `wave`
-  float2 A = make_float2(0.0f, 0.0f);
+  // ---- this wave's 32 channels of the 4 heads' partials; Z and l of head `wave`
+  if (grp < 2) {
 #pragma unroll
-  for (int w2 = 0; w2 < 4; ++w2) {
-    const float2 x = reinterpret_cast<const float2*>(&red[w2][wave][0])[lane];
-    A.x += x.x;
-    A.y += x.y;
+    for (int h = 0; h < GQA; ++h) a.ws.prot[(qb + h) * kPart + 32 * wave + 16 * grp + r16] = acc[h];
   }
-  float* P = a.ws.prot + (qb + wave) * kPart;
-  reinterpret_cast<float2*>(P)[lane] = A;
   if (lane == 0) {
+    float* P = a.ws.prot + (qb + wave) * kPart;
     P[128] = Z;
     P[129] = ls;
   }
@@ -448,10 +450,6 @@ __device__ __forceinline__ int pcode_slot(int t) { return 8 * (t >> 3) + 4 * (t 
 // followed by 256 B where the P operand is assembled and 512 B where the
 // query codes of a group are rearranged into the MFMA operand order.
 constexpr int kSlotK = 0, kSlotV = 4096, kSlotMeta = 8192, kSlotP = 8704, kSlotQ = 8960, kSlotBytes = 9472;
-// Cache policy of the page loads: non-temporal.  Every page block of a step is
-// read once, so the loads stream past the caches instead of allocating in
-// them (about 10% faster for the whole main kernel than default loads).
-constexpr int kNT = 2;
 
 struct QuadRegs {
   uint4 kq[4], vq[4];
@@ -496,6 +494,9 @@ struct MainState {
 
 // One quad of 4 tiles (pages) for the 4 heads of a group.  Lane = (head grp,
 // position r16) for the softmax; MFMA operand layouts as described above.
+// A position outside the region gets the logit -inf (so its weight is 0)
+// and a zero V metadata word (so its u and e m_v are +0): two selects per
+// tile, no branches.
 template <bool DEBUG>
 __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, const QuadRegs& q,
                                              int np, v4i qa0, v4i qa1, float c_q, float S_q,
@@ -513,17 +514,22 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
   for (int t = 0; t < 4; ++t) {
     const int D = qk_rows(d[t]);
     const int pos = PAGE * (j0 + t) + r16;
-    const bool valid = (t < np) && (pos < main_end);
+    const bool valid = pos < (t < np ? main_end : 0);
     const float dk = f16_value(q.km[t] & 0xFFFFu);
     // q.k^ = s_q (delta * sum(qc*c) + m * sum(qc)); c_q carries s_q, the scale and log2(e)
-    const float z = valid ? __builtin_fmaf(dk, static_cast<float>(D), mul_f16(S_q, q.km[t] >> 16)) * c_q : -INFINITY;
+    const float z0 = __builtin_fmaf(dk, static_cast<float>(D), mul_f16(S_q, q.km[t] >> 16)) * c_q;
+    const float z = valid ? z0 : -INFINITY;
     zmax[t] = row16_max_ord(z);
-    // (metadata of positions outside the region may be any bits: selected away)
-    e[t] = valid ? exp2s(z - zmax[t]) : 0.0f;
-    u[t] = valid ? mul_f16(e[t], q.vm[t] & 0xFFFFu) : 0.0f;  // V scale folded into P
-    emv[t] = valid ? mul_f16(e[t], q.vm[t] >> 16) : 0.0f;    // V offset applied after the dot
+    // a masked position: exp2s(-inf - zmax) = 0 (NaN when the whole tile is
+    // masked, which exp2s also maps to 0); its metadata, which may be any
+    // bits, is replaced by zeros
+    e[t] = exp2s(z - zmax[t]);
+    const uint32_t vmt = valid ? q.vm[t] : 0u;
+    u[t] = mul_f16(e[t], vmt & 0xFFFFu);  // V scale folded into P
+    emv[t] = mul_f16(e[t], vmt >> 16);    // V offset applied after the dot
     umax[t] = __uint_as_float(row16_max_u32(__float_as_uint(u[t])));
     if (DEBUG && valid && a.dbg.qk) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + pos] = D;
+    __builtin_amdgcn_sched_barrier(0);  // one tile at a time: keeps the register count under 128
   }
   // 127 / u_max of the 16 (tile, head) pairs with one IEEE division:
   // lane (h, r16) divides for tile r16 % 4, then quads broadcast.
@@ -543,13 +549,16 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
       if (t < np && pos < main_end) a.dbg.pcode[(qb + grp) * a.dbg.max_ctx + pos] = static_cast<uint8_t>(uc);
     }
   }
-  // running reference max of each head; rescale what is accumulated
+  // running reference max of each head; rescale what is accumulated when
+  // some head's maximum moved (otherwise every factor would be exactly 1)
   const float Zn = fmaxf(st.Zr, fmaxf(fmaxf(zmax[0], zmax[1]), fmaxf(zmax[2], zmax[3])));
-  const float al = __builtin_amdgcn_exp2f(st.Zr - Zn);
+  if (__builtin_amdgcn_ballot_w64(Zn != st.Zr) != 0) {
+    const float al = __builtin_amdgcn_exp2f(st.Zr - Zn);
 #pragma unroll
-  for (int o = 0; o < 8; ++o) st.O[o] *= al;
-  st.Ls *= al;
-  st.Ms *= al;
+    for (int o = 0; o < 8; ++o) st.O[o] *= al;
+    st.Ls *= al;
+    st.Ms *= al;
+  }
   st.Zr = Zn;
   float wsu[4];
 #pragma unroll
@@ -594,9 +603,6 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
 // The main kernel streams units of kUnit pages of one segment through its
 // per-wave LDS slot; a format supplies the staging, the compute step, the
 // order of the query operand and the partial it leaves.
-
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // KV4-RL main region: quads of 4 INT4 pages (layouts above).
 enum class QueryMode { Int8EvenOdd, Int8Natural, Bf16 };
@@ -674,13 +680,6 @@ struct Kv8State {
   float Zr, Ls;
   v4f O[2];
 };
-
-// Two FP32 values as packed BF16 (nearest even).
-__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{x, y}), b2));
-}
 
 template <bool DEBUG>
 __device__ __forceinline__ void compute_pair(const DecArgs& a, Kv8State& st, const Kv8Regs& r, int np,
@@ -890,12 +889,10 @@ __device__ __forceinline__ void compute_mx_pair(const DecArgs& a, Kv8State& st, 
                                                 uint8_t* slot, int r16, int grp) {
   (void)qb;
   // QK on BF16 MFMAs; lane (head grp, position r16) after the move
-  v8bf qa[4] = {v8bf{}, v8bf{}, v8bf{}, v8bf{}};
-  if (r16 < GQA) {  // A operand: head r16, channels 32 m + 8 grp .. + 7
+  v8bf qa[4];  // A operand: row r16 = head r16 / 4, channels 32 m + 8 grp .. + 7
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      qa[m] = *reinterpret_cast<const v8bf*>(slot + kmxQ + 2 * (HD * r16 + 32 * m + 8 * grp));
-  }
+  for (int m = 0; m < 4; ++m)
+    qa[m] = *reinterpret_cast<const v8bf*>(slot + kmxQ + 2 * (HD * (r16 >> 2) + 32 * m + 8 * grp));
   float z[2];
   bool valid[2];
 #pragma unroll
@@ -905,9 +902,7 @@ __device__ __forceinline__ void compute_mx_pair(const DecArgs& a, Kv8State& st, 
     for (int m = 0; m < 4; ++m)
       d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], fp4x8_bf16(r.k[t][m], e8m0_value((r.ks[t] >> (8 * m)) & 0xFFu)),
                                                   d, 0, 0, 0);
-    const auto r01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[0]), __float_as_uint(d[1]), false, false);
-    const auto r23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[2]), __float_as_uint(d[3]), false, false);
-    const float D = __uint_as_float(__builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false)[0]);
+    const float D = d[0];  // rows 4 grp .. 4 grp + 3 all hold head grp
     const int pos = PAGE * (j0 + t) + r16;
     valid[t] = (t < np) && (pos < main_end);
     z[t] = valid[t] ? D * a.scale_log2 : -INFINITY;
@@ -1160,9 +1155,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
         for (int j = 0; j < 8; ++j) a.dbg.qcodes[bh * HD + 8 * r16 + j] = static_cast<int8_t>(gq.c[j]);
       if (a.dbg.qsum && r16 == 0) a.dbg.qsum[bh] = gq.S;
     }
-    // A operand of QK: rows 0..3 = the group's heads, k = channels (lane
-    // group grp covers channels 32grp..32grp+31, even / odd split); the codes
-    // go through the slot's query area to reach that layout.
+    // A operand of QK: row r = head r / 4, k = channels (lane group grp
+    // covers channels 32grp..32grp+31, even / odd split); the codes go
+    // through the slot's query area to reach that layout.
     uint8_t* qs = slot + kSlotQ + grp * HD;
     if constexpr (F::kQuery == QueryMode::Int8Natural) {  // channels 8 r16 .. 8 r16 + 7 in place
       const uint32_t lo = (gq.c[0] & 0xFF) | ((gq.c[1] & 0xFF) << 8) | ((gq.c[2] & 0xFF) << 16) |
@@ -1181,10 +1176,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (r16 < GQA) {
-      nqa0 = *reinterpret_cast<const v4i*>(slot + kSlotQ + r16 * HD + 16 * grp);
-      nqa1 = *reinterpret_cast<const v4i*>(slot + kSlotQ + r16 * HD + 64 + 16 * grp);
-    }
+    // A operand of QK: row r16 = head r16 / 4 (qk_rows)
+    nqa0 = *reinterpret_cast<const v4i*>(slot + kSlotQ + (r16 >> 2) * HD + 16 * grp);
+    nqa1 = *reinterpret_cast<const v4i*>(slot + kSlotQ + (r16 >> 2) * HD + 64 + 16 * grp);
     nqi = make_float2(gq.c_q, __int_as_float(gq.S));
   };
 
