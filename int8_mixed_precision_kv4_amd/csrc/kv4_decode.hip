@@ -1006,16 +1006,20 @@ struct MxFormat {
 
 // Work split of the main region: the global page list (sequence-major, then
 // kv-head, then logical page; T pages) is cut into one contiguous chunk per
-// wave, chunk c = [c q + min(c, r), (c+1) q + min(c+1, r)) with q = T / nw,
-// r = T % nw.  A wave writes one partial per segment its chunk touches, at
-// slot c + b*Hkv + g: chunks visit segments in list order, so slots never
-// collide and nw + B*Hkv slots suffice.  The waves holding a segment's first
-// and last pages record their chunk indices for the merge.
+// wave, chunk c = [floor(T c / nw), floor(T (c+1) / nw)) when T >= nw (no
+// chunk empty), else [min(c, T), min(c+1, T)) (empty chunks only at the end).
+// A wave writes one partial per segment its chunk touches, at slot
+// c + b*Hkv + g: chunks visit segments in list order, so slots never collide
+// and nw + B*Hkv slots suffice.  The waves holding a segment's first and last
+// pages record their chunk indices for the merge, which reads every chunk in
+// between: none of them may be empty.
 struct Split {
-  int q, r;
+  int T, nw;
 };
-__device__ __forceinline__ Split make_split(int T, int nw) { return Split{T / nw, T % nw}; }
-__device__ __forceinline__ int chunk_begin(const Split& s, int c) { return c * s.q + min(c, s.r); }
+__device__ __forceinline__ Split make_split(int T, int nw) { return Split{T, nw}; }
+__device__ __forceinline__ int chunk_begin(const Split& s, int c) {  // wave-uniform, scalar
+  return s.T >= s.nw ? static_cast<int>((static_cast<int64_t>(s.T) * c) / s.nw) : min(c, s.T);
+}
 
 // The plan as seen by one main-kernel wave.  For up to 256 sequences every
 // wave builds it in registers from the context lengths (entry i, 1 <= i <= B,
