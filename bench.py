@@ -518,6 +518,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--library", default=None,
+                    help="another build of libkv4 to load instead of the package's (for A/B measurements of "
+                         "build variants, e.g. the v_dot4 decode quad)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the 8 x 16384-token re-prefill leg (quantize + attention) and "
                          "print its figures (for profiling those kernels)")
@@ -542,6 +545,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.library:
+        kv4.LIB_PATH = os.path.abspath(args.library)
     kv4.lib()
     wl = make_workload(WORKLOAD)
     if args.prefill_only:

@@ -20,14 +20,19 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source to an object in parallel, then link; returns the library path."""
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, jobs: int = 4, defines=(), out: str | None = None) -> str:
+    """Compile every source to an object in parallel, then link; returns the
+    library path.  defines / out: a variant build of the same sources (for
+    instance KV4_QUAD_DOT4=1, the v_dot4 form of the decode quad kept for
+    measurement) into another library file; the default is libkv4.so."""
+    lib = out or LIB
+    objdir = os.path.join(HERE, "_build" if not defines else "_build_" + "_".join(d.replace("=", "") for d in defines))
     os.makedirs(objdir, exist_ok=True)
     procs, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *[f for f in FLAGS if f != "-shared"], "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *[f for f in FLAGS if f != "-shared"], *["-D" + d for d in defines], "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd)))
@@ -35,14 +40,20 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     failed = [src for src, p in procs if p.wait() != 0]
     if failed:
         raise RuntimeError(f"hipcc failed on {failed}")
-    tmp = LIB + f".tmp{os.getpid()}"
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("--define", action="append", default=[], help="NAME=VALUE for every source")
+    ap.add_argument("--out", default=None, help="library path (default: libkv4.so in the package)")
+    args = ap.parse_args()
+    print(build(verbose=args.v, defines=tuple(args.define), out=args.out))
