@@ -520,7 +520,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--library", default=None,
                     help="another build of libkv4 to load instead of the package's (for A/B measurements of "
-                         "build variants, e.g. the v_dot4 decode quad)")
+                         "build variants made with int8_mixed_precision_kv4_amd/build.py --define/--out)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the 8 x 16384-token re-prefill leg (quantize + attention) and "
                          "print its figures (for profiling those kernels)")

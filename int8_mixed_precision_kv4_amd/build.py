@@ -23,8 +23,8 @@ FLAGS = [
 def build(verbose: bool = False, jobs: int = 4, defines=(), out: str | None = None) -> str:
     """Compile every source to an object in parallel, then link; returns the
     library path.  defines / out: a variant build of the same sources (for
-    instance KV4_QUAD_DOT4=1, the v_dot4 form of the decode quad kept for
-    measurement) into another library file; the default is libkv4.so."""
+    instance KV4_MAIN_WAVES_PER_SIMD=3) into another library file, for A/B
+    measurements; the default is libkv4.so."""
     lib = out or LIB
     objdir = os.path.join(HERE, "_build" if not defines else "_build_" + "_".join(d.replace("=", "") for d in defines))
     os.makedirs(objdir, exist_ok=True)

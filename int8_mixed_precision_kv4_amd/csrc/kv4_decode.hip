@@ -492,26 +492,6 @@ struct MainState {
   float O[8];
 };
 
-#ifndef KV4_QUAD_DOT4
-#define KV4_QUAD_DOT4 0
-#endif
-#if KV4_QUAD_DOT4
-// VALU form of the quad's integer products (v_dot4_i32_i8), built only to
-// compare it with the MFMA form; the results are the same integers.
-// 4x4 transpose across the 4 rows of 16 lanes: value v of row g -> value g
-// of row v.
-__device__ __forceinline__ void transpose_rows4(int v[4]) {
-  const auto a = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[2]), false, false);
-  const auto b = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[3]), false, false);
-  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  v[0] = static_cast<int>(c[0]);
-  v[1] = static_cast<int>(c[1]);
-  v[2] = static_cast<int>(d[0]);
-  v[3] = static_cast<int>(d[1]);
-}
-#endif
-
 // One quad of 4 tiles (pages) for the 4 heads of a group.  Lane = (head grp,
 // position r16) for the softmax; MFMA operand layouts as described above.
 // A position outside the region gets the logit -inf (so its weight is 0)
@@ -524,40 +504,11 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
                                              int r16, int grp, int pslot) {
   // integer QK of the four tiles
   v4i d[4];
-#if KV4_QUAD_DOT4
-  // lane (r16, grp) holds channels 32 grp .. + 31 of position r16: partial dot
-  // products for all 4 heads, then a transpose across the row groups and a sum
-  (void)qa0;
-  (void)qa1;
-  const uint8_t* qarea = stage + (kSlotQ - kSlotP);  // head h: even-channel codes, then odd
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t kd[4] = {q.kq[t].x, q.kq[t].y, q.kq[t].z, q.kq[t].w};
-    int dp[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const uint4 qe = *reinterpret_cast<const uint4*>(qarea + h * HD + 16 * grp);
-      const uint4 qo = *reinterpret_cast<const uint4*>(qarea + h * HD + 64 + 16 * grp);
-      const uint32_t qev[4] = {qe.x, qe.y, qe.z, qe.w}, qov[4] = {qo.x, qo.y, qo.z, qo.w};
-      int acc = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc = __builtin_amdgcn_sdot4(static_cast<int>(qev[j]), static_cast<int>(lo_nibbles(kd[j])), acc, false);
-        acc = __builtin_amdgcn_sdot4(static_cast<int>(qov[j]), static_cast<int>(lo_nibbles(kd[j] >> 4)), acc, false);
-      }
-      dp[h] = acc;
-    }
-    transpose_rows4(dp);
-    const int D = (dp[0] + dp[1]) + (dp[2] + dp[3]);
-    d[t] = v4i{D, D, D, D};
-  }
-#else
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     d[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa0, nib_lo(q.kq[t]), v4i{0, 0, 0, 0}, 0, 0, 0);
     d[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa1, nib_hi(q.kq[t]), d[t], 0, 0, 0);
   }
-#endif
   float zmax[4], e[4], u[4], umax[4], emv[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -620,37 +571,15 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#if KV4_QUAD_DOT4
-  // P codes of tile grp (this lane's V data) for the 4 heads: positions
-  // 0,2,4,6 | 1,3,5,7 | 8,10,12,14 | 9,11,13,15
-  uint4 pc[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) pc[h] = *reinterpret_cast<const uint4*>(stage + (grp * 4 + h) * 16);
-#else
   // A operand of PV: row 4h + tile, k-group = tile (block diagonal)
   v4i pa = *reinterpret_cast<const v4i*>(stage + (grp * 4 + (r16 >> 2)) * 16);
   if ((r16 & 3) != grp) pa = v4i{0, 0, 0, 0};
-#endif
 #pragma unroll
   for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
-#if KV4_QUAD_DOT4
-      const uint32_t w0 = e2 == 0 ? q.vq[s2].x : q.vq[s2].z, w1 = e2 == 0 ? q.vq[s2].y : q.vq[s2].w;
-      int xv[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        int x = __builtin_amdgcn_sdot4(static_cast<int>(pc[h].x), static_cast<int>(lo_nibbles(w0)), 0, false);
-        x = __builtin_amdgcn_sdot4(static_cast<int>(pc[h].y), static_cast<int>(lo_nibbles(w0 >> 4)), x, false);
-        x = __builtin_amdgcn_sdot4(static_cast<int>(pc[h].z), static_cast<int>(lo_nibbles(w1)), x, false);
-        xv[h] = __builtin_amdgcn_sdot4(static_cast<int>(pc[h].w), static_cast<int>(lo_nibbles(w1 >> 4)), x, false);
-      }
-      transpose_rows4(xv);  // row grp now holds head grp, tile v in value v
-      const v4i acc = v4i{xv[0], xv[1], xv[2], xv[3]};
-#else
       const v4i bv = e2 == 0 ? nib_positions(q.vq[s2].x, q.vq[s2].y) : nib_positions(q.vq[s2].z, q.vq[s2].w);
       const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, bv, v4i{0, 0, 0, 0}, 0, 0, 0);
-#endif
       // lane: head grp, channel 8 r16 + 2 s2 + e2, tile v in register v
       const int o = 2 * s2 + e2;
       float x = st.O[o];
