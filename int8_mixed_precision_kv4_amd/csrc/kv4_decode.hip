@@ -622,7 +622,10 @@ struct Kv4Format {
     (void)grp;
     quad_from_lds(q, slot, lane, r16);
   }
-  __device__ static void reset(State& st) {
+  __device__ static void reset(State& st, const uint8_t* slot, int r16, int grp) {
+    (void)slot;
+    (void)r16;
+    (void)grp;
     st.Zr = -INFINITY;
     st.Ls = 0.0f;
     st.Ms = 0.0f;
@@ -812,7 +815,10 @@ struct Kv8Format {
     for (int t = 0; t < 2; ++t) r.sk[t] = *reinterpret_cast<const uint16_t*>(slot + k8S + 64 * t + 2 * r16);
     r.sv = *reinterpret_cast<const uint4*>(slot + k8S + 64 * (grp >> 1) + 32 + 16 * (grp & 1));
   }
-  __device__ static void reset(State& st) {
+  __device__ static void reset(State& st, const uint8_t* slot, int r16, int grp) {
+    (void)slot;
+    (void)r16;
+    (void)grp;
     st.Zr = -INFINITY;
     st.Ls = 0.0f;
     st.O[0] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -849,8 +855,12 @@ struct Kv8Format {
 // appendix D.4): pairs of 2 pages in OCP MXFP4, attended on their exactly
 // dequantized values.  QK: the BF16-rounded rotated query against K codes
 // converted to BF16 by the hardware FP4 conversion with the block's E8M0 scale
-// (v_cvt_scalef32_pk_bf16_fp4; a lane's 8 channels share one block), BF16
-// MFMA 16x16x32 with FP32 accumulation.  PV: the FP32 weight of a position
+// (v_cvt_scalef32_pk_bf16_fp4), BF16 MFMA 16x16x32 with FP32 accumulation.
+// The four MFMAs of a tile take the channels in a relabelled order that is the
+// same for both operands: MFMA m, lane group grp covers channels
+// 32 grp + 8 m .. + 7, so a lane's operands of all four come from its own
+// 16 bytes of the position's K codes (one LDS read) and one block scale; the
+// query operands follow the same order and are read once per piece.  PV: the FP32 weight of a position
 // times 2^(V block exponent) is split into two BF16 parts per V block and
 // meets the unscaled V codes (converted at unit scale) on the same MFMA, rows
 // rotated as for KV8.  Slot layout:
@@ -863,8 +873,13 @@ struct Kv8Format {
 constexpr int kmxK = 0, kmxV = 2048, kmxS = 4096, kmxP = 4352, kmxQ = 6400;
 static_assert(kmxQ + 1024 <= kSlotBytes, "the MXFP4 slot must fit the per-wave LDS slot");
 
+struct MxState {
+  Kv8State s;
+  v8bf qa[4];  // A operands of QK: row r16 = head r16 / 4, channels 32 grp + 8 m .. + 7
+};
+
 struct MxRegs {
-  uint32_t k[2][4];  // 8 FP4 codes: channels 32 m + 8 grp .. of position r16
+  uint4 k[2];        // channel block grp of position r16: component m = channels 32 grp + 8 m .. + 7
   uint32_t ks[2], vs[2];
   uint32_t vq[8];    // 8 FP4 codes: positions 8 (grp & 1) .. of channel 16 s + r16, page grp >> 1
 };
@@ -884,24 +899,21 @@ __device__ __forceinline__ v8bf fp4x8_bf16(uint32_t w, float scale) {
 }
 
 template <bool DEBUG>
-__device__ __forceinline__ void compute_mx_pair(const DecArgs& a, Kv8State& st, const MxRegs& r,
+__device__ __forceinline__ void compute_mx_pair(const DecArgs& a, MxState& ms, const MxRegs& r,
                                                 int np, int j0, int main_end, size_t qb,
                                                 uint8_t* slot, int r16, int grp) {
   (void)qb;
+  Kv8State& st = ms.s;
   // QK on BF16 MFMAs; lane (head grp, position r16) after the move
-  v8bf qa[4];  // A operand: row r16 = head r16 / 4, channels 32 m + 8 grp .. + 7
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-    qa[m] = *reinterpret_cast<const v8bf*>(slot + kmxQ + 2 * (HD * (r16 >> 2) + 32 * m + 8 * grp));
   float z[2];
   bool valid[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
+    const float sc = e8m0_value((r.ks[t] >> (8 * grp)) & 0xFFu);  // this lane's K block
+    const uint32_t kw[4] = {r.k[t].x, r.k[t].y, r.k[t].z, r.k[t].w};
     v4f d = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], fp4x8_bf16(r.k[t][m], e8m0_value((r.ks[t] >> (8 * m)) & 0xFFu)),
-                                                  d, 0, 0, 0);
+    for (int m = 0; m < 4; ++m) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ms.qa[m], fp4x8_bf16(kw[m], sc), d, 0, 0, 0);
     const float D = d[0];  // rows 4 grp .. 4 grp + 3 all hold head grp
     const int pos = PAGE * (j0 + t) + r16;
     valid[t] = (t < np) && (pos < main_end);
@@ -963,7 +975,7 @@ struct MxFormat {
   static constexpr int kBlock = BLOCK_BYTES;
   static constexpr bool kProtected = true;
   typedef MxRegs Regs;
-  typedef Kv8State State;
+  typedef MxState State;
   __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -978,9 +990,7 @@ struct MxFormat {
     (void)lane;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        r.k[t][m] = *reinterpret_cast<const uint32_t*>(slot + kmxK + 1024 * t + 16 * (r16 + 16 * m) + 4 * grp);
+      r.k[t] = *reinterpret_cast<const uint4*>(slot + kmxK + 1024 * t + 16 * (r16 + 16 * grp));
       r.ks[t] = *reinterpret_cast<const uint32_t*>(slot + kmxS + 128 * t + 4 * r16);
       r.vs[t] = *reinterpret_cast<const uint32_t*>(slot + kmxS + 128 * t + 64 + 4 * r16);
     }
@@ -988,7 +998,13 @@ struct MxFormat {
 #pragma unroll
     for (int s = 0; s < 8; ++s) r.vq[s] = *reinterpret_cast<const uint32_t*>(vb + 128 * s);
   }
-  __device__ static void reset(State& st) { Kv8Format::reset(st); }
+  // a new piece: fresh state, and the query operands from the slot's query area
+  __device__ static void reset(State& st, const uint8_t* slot, int r16, int grp) {
+    Kv8Format::reset(st.s, slot, r16, grp);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      st.qa[m] = *reinterpret_cast<const v8bf*>(slot + kmxQ + 2 * (HD * (r16 >> 2) + 32 * grp + 8 * m));
+  }
   template <bool DEBUG>
   __device__ static void compute(const DecArgs& a, State& st, const Regs& r, int np, v4i qa0, v4i qa1,
                                  float c_q, float S_q, int j0, int main_end, size_t qb, uint8_t* slot,
@@ -1000,7 +1016,7 @@ struct MxFormat {
     (void)pslot;
     compute_mx_pair<DEBUG>(a, st, r, np, j0, main_end, qb, slot, r16, grp);
   }
-  __device__ static void finish(const State& st, float A[8], float& Z, float& L) { Kv8Format::finish(st, A, Z, L); }
+  __device__ static void finish(const State& st, float A[8], float& Z, float& L) { Kv8Format::finish(st.s, A, Z, L); }
   __device__ static void store(float* P0, const float A[8], int r16, int grp) { Kv8Format::store(P0, A, r16, grp); }
 };
 
@@ -1280,7 +1296,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
       c_q = nqi.x;
       S_q = static_cast<float>(__float_as_int(nqi.y));
       main_end = cd.main_end;
-      F::reset(st);
+      F::reset(st, slot, r16, grp);
     }
     have1 = have2;
     if (have2) {
