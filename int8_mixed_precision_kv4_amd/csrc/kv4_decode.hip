@@ -449,7 +449,7 @@ __device__ __forceinline__ int pcode_slot(int t) { return 8 * (t >> 3) + 4 * (t 
 //   [8192, 8704)  metadata, page t at 8192 + 128 t: 16 x {delta, m} K, then V
 // followed by 256 B where the P operand is assembled and 512 B where the
 // query codes of a group are rearranged into the MFMA operand order.
-constexpr int kSlotK = 0, kSlotV = 4096, kSlotMeta = 8192, kSlotP = 8704, kSlotQ = 8960, kSlotBytes = 9472;
+constexpr int kSlotK = 0, kSlotV = 4096, kSlotMeta = 8192, kSlotP = 8704, kSlotQ = 8960, kQuadSlotBytes = 9472;
 
 struct QuadRegs {
   uint4 kq[4], vq[4];
@@ -610,6 +610,7 @@ enum class QueryMode { Int8EvenOdd, Int8Natural, Bf16 };
 struct Kv4Format {
   static constexpr QueryMode kQuery = QueryMode::Int8EvenOdd;
   static constexpr int kUnit = 4;
+  static constexpr int kSlotBytes = kQuadSlotBytes;
   static constexpr int kWavesPerSimd = KV4_MAIN_WAVES_PER_SIMD;
   static constexpr int kBlock = BLOCK_BYTES;
   static constexpr bool kProtected = true;      // protected-region workgroups in the grid tail
@@ -622,6 +623,8 @@ struct Kv4Format {
     (void)grp;
     quad_from_lds(q, slot, lane, r16);
   }
+  // work done on a unit before the next unit's loads are issued into the slot: none
+  __device__ static void before_issue(const DecArgs&, State&, Regs&, int, int, int, uint8_t*, int, int) {}
   __device__ static void reset(State& st, const uint8_t* slot, int r16, int grp) {
     (void)slot;
     (void)r16;
@@ -780,6 +783,7 @@ __device__ __forceinline__ void compute_pair(const DecArgs& a, Kv8State& st, con
 struct Kv8Format {
   static constexpr QueryMode kQuery = QueryMode::Int8Natural;
   static constexpr int kUnit = 2;
+  static constexpr int kSlotBytes = kQuadSlotBytes;
   static constexpr int kWavesPerSimd = KV8_MAIN_WAVES_PER_SIMD;
   static constexpr int kBlock = KV8_BLOCK_BYTES;
   static constexpr bool kProtected = false;
@@ -815,6 +819,7 @@ struct Kv8Format {
     for (int t = 0; t < 2; ++t) r.sk[t] = *reinterpret_cast<const uint16_t*>(slot + k8S + 64 * t + 2 * r16);
     r.sv = *reinterpret_cast<const uint4*>(slot + k8S + 64 * (grp >> 1) + 32 + 16 * (grp & 1));
   }
+  __device__ static void before_issue(const DecArgs&, State&, Regs&, int, int, int, uint8_t*, int, int) {}
   __device__ static void reset(State& st, const uint8_t* slot, int r16, int grp) {
     (void)slot;
     (void)r16;
@@ -852,7 +857,7 @@ struct Kv8Format {
 };
 
 // MXFP4 variant of the main region (KV4-RL pages, comparison of 4-bit formats,
-// appendix D.4): pairs of 2 pages in OCP MXFP4, attended on their exactly
+// appendix D.4): units of 4 pages in OCP MXFP4, attended on their exactly
 // dequantized values.  QK: the BF16-rounded rotated query against K codes
 // converted to BF16 by the hardware FP4 conversion with the block's E8M0 scale
 // (v_cvt_scalef32_pk_bf16_fp4), BF16 MFMA 16x16x32 with FP32 accumulation.
@@ -863,25 +868,29 @@ struct Kv8Format {
 // query operands follow the same order and are read once per piece.  PV: the FP32 weight of a position
 // times 2^(V block exponent) is split into two BF16 parts per V block and
 // meets the unscaled V codes (converted at unit scale) on the same MFMA, rows
-// rotated as for KV8.  Slot layout:
-//   [0, 2048)     K codes in operand order, page t at 1024 t: lane (r16, c)
+// rotated as for KV8; the P operands of one V block at a time pass through
+// the slot (double buffered), which keeps the slot at 9728 B.  A unit is two
+// pairs: the first is computed before the next unit's loads are issued, then
+// the second pair's codes are read into registers, the loads go out, and the
+// second pair is computed while they stream.  Slot layout:
+//   [0, 4096)     K codes in operand order, page t at 1024 t: lane (r16, c)
 //                 holds channel block c of position r16 at 16 (r16 + 16 c)
-//   [2048, 4096)  V codes, page t at 2048 + 1024 t (the block's channel-major copy)
-//   [4096, 4352)  scales, page t at 4096 + 128 t: K E8M0 [16][4], V E8M0 [16][4]
-//   [4352, 6400)  P operand [V block][hi, lo][head][32 positions] BF16
-//   [6400, 7424)  BF16 rotated query [head][128]
-constexpr int kmxK = 0, kmxV = 2048, kmxS = 4096, kmxP = 4352, kmxQ = 6400;
-static_assert(kmxQ + 1024 <= kSlotBytes, "the MXFP4 slot must fit the per-wave LDS slot");
+//   [4096, 8192)  V codes, page t at 4096 + 1024 t (the block's channel-major copy)
+//   [8192, 8704)  scales, page t at 8192 + 128 t: K E8M0 [16][4], V E8M0 [16][4]
+//   [8704, 9728)  the BF16 rotated query [head][128] when a piece starts (read
+//                 into registers), then P operands of V block b at
+//                 8704 + 512 (b & 1): [hi, lo][head][32 positions] BF16
+constexpr int kmxK = 0, kmxV = 4096, kmxS = 8192, kmxQ = 8704, kmxP = 8704, kmxSlotBytes = 9728;
 
 struct MxState {
   Kv8State s;
   v8bf qa[4];  // A operands of QK: row r16 = head r16 / 4, channels 32 grp + 8 m .. + 7
 };
 
-struct MxRegs {
-  uint4 k[2];        // channel block grp of position r16: component m = channels 32 grp + 8 m .. + 7
+struct MxRegs {  // one pair of pages
+  uint4 k[2];        // page t, channel block grp of position r16: component m = channels 32 grp + 8 m .. + 7
   uint32_t ks[2], vs[2];
-  uint32_t vq[8];    // 8 FP4 codes: positions 8 (grp & 1) .. of channel 16 s + r16, page grp >> 1
+  uint32_t vq[8];    // 8 FP4 codes: positions 8 (grp & 1) .. of channel 16 s + r16, page grp >> 1 of the pair
 };
 
 __device__ __forceinline__ float e8m0_value(uint32_t e) {
@@ -898,11 +907,9 @@ __device__ __forceinline__ v8bf fp4x8_bf16(uint32_t w, float scale) {
   return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-template <bool DEBUG>
-__device__ __forceinline__ void compute_mx_pair(const DecArgs& a, MxState& ms, const MxRegs& r,
-                                                int np, int j0, int main_end, size_t qb,
-                                                uint8_t* slot, int r16, int grp) {
-  (void)qb;
+// One pair of pages (np of them in the region, the first at logical page j0).
+__device__ __forceinline__ void compute_mx_pair(const DecArgs& a, MxState& ms, const MxRegs& r, int np,
+                                                int j0, int main_end, uint8_t* slot, int r16, int grp) {
   Kv8State& st = ms.s;
   // QK on BF16 MFMAs; lane (head grp, position r16) after the move
   float z[2];
@@ -926,21 +933,6 @@ __device__ __forceinline__ void compute_mx_pair(const DecArgs& a, MxState& ms, c
 #pragma unroll
   for (int t = 0; t < 2; ++t) e[t] = valid[t] ? exp2s(z[t] - Zn) : 0.0f;
   st.Ls = __builtin_fmaf(st.Ls, al, e[0] + e[1]);
-  // P operand per V block b: e 2^(E_v(b) - 127), split into two BF16 parts
-  uint16_t* pst = reinterpret_cast<uint16_t*>(slot + kmxP);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float p = __builtin_ldexpf(e[t], static_cast<int>((r.vs[t] >> (8 * b)) & 0xFFu) - 127);
-      const uint32_t hi = pack_bf16x2(p, 0.0f) & 0xFFFFu;
-      const uint32_t lo = pack_bf16x2(p - __uint_as_float(hi << 16), 0.0f) & 0xFFFFu;
-      pst[((2 * b) * 4 + grp) * 32 + 16 * t + r16] = static_cast<uint16_t>(hi);
-      pst[((2 * b + 1) * 4 + grp) * 32 + 16 * t + r16] = static_cast<uint16_t>(lo);
-    }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     const float alh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * h));
@@ -951,18 +943,31 @@ __device__ __forceinline__ void compute_mx_pair(const DecArgs& a, MxState& ms, c
   const u4 zero4 = u4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    // A operand of V block b: head r16 % 4, positions 8 grp .. 8 grp + 7
-    const u4 ph = *reinterpret_cast<const u4*>(pst + ((2 * b) * 4 + (r16 & 3)) * 32 + 8 * grp);
-    const u4 pl = *reinterpret_cast<const u4*>(pst + ((2 * b + 1) * 4 + (r16 & 3)) * 32 + 8 * grp);
+    // P operand of V block b: e 2^(E_v(b) - 127), split into two BF16 parts
+    uint16_t* pst = reinterpret_cast<uint16_t*>(slot + kmxP + 512 * (b & 1));  // [hi, lo][head][32]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float pv = __builtin_ldexpf(e[t], static_cast<int>((r.vs[t] >> (8 * b)) & 0xFFu) - 127);
+      const uint32_t hi = pack_bf16x2(pv, 0.0f) & 0xFFFFu;
+      const uint32_t lo = pack_bf16x2(pv - __uint_as_float(hi << 16), 0.0f) & 0xFFFFu;
+      pst[grp * 32 + 16 * t + r16] = static_cast<uint16_t>(hi);
+      pst[(4 + grp) * 32 + 16 * t + r16] = static_cast<uint16_t>(lo);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // A operand: head r16 % 4, positions 8 grp .. 8 grp + 7
+    const u4 ph = *reinterpret_cast<const u4*>(pst + (r16 & 3) * 32 + 8 * grp);
+    const u4 pl = *reinterpret_cast<const u4*>(pst + (4 + (r16 & 3)) * 32 + 8 * grp);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int s = 2 * b + half;  // channels 16 s .. 16 s + 15 = 4 acc + r
-      const v8bf vb = fp4x8_bf16(r.vq[s], 1.0f);
-      const bool mine = (r16 >> 2) == (s & 3);
-      v4f o = st.O[s >> 2];
+      const int sv = 2 * b + half;  // channels 16 sv .. 16 sv + 15 = 4 acc + r
+      const v8bf vb = fp4x8_bf16(r.vq[sv], 1.0f);
+      const bool mine = (r16 >> 2) == (sv & 3);
+      v4f o = st.O[sv >> 2];
       o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, mine ? ph : zero4), vb, o, 0, 0, 0);
-      st.O[s >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, mine ? pl : zero4), vb, o,
-                                                             0, 0, 0);
+      st.O[sv >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, mine ? pl : zero4), vb, o,
+                                                              0, 0, 0);
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -970,7 +975,8 @@ __device__ __forceinline__ void compute_mx_pair(const DecArgs& a, MxState& ms, c
 
 struct MxFormat {
   static constexpr QueryMode kQuery = QueryMode::Bf16;
-  static constexpr int kUnit = 2;
+  static constexpr int kUnit = 4;
+  static constexpr int kSlotBytes = kmxSlotBytes;
   static constexpr int kWavesPerSimd = KV4_MAIN_WAVES_PER_SIMD;
   static constexpr int kBlock = BLOCK_BYTES;
   static constexpr bool kProtected = true;
@@ -978,25 +984,37 @@ struct MxFormat {
   typedef MxState State;
   __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 4; ++t) {
       __builtin_amdgcn_global_load_lds(blk[t] + 64 * r16 + 16 * grp, (lptr)(slot + kmxK + 1024 * t), 16, 0, kNT);
       __builtin_amdgcn_global_load_lds(blk[t] + OFF_VCODE + 16 * lane, (lptr)(slot + kmxV + 1024 * t), 16, 0, kNT);
     }
-    if (lane < 16)  // 2 pages x 128 B of scales
-      __builtin_amdgcn_global_load_lds((lane < 8 ? blk[0] : blk[1]) + OFF_KMETA + 16 * (lane & 7),
-                                       (lptr)(slot + kmxS), 16, 0, kNT);
+    if (lane < 32)  // 4 pages x 128 B of scales
+      __builtin_amdgcn_global_load_lds(blk[lane >> 3] + OFF_KMETA + 16 * (lane & 7), (lptr)(slot + kmxS), 16, 0, kNT);
+  }
+  // the codes and scales of pair p (pages 2p, 2p + 1 of the unit)
+  __device__ static void pair_from_lds(Regs& r, const uint8_t* slot, int p, int r16, int grp) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int pg = 2 * p + t;
+      r.k[t] = *reinterpret_cast<const uint4*>(slot + kmxK + 1024 * pg + 16 * (r16 + 16 * grp));
+      r.ks[t] = *reinterpret_cast<const uint32_t*>(slot + kmxS + 128 * pg + 4 * r16);
+      r.vs[t] = *reinterpret_cast<const uint32_t*>(slot + kmxS + 128 * pg + 64 + 4 * r16);
+    }
+    const uint8_t* vb = slot + kmxV + 1024 * (2 * p + (grp >> 1)) + 8 * r16 + 4 * (grp & 1);
+#pragma unroll
+    for (int sv = 0; sv < 8; ++sv) r.vq[sv] = *reinterpret_cast<const uint32_t*>(vb + 128 * sv);
   }
   __device__ static void from_lds(Regs& r, const uint8_t* slot, int lane, int r16, int grp) {
     (void)lane;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      r.k[t] = *reinterpret_cast<const uint4*>(slot + kmxK + 1024 * t + 16 * (r16 + 16 * grp));
-      r.ks[t] = *reinterpret_cast<const uint32_t*>(slot + kmxS + 128 * t + 4 * r16);
-      r.vs[t] = *reinterpret_cast<const uint32_t*>(slot + kmxS + 128 * t + 64 + 4 * r16);
-    }
-    const uint8_t* vb = slot + kmxV + 1024 * (grp >> 1) + 8 * r16 + 4 * (grp & 1);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) r.vq[s] = *reinterpret_cast<const uint32_t*>(vb + 128 * s);
+    pair_from_lds(r, slot, 0, r16, grp);
+  }
+  // the unit's first pair, then the second pair's codes into registers (the
+  // slot is then free for the next unit's loads)
+  __device__ static void before_issue(const DecArgs& a, State& st, Regs& r, int np, int j0, int main_end,
+                                      uint8_t* slot, int r16, int grp) {
+    compute_mx_pair(a, st, r, min(np, 2), j0, main_end, slot, r16, grp);
+    if (np > 2) pair_from_lds(r, slot, 1, r16, grp);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
   // a new piece: fresh state, and the query operands from the slot's query area
   __device__ static void reset(State& st, const uint8_t* slot, int r16, int grp) {
@@ -1014,7 +1032,8 @@ struct MxFormat {
     (void)c_q;
     (void)S_q;
     (void)pslot;
-    compute_mx_pair<DEBUG>(a, st, r, np, j0, main_end, qb, slot, r16, grp);
+    (void)qb;
+    if (np > 2) compute_mx_pair(a, st, r, np - 2, j0 + 2, main_end, slot, r16, grp);
   }
   __device__ static void finish(const State& st, float A[8], float& Z, float& L) { Kv8Format::finish(st.s, A, Z, L); }
   __device__ static void store(float* P0, const float A[8], int r16, int grp) { Kv8Format::store(P0, A, r16, grp); }
@@ -1122,8 +1141,8 @@ struct QuadDesc {
 
 template <class F, bool DEBUG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPerSimd, F::kWavesPerSimd))) void main_kernel(DecArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4][kSlotBytes];
-  static_assert(kProtLdsFused <= 4 * kSlotBytes, "the protected role reuses the main role's LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4][F::kSlotBytes];
+  static_assert(kProtLdsFused <= 4 * F::kSlotBytes, "the protected role reuses the main role's LDS");
   const int nw = a.ws.n_waves;
   if constexpr (F::kProtected) {
     if (blockIdx.x >= nw / 4) {  // protected-region workgroups fill the tail of the grid
@@ -1298,6 +1317,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
       main_end = cd.main_end;
       F::reset(st, slot, r16, grp);
     }
+    F::before_issue(a, st, q, cd.np, cd.j0, main_end, slot, r16, grp);
     have1 = have2;
     if (have2) {
       d1 = d2;
