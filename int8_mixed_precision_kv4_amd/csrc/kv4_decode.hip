@@ -941,17 +941,24 @@ __device__ __forceinline__ void compute_mx_pair(const DecArgs& a, MxState& ms, c
   }
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
   const u4 zero4 = u4{0u, 0u, 0u, 0u};
+  // the weight as two BF16 parts, hi = bf16(e) and lo = bf16(e - hi), kept
+  // as FP32 values whose low 16 bits are zero
+  float ehi[2], elo[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    ehi[t] = __uint_as_float(pack_bf16x2(0.0f, e[t]) & 0xFFFF0000u);
+    elo[t] = __uint_as_float(pack_bf16x2(0.0f, e[t] - ehi[t]) & 0xFFFF0000u);
+  }
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    // P operand of V block b: e 2^(E_v(b) - 127), split into two BF16 parts
+    // P operand of V block b: both parts times 2^(E_v(b) - 127), a power of
+    // two, so each stays a BF16 value (its high 16 bits are stored)
     uint16_t* pst = reinterpret_cast<uint16_t*>(slot + kmxP + 512 * (b & 1));  // [hi, lo][head][32]
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float pv = __builtin_ldexpf(e[t], static_cast<int>((r.vs[t] >> (8 * b)) & 0xFFu) - 127);
-      const uint32_t hi = pack_bf16x2(pv, 0.0f) & 0xFFFFu;
-      const uint32_t lo = pack_bf16x2(pv - __uint_as_float(hi << 16), 0.0f) & 0xFFFFu;
-      pst[grp * 32 + 16 * t + r16] = static_cast<uint16_t>(hi);
-      pst[(4 + grp) * 32 + 16 * t + r16] = static_cast<uint16_t>(lo);
+      const int ex = static_cast<int>((r.vs[t] >> (8 * b)) & 0xFFu) - 127;
+      pst[grp * 32 + 16 * t + r16] = static_cast<uint16_t>(__float_as_uint(__builtin_ldexpf(ehi[t], ex)) >> 16);
+      pst[(4 + grp) * 32 + 16 * t + r16] = static_cast<uint16_t>(__float_as_uint(__builtin_ldexpf(elo[t], ex)) >> 16);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
