@@ -710,6 +710,7 @@ __device__ __forceinline__ void compute_pair(const DecArgs& a, Kv8State& st, con
   }
   // running max of each head; weights relative to it, earlier sums rescaled
   const float Zn = fmaxf(st.Zr, row16_max(fmaxf(z[0], z[1])));
+  const bool moved = __builtin_amdgcn_ballot_w64(Zn != st.Zr) != 0;  // rescale needed
   const float al = __builtin_amdgcn_exp2f(st.Zr - Zn);
   st.Zr = Zn;
   float e[2];
@@ -745,12 +746,15 @@ __device__ __forceinline__ void compute_pair(const DecArgs& a, Kv8State& st, con
     svw[i] &= keep;
   }
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  // rescale what is accumulated: head h in register h
+  // rescale what is accumulated (head h in register h) when some head's
+  // maximum moved; otherwise every factor is exactly 1
+  if (moved) {
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const float alh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * h));
-    st.O[0][h] *= alh;
-    st.O[1][h] *= alh;
+    for (int h = 0; h < 4; ++h) {
+      const float alh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * h));
+      st.O[0][h] *= alh;
+      st.O[1][h] *= alh;
+    }
   }
   const u4 zero4 = u4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -927,17 +931,22 @@ __device__ __forceinline__ void compute_mx_pair(const DecArgs& a, MxState& ms, c
     z[t] = valid[t] ? D * a.scale_log2 : -INFINITY;
   }
   const float Zn = fmaxf(st.Zr, row16_max(fmaxf(z[0], z[1])));
+  // what is accumulated is rescaled only when some head's maximum moved
+  // (otherwise every factor is exactly 1)
+  const bool moved = __builtin_amdgcn_ballot_w64(Zn != st.Zr) != 0;
   const float al = __builtin_amdgcn_exp2f(st.Zr - Zn);
   st.Zr = Zn;
   float e[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) e[t] = valid[t] ? exp2s(z[t] - Zn) : 0.0f;
   st.Ls = __builtin_fmaf(st.Ls, al, e[0] + e[1]);
+  if (moved) {
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const float alh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * h));
-    st.O[0][h] *= alh;
-    st.O[1][h] *= alh;
+    for (int h = 0; h < 4; ++h) {
+      const float alh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * h));
+      st.O[0][h] *= alh;
+      st.O[1][h] *= alh;
+    }
   }
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
   const u4 zero4 = u4{0u, 0u, 0u, 0u};
