@@ -884,7 +884,9 @@ struct Kv8Format {
 //   [8704, 9728)  the BF16 rotated query [head][128] when a piece starts (read
 //                 into registers), then P operands of V block b at
 //                 8704 + 512 (b & 1): [hi, lo][head][32 positions] BF16
-constexpr int kmxK = 0, kmxV = 4096, kmxS = 8192, kmxQ = 8704, kmxP = 8704, kmxSlotBytes = 9728;
+//   [9728, 9744)  16 zero bytes: the A operand of the lanes whose rows carry
+//                 no P in an MFMA is read from here (no selects)
+constexpr int kmxK = 0, kmxV = 4096, kmxS = 8192, kmxQ = 8704, kmxP = 8704, kmxZ = 9728, kmxSlotBytes = 9744;
 
 struct MxState {
   Kv8State s;
@@ -949,7 +951,7 @@ __device__ __forceinline__ void compute_mx_pair(const DecArgs& a, MxState& ms, c
     }
   }
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-  const u4 zero4 = u4{0u, 0u, 0u, 0u};
+  const uint8_t* zrow = slot + kmxZ;
   // the weight as two BF16 parts, hi = bf16(e) and lo = bf16(e - hi), kept
   // as FP32 values whose low 16 bits are zero
   float ehi[2], elo[2];
@@ -972,18 +974,20 @@ __device__ __forceinline__ void compute_mx_pair(const DecArgs& a, MxState& ms, c
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // A operand: head r16 % 4, positions 8 grp .. 8 grp + 7
-    const u4 ph = *reinterpret_cast<const u4*>(pst + (r16 & 3) * 32 + 8 * grp);
-    const u4 pl = *reinterpret_cast<const u4*>(pst + (4 + (r16 & 3)) * 32 + 8 * grp);
+    // A operand: head r16 % 4, positions 8 grp .. 8 grp + 7, in the rows of
+    // MFMA r only (r = sv % 4), zero elsewhere
+    const uint8_t* hrow = reinterpret_cast<const uint8_t*>(pst + (r16 & 3) * 32 + 8 * grp);
+    const uint8_t* lrow = reinterpret_cast<const uint8_t*>(pst + (4 + (r16 & 3)) * 32 + 8 * grp);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int sv = 2 * b + half;  // channels 16 sv .. 16 sv + 15 = 4 acc + r
       const v8bf vb = fp4x8_bf16(r.vq[sv], 1.0f);
       const bool mine = (r16 >> 2) == (sv & 3);
+      const u4 ph = *reinterpret_cast<const u4*>(mine ? hrow : zrow);
+      const u4 pl = *reinterpret_cast<const u4*>(mine ? lrow : zrow);
       v4f o = st.O[sv >> 2];
-      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, mine ? ph : zero4), vb, o, 0, 0, 0);
-      st.O[sv >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, mine ? pl : zero4), vb, o,
-                                                              0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, ph), vb, o, 0, 0, 0);
+      st.O[sv >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pl), vb, o, 0, 0, 0);
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -1033,8 +1037,9 @@ struct MxFormat {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
   // a new piece: fresh state, and the query operands from the slot's query area
-  __device__ static void reset(State& st, const uint8_t* slot, int r16, int grp) {
+  __device__ static void reset(State& st, uint8_t* slot, int r16, int grp) {
     Kv8Format::reset(st.s, slot, r16, grp);
+    if (r16 == 0 && grp == 0) *reinterpret_cast<uint4*>(slot + kmxZ) = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       st.qa[m] = *reinterpret_cast<const v8bf*>(slot + kmxQ + 2 * (HD * (r16 >> 2) + 32 * grp + 8 * m));
