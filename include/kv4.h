@@ -49,12 +49,12 @@ enum {
   KV4_ERR_NULLPTR = -1,     /* a required pointer is NULL */
   KV4_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_size != 16, sink < 0,
                                window < 0, sink % 16 != 0, sink + window > 144,
-                               Hq % Hkv != 0 or Hq / Hkv != 4 (the kernels are
-                               built for groups of 4 query heads per kv-head,
-                               the GQA shape of the pages' Qwen3 models and of
-                               their TP shards), or abi_version mismatch */
+                               Hq % Hkv != 0 (any G = Hq / Hkv >= 1 is taken:
+                               the kernels work on groups of up to 4 query
+                               heads of one kv-head; only the BF16 comparator
+                               needs G = 4), or abi_version mismatch */
   KV4_ERR_SHAPE = -3,       /* a size is out of range (B <= 0, max_ctx > pt_stride*16,
-                               B * num_kv_heads * (max_ctx/16 + 1) > INT32_MAX, ...) */
+                               B * num_kv_heads * ceil(G/4) * (max_ctx/16 + 1) > INT32_MAX, ...) */
   KV4_ERR_WORKSPACE = -4,   /* workspace missing or smaller than kv4_decode_workspace_bytes
                                (no-allocation entry point: more than its fixed scratch) */
   KV4_ERR_HIP = -5          /* a HIP call failed; kv4_strerror gives the HIP message */
@@ -212,7 +212,8 @@ int kv4_decode_attention_debug(const kv4_cache_desc *cache, const void *q,
  *   slot, page_table, pt_stride: per sequence, as for kv4_prefill_quantize
  *   max_ctx    host upper bound of E_s
  *   out, lse   fp32 [total_q][Hq][128], [total_q][Hq]
- * One workgroup per (block of 8 consecutive tokens of a chunk, kv-head) covers
+ * One workgroup per (block of 8 consecutive tokens of a chunk, group of up to 4
+ * query heads of one kv-head) covers
  * the block's protected rows and main tiles, so every INT4 tile and side row
  * is read once per 8 tokens; the integer intermediates (query codes, QK, P
  * codes, PV accumulators) are those of the decode step, and out / lse equal it
@@ -242,7 +243,8 @@ const char *kv4_strerror(int status);
  * The baseline the pages compare against is ordinary BF16 paged attention.
  *   pages   bf16 [num_pages][Hkv][2][16][128]: per (page, kv-head) 16 K rows
  *           then 16 V rows, unrotated
- *   q, ctx_len, page_table, out, lse as for kv4_decode_attention; Hq/Hkv = 4 */
+ *   q, ctx_len, page_table, out, lse as for kv4_decode_attention; Hq/Hkv = 4
+ *   (other group sizes: KV4_ERR_UNSUPPORTED) */
 size_t kv4bench_bf16_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx);
 int kv4bench_bf16_paged_decode(const void *pages, int32_t num_pages, int32_t Hkv, const void *q,
                                const int32_t *ctx_len, const int32_t *page_table,

@@ -51,13 +51,13 @@ int check_decode(const kv4_cache_desc* c, const void* q, const int32_t* ctx,
   int rc = check_cache(c);
   if (rc != KV4_OK) return rc;
   if (!q || !ctx || !page_table || !out || !lse) return KV4_ERR_NULLPTR;
-  if (Hq <= 0 || Hq % c->num_kv_heads != 0 || Hq / c->num_kv_heads != kv4::GQA)
-    return KV4_ERR_UNSUPPORTED;
+  if (Hq <= 0 || Hq % c->num_kv_heads != 0) return KV4_ERR_UNSUPPORTED;
   if (B <= 0 || pt_stride <= 0 || max_ctx <= 0 ||
       static_cast<int64_t>(max_ctx) > static_cast<int64_t>(pt_stride) * 16)
     return KV4_ERR_SHAPE;
-  // main-region pages of all (sequence, kv-head) pairs are counted in int32
-  if (static_cast<int64_t>(B) * c->num_kv_heads * (max_ctx / 16 + 1) > INT32_MAX) return KV4_ERR_SHAPE;
+  // main-region pages of all (sequence, query-head group) pairs are counted in int32
+  if (static_cast<int64_t>(B) * kv4::query_head_groups(Hq, c->num_kv_heads) * (max_ctx / 16 + 1) > INT32_MAX)
+    return KV4_ERR_SHAPE;
   return KV4_OK;
 }
 
@@ -130,7 +130,8 @@ const char* kv4_strerror(int status) {
     case KV4_ERR_NULLPTR: return "a required pointer is NULL";
     case KV4_ERR_UNSUPPORTED:
       return "unsupported configuration (needs abi_version 1, page 16, head_dim 128, "
-             "sink a multiple of 16, sink + window <= 144, Hq/Hkv = 4)";
+             "sink a multiple of 16, sink + window <= 144, Hq a multiple of Hkv; the BF16 "
+             "comparator: Hq/Hkv = 4)";
     case KV4_ERR_SHAPE: return "a size argument is out of range";
     case KV4_ERR_WORKSPACE:
       return "workspace missing or smaller than kv4_decode_workspace_bytes (for "
@@ -171,7 +172,8 @@ int kv4_prefill_quantize(const kv4_cache_desc* cache, const void* k, const void*
 
 size_t kv4_decode_workspace_bytes(const kv4_cache_desc* cache, int32_t B, int32_t Hq,
                                   int32_t max_ctx) {
-  if (check_cache(cache) != KV4_OK || B <= 0 || Hq <= 0 || max_ctx <= 0) return 0;
+  if (check_cache(cache) != KV4_OK || B <= 0 || Hq <= 0 || Hq % cache->num_kv_heads != 0 || max_ctx <= 0)
+    return 0;
   return kv4::decode_workspace_bytes(B, Hq, cache->num_kv_heads, kv4::main_region_waves());
 }
 
@@ -310,7 +312,9 @@ int kv4bench_bf16_paged_decode(const void* pages, int32_t num_pages, int32_t Hkv
 
 size_t kv4_prefill_attention_workspace_bytes(const kv4_cache_desc* cache, int32_t total_q,
                                              int32_t Hq, int32_t max_ctx) {
-  if (check_cache(cache) != KV4_OK || total_q <= 0 || Hq <= 0 || max_ctx <= 0) return 0;
+  if (check_cache(cache) != KV4_OK || total_q <= 0 || Hq <= 0 || Hq % cache->num_kv_heads != 0 ||
+      max_ctx <= 0)
+    return 0;
   return kv4::chunk_workspace_bytes(total_q, Hq, cache->num_kv_heads, kv4::main_region_waves());
 }
 
@@ -323,11 +327,12 @@ static int chunk_common(const kv4_cache_desc* cache, const void* q, const int32_
   if (rc != KV4_OK) return rc;
   if (!q || !cu_seqlens || !start_pos || !page_table || !out || !lse) return KV4_ERR_NULLPTR;
   const int Hkv = cache->num_kv_heads;
-  if (Hq <= 0 || Hq % Hkv != 0 || Hq / Hkv != kv4::GQA) return KV4_ERR_UNSUPPORTED;
+  if (Hq <= 0 || Hq % Hkv != 0) return KV4_ERR_UNSUPPORTED;
   if (nseq <= 0 || total_q <= 0 || pt_stride <= 0 || max_ctx <= 0 ||
       static_cast<int64_t>(max_ctx) > static_cast<int64_t>(pt_stride) * 16)
     return KV4_ERR_SHAPE;
-  if (static_cast<int64_t>(total_q) * Hkv * (max_ctx / 16 + 1) > INT32_MAX) return KV4_ERR_SHAPE;
+  if (static_cast<int64_t>(total_q) * kv4::query_head_groups(Hq, Hkv) * (max_ctx / 16 + 1) > INT32_MAX)
+    return KV4_ERR_SHAPE;
   const int nw = kv4::main_region_waves();
   if (!workspace || workspace_bytes < kv4::chunk_workspace_bytes(total_q, Hq, Hkv, nw))
     return KV4_ERR_WORKSPACE;
@@ -443,7 +448,8 @@ int kv8_prefill_quantize(const kv8_cache_desc* cache, const void* k, const void*
 
 size_t kv8_decode_workspace_bytes(const kv8_cache_desc* cache, int32_t B, int32_t Hq,
                                   int32_t max_ctx) {
-  if (check_kv8(cache) != KV4_OK || B <= 0 || Hq <= 0 || max_ctx <= 0) return 0;
+  if (check_kv8(cache) != KV4_OK || B <= 0 || Hq <= 0 || Hq % cache->num_kv_heads != 0 || max_ctx <= 0)
+    return 0;
   return kv4::decode_workspace_bytes(B, Hq, cache->num_kv_heads, kv4::kv8_region_waves());
 }
 
@@ -456,11 +462,12 @@ static int kv8_decode_common(const kv8_cache_desc* cache, const void* q, const i
   if (rc != KV4_OK) return rc;
   if (!q || !ctx_len || !page_table || !out || !lse) return KV4_ERR_NULLPTR;
   const int Hkv = cache->num_kv_heads;
-  if (Hq <= 0 || Hq % Hkv != 0 || Hq / Hkv != kv4::GQA) return KV4_ERR_UNSUPPORTED;
+  if (Hq <= 0 || Hq % Hkv != 0) return KV4_ERR_UNSUPPORTED;
   if (B <= 0 || B > 65535 || pt_stride <= 0 || max_ctx <= 0 ||
       static_cast<int64_t>(max_ctx) > static_cast<int64_t>(pt_stride) * 16)
     return KV4_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * Hkv * (max_ctx / 16 + 1) > INT32_MAX) return KV4_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * kv4::query_head_groups(Hq, Hkv) * (max_ctx / 16 + 1) > INT32_MAX)
+    return KV4_ERR_SHAPE;
   const int nw = kv4::kv8_region_waves();
   if (!workspace || workspace_bytes < kv4::decode_workspace_bytes(B, Hq, Hkv, nw))
     return KV4_ERR_WORKSPACE;

@@ -13,11 +13,11 @@
 //      query x unpacked INT4 keys), delta/m applied after the dot, tile
 //      softmax, INT8 P operand with the V scale folded in, integer PV on
 //      MFMA, FP32 running merge; a wave writes one partial per segment it
-//      touches.  Its last B*Hkv workgroups compute the protected region of one
-//      (sequence, kv-head) each (INT8 QK against the side keys, FP32 softmax,
+//      touches.  Its last B*Hv workgroups compute the protected region of one
+//      (sequence, query-head group) each (INT8 QK against the side keys, FP32 softmax,
 //      PV over BF16-dequantized side values); they are dispatched as the
 //      main-region waves retire, so they run in the main region's tail.
-//   2. merge_kernel, one workgroup per (kv-head, sequence): exact
+//   2. merge_kernel, one workgroup per (query-head group, sequence): exact
 //      log-sum-exp merge of the protected partial with the main partials,
 //      written as out and lse.
 #include <type_traits>
@@ -33,6 +33,10 @@ struct DecArgs {
   const int8_t* side_codes;
   const uint16_t* side_scales;
   int Hkv, Hq, B;
+  // query-head groups: each kv-head's G = Hq / Hkv query heads form R =
+  // ceil(G / 4) groups of up to 4 (the rows of the kernels' operands), Hv =
+  // Hkv * R groups per sequence
+  int G, R, Hv;
   const uint32_t* q;  // bf16 pairs
   const int32_t* ctx;
   const int32_t* slot;
@@ -53,6 +57,19 @@ struct DecArgs {
   DecodeDebug dbg;
 };
 
+// Query-head group v (0 <= v < Hv) of a sequence: kv-head gp = v / R and
+// query heads h0 .. h0 + nh - 1 (nh = 4 except in the last group of a kv-head
+// when G is not a multiple of 4).  The kernels compute all 4 rows of a group;
+// the rows past nh repeat head h0 + nh - 1 and are never stored.
+struct HeadGroup {
+  int gp, h0, nh;
+};
+__device__ __forceinline__ HeadGroup head_group(const DecArgs& a, int v) {
+  if (a.R == 1) return HeadGroup{v, v * a.G, a.G};  // G <= 4: one group per kv-head
+  const int gp = v / a.R, k = v - gp * a.R;
+  return HeadGroup{gp, gp * a.G + 4 * k, min(4, a.G - 4 * k)};
+}
+
 // Main region of a query attending [0, L) of a cache that ends at E (E = L
 // for a decode step): M = [s, min(L, E-w)), logical pages s/16 .. (end-1)/16
 // (s is a multiple of 16, so the first page starts at s).
@@ -62,7 +79,7 @@ __device__ __forceinline__ int main_pages(int L, int E, int s, int w) {
   return me > s ? (me - 1) / PAGE - s / PAGE + 1 : 0;
 }
 
-// plan[b] = sum over earlier sequences of main_pages * Hkv (one workgroup).
+// plan[b] = sum over earlier sequences of main_pages * Hv (one workgroup).
 __device__ void build_plan(const DecArgs& a) {
   __shared__ int32_t scan[256];
   __shared__ int32_t carry;
@@ -74,7 +91,7 @@ __device__ void build_plan(const DecArgs& a) {
   for (int base = 0; base < a.B; base += 256) {
     const int b = base + threadIdx.x;
     scan[threadIdx.x] = (b < a.B) ? main_pages(a.ctx[b], a.ctx[b], a.sink,
-                                               a.window) * a.Hkv : 0;
+                                               a.window) * a.Hv : 0;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
       const int t = (threadIdx.x >= off) ? scan[threadIdx.x - off] : 0;
@@ -175,8 +192,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{x, y}), b2));
 }
 
-// Protected-region partial of one (kv-head g, sequence b), computed by one
-// workgroup of the main kernel (the last B*Hkv workgroups of its grid, which
+// Protected-region partial of one (query-head group v, sequence b), computed by
+// one workgroup of the main kernel (the last B*Hv workgroups of its grid, which
 // the dispatcher starts as main-region workgroups retire; none when s = w = 0).
 // Only rows [0, s+w) are read.  QK: up to 9 MFMA row groups of 16 side rows
 // spread over the 4 waves.  Softmax: wave h for head h, its FP32 weights
@@ -199,7 +216,7 @@ constexpr int kProtLdsFused = kProtLds + 2 * HD + 8;     // plus this step's INT
 static_assert(kPrV + kPvRows * HD <= kProtLdsFused + 2048, "padded V rows inside the protected LDS");
 
 template <bool DEBUG>
-__device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b, uint8_t* lds_raw) {
+__device__ __forceinline__ void protected_partial(const DecArgs& a, int v, int b, uint8_t* lds_raw) {
   const int wave = wave_id(), lane = threadIdx.x & 63, tid = threadIdx.x;
   const int r16 = lane & 15, grp = lane >> 4;
   auto se = reinterpret_cast<float (*)[GQA]>(lds_raw + kPrSe);
@@ -216,26 +233,31 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   const int nrows = L > max(a.sink, E - a.window) ? a.sink + a.window : min(a.sink, L);
   const int sq = b;
   const int slot = a.slot ? ld_const(a.slot + sq) : sq;
+  const HeadGroup hg = head_group(a, v);  // wave h: query head hg.h0 + h (h < hg.nh)
+  const int g = hg.gp;
   const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
   const gptr side = (gptr)a.side_codes + row0 * 2 * HD;
   typedef const __attribute__((address_space(1))) uint16_t* gptr16;
   const gptr16 scales = (gptr16)(a.side_scales + row0 * 2);
-  const size_t qb = static_cast<size_t>(b) * a.Hq + g * GQA;
+  const size_t qb = static_cast<size_t>(b) * a.Hq + hg.h0;
 
   // ---- every load first: this step's token (fused append) with the side
   // rows, so that the append overlaps their arrival.  Wave 0 makes the INT8
-  // row, wave 1 the INT4 K half of the page entry, wave 2 its V half.
+  // row, wave 1 the INT4 K half of the page entry, wave 2 its V half.  Only
+  // the kv-head's first query-head group writes them; every group makes the
+  // INT8 row for itself (the side row it loads may be read before that write).
   int r_new = -1, new_pos = 0;
   uint32_t kw = 0, vw = 0;
   uint8_t* new_blk = nullptr;
   VBytes new_vb{0, 0};
+  const bool writer = hg.h0 == g * a.G;
   if (a.k_new) {
     new_pos = ld_const(a.pos_new + b);
     r_new = new_pos < a.sink ? new_pos : a.sink + new_pos % a.window;  // w > 0 on this path
     const size_t vec = static_cast<size_t>(b) * a.Hkv + g;
-    if (wave == 0 || wave == 1) kw = a.k_new[vec * 64 + lane];
-    if (wave == 0 || wave == 2) vw = a.v_new[vec * 64 + lane];
-    if (wave == 1 || wave == 2) {
+    if (wave == 0 || (writer && wave == 1)) kw = a.k_new[vec * 64 + lane];
+    if (wave == 0 || (writer && wave == 2)) vw = a.v_new[vec * 64 + lane];
+    if (writer && (wave == 1 || wave == 2)) {
       const int phys = ld_const(a.page_table + static_cast<size_t>(sq) * a.pt_stride + (new_pos >> 4));
       new_blk = const_cast<uint8_t*>(a.pages) + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
       if (wave == 2) new_vb = v_bytes_of(new_blk, new_pos & (PAGE - 1), lane);
@@ -271,15 +293,16 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   // what it loaded for that row (the loads above may have seen the old row).
   int8_t* nrow = reinterpret_cast<int8_t*>(lds_raw + kProtLds);   // [2][128] K, V codes
   float* nscale = reinterpret_cast<float*>(lds_raw + kProtLds + 2 * HD);  // s_k, s_v
-  if (r_new >= 0 && wave < 3) {
+  if (r_new >= 0 && (wave == 0 || (writer && wave < 3))) {
     const int t = new_pos & (PAGE - 1);
     float k0 = bf16_lo(kw), k1 = bf16_hi(kw);
     const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
     if (wave != 2) fwht128_wave(k0, k1);
     if (wave == 0) {
       const size_t rr = row0 + r_new;
-      const Int8Row nr = write_int8_row(const_cast<int8_t*>(a.side_codes) + rr * 2 * HD,
-                                        const_cast<uint16_t*>(a.side_scales) + rr * 2, k0, k1, v0, v1, lane);
+      const Int8Row nr = writer ? write_int8_row(const_cast<int8_t*>(a.side_codes) + rr * 2 * HD,
+                                                 const_cast<uint16_t*>(a.side_scales) + rr * 2, k0, k1, v0, v1, lane)
+                                : make_int8_row(k0, k1, v0, v1);
       reinterpret_cast<uint16_t*>(nrow)[lane] = static_cast<uint16_t>(nr.kp);
       reinterpret_cast<uint16_t*>(nrow)[64 + lane] = static_cast<uint16_t>(nr.vp);
       if (lane == 0) {
@@ -295,7 +318,7 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   // Query of head `wave`: rotate like the keys, then symmetric INT8 with an
   // FP32 scale (lane l holds channels 2l, 2l+1); codes in natural order to LDS.
   {
-    const size_t bh = qb + wave;
+    const size_t bh = qb + min(wave, hg.nh - 1);
     const uint32_t qw = a.q[bh * 64 + lane];
     float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
     fwht128_wave(x0, x1);
@@ -308,7 +331,7 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
     }
     reinterpret_cast<uint16_t*>(qn + wave * HD)[lane] = static_cast<uint16_t>((c0 & 0xFF) | ((c1 & 0xFF) << 8));
     if (lane == 0) cqs[wave] = s_q * a.scale_log2;
-    if (DEBUG) {
+    if (DEBUG && wave < hg.nh) {
       const int S = wave_sum_i(c0 + c1);
       if (a.dbg.qsum && lane == 0) a.dbg.qsum[bh] = S;
       if (a.dbg.qcodes) {
@@ -351,7 +374,7 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
       const int r = 16 * rg + r16;
       const int p = side_position(r, L, E, a.sink, a.window);
       se[r][grp] = (p >= 0) ? (static_cast<float>(D8) * sk[k]) * c_q : -INFINITY;
-      if (DEBUG && a.dbg.qk && p >= 0) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + p] = D8;
+      if (DEBUG && a.dbg.qk && p >= 0 && grp < hg.nh) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + p] = D8;
     }
   }
   __syncthreads();
@@ -407,9 +430,10 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int g, int b
   // ---- this wave's 32 channels of the 4 heads' partials; Z and l of head `wave`
   if (grp < 2) {
 #pragma unroll
-    for (int h = 0; h < GQA; ++h) a.ws.prot[(qb + h) * kPart + 32 * wave + 16 * grp + r16] = acc[h];
+    for (int h = 0; h < GQA; ++h)
+      if (h < hg.nh) a.ws.prot[(qb + h) * kPart + 32 * wave + 16 * grp + r16] = acc[h];
   }
-  if (lane == 0) {
+  if (lane == 0 && wave < hg.nh) {
     float* P = a.ws.prot + (qb + wave) * kPart;
     P[128] = Z;
     P[129] = ls;
@@ -500,7 +524,7 @@ struct MainState {
 template <bool DEBUG>
 __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, const QuadRegs& q,
                                              int np, v4i qa0, v4i qa1, float c_q, float S_q,
-                                             int j0, int main_end, size_t qb, uint8_t* stage,
+                                             int j0, int main_end, size_t qb, int nh, uint8_t* stage,
                                              int r16, int grp, int pslot) {
   // integer QK of the four tiles
   v4i d[4];
@@ -528,7 +552,7 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
     u[t] = mul_f16(e[t], vmt & 0xFFFFu);  // V scale folded into P
     emv[t] = mul_f16(e[t], vmt >> 16);    // V offset applied after the dot
     umax[t] = __uint_as_float(row16_max_u32(__float_as_uint(u[t])));
-    if (DEBUG && valid && a.dbg.qk) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + pos] = D;
+    if (DEBUG && valid && a.dbg.qk && grp < nh) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + pos] = D;
     __builtin_amdgcn_sched_barrier(0);  // one tile at a time: keeps the register count under 128
   }
   // 127 / u_max of the 16 (tile, head) pairs with one IEEE division:
@@ -544,7 +568,7 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
     const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(u[t] * inv[t]), 0.0f, 127.0f);
     const uint32_t uc = static_cast<uint32_t>(r);
     stage[(t * 4 + grp) * 16 + pslot] = static_cast<uint8_t>(uc);
-    if (DEBUG && a.dbg.pcode) {
+    if (DEBUG && a.dbg.pcode && grp < nh) {
       const int pos = PAGE * (j0 + t) + r16;
       if (t < np && pos < main_end) a.dbg.pcode[(qb + grp) * a.dbg.max_ctx + pos] = static_cast<uint8_t>(uc);
     }
@@ -588,7 +612,7 @@ __device__ __forceinline__ void compute_quad(const DecArgs& a, MainState& st, co
       x = __builtin_fmaf(wsu[2], static_cast<float>(acc[2]), x);
       x = __builtin_fmaf(wsu[3], static_cast<float>(acc[3]), x);
       st.O[o] = x;
-      if (DEBUG && a.dbg.pv) {
+      if (DEBUG && a.dbg.pv && grp < nh) {
         const int ch = 8 * r16 + 2 * s2 + e2;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -637,9 +661,9 @@ struct Kv4Format {
   }
   template <bool DEBUG>
   __device__ static void compute(const DecArgs& a, State& st, const Regs& q, int np, v4i qa0, v4i qa1,
-                                 float c_q, float S_q, int j0, int main_end, size_t qb, uint8_t* slot,
+                                 float c_q, float S_q, int j0, int main_end, size_t qb, int nh, uint8_t* slot,
                                  int r16, int grp, int pslot) {
-    compute_quad<DEBUG>(a, st, q, np, qa0, qa1, c_q, S_q, j0, main_end, qb, slot + kSlotP, r16, grp,
+    compute_quad<DEBUG>(a, st, q, np, qa0, qa1, c_q, S_q, j0, main_end, qb, nh, slot + kSlotP, r16, grp,
                         pslot);
   }
   // A = O + sum(w e m_v); lane (head grp, r16) holds channels 8 r16 .. 8 r16 + 7 in A[0..7]
@@ -689,7 +713,7 @@ struct Kv8State {
 
 template <bool DEBUG>
 __device__ __forceinline__ void compute_pair(const DecArgs& a, Kv8State& st, const Kv8Regs& r, int np,
-                                             v4i qa0, v4i qa1, float c_q, int j0, int L, size_t qb,
+                                             v4i qa0, v4i qa1, float c_q, int j0, int L, size_t qb, int nh,
                                              uint8_t* slot, int r16, int grp) {
   // INT8 QK of the two pages; lane (head grp, position r16) after the move
   v4i d[2];
@@ -706,7 +730,7 @@ __device__ __forceinline__ void compute_pair(const DecArgs& a, Kv8State& st, con
     const int pos = PAGE * (j0 + t) + r16;
     valid[t] = (t < np) && (pos < L);
     z[t] = valid[t] ? (static_cast<float>(D8) * f16_value(r.sk[t])) * c_q : -INFINITY;
-    if (DEBUG && valid[t] && a.dbg.qk) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + pos] = D8;
+    if (DEBUG && valid[t] && a.dbg.qk && grp < nh) a.dbg.qk[(qb + grp) * a.dbg.max_ctx + pos] = D8;
   }
   // running max of each head; weights relative to it, earlier sums rescaled
   const float Zn = fmaxf(st.Zr, row16_max(fmaxf(z[0], z[1])));
@@ -835,11 +859,11 @@ struct Kv8Format {
   }
   template <bool DEBUG>
   __device__ static void compute(const DecArgs& a, State& st, const Regs& r, int np, v4i qa0, v4i qa1,
-                                 float c_q, float S_q, int j0, int main_end, size_t qb, uint8_t* slot,
+                                 float c_q, float S_q, int j0, int main_end, size_t qb, int nh, uint8_t* slot,
                                  int r16, int grp, int pslot) {
     (void)S_q;
     (void)pslot;
-    compute_pair<DEBUG>(a, st, r, np, qa0, qa1, c_q, j0, main_end, qb, slot, r16, grp);
+    compute_pair<DEBUG>(a, st, r, np, qa0, qa1, c_q, j0, main_end, qb, nh, slot, r16, grp);
   }
   // A[4 acc + h]: head h, channel 64 acc + 16 grp + r16
   __device__ static void finish(const State& st, float A[8], float& Z, float& L) {
@@ -1046,8 +1070,9 @@ struct MxFormat {
   }
   template <bool DEBUG>
   __device__ static void compute(const DecArgs& a, State& st, const Regs& r, int np, v4i qa0, v4i qa1,
-                                 float c_q, float S_q, int j0, int main_end, size_t qb, uint8_t* slot,
+                                 float c_q, float S_q, int j0, int main_end, size_t qb, int nh, uint8_t* slot,
                                  int r16, int grp, int pslot) {
+    (void)nh;
     (void)qa0;
     (void)qa1;
     (void)c_q;
@@ -1061,12 +1086,13 @@ struct MxFormat {
 };
 
 // Work split of the main region: the global page list (sequence-major, then
-// kv-head, then logical page; T pages) is cut into one contiguous chunk per
+// query-head group, then logical page; T pages; a kv-head with more than 4
+// query heads has its pages listed once per group) is cut into one contiguous chunk per
 // wave, chunk c = [floor(T c / nw), floor(T (c+1) / nw)) when T >= nw (no
 // chunk empty), else [min(c, T), min(c+1, T)) (empty chunks only at the end).
 // A wave writes one partial per segment its chunk touches, at slot
-// c + b*Hkv + g: chunks visit segments in list order, so slots never collide
-// and nw + B*Hkv slots suffice.  The waves holding a segment's first and last
+// c + b*Hv + v: chunks visit segments in list order, so slots never collide
+// and nw + B*Hv slots suffice.  The waves holding a segment's first and last
 // pages record their chunk indices for the merge, which reads every chunk in
 // between: none of them may be empty.
 struct Split {
@@ -1105,7 +1131,7 @@ __device__ __forceinline__ PlanView plan_view(const DecArgs& a, int lane) {
     const int i = 4 * lane + k;
     const int L = a.ctx[min(i, a.B - 1)];
     const int E = L;
-    m[k] = i < a.B ? main_pages(L, E, a.sink, a.window) * a.Hkv : 0;
+    m[k] = i < a.B ? main_pages(L, E, a.sink, a.window) * a.Hv : 0;
   }
   m[1] += m[0];
   m[2] += m[1];
@@ -1156,6 +1182,7 @@ struct PageIds {  // physical pages of a unit's tiles (wave-uniform)
 
 struct QuadDesc {
   int b, g, j0, np, slot, main_end;
+  int gp, h0;          // the group's kv-head and first query head
   bool first, last;    // first / last quad of its piece
   bool opens, closes;  // the piece starts at the segment's first page / ends at its last
 };
@@ -1168,7 +1195,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
   if constexpr (F::kProtected) {
     if (blockIdx.x >= nw / 4) {  // protected-region workgroups fill the tail of the grid
       const int u = blockIdx.x - nw / 4;
-      protected_partial<DEBUG>(a, u % a.Hkv, u / a.Hkv, &lds[0][0]);
+      protected_partial<DEBUG>(a, u % a.Hv, u / a.Hv, &lds[0][0]);
       return;
     }
   }
@@ -1186,7 +1213,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
   const int iend = chunk_begin(sp, w + 1);
   const int chunk0 = ip;
   int ib = ip < iend ? find_seq(pv, ip, 0, lane) : 0;
-  int seg0 = 0, seg_end = 0, seg_g = 0;  // segment holding ip: pages [seg0, seg_end), kv-head seg_g
+  int seg0 = 0, seg_end = 0, seg_g = 0;  // segment holding ip: pages [seg0, seg_end), head group seg_g
+  HeadGroup seg_hg{0, 0, 1};               // seg_g's kv-head and query heads
   // Q operands of the next piece: the raw query is loaded when its first quad
   // is described (raw2, moved to raw1 with the quad), and rotated/quantized
   // after the compute of the iteration that issued that quad.
@@ -1209,11 +1237,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
     }
     const GroupQuery gq = quantize_group_query(raw, a.scale_log2, r16);
     if (DEBUG) {  // lane (grp, r16) holds rotated channels 8 r16 .. 8 r16 + 7 (same values from every piece)
-      const size_t bh = static_cast<size_t>(d.b) * a.Hq + d.g * GQA + grp;
-      if (a.dbg.qcodes)
+      const size_t bh = static_cast<size_t>(d.b) * a.Hq + d.h0 + grp;
+      if (grp < min(4, (d.gp + 1) * a.G - d.h0) && a.dbg.qcodes)
 #pragma unroll
         for (int j = 0; j < 8; ++j) a.dbg.qcodes[bh * HD + 8 * r16 + j] = static_cast<int8_t>(gq.c[j]);
-      if (a.dbg.qsum && r16 == 0) a.dbg.qsum[bh] = gq.S;
+      if (grp < min(4, (d.gp + 1) * a.G - d.h0) && a.dbg.qsum && r16 == 0) a.dbg.qsum[bh] = gq.S;
     }
     // A operand of QK: row r = head r / 4, k = channels (lane group grp
     // covers channels 32grp..32grp+31, even / odd split); the codes go
@@ -1251,17 +1279,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
     if (ip >= seg_end || ip == chunk0) {  // entering a segment: locate it once
       while (plan_at(pv, ib + 1) <= ip) ++ib;
       const int pb = plan_at(pv, ib);
-      const int mp = (plan_at(pv, ib + 1) - pb) / a.Hkv;
+      const int mp = (plan_at(pv, ib + 1) - pb) / a.Hv;
       seg_g = (ip - pb) / mp;
       seg0 = pb + seg_g * mp;
       seg_end = seg0 + mp;
+      seg_hg = head_group(a, seg_g);
     }
     const int stop = min(iend, seg_end);
     d.b = ib;
     d.g = seg_g;
+    d.gp = seg_hg.gp;
+    d.h0 = seg_hg.h0;
     d.j0 = a.sink / PAGE + (ip - seg0);
     d.np = min(F::kUnit, stop - ip);
-    d.slot = w + ib * a.Hkv + seg_g;
+    d.slot = w + ib * a.Hv + seg_g;
     d.first = (ip == chunk0) || (ip == seg0);
     d.last = ip + d.np >= stop;
     d.opens = ip == seg0;
@@ -1270,13 +1301,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
 #pragma unroll
     for (int t = 0; t < F::kUnit; ++t) pt.id[t] = ld_const(ptrow + d.j0 + min(t, d.np - 1));
     if (d.first)  // BF16 query of head grp, channels 8 r16 .. 8 r16 + 7
-      raw2 = reinterpret_cast<const uint4*>(a.q + ((static_cast<size_t>(ib) * a.Hq + seg_g * GQA + grp) * HD) / 2)[r16];
+      raw2 = reinterpret_cast<const uint4*>(
+          a.q + ((static_cast<size_t>(ib) * a.Hq + seg_hg.h0 + min(grp, seg_hg.nh - 1)) * HD) / 2)[r16];
     ip += d.np;
     return true;
   };
   // Stage 2: start the page loads of a described quad into the LDS slot.
   auto issue_quad = [&](QuadDesc& d, const PageIds& pt) {
-    const gptr gbase = (gptr)a.pages + static_cast<size_t>(d.g) * F::kBlock;
+    const gptr gbase = (gptr)a.pages + static_cast<size_t>(d.gp) * F::kBlock;
     gptr blk[F::kUnit];
 #pragma unroll
     for (int t = 0; t < F::kUnit; ++t)
@@ -1347,14 +1379,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
       issue_quad(d1, pt1);
       have2 = plan_quad(d2, pt2);
     }
-    const size_t qb = static_cast<size_t>(cd.b) * a.Hq + cd.g * GQA;
-    F::template compute<DEBUG>(a, st, q, cd.np, qa0, qa1, c_q, S_q, cd.j0, main_end, qb, slot, r16,
+    const size_t qb = static_cast<size_t>(cd.b) * a.Hq + cd.h0;
+    const int nh = min(4, (cd.gp + 1) * a.G - cd.h0);
+    F::template compute<DEBUG>(a, st, q, cd.np, qa0, qa1, c_q, S_q, cd.j0, main_end, qb, nh, slot, r16,
                                grp, pslot);
     if (cd.last) {  // partial of the piece
       if (pend) store_partial();
       F::finish(st, pend_A, pend_Z, pend_L);
       pend_P = a.ws.parts + static_cast<size_t>(cd.slot) * GQA * kPart;
-      pend_bg = cd.b * a.Hkv + cd.g;
+      pend_bg = cd.b * a.Hv + cd.g;
       pend_opens = piece_opens;
       pend_closes = cd.closes;
       pend = true;
@@ -1365,13 +1398,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
 }
 
 // Exact log-sum-exp merge of the protected partial (none when s = w = 0) and
-// the main partials of each head, one workgroup per (kv-head g, sequence b),
-// wave h for head h, lane l for channels 2l, 2l+1.  Writes out and lse.
+// the main partials of each head, one workgroup per (query-head group v,
+// sequence b), wave h for the group's head h, lane l for channels 2l, 2l+1.
+// Writes out and lse.
 __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
-  const int g = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.Hkv));
-  const int b = static_cast<int>(blockIdx.x / static_cast<unsigned>(a.Hkv));
+  const int g = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.Hv));
+  const int b = static_cast<int>(blockIdx.x / static_cast<unsigned>(a.Hv));
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  const size_t bh = static_cast<size_t>(b) * a.Hq + g * GQA + wave;
+  const HeadGroup hg = head_group(a, g);
+  if (wave >= hg.nh) return;  // a row past the group's heads (no barrier below)
+  const size_t bh = static_cast<size_t>(b) * a.Hq + hg.h0 + wave;
   float2 Am = make_float2(0.0f, 0.0f);
   float Zm = -INFINITY, lm = 0.0f;
   if (a.sink + a.window > 0) {
@@ -1380,8 +1416,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
     Zm = Pp[128];
     lm = Pp[129];
   }
-  // main partials: chunks c_lo..c_hi (recorded by the main kernel) at slots c + b*Hkv + g
-  const int bg = b * a.Hkv + g;
+  // main partials: chunks c_lo..c_hi (recorded by the main kernel) at slots c + b*Hv + g
+  const int bg = b * a.Hv + g;
   const int2 cr = a.ws.mrange[bg];  // written by the main kernel when the segment has pages
   const int Lb = ld_const(a.ctx + b);
   const int c_lo = cr.x, n_parts = main_pages(Lb, Lb, a.sink, a.window) > 0 ? cr.y - cr.x + 1 : 0;
@@ -1416,22 +1452,24 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
 
 }  // namespace
 
-// Partial slots of the main region: chunk c writes segment (b, g) at c + b*Hkv + g.
-static size_t part_slots(int B, int Hkv, int n_waves) {
-  return static_cast<size_t>(n_waves) + static_cast<size_t>(B) * Hkv;
+// Partial slots of the main region: chunk c writes segment (b, v) at c + b*Hv + v.
+static size_t part_slots(int B, int Hv, int n_waves) {
+  return static_cast<size_t>(n_waves) + static_cast<size_t>(B) * Hv;
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int n_waves) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const int Hv = query_head_groups(Hq, Hkv);
   size_t n = up(static_cast<size_t>(B + 1) * 4);
   n += up(static_cast<size_t>(B) * Hq * kPart * 4);
-  n += up(static_cast<size_t>(B) * Hkv * 8);
-  n += up(part_slots(B, Hkv, n_waves) * GQA * kPart * 4);
+  n += up(static_cast<size_t>(B) * Hv * 8);
+  n += up(part_slots(B, Hv, n_waves) * GQA * kPart * 4);
   return n;
 }
 
 DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const int Hv = query_head_groups(Hq, Hkv);
   char* p = static_cast<char*>(base);
   DecodeWorkspace w;
   w.plan = reinterpret_cast<int32_t*>(p);
@@ -1439,7 +1477,7 @@ DecodeWorkspace carve_workspace(void* base, int B, int Hq, int Hkv, int n_waves)
   w.prot = reinterpret_cast<float*>(p);
   p += up(static_cast<size_t>(B) * Hq * kPart * 4);
   w.mrange = reinterpret_cast<int2*>(p);
-  p += up(static_cast<size_t>(B) * Hkv * 8);
+  p += up(static_cast<size_t>(B) * Hv * 8);
   w.parts = reinterpret_cast<float*>(p);
   w.n_waves = n_waves;
   return w;
@@ -1462,6 +1500,9 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   a.side_scales = c.side_scales;
   a.Hkv = c.Hkv;
   a.Hq = Hq;
+  a.G = Hq / c.Hkv;
+  a.R = (a.G + GQA - 1) / GQA;
+  a.Hv = c.Hkv * a.R;
   a.B = B;
   a.q = reinterpret_cast<const uint32_t*>(q);
   a.ctx = ctx;
@@ -1479,8 +1520,8 @@ hipError_t launch_decode(const CacheView& c, const uint16_t* q, const int32_t* c
   a.ws = ws;
   if (dbg) a.dbg = *dbg;
   // main-region workgroups, then one protected-region workgroup per (b, g)
-  const int prot_groups = c.sink + c.window > 0 ? B * c.Hkv : 0;
-  const dim3 block(256), groups(c.Hkv * B), grid(ws.n_waves / 4 + prot_groups);
+  const int prot_groups = c.sink + c.window > 0 ? B * a.Hv : 0;
+  const dim3 block(256), groups(a.Hv * B), grid(ws.n_waves / 4 + prot_groups);
   if (B > 256) hipLaunchKernelGGL(plan_kernel, dim3(1), block, 0, s, a);
   if (dbg) {
     hipLaunchKernelGGL((main_kernel<Kv4Format, true>), grid, block, 0, s, a);
@@ -1529,6 +1570,9 @@ hipError_t launch_kv8_decode(const uint8_t* pages, int Hkv, const uint16_t* q, c
   a.pages = pages;
   a.Hkv = Hkv;
   a.Hq = Hq;
+  a.G = Hq / Hkv;
+  a.R = (a.G + GQA - 1) / GQA;
+  a.Hv = Hkv * a.R;
   a.B = B;
   a.q = reinterpret_cast<const uint32_t*>(q);
   a.ctx = ctx;
@@ -1541,7 +1585,7 @@ hipError_t launch_kv8_decode(const uint8_t* pages, int Hkv, const uint16_t* q, c
   a.lse = lse;
   a.ws = ws;
   if (dbg) a.dbg = *dbg;
-  const dim3 block(256), groups(Hkv * B), grid(ws.n_waves / 4);
+  const dim3 block(256), groups(a.Hv * B), grid(ws.n_waves / 4);
   if (B > 256) hipLaunchKernelGGL(plan_kernel, dim3(1), block, 0, s, a);
   if (dbg) hipLaunchKernelGGL((main_kernel<Kv8Format, true>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((main_kernel<Kv8Format, false>), grid, block, 0, s, a);

@@ -17,7 +17,7 @@ constexpr int BLOCK_BYTES = 2176;  // per (page, kv-head): 16 x (64 + 64 + 4 + 4
 constexpr int OFF_VCODE = 1024;
 constexpr int OFF_KMETA = 2048;
 constexpr int OFF_VMETA = 2112;
-constexpr int GQA = 4;           // query heads per kv-head handled by the decode kernels
+constexpr int GQA = 4;           // query heads per group (the rows of the kernels' operands)
 // KV8-everywhere pool block per (page, kv-head): K codes [16][128] | V codes
 // [128][16] | s_k FP16 [16] | s_v FP16 [16]
 constexpr int KV8_BLOCK_BYTES = 4160;
@@ -366,8 +366,7 @@ __device__ __forceinline__ void write_int4_entry(uint8_t* blk, int t, float k0, 
 struct Int8Row {
   uint32_t kp, vp, ks16, vs16;
 };
-__device__ __forceinline__ Int8Row write_int8_row(int8_t* codes, uint16_t* scales, float k0, float k1,
-                                                  float v0, float v1, int lane) {
+__device__ __forceinline__ Int8Row make_int8_row(float k0, float k1, float v0, float v1) {
   const Int8Meta ks = int8_meta(wave_max(fmaxf(fabsf(k0), fabsf(k1))));
   const Int8Meta vs = int8_meta(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
   Int8Row r;
@@ -375,11 +374,16 @@ __device__ __forceinline__ Int8Row write_int8_row(int8_t* codes, uint16_t* scale
   r.vp = (static_cast<uint32_t>(int8_code(v0, vs)) & 0xFFu) | ((static_cast<uint32_t>(int8_code(v1, vs)) & 0xFFu) << 8);
   r.ks16 = ks.s16;
   r.vs16 = vs.s16;
+  return r;
+}
+__device__ __forceinline__ Int8Row write_int8_row(int8_t* codes, uint16_t* scales, float k0, float k1,
+                                                  float v0, float v1, int lane) {
+  const Int8Row r = make_int8_row(k0, k1, v0, v1);
   reinterpret_cast<uint16_t*>(codes)[lane] = static_cast<uint16_t>(r.kp);
   reinterpret_cast<uint16_t*>(codes)[64 + lane] = static_cast<uint16_t>(r.vp);
   if (lane == 0) {
-    scales[0] = static_cast<uint16_t>(ks.s16);
-    scales[1] = static_cast<uint16_t>(vs.s16);
+    scales[0] = static_cast<uint16_t>(r.ks16);
+    scales[1] = static_cast<uint16_t>(r.vs16);
   }
   return r;
 }

@@ -27,13 +27,17 @@ struct DecodeDebug {
 
 // Workspace carve-up of one decode call.
 struct DecodeWorkspace {
-  int32_t* plan;   // [B+1] prefix sums of (main pages x Hkv) over sequences (B > 256 only)
+  int32_t* plan;   // [B+1] prefix sums of (main pages x Hv) over sequences (B > 256 only)
   float* prot;     // [B][Hq][kPart] partials of the protected region
-  int2* mrange;    // [B*Hkv] first and last chunk holding pages of each segment (0, -1: none)
+  int2* mrange;    // [B*Hv] first and last chunk holding pages of each segment (0, -1: none)
   float* parts;    // [slots][4][kPart] partials of the main region
   int n_waves;     // waves of the main-region grid
 };
 constexpr int kPart = 132;  // A[128], Z, l, 2 pad
+
+// Query-head groups per sequence: each kv-head's G = Hq / Hkv query heads in
+// groups of up to 4 (the row count of the kernels' operands).
+inline int query_head_groups(int Hq, int Hkv) { return Hkv * ((Hq / Hkv + 3) / 4); }
 
 // Waves per SIMD of the main-region grid; every wave of the grid is resident
 // at once (the equal-chunk split assumes it).

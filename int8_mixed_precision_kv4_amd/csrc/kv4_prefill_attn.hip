@@ -8,9 +8,10 @@
 // rule (integer QK, Delta/m after the dot, tile softmax with exp2s, P-operand
 // codes with the V step folded in, integer PV, FP32 running merge).
 //
-// One workgroup per (block of 8 consecutive tokens of a chunk, kv-head), its
-// 4 waves splitting the block's side-row groups and main tiles, each tile and
-// side row read once for 8 tokens x 4 heads.  Every product takes the 32 rows
+// One workgroup per (block of 8 consecutive tokens of a chunk, query-head group
+// of up to 4 heads of one kv-head), its 4 waves splitting the block's side-row
+// groups and main tiles, each tile and side row read once for 8 tokens x 4
+// heads.  Every product takes the 32 rows
 // n = 4 * token + head as its N dimension and is computed transposed:
 //   QK:  D^T[32 positions][32 rows] = K[positions][16 channels] q^T   (i8)
 //   PV:  O^T[32 channels][32 rows]  = V^T[channels][16 positions] P^T (i8 for
@@ -47,6 +48,7 @@ struct PaArgs {
   const int8_t* side_codes;
   const uint16_t* side_scales;
   int Hkv, Hq, sink, window;
+  int G, R, Hv;       // query heads per kv-head, groups of up to 4 per kv-head, groups per token
   const uint32_t* q;  // BF16 pairs [T][Hq][64]
   const int32_t* cu;
   const int32_t* start;
@@ -124,9 +126,13 @@ constexpr int kLdsBytes = kLdsZL + 2 * 4 * NR * 4;
 template <bool DEBUG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(PaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-  const int g = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.Hkv));
+  // query-head group v: kv-head g, query heads h0 .. h0 + nh - 1 (rows of a
+  // head past nh repeat head h0 + nh - 1 and are never stored)
+  const int v = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.Hv));
+  const int g = v / a.R;
+  const int h0 = g * a.G + GQA * (v - g * a.R), nh = min(GQA, a.G - (h0 - g * a.G));
   const int total = ldc(a.blk_base + a.nseq);
-  const int rev = static_cast<int>(blockIdx.x / static_cast<unsigned>(a.Hkv));
+  const int rev = static_cast<int>(blockIdx.x / static_cast<unsigned>(a.Hv));
   if (rev >= total) return;
   const int bq = total - 1 - rev;  // later (longer) blocks first
   int lo = 0, hi = a.nseq;         // blk_base[lo] <= bq < blk_base[hi]
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int c0 = 0, c1 = 0;
     float s_q = 0.0f;
     if (ti < ntok) {
-      const size_t bh = static_cast<size_t>(tok0 + ti) * a.Hq + g * GQA + h;
+      const size_t bh = static_cast<size_t>(tok0 + ti) * a.Hq + h0 + min(h, nh - 1);
       const uint32_t qw = a.q[bh * 64 + lane];
       float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
       fwht128_wave(x0, x1);
@@ -170,14 +176,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         c0 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x0 / s_q), -127.0f), 127.0f));
         c1 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x1 / s_q), -127.0f), 127.0f));
       }
-      if (DEBUG && a.dbg.qcodes) {
+      if (DEBUG && a.dbg.qcodes && h < nh) {
         a.dbg.qcodes[bh * HD + 2 * lane] = static_cast<int8_t>(c0);
         a.dbg.qcodes[bh * HD + 2 * lane + 1] = static_cast<int8_t>(c1);
       }
     }
     const int S = wave_sum_i(c0 + c1);
-    if (DEBUG && a.dbg.qsum && lane == 0 && ti < ntok)
-      a.dbg.qsum[static_cast<size_t>(tok0 + ti) * a.Hq + g * GQA + h] = S;
+    if (DEBUG && a.dbg.qsum && lane == 0 && ti < ntok && h < nh)
+      a.dbg.qsum[static_cast<size_t>(tok0 + ti) * a.Hq + h0 + h] = S;
     qlds[row * kQRowBytes + lane] = static_cast<int8_t>(c0);
     qlds[row * kQRowBytes + 64 + lane] = static_cast<int8_t>(c1);
     if (lane == 0) {
@@ -260,8 +266,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float sk = f16_value(sc[r >> 2][r & 3] & 0xFFFFu);
       z[r] = pos >= 0 ? (static_cast<float>(d[r]) * sk) * c_q : -INFINITY;
       zm = fmaxf(zm, z[r]);
-      if (DEBUG && pos >= 0 && a.dbg.qk) {
-        const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + g * GQA + (n & 3);
+      if (DEBUG && pos >= 0 && a.dbg.qk && (n & 3) < nh) {
+        const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + h0 + (n & 3);
         a.dbg.qk[bh * a.dbg.max_ctx + pos] = d[r];
       }
     }
@@ -383,8 +389,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const uint32_t km = kmeta[j4][i];
       const float dk = f16_value(km & 0xFFFFu);
       z[r] = valid[r] ? __builtin_fmaf(dk, static_cast<float>(d[r]), mul_f16(S_q, km >> 16)) * c_q : -INFINITY;
-      if (DEBUG && valid[r] && a.dbg.qk) {
-        const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + g * GQA + (n & 3);
+      if (DEBUG && valid[r] && a.dbg.qk && (n & 3) < nh) {
+        const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + h0 + (n & 3);
         a.dbg.qk[bh * a.dbg.max_ctx + pos] = d[r];
       }
     }
@@ -419,10 +425,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int k = 0; k < 8; ++k) {
         const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(u[8 * t + k] * inv), 0.0f, 127.0f);
         uc[k] = static_cast<uint32_t>(r);
-        if (DEBUG && valid[8 * t + k] && a.dbg.pcode) {
+        if (DEBUG && valid[8 * t + k] && a.dbg.pcode && (n & 3) < nh) {
           const int j4 = (8 * t + k) >> 2, i = k & 3;
           const int pos = PAGE * (ja + t) + 8 * (j4 & 1) + 4 * kg + i;
-          const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + g * GQA + (n & 3);
+          const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + h0 + (n & 3);
           a.dbg.pcode[bh * a.dbg.max_ctx + pos] = static_cast<uint8_t>(uc[k]);
         }
       }
@@ -459,8 +465,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const v16i acc = __builtin_amdgcn_mfma_i32_32x32x16_i8(va, pb[t], v16i{}, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[s2][r] = __builtin_fmaf(wsu[t], static_cast<float>(acc[r]), O[s2][r]);
-        if (DEBUG && a.dbg.pv && row_live && (t == 0 || has_b)) {
-          const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + g * GQA + (n & 3);
+        if (DEBUG && a.dbg.pv && row_live && (t == 0 || has_b) && (n & 3) < nh) {
+          const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + h0 + (n & 3);
           // a tile outside this row's main region leaves its accumulators unwritten
           if (PAGE * (ja + t) < me_row) {
 #pragma unroll
@@ -502,8 +508,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int k = 0; k < QB; ++k) {
     const int row = QB * wave + k;
     const int ti = row >> 2, h = row & 3;
-    if (ti >= ntok) continue;
-    const size_t bh = static_cast<size_t>(tok0 + ti) * a.Hq + g * GQA + h;
+    if (ti >= ntok || h >= nh) continue;
+    const size_t bh = static_cast<size_t>(tok0 + ti) * a.Hq + h0 + h;
     float Zs[4], Lv[4];
     float2 Av[4];
 #pragma unroll
@@ -543,6 +549,9 @@ hipError_t launch_prefill_blocked(const CacheView& c, const uint16_t* q, const i
   a.side_scales = c.side_scales;
   a.Hkv = c.Hkv;
   a.Hq = Hq;
+  a.G = Hq / c.Hkv;
+  a.R = (a.G + GQA - 1) / GQA;
+  a.Hv = c.Hkv * a.R;
   a.sink = c.sink;
   a.window = c.window;
   a.q = reinterpret_cast<const uint32_t*>(q);
@@ -560,7 +569,7 @@ hipError_t launch_prefill_blocked(const CacheView& c, const uint16_t* q, const i
   hipLaunchKernelGGL(block_base_kernel, dim3(1), dim3(256), 0, s, cu, nseq, blk_base);
   // blocks: sum of ceil(n / 8) <= (T + 7 nseq) / 8
   const long long nblk = (static_cast<long long>(T) + 7LL * nseq) / QB;
-  const long long groups = nblk * c.Hkv;
+  const long long groups = nblk * a.Hv;
   if (groups > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(groups)), block(256);
   if (dbg) hipLaunchKernelGGL((prefill_attn_kernel<true>), grid, block, 0, s, a);

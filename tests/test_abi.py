@@ -94,11 +94,12 @@ def test_noalloc_entry_point_refuses_beyond_its_scratch_without_gpu():
     assert L.kv4_decode_workspace_bytes(ctypes.byref(d), 256, 32, 16384) <= kv4.NOALLOC_SCRATCH_BYTES
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (64, 8), (6, 2), (5, 1)])
-def test_gqa_groups_other_than_four_are_refused_without_gpu(Hq, Hkv):
-    """The kernels take exactly 4 query heads per kv-head (the pages' GQA
-    models have 32/8 heads); any other group is refused as unsupported on the
-    host, before any launch, by every decode-side entry point."""
+@pytest.mark.parametrize("Hq,Hkv", [(6, 4), (5, 2), (12, 8), (3, 4), (0, 8), (-8, 8)])
+def test_query_heads_not_a_multiple_of_kv_heads_are_refused_without_gpu(Hq, Hkv):
+    """Every query head reads one kv-head, so Hq must be a positive multiple of
+    Hkv; anything else is refused as unsupported on the host, before any
+    launch, by every decode-side entry point (the pointers are dummies and
+    never touched), and its workspace size is 0."""
     import int8_mixed_precision_kv4_amd as kv4
     if not os.path.exists(kv4.LIB_PATH):
         pytest.skip("libkv4.so not built")
@@ -114,8 +115,32 @@ def test_gqa_groups_other_than_four_are_refused_without_gpu(Hq, Hkv):
                                    1 << 30, None) == -2
     assert L.kv4mx_decode_attention(ctypes.byref(d), 1, 1, None, 1, 1, 1, Hq, 16, 1.0, 1, 1, 1, 1 << 30,
                                     None) == -2
+    assert L.kv4_decode_workspace_bytes(ctypes.byref(d), 4, Hq, 64) == 0
+    assert L.kv4_prefill_attention_workspace_bytes(ctypes.byref(d), 4, Hq, 64) == 0
     d8 = kv4._Kv8Desc(1, 4, 16, Hkv, 128, 1)
     assert L.kv8_decode_attention(ctypes.byref(d8), 1, 1, 1, 1, 1, Hq, 16, 1.0, 1, 1, 1, 1 << 30, None) == -2
+    assert L.kv8_decode_workspace_bytes(ctypes.byref(d8), 4, Hq, 64) == 0
+    assert L.kv4bench_bf16_paged_decode(1, 4, Hkv, 1, 1, 1, 1, 1, Hq, 16, 1.0, 1, 1, 1, 1 << 30, None) == -2
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (64, 8), (6, 2), (5, 1)])
+def test_group_sizes_other_than_four_take_more_groups_without_gpu(Hq, Hkv):
+    """Any whole group size G = Hq/Hkv is taken: the kernels' rows are virtual
+    groups of at most 4 query heads of one kv-head, ceil(G/4) of them per
+    kv-head, each with its own chunk partials. Only the BF16 comparator keeps
+    G = 4."""
+    import int8_mixed_precision_kv4_amd as kv4
+    if not os.path.exists(kv4.LIB_PATH):
+        pytest.skip("libkv4.so not built")
+    L = kv4.lib()
+    d = kv4._Desc(1, 4, 16, Hkv, 128, 16, 128, 1, 1, 1, 1)
+    ws = L.kv4_decode_workspace_bytes(ctypes.byref(d), 4, Hq, 64)
+    assert ws > 0
+    # four more query heads per kv-head add one group per kv-head: more partials
+    assert L.kv4_decode_workspace_bytes(ctypes.byref(d), 4, Hq + 4 * Hkv, 64) > ws
+    assert L.kv4_prefill_attention_workspace_bytes(ctypes.byref(d), 4, Hq, 64) > 0
+    d8 = kv4._Kv8Desc(1, 4, 16, Hkv, 128, 1)
+    assert L.kv8_decode_workspace_bytes(ctypes.byref(d8), 4, Hq, 64) > 0
     assert L.kv4bench_bf16_paged_decode(1, 4, Hkv, 1, 1, 1, 1, 1, Hq, 16, 1.0, 1, 1, 1, 1 << 30, None) == -2
 
 
