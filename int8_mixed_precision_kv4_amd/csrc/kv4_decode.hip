@@ -300,9 +300,9 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int v, int b
     if (wave != 2) fwht128_wave(k0, k1);
     if (wave == 0) {
       const size_t rr = row0 + r_new;
-      const Int8Row nr = writer ? write_int8_row(const_cast<int8_t*>(a.side_codes) + rr * 2 * HD,
-                                                 const_cast<uint16_t*>(a.side_scales) + rr * 2, k0, k1, v0, v1, lane)
-                                : make_int8_row(k0, k1, v0, v1);
+      const Int8Row nr = make_int8_row(k0, k1, v0, v1);
+      if (writer) store_int8_row(const_cast<int8_t*>(a.side_codes) + rr * 2 * HD,
+                                 const_cast<uint16_t*>(a.side_scales) + rr * 2, nr, lane);
       reinterpret_cast<uint16_t*>(nrow)[lane] = static_cast<uint16_t>(nr.kp);
       reinterpret_cast<uint16_t*>(nrow)[64 + lane] = static_cast<uint16_t>(nr.vp);
       if (lane == 0) {

@@ -376,15 +376,18 @@ __device__ __forceinline__ Int8Row make_int8_row(float k0, float k1, float v0, f
   r.vs16 = vs.s16;
   return r;
 }
-__device__ __forceinline__ Int8Row write_int8_row(int8_t* codes, uint16_t* scales, float k0, float k1,
-                                                  float v0, float v1, int lane) {
-  const Int8Row r = make_int8_row(k0, k1, v0, v1);
+__device__ __forceinline__ void store_int8_row(int8_t* codes, uint16_t* scales, const Int8Row& r, int lane) {
   reinterpret_cast<uint16_t*>(codes)[lane] = static_cast<uint16_t>(r.kp);
   reinterpret_cast<uint16_t*>(codes)[64 + lane] = static_cast<uint16_t>(r.vp);
   if (lane == 0) {
     scales[0] = static_cast<uint16_t>(r.ks16);
     scales[1] = static_cast<uint16_t>(r.vs16);
   }
+}
+__device__ __forceinline__ Int8Row write_int8_row(int8_t* codes, uint16_t* scales, float k0, float k1,
+                                                  float v0, float v1, int lane) {
+  const Int8Row r = make_int8_row(k0, k1, v0, v1);
+  store_int8_row(codes, scales, r, lane);
   return r;
 }
 
