@@ -482,17 +482,23 @@ struct QuadRegs {
 
 // Issue the direct-to-LDS loads of one quad.  Tile t reads physical page
 // blk[t]; lane (r16, grp) fetches bytes 64 r16 + 16 grp of the tile's K codes
-// and of its V codes (1 KB contiguous per instruction for both).
-__device__ __forceinline__ void quad_to_lds(uint8_t* slot, const gptr blk[4], int lane, int r16,
+// and of its V codes (1 KB contiguous per instruction for both).  Tiles
+// t >= np (past the piece's last page) are not loaded: the slot keeps whatever
+// it held, and the compute masks those tiles by position (logit -inf, V
+// metadata zero, P codes 0), which no bit pattern of theirs can undo, since
+// their codes only meet P codes of 0 in the integer products.
+__device__ __forceinline__ void quad_to_lds(uint8_t* slot, const gptr blk[4], int np, int lane, int r16,
                                             int grp) {
   const int koff = 64 * r16 + 16 * grp;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    __builtin_amdgcn_global_load_lds(blk[t] + koff, (lptr)(slot + kSlotK + 1024 * t), 16, 0, kNT);
+    if (t < np)
+      __builtin_amdgcn_global_load_lds(blk[t] + koff, (lptr)(slot + kSlotK + 1024 * t), 16, 0, kNT);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    __builtin_amdgcn_global_load_lds(blk[t] + OFF_VCODE + koff, (lptr)(slot + kSlotV + 1024 * t), 16, 0, kNT);
-  if (lane < 32) {  // 4 pages x 128 B of metadata
+    if (t < np)
+      __builtin_amdgcn_global_load_lds(blk[t] + OFF_VCODE + koff, (lptr)(slot + kSlotV + 1024 * t), 16, 0, kNT);
+  if (lane < 8 * np) {  // np pages x 128 B of metadata
     const int t = lane >> 3;
     const gptr mb = t == 0 ? blk[0] : t == 1 ? blk[1] : t == 2 ? blk[2] : blk[3];
     __builtin_amdgcn_global_load_lds(mb + OFF_KMETA + 16 * (lane & 7), (lptr)(slot + kSlotMeta), 16, 0, kNT);
@@ -640,8 +646,8 @@ struct Kv4Format {
   static constexpr bool kProtected = true;      // protected-region workgroups in the grid tail
   typedef QuadRegs Regs;
   typedef MainState State;
-  __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
-    quad_to_lds(slot, blk, lane, r16, grp);
+  __device__ static void to_lds(uint8_t* slot, const gptr* blk, int np, int lane, int r16, int grp) {
+    quad_to_lds(slot, blk, np, lane, r16, grp);
   }
   __device__ static void from_lds(Regs& q, const uint8_t* slot, int lane, int r16, int grp) {
     (void)grp;
@@ -817,7 +823,9 @@ struct Kv8Format {
   static constexpr bool kProtected = false;
   typedef Kv8Regs Regs;
   typedef Kv8State State;
-  __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
+  // every tile is loaded (past the piece's last page: that page again)
+  __device__ static void to_lds(uint8_t* slot, const gptr* blk, int np, int lane, int r16, int grp) {
+    (void)np;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1026,7 +1034,9 @@ struct MxFormat {
   static constexpr bool kProtected = true;
   typedef MxRegs Regs;
   typedef MxState State;
-  __device__ static void to_lds(uint8_t* slot, const gptr* blk, int lane, int r16, int grp) {
+  // every tile is loaded (past the piece's last page: that page again)
+  __device__ static void to_lds(uint8_t* slot, const gptr* blk, int np, int lane, int r16, int grp) {
+    (void)np;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       __builtin_amdgcn_global_load_lds(blk[t] + 64 * r16 + 16 * grp, (lptr)(slot + kmxK + 1024 * t), 16, 0, kNT);
@@ -1313,7 +1323,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
 #pragma unroll
     for (int t = 0; t < F::kUnit; ++t)
       blk[t] = gbase + static_cast<size_t>(static_cast<uint32_t>(pt.id[t])) * pstride;
-    F::to_lds(slot, blk, lane, r16, grp);
+    F::to_lds(slot, blk, d.np, lane, r16, grp);
     if (d.first) {
       const int L = ld_const(a.ctx + d.b);
       d.main_end = main_end_of(L, L, a.window);
