@@ -121,6 +121,9 @@ constexpr int kWaitLgkm0 = 0xC07F;
 // read once, so the loads stream past the caches instead of allocating in
 // them (about 10% faster for the whole main kernel than default loads).
 constexpr int kNT = 2;
+// Word 3 of a buffer resource on gfx9 (32-bit data format, no swizzle): a raw
+// buffer load past num_records returns zeros.
+constexpr int kBufferWord3 = 0x00020000;
 
 // Plan for batches of more than 256 sequences (smaller batches build it in
 // registers in every main-kernel wave): one workgroup.
@@ -226,58 +229,60 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int v, int b
   int8_t* qn = reinterpret_cast<int8_t*>(lds_raw + kPrQ);
   float* cqs = reinterpret_cast<float*>(lds_raw + kPrC);
 
+  // ---- every load is issued before anything waits on one: the scalar
+  // lookups, this step's token (fused append) and the query, then the side
+  // rows (K into registers, V into LDS) and their scales as raw bits.  Values
+  // are converted only after the last load has gone out, so that the phase is
+  // one round trip (plus the slot and page-table lookups it depends on) instead
+  // of a chain of them.  Wave 0 makes the INT8 row, wave 1 the INT4 K half of
+  // the page entry, wave 2 its V half.  Only the kv-head's first query-head
+  // group writes them; every group makes the INT8 row for itself (the side row
+  // it loads may be read before that write).
   const int L = ld_const(a.ctx + b);
   const int E = L;  // the cache ends at this step's token
-  // rows that can hold a position of the region: the sinks below L, and the
-  // ring when the window [max(s, L - w), L) is not empty
-  const int nrows = L > max(a.sink, E - a.window) ? a.sink + a.window : min(a.sink, L);
   const int sq = b;
   const int slot = a.slot ? ld_const(a.slot + sq) : sq;
+  const int new_pos = a.k_new ? ld_const(a.pos_new + b) : 0;
   const HeadGroup hg = head_group(a, v);  // wave h: query head hg.h0 + h (h < hg.nh)
   const int g = hg.gp;
-  const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
-  const gptr side = (gptr)a.side_codes + row0 * 2 * HD;
-  typedef const __attribute__((address_space(1))) uint16_t* gptr16;
-  const gptr16 scales = (gptr16)(a.side_scales + row0 * 2);
   const size_t qb = static_cast<size_t>(b) * a.Hq + hg.h0;
-
-  // ---- every load first: this step's token (fused append) with the side
-  // rows, so that the append overlaps their arrival.  Wave 0 makes the INT8
-  // row, wave 1 the INT4 K half of the page entry, wave 2 its V half.  Only
-  // the kv-head's first query-head group writes them; every group makes the
-  // INT8 row for itself (the side row it loads may be read before that write).
-  int r_new = -1, new_pos = 0;
-  uint32_t kw = 0, vw = 0;
-  uint8_t* new_blk = nullptr;
-  VBytes new_vb{0, 0};
+  const size_t bh = qb + min(wave, hg.nh - 1);  // the query of head `wave`
+  const uint32_t qw = a.q[bh * 64 + lane];
   const bool writer = hg.h0 == g * a.G;
+  uint32_t kw = 0, vw = 0;
   if (a.k_new) {
-    new_pos = ld_const(a.pos_new + b);
-    r_new = new_pos < a.sink ? new_pos : a.sink + new_pos % a.window;  // w > 0 on this path
     const size_t vec = static_cast<size_t>(b) * a.Hkv + g;
     if (wave == 0 || (writer && wave == 1)) kw = a.k_new[vec * 64 + lane];
     if (wave == 0 || (writer && wave == 2)) vw = a.v_new[vec * 64 + lane];
-    if (writer && (wave == 1 || wave == 2)) {
-      const int phys = ld_const(a.page_table + static_cast<size_t>(sq) * a.pt_stride + (new_pos >> 4));
-      new_blk = const_cast<uint8_t*>(a.pages) + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
-      if (wave == 2) new_vb = v_bytes_of(new_blk, new_pos & (PAGE - 1), lane);
-    }
   }
-  // K operands and scales of this wave's row groups (rg = wave + 4k)
+  // rows that can hold a position of the region: the sinks below L, and the
+  // ring when the window [max(s, L - w), L) is not empty
+  const int nrows = L > max(a.sink, E - a.window) ? a.sink + a.window : min(a.sink, L);
+  const size_t row0 = (static_cast<size_t>(slot) * a.Hkv + g) * SIDE_ROWS;
+  const gptr side = (gptr)a.side_codes + row0 * 2 * HD;
+  // The K rows and scales as buffers of nrows rows: a load of a row past
+  // nrows returns zeros and touches no memory, so these loads need no branch
+  // (a branch around a load lets the compiler wait for it at the join, which
+  // made the row groups dependent round trips).
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.side_codes) + row0 * 2 * HD, 0, nrows * 2 * HD,
+                                        kBufferWord3);
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.side_scales) + row0 * 2, 0, nrows * 4,
+                                        kBufferWord3);
+  // K operands and scale bits of this wave's row groups (rg = wave + 4k; row
+  // groups past the 9 of the buffer read as zeros)
   v4i kop[3][2];
-  float sk[3];
+  uint32_t skr[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
-    const int rg = wave + 4 * k;
-    kop[k][0] = kop[k][1] = v4i{0, 0, 0, 0};
-    sk[k] = 0.0f;
-    if (rg < SIDE_ROWS / 16 && 16 * rg < nrows) {
-      const gptr krow = side + (16 * rg + r16) * 2 * HD;
-      kop[k][0] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 16 * grp));
-      kop[k][1] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) v4i*>(krow + 64 + 16 * grp));
-      sk[k] = f16_value(__builtin_nontemporal_load(scales + 2 * (16 * rg + r16)));
-    }
+    const int row = 16 * (wave + 4 * k) + r16;
+    kop[k][0] = __builtin_amdgcn_raw_buffer_load_b128(krs, row * 2 * HD + 16 * grp, 0, kNT);
+    kop[k][1] = __builtin_amdgcn_raw_buffer_load_b128(krs, row * 2 * HD + 64 + 16 * grp, 0, kNT);
+    skr[k] = __builtin_amdgcn_raw_buffer_load_b16(srs, 4 * row, 0, kNT);
   }
+  // V scale bits of row tid (selected away below for a row outside the region)
+  const uint32_t svr = __builtin_amdgcn_raw_buffer_load_b16(srs, 4 * tid + 2, 0, kNT);
   // V codes of the used rows into LDS, 8 rows (1 KB) per instruction: lane l
   // moves bytes 16 (l % 8) .. of row 8 j + l / 8 (blocks j = wave, wave + 4, ..)
   for (int j = wave; 8 * j < nrows; j += 4) {
@@ -285,9 +290,47 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int v, int b
     __builtin_amdgcn_global_load_lds(side + (2 * r + 1) * HD + 16 * (lane & 7), (lptr)(vst + 1024 * j), 16, 0,
                                      kNT);
   }
-  if (tid < kPvRows)
-    ssv[tid] = tid < SIDE_ROWS && side_position(tid, L, E, a.sink, a.window) >= 0 ? f16_value(scales[2 * tid + 1])
-                                                                                 : 0.0f;
+  // the page slot of this step's token (writer waves 1 and 2), then the two
+  // V bytes that wave 2 rewrites around its nibble
+  int r_new = -1;
+  uint8_t* new_blk = nullptr;
+  uint32_t vb0 = 0, vb1 = 0;
+  if (a.k_new) {
+    r_new = new_pos < a.sink ? new_pos : a.sink + new_pos % a.window;  // w > 0 on this path
+    if (writer && (wave == 1 || wave == 2)) {
+      const int phys = ld_const(a.page_table + static_cast<size_t>(sq) * a.pt_stride + (new_pos >> 4));
+      new_blk = const_cast<uint8_t*>(a.pages) + (static_cast<size_t>(phys) * a.Hkv + g) * BLOCK_BYTES;
+      if (wave == 2) {
+        const uint8_t* vb = new_blk + OFF_VCODE + 8 * (2 * lane) + ((new_pos & (PAGE - 1)) >> 1);
+        vb0 = vb[0];
+        vb1 = vb[8];
+      }
+    }
+  }
+  // ---- arithmetic on what arrives: the query first, then this step's token
+  // Query of head `wave`: rotate like the keys, then symmetric INT8 with an
+  // FP32 scale (lane l holds channels 2l, 2l+1); codes in natural order to LDS.
+  {
+    float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
+    fwht128_wave(x0, x1);
+    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    const float s_q = amax / 127.0f;
+    int c0 = 0, c1 = 0;
+    if (s_q != 0.0f) {
+      c0 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x0 / s_q), -127.0f), 127.0f));
+      c1 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x1 / s_q), -127.0f), 127.0f));
+    }
+    reinterpret_cast<uint16_t*>(qn + wave * HD)[lane] = static_cast<uint16_t>((c0 & 0xFF) | ((c1 & 0xFF) << 8));
+    if (lane == 0) cqs[wave] = s_q * a.scale_log2;
+    if (DEBUG && wave < hg.nh) {
+      const int S = wave_sum_i(c0 + c1);
+      if (a.dbg.qsum && lane == 0) a.dbg.qsum[bh] = S;
+      if (a.dbg.qcodes) {
+        a.dbg.qcodes[bh * HD + 2 * lane] = static_cast<int8_t>(c0);
+        a.dbg.qcodes[bh * HD + 2 * lane + 1] = static_cast<int8_t>(c1);
+      }
+    }
+  }
   // Fused append: this step's token goes to its page slot and its side row,
   // and the INT8 row also to LDS; after the barrier below every wave replaces
   // what it loaded for that row (the loads above may have seen the old row).
@@ -312,34 +355,14 @@ __device__ __forceinline__ void protected_partial(const DecArgs& a, int v, int b
     } else if (wave == 1) {
       write_int4_k(new_blk, t, k0, k1, lane);
     } else {
-      write_int4_v(new_blk, t, v0, v1, lane, new_vb);
+      write_int4_v(new_blk, t, v0, v1, lane, VBytes{static_cast<uint8_t>(vb0), static_cast<uint8_t>(vb1)});
     }
   }
-  // Query of head `wave`: rotate like the keys, then symmetric INT8 with an
-  // FP32 scale (lane l holds channels 2l, 2l+1); codes in natural order to LDS.
-  {
-    const size_t bh = qb + min(wave, hg.nh - 1);
-    const uint32_t qw = a.q[bh * 64 + lane];
-    float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
-    fwht128_wave(x0, x1);
-    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-    const float s_q = amax / 127.0f;
-    int c0 = 0, c1 = 0;
-    if (s_q != 0.0f) {
-      c0 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x0 / s_q), -127.0f), 127.0f));
-      c1 = static_cast<int>(fminf(fmaxf(__builtin_rintf(x1 / s_q), -127.0f), 127.0f));
-    }
-    reinterpret_cast<uint16_t*>(qn + wave * HD)[lane] = static_cast<uint16_t>((c0 & 0xFF) | ((c1 & 0xFF) << 8));
-    if (lane == 0) cqs[wave] = s_q * a.scale_log2;
-    if (DEBUG && wave < hg.nh) {
-      const int S = wave_sum_i(c0 + c1);
-      if (a.dbg.qsum && lane == 0) a.dbg.qsum[bh] = S;
-      if (a.dbg.qcodes) {
-        a.dbg.qcodes[bh * HD + 2 * lane] = static_cast<int8_t>(c0);
-        a.dbg.qcodes[bh * HD + 2 * lane + 1] = static_cast<int8_t>(c1);
-      }
-    }
-  }
+  float sk[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) sk[k] = f16_value(skr[k]);
+  if (tid < kPvRows)
+    ssv[tid] = tid < SIDE_ROWS && side_position(tid, L, E, a.sink, a.window) >= 0 ? f16_value(svr) : 0.0f;
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the staged V rows have landed
   __syncthreads();
   if (r_new >= 0) {  // this step's row from LDS, one read per lane, selected in place
@@ -1135,13 +1158,17 @@ __device__ __forceinline__ PlanView plan_view(const DecArgs& a, int lane) {
     for (int k = 0; k < 4; ++k) r.v[k] = 0;
     return r;
   }
-  int m[4];
+  // the four context lengths of the lane, loaded together (the empty asm
+  // statement keeps the compiler from moving each load into the branch that
+  // uses it, which made them four dependent round trips)
+  int Lv[4], m[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) Lv[k] = a.ctx[min(4 * lane + k, a.B - 1)];
+  asm volatile("" : "+v"(Lv[0]), "+v"(Lv[1]), "+v"(Lv[2]), "+v"(Lv[3]));
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int i = 4 * lane + k;
-    const int L = a.ctx[min(i, a.B - 1)];
-    const int E = L;
-    m[k] = i < a.B ? main_pages(L, E, a.sink, a.window) * a.Hv : 0;
+    const int mp = main_pages(Lv[k], Lv[k], a.sink, a.window) * a.Hv;
+    m[k] = 4 * lane + k < a.B ? mp : 0;
   }
   m[1] += m[0];
   m[2] += m[1];
@@ -1433,25 +1460,28 @@ __global__ __launch_bounds__(256) void merge_kernel(DecArgs a) {
   const int c_lo = cr.x, n_parts = main_pages(Lb, Lb, a.sink, a.window) > 0 ? cr.y - cr.x + 1 : 0;
   constexpr int kBatch = 4;
   for (int k0 = 0; k0 < n_parts; k0 += kBatch) {
-    float2 Ac[kBatch];
-    float Zc[kBatch], lc[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {  // loads of the batch first
-      const int c = c_lo + k0 + i;
-      const bool live = k0 + i < n_parts;
-      const float* Pc = a.ws.parts + ((static_cast<size_t>(live ? c : c_lo) + bg) * GQA + wave) * kPart;
-      Ac[i] = live ? reinterpret_cast<const float2*>(Pc)[lane] : make_float2(0.0f, 0.0f);
-      Zc[i] = live ? Pc[128] : -INFINITY;
-      lc[i] = live ? Pc[129] : 0.0f;
-    }
+    // loads of the batch first, all of them (indices past the last partial
+    // repeat it and are skipped below), held together by the empty asm
+    // statement so that they form one round trip
+    float2 Ac[kBatch], Zl[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (Zc[i] == -INFINITY) continue;
-      const float Zn = fmaxf(Zm, Zc[i]);
-      const float w0 = __builtin_amdgcn_exp2f(Zm - Zn), w1 = __builtin_amdgcn_exp2f(Zc[i] - Zn);
+      const int c = c_lo + min(k0 + i, n_parts - 1);
+      const float* Pc = a.ws.parts + ((static_cast<size_t>(c) + bg) * GQA + wave) * kPart;
+      Ac[i] = reinterpret_cast<const float2*>(Pc)[lane];
+      Zl[i] = *reinterpret_cast<const float2*>(Pc + 128);  // Z, l
+    }
+    asm volatile("" : "+v"(Ac[0].x), "+v"(Ac[0].y), "+v"(Ac[1].x), "+v"(Ac[1].y), "+v"(Ac[2].x), "+v"(Ac[2].y),
+                 "+v"(Ac[3].x), "+v"(Ac[3].y), "+v"(Zl[0].x), "+v"(Zl[0].y), "+v"(Zl[1].x), "+v"(Zl[1].y),
+                 "+v"(Zl[2].x), "+v"(Zl[2].y), "+v"(Zl[3].x), "+v"(Zl[3].y));
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (k0 + i >= n_parts || Zl[i].x == -INFINITY) continue;
+      const float Zn = fmaxf(Zm, Zl[i].x);
+      const float w0 = __builtin_amdgcn_exp2f(Zm - Zn), w1 = __builtin_amdgcn_exp2f(Zl[i].x - Zn);
       Am.x = Am.x * w0 + Ac[i].x * w1;
       Am.y = Am.y * w0 + Ac[i].y * w1;
-      lm = lm * w0 + lc[i] * w1;
+      lm = lm * w0 + Zl[i].y * w1;
       Zm = Zn;
     }
   }
