@@ -113,7 +113,8 @@ int main_region_waves() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cached[dev] = cus * 4 * KV4_MAIN_WAVES_PER_SIMD;  // 4 SIMDs per compute unit
+    // 4 SIMDs per compute unit; at most 65536 waves (the split's 32-bit arithmetic)
+    cached[dev] = std::min(cus, 4096) * 4 * KV4_MAIN_WAVES_PER_SIMD;
   }
   return cached[dev];
 }

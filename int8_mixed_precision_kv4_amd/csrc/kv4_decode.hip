@@ -1128,12 +1128,20 @@ struct MxFormat {
 // and nw + B*Hv slots suffice.  The waves holding a segment's first and last
 // pages record their chunk indices for the merge, which reads every chunk in
 // between: none of them may be empty.
+// floor(T c / nw) is evaluated in 32 bits as q c + floor(r c / nw) with
+// T = q nw + r (r c < nw^2 <= 2^32 for the at most 65536 waves of a grid),
+// two 32-bit divisions in place of a 64-bit one.
 struct Split {
   int T, nw;
+  uint32_t q, r;
 };
-__device__ __forceinline__ Split make_split(int T, int nw) { return Split{T, nw}; }
+__device__ __forceinline__ Split make_split(int T, int nw) {
+  const uint32_t q = static_cast<uint32_t>(T) / static_cast<uint32_t>(nw);
+  return Split{T, nw, q, static_cast<uint32_t>(T) - q * static_cast<uint32_t>(nw)};
+}
 __device__ __forceinline__ int chunk_begin(const Split& s, int c) {  // wave-uniform, scalar
-  return s.T >= s.nw ? static_cast<int>((static_cast<int64_t>(s.T) * c) / s.nw) : min(c, s.T);
+  const uint32_t uc = static_cast<uint32_t>(c);
+  return s.T >= s.nw ? static_cast<int>(s.q * uc + (s.r * uc) / static_cast<uint32_t>(s.nw)) : min(c, s.T);
 }
 
 // The plan as seen by one main-kernel wave.  For up to 256 sequences every
