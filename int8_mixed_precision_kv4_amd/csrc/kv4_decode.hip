@@ -1181,12 +1181,7 @@ __device__ __forceinline__ PlanView plan_view(const DecArgs& a, int lane) {
   m[1] += m[0];
   m[2] += m[1];
   m[3] += m[2];
-  int x = m[3];  // inclusive prefix of the lane totals
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_incl_sum_i(m[3], lane);  // inclusive prefix of the lane totals
   const int excl = x - m[3];
 #pragma unroll
   for (int k = 0; k < 4; ++k) r.v[k] = excl + m[k];

@@ -197,6 +197,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += xor_lane_f<2>(v);
   return v + xor_lane_f<1>(v);
 }
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// row of 16 lanes (DPP row_shr, zero shifted in), then the totals of the
+// rows below added from lanes 15, 31 and 47.  No LDS round trips.
+__device__ __forceinline__ int wave_incl_sum_i(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
 __device__ __forceinline__ int wave_sum_i(int v) {
   v += xor_lane_i<32>(v);
   v += xor_lane_i<16>(v);
