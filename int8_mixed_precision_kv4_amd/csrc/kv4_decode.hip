@@ -1341,8 +1341,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F::kWavesPe
 #pragma unroll
     for (int t = 0; t < F::kUnit; ++t) pt.id[t] = ld_const(ptrow + d.j0 + min(t, d.np - 1));
     if (d.first)  // BF16 query of head grp, channels 8 r16 .. 8 r16 + 7
-      raw2 = reinterpret_cast<const uint4*>(
-          a.q + ((static_cast<size_t>(ib) * a.Hq + seg_hg.h0 + min(grp, seg_hg.nh - 1)) * HD) / 2)[r16];
+      // (a 32-bit byte offset from the query array's base, so that the base
+      // stays in scalar registers: a 64-bit per-lane pointer held across the
+      // loop was spilled in the MXFP4 instantiation and its reload waited for
+      // every load in flight)
+      raw2 = *reinterpret_cast<const uint4*>(
+          reinterpret_cast<const uint8_t*>(a.q) +
+          (static_cast<uint32_t>(ib * a.Hq + seg_hg.h0 + min(grp, seg_hg.nh - 1)) * (2u * HD) + 16u * r16));
     ip += d.np;
     return true;
   };
