@@ -6,10 +6,10 @@
 // when a one-workgroup plan_kernel first writes the work plan):
 //   1. main_kernel.  Its first workgroups are a fixed set of independent
 //      waves: the concatenated list of main-region pages of all (sequence,
-//      kv-head) pairs is cut into equal contiguous chunks, one per wave
-//      (split-K with exact load balance); each wave builds the plan (prefix
-//      sums of main pages) in registers and rotates / INT8-quantizes the 4
-//      queries of each group it visits.  Per page: integer QK on MFMA (INT8
+//      query-head group) segments is cut into equal contiguous chunks, one
+//      per wave (split-K with exact load balance); each wave builds the plan
+//      (prefix sums of main pages) in registers and rotates / INT8-quantizes
+//      the (up to) 4 queries of each group it visits.  Per page: integer QK on MFMA (INT8
 //      query x unpacked INT4 keys), delta/m applied after the dot, tile
 //      softmax, INT8 P operand with the V scale folded in, integer PV on
 //      MFMA, FP32 running merge; a wave writes one partial per segment it
