@@ -1,6 +1,6 @@
 """Group sizes other than 4 on the GPU against the oracle: G = Hq / Hkv query
-heads per kv-head with G in {1, 2, 3, 5, 8} (one partial virtual group of
-query heads when G % 4 != 0, two groups when G = 5 or 8).  The kernels' rows
+heads per kv-head with G in {1, 2, 3, 5, 8, 16} (one partial virtual group of
+query heads when G % 4 != 0; two groups when G = 5 or 8, four when G = 16).  The kernels' rows
 are groups of at most 4 query heads of one kv-head; the oracle maps query
 head h to kv-head h // G directly, so a wrong head-to-group mapping, a row
 past a group's last head that is stored, or a group that appends a kv-head
@@ -24,7 +24,7 @@ from tests.wl import host_inputs, oracle_cache
 pytestmark = pytest.mark.gpu
 
 OUT_TOL, LSE_TOL = 2e-3, 1e-4
-GROUPS = [1, 2, 3, 5, 8]
+GROUPS = [1, 2, 3, 5, 8, 16]
 
 
 @pytest.fixture(autouse=True)
