@@ -628,7 +628,9 @@ def main():
     main_bytes = main_kernel_bytes(wl.ctx, wl.Hkv)
     achieved = main_bytes / (main_ms * 1e-3) / 1e9
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if os.path.exists(TRAFFIC_FILE) and args.workload == "qwen8b":
+        # the stored counters were taken on the qwen8b contexts: another
+        # context mix moves other bytes, so the figure applies to this one only
         rec = json.load(open(TRAFFIC_FILE))
         if rec.get("source_hash") == source_hash():
             traffic = rec.get("bytes_per_launch")
