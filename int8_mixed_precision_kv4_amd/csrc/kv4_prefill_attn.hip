@@ -14,13 +14,14 @@
 // heads.  Every product takes the 32 rows
 // n = 4 * token + head as its N dimension and is computed transposed:
 //   QK:  D^T[32 positions][32 rows] = K[positions][16 channels] q^T   (i8)
-//   PV:  O^T[32 channels][32 rows]  = V^T[channels][16 positions] P^T (i8 for
-//        the main tiles; BF16 hi / lo parts of the FP32 weights for the
-//        protected rows)
+//   PV:  O^T[32 channels][32 rows]  = V^T[channels][16 positions] P^T (the
+//        integer codes on the f16 MFMA, exact, for the main tiles; BF16 hi /
+//        lo parts of the FP32 weights for the protected rows)
 // so that lane (n, kg) (n = lane % 32, kg = lane / 32) owns row n: it holds
-// D of positions 8 (r / 4) + 4 kg + r % 4 (register r) of the two tiles of a
-// pair, reduces a tile's max over its own 8 values and its partner lane's,
-// and its 8 P codes of a tile are already the B operand of the PV product.
+// D of slots 8 kg .. 8 kg + 7 of both tiles of a pair (the K rows are loaded
+// in that order), reduces a tile's max over its own 8 values and its partner
+// lane's, and its 8 P codes of a tile are already the B operand of the PV
+// product.
 // Both regions accumulate into one running state per row (an exact
 // log-sum-exp merge); the 4 waves' states merge through LDS into out, lse.
 #include <hip/hip_runtime.h>
@@ -40,8 +41,24 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+// The main tiles' PV product comes out of the f16 MFMA as the integer sum
+// times 2^-20.
+constexpr float kPvScale = 1048576.0f;
+
+// Slot of a tile (0..15) that row m' of its half of the QK product holds:
+// register r of lane (n, kg) holds rows 8 (r / 4) + 4 kg + r % 4, i.e. slots
+// 8 kg + 4 ((r / 4) % 2) + r % 4 of tile r / 8, so that the lane's 8 values of
+// a tile are slots 8 kg .. 8 kg + 7 in order.
+__device__ __forceinline__ int tile_slot(int m) { return 8 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+// Two floats holding integers below 2048 as an f16 pair (exact).
+__device__ __forceinline__ h2 f16_pair(float a, float b) {
+  return __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
 
 struct PaArgs {
   const uint8_t* pages;
@@ -333,42 +350,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // A pair every row sees whole (all 8 tokens live, both tiles below the
   // first token's main end) skips the masks.
   const int me_min = min(p0 + 1, E - a.window);
-  auto pair_step = [&](int pr, auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
+  // The loads of a pair: K codes (A operands of QK: row m of the pair is tile
+  // m / 16, slot tile_slot(m % 16), code bytes 16 c + 8 kg .. + 7), V codes (A
+  // operands of PV per tile t and channel block s2: channel 32 s2 + n, the 4
+  // code bytes of slots 8 kg .. 8 kg + 7) and the (delta, m) of the lane's
+  // positions (registers 4 j4 .. 4 j4 + 3 hold rows 8 j4 + 4 kg .. + 3 of the
+  // pair, i.e. tile j4 / 2, slots 8 kg + 4 (j4 % 2) .. + 3).
+  struct PairData {
+    long ka[4];
+    uint32_t vw[2][4];
+    u4v kmeta[4], vmeta[4];
+  };
+  auto pair_load = [&](int pr) {
+    PairData L;
     const int ja = j_lo + 2 * pr;
     const bool has_b = 2 * pr + 1 < n_tiles;
     const int pta = ldc(ptrow + ja);
     const int ptb = has_b ? ldc(ptrow + ja + 1) : pta;
     const gbytes blk[2] = {gbase + static_cast<size_t>(static_cast<uint32_t>(pta)) * pstride,
                            gbase + static_cast<size_t>(static_cast<uint32_t>(ptb)) * pstride};
-    // A operands of QK: position m = n of the pair (tile m / 16, slot m % 16),
-    // K code bytes 16 c + 8 kg .. + 7
-    const gbytes kb = blk[n >> 4] + 64 * (n & 15);
-    long ka[4];
+    const gbytes kb = blk[n >> 4] + 64 * tile_slot(n & 15);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ka[c] = *reinterpret_cast<const __attribute__((address_space(1))) long*>(kb + 16 * c + 8 * kg);
-    // A operands of PV (per tile t and channel block s2): channel 32 s2 + n,
-    // bytes holding positions 4 kg .. 4 kg + 3 and 8 + 4 kg .. 8 + 4 kg + 3
-    uint32_t vw[2][4];
+    for (int c = 0; c < 4; ++c) L.ka[c] = *reinterpret_cast<const __attribute__((address_space(1))) long*>(kb + 16 * c + 8 * kg);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const u2v w = *reinterpret_cast<const __attribute__((address_space(1))) u2v*>(
-            blk[t] + OFF_VCODE + 8 * (32 * s2 + n));
-        // bytes {2kg, 2kg+1} of w[0] and of w[1]
-        vw[t][s2] = __builtin_amdgcn_perm(w[1], w[0], kg ? 0x07060302u : 0x05040100u);
-      }
-    // (delta, m) of the lane's positions: registers 4 j4 .. 4 j4 + 3 hold
-    // positions 8 j4 + 4 kg .. + 3 of the pair, i.e. tile j4 / 2, slots
-    // 8 (j4 % 2) + 4 kg .. + 3
-    u4v kmeta[4], vmeta[4];
+      for (int s2 = 0; s2 < 4; ++s2)
+        L.vw[t][s2] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(
+            blk[t] + OFF_VCODE + 8 * (32 * s2 + n) + 4 * kg);
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
-      const gbytes mb = blk[j4 >> 1] + 4 * (8 * (j4 & 1) + 4 * kg);
-      kmeta[j4] = *reinterpret_cast<const __attribute__((address_space(1))) u4v*>(mb + OFF_KMETA);
-      vmeta[j4] = *reinterpret_cast<const __attribute__((address_space(1))) u4v*>(mb + OFF_VMETA);
+      const gbytes mb = blk[j4 >> 1] + 4 * (8 * kg + 4 * (j4 & 1));
+      L.kmeta[j4] = *reinterpret_cast<const __attribute__((address_space(1))) u4v*>(mb + OFF_KMETA);
+      L.vmeta[j4] = *reinterpret_cast<const __attribute__((address_space(1))) u4v*>(mb + OFF_VMETA);
     }
+    return L;
+  };
+  auto pair_step = [&](int pr, const PairData& L, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int ja = j_lo + 2 * pr;
+    const bool has_b = 2 * pr + 1 < n_tiles;
+    const long* ka = L.ka;
+    const auto& vw = L.vw;
+    const u4v* kmeta = L.kmeta;
+    const u4v* vmeta = L.vmeta;
     // integer QK^T of the pair
     v16i d = {};
 #pragma unroll
@@ -383,7 +408,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int r = 0; r < 16; ++r) {
       const int j4 = r >> 2, i = r & 3;
       const int t = j4 >> 1;
-      const int slot16 = 8 * (j4 & 1) + 4 * kg + i;
+      const int slot16 = 8 * kg + 4 * (j4 & 1) + i;
       const int pos = PAGE * (ja + t) + slot16;
       valid[r] = FULL || (row_live && (t == 0 || has_b) && pos < me_row);
       const uint32_t km = kmeta[j4][i];
@@ -413,28 +438,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       umax[t] = partner_max(um);
     }
-    // P codes; B operand of PV per tile: bytes in the order of the V operand's
-    // nibble split (registers 0, 2, 4, 6 then 1, 3, 5, 7 of the tile)
-    long pb[2];
+    // P codes; B operand of PV per tile, slot k of the lane's register k
+    // (slot 8 kg + k of the tile), in the V operand's order: halves
+    // (k, k + 4) for k = 0..3, the even k scaled by 16 (they meet the V codes
+    // read at 1/16 of the odd slots' scale)
+    h8 pb[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float qx = 127.0f / umax[t];
       const float inv = umax[t] == 0.0f ? 0.0f : qx;
-      uint32_t uc[8];
+      float pc[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(u[8 * t + k] * inv), 0.0f, 127.0f);
-        uc[k] = static_cast<uint32_t>(r);
+        pc[k] = __builtin_amdgcn_fmed3f(__builtin_rintf(u[8 * t + k] * inv), 0.0f, 127.0f);
         if (DEBUG && valid[8 * t + k] && a.dbg.pcode && (n & 3) < nh) {
-          const int j4 = (8 * t + k) >> 2, i = k & 3;
-          const int pos = PAGE * (ja + t) + 8 * (j4 & 1) + 4 * kg + i;
+          const int pos = PAGE * (ja + t) + 8 * kg + k;
           const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + h0 + (n & 3);
-          a.dbg.pcode[bh * a.dbg.max_ctx + pos] = static_cast<uint8_t>(uc[k]);
+          a.dbg.pcode[bh * a.dbg.max_ctx + pos] = static_cast<uint8_t>(pc[k]);
         }
       }
-      const uint32_t w0 = uc[0] | (uc[2] << 8) | (uc[4] << 16) | (uc[6] << 24);
-      const uint32_t w1 = uc[1] | (uc[3] << 8) | (uc[5] << 16) | (uc[7] << 24);
-      pb[t] = static_cast<long>(w0) | (static_cast<long>(w1) << 32);
+      const h2 sixteen = {16.0f16, 16.0f16};
+      const h2 p0 = f16_pair(pc[0], pc[4]) * sixteen, p1 = f16_pair(pc[1], pc[5]);
+      const h2 p2 = f16_pair(pc[2], pc[6]) * sixteen, p3 = f16_pair(pc[3], pc[7]);
+      pb[t] = h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
     }
     // running reference max of the row; rescale what is accumulated
     // (rows with no valid position yet keep Z = -inf and a scale of 1)
@@ -453,18 +479,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float wt = zmax[t] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(zmax[t] - Zn);
       Ls = __builtin_fmaf(wt, e_t[t], Ls);
       Ms = __builtin_fmaf(wt, emv_t[t], Ms);
-      wsu[t] = wt * (umax[t] * (1.0f / 127.0f));
+      wsu[t] = wt * (umax[t] * (kPvScale / 127.0f));  // (u_max / 127) * 2^20: exact rescale
     }
-    // integer PV^T per tile and channel block
+    // integer PV^T per tile and channel block, on the f16 MFMA: V codes enter
+    // as f16 subnormals (bits c -> c 2^-24, or 16 c 2^-24 for a high nibble
+    // left in place), P codes as f16 integers; every product and partial sum
+    // is an integer multiple of 2^-24 below 2^24 ulps, so the FP32 result is
+    // the integer sum times 2^-20, exactly
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) {
-        const uint32_t x = vw[t][s2];
-        const long va = static_cast<long>(x & 0x0F0F0F0Fu) | (static_cast<long>((x >> 4) & 0x0F0F0F0Fu) << 32);
-        const v16i acc = __builtin_amdgcn_mfma_i32_32x32x16_i8(va, pb[t], v16i{}, 0, 0, 0);
+        // byte b of x holds slots 8 kg + 2 b (low nibble) and 8 kg + 2 b + 1
+        const uint32_t x = vw[t][s2], y = x >> 8;
+        const h8 va = __builtin_bit_cast(h8, u4v{x & 0x000F000Fu, x & 0x00F000F0u, y & 0x000F000Fu, y & 0x00F000F0u});
+        const v16f acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[t], v16f{}, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) O[s2][r] = __builtin_fmaf(wsu[t], static_cast<float>(acc[r]), O[s2][r]);
+        for (int r = 0; r < 16; ++r) O[s2][r] = __builtin_fmaf(wsu[t], acc[r], O[s2][r]);
         if (DEBUG && a.dbg.pv && row_live && (t == 0 || has_b) && (n & 3) < nh) {
           const size_t bh = static_cast<size_t>(tok0 + tn) * a.Hq + h0 + (n & 3);
           // a tile outside this row's main region leaves its accumulators unwritten
@@ -472,19 +503,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int ch = 32 * s2 + 8 * (r >> 2) + 4 * kg + (r & 3);
-              a.dbg.pv[(bh * a.dbg.max_pages + (ja + t)) * HD + ch] = acc[r];
+              a.dbg.pv[(bh * a.dbg.max_pages + (ja + t)) * HD + ch] = static_cast<int32_t>(acc[r] * kPvScale);
             }
           }
         }
       }
     }
     };
+  // The pairs every row sees whole (all 8 tokens live, 2 pr + 2 <= n_tiles
+  // and PAGE (j_lo + 2 pr + 2) <= me_min) are a prefix of the wave's pairs;
+  // one loop each keeps the running state in the same registers throughout.
+  const int lim = min(n_tiles, me_min >= 0 ? me_min / PAGE - j_lo : -1);
+  const int pf = ntok == QB && lim >= 2 ? max(pr0, min(pr1, lim >> 1)) : pr0;
+  // Whole pairs: the next pair's loads go out before this pair's arithmetic
+  // (two register sets in turn; past the end the last pair is loaded again).
+  if (pr0 < pf) {
+    PairData A = pair_load(pr0);
 #pragma unroll 1
-  for (int pr = pr0; pr < pr1; ++pr) {
-    const int ja = j_lo + 2 * pr;
-    if (ntok == QB && 2 * pr + 1 < n_tiles && PAGE * (ja + 2) <= me_min) pair_step(pr, std::true_type{});
-    else pair_step(pr, std::false_type{});
+    for (int pr = pr0;; pr += 2) {
+      const PairData B = pair_load(min(pr + 1, pf - 1));
+      pair_step(pr, A, std::true_type{});
+      if (pr + 1 >= pf) break;
+      A = pair_load(min(pr + 2, pf - 1));
+      pair_step(pr + 1, B, std::true_type{});
+      if (pr + 2 >= pf) break;
+    }
   }
+#pragma unroll 1
+  for (int pr = pf; pr < pr1; ++pr) pair_step(pr, pair_load(pr), std::false_type{});
 
   // ---- this wave's partial: A = O + sum(w e m_v), Z, l (rows n; both lanes
   // of a row hold half of the sums)
