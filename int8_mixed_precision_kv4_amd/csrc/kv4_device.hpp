@@ -421,11 +421,10 @@ constexpr float kC6 = static_cast<float>(kLn2 * kLn2 * kLn2 * kLn2 * kLn2 * kLn2
 constexpr float kC7 = static_cast<float>(kLn2 * kLn2 * kLn2 * kLn2 * kLn2 * kLn2 * kLn2 / 5040.0);
 }  // namespace detail
 
-__device__ __forceinline__ float exp2s(float y) {
+// The steps of exp2s without its final select: equal to exp2s(y) for
+// y >= -125.
+__device__ __forceinline__ float exp2s_normal(float y) {
   using namespace detail;
-  // below -125 (and for -inf) the polynomial runs on whatever y gives and
-  // the select returns 0
-  const bool live = (y >= -125.0f);
   const float n = __builtin_rintf(y);
   const float f = y - n;
   float p = kC7;
@@ -436,7 +435,14 @@ __device__ __forceinline__ float exp2s(float y) {
   p = __builtin_fmaf(p, f, kC2);
   p = __builtin_fmaf(p, f, kC1);
   p = __builtin_fmaf(p, f, kC0);
-  const float r = __builtin_ldexpf(p, static_cast<int>(n));
+  return __builtin_ldexpf(p, static_cast<int>(n));
+}
+
+__device__ __forceinline__ float exp2s(float y) {
+  // below -125 (and for -inf) the polynomial runs on whatever y gives and
+  // the select returns 0
+  const bool live = (y >= -125.0f);
+  const float r = exp2s_normal(y);
   return live ? r : 0.0f;
 }
 

@@ -128,6 +128,13 @@ __device__ __forceinline__ float tile_max8(const float* v) {
   float m = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
   return partner_max(m);
 }
+// Smallest of 8 values, NaN if any is NaN (v_minimum3_f32).
+__device__ __forceinline__ float z_lo8(const float* v) {
+  float m = __builtin_elementwise_minimum(__builtin_elementwise_minimum(v[0], v[1]), v[2]);
+  m = __builtin_elementwise_minimum(__builtin_elementwise_minimum(m, v[3]), v[4]);
+  m = __builtin_elementwise_minimum(__builtin_elementwise_minimum(m, v[5]), v[6]);
+  return __builtin_elementwise_minimum(m, v[7]);
+}
 __device__ __forceinline__ float partner_sum(float v) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
@@ -402,7 +409,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       d = __builtin_amdgcn_mfma_i32_32x32x16_i8(hi_nib64(ka[c]), qb[c][1], d, 0, 0, 0);
     }
     float z[16], e[16], u[16];
-    float emv_t[2] = {0.0f, 0.0f}, e_t[2] = {0.0f, 0.0f};
+    float emv_t[2], e_t[2];
     bool valid[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -420,23 +427,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     const float zmax[2] = {tile_max8(&z[0]), tile_max8(&z[8])};
+    // weights, u = e Delta_v, the tile sums l and sum(e m_v), and u_max
     float umax[2];
+    auto tile_weights = [&](auto normal_tag) {
+      constexpr bool NORMAL = decltype(normal_tag)::value;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float um = 0.0f;
+      for (int t = 0; t < 2; ++t) {
+        float um = 0.0f;
+        e_t[t] = -0.0f;  // -0 + e = e: no add for the first term
+        emv_t[t] = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = 8 * t + k;
-        const int j4 = r >> 2, i = r & 3;
-        e[r] = exp2s(z[r] - zmax[t]);
-        const uint32_t vm = vmeta[j4][i];
-        // (metadata of positions outside the region may be any bits: selected away)
-        u[r] = valid[r] ? mul_f16(e[r], vm & 0xFFFFu) : 0.0f;
-        e_t[t] += valid[r] ? e[r] : 0.0f;
-        emv_t[t] = valid[r] ? __builtin_fmaf(e[r], f16_value(vm >> 16), emv_t[t]) : emv_t[t];
-        um = fmaxf(um, u[r]);
+        for (int k = 0; k < 8; ++k) {
+          const int r = 8 * t + k;
+          const int j4 = r >> 2, i = r & 3;
+          e[r] = NORMAL ? exp2s_normal(z[r] - zmax[t]) : exp2s(z[r] - zmax[t]);
+          const uint32_t vm = vmeta[j4][i];
+          // (metadata of positions outside the region may be any bits: selected away)
+          u[r] = valid[r] ? mul_f16(e[r], vm & 0xFFFFu) : 0.0f;
+          e_t[t] += valid[r] ? e[r] : 0.0f;
+          emv_t[t] = valid[r] ? __builtin_fmaf(e[r], f16_value(vm >> 16), emv_t[t]) : emv_t[t];
+          um = fmaxf(um, u[r]);
+        }
+        umax[t] = partner_max(um);
       }
-      umax[t] = partner_max(um);
+    };
+    if constexpr (FULL) {
+      // exp2s selects 0 below -125.  When no logit of the pair lies more than
+      // 125 below its tile's max (each lane tests the smallest of its 8 of
+      // each tile; a NaN fails the test) the select is left out.
+      const bool narrow = z_lo8(&z[0]) - zmax[0] >= -125.0f && z_lo8(&z[8]) - zmax[1] >= -125.0f;
+      if (!__builtin_amdgcn_ballot_w64(!narrow)) tile_weights(std::true_type{});
+      else tile_weights(std::false_type{});
+    } else {
+      tile_weights(std::false_type{});
     }
     // P codes; B operand of PV per tile, slot k of the lane's register k
     // (slot 8 kg + k of the tile), in the V operand's order: halves
