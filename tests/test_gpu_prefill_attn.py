@@ -37,12 +37,17 @@ def _queries(T, Hq, seed):
     return torch.from_numpy(q).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def _setup(ctx, n, Hq, Hkv, seed, sink=16, window=128):
+def _setup(ctx, n, Hq, Hkv, seed, sink=16, window=128, k_scale_every=0):
     """Caches (GPU and oracle) holding [0, ctx) of every sequence, written by
-    re-prefill; chunk = the last n[s] positions."""
+    re-prefill; chunk = the last n[s] positions.  k_scale_every = j > 0: the
+    keys of every j-th row (all sequences back to back) times 1000."""
     dev = torch.device("cuda")
     wl = make_workload(0, ctx=ctx, Hq=Hq, Hkv=Hkv, seed=seed)
     hi = host_inputs(wl)
+    if k_scale_every:
+        kf = torch.from_numpy(hi.k.view(np.int16)).view(torch.bfloat16).float()
+        kf[::k_scale_every] *= 1000.0
+        hi.k = kf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     k, v, cu_all = hi.prefix(wl.ctx)
     ref = oracle.Cache(wl.num_pages, wl.Hkv, wl.max_slots, sink, window)
     oracle.prefill(ref, k, v, cu_all, np.zeros(wl.B, np.int32), wl.slots, wl.page_table)
@@ -119,6 +124,41 @@ def test_chunk_blocks_and_budgets():
         lerr = float(np.abs(lse.cpu().numpy() - r_lse).max())
         _say(f"[chunk] budget {sw}: out {err:.2e} lse {lerr:.2e}")
         assert err <= OUT_TOL and lerr <= LSE_TOL, (sw, err, lerr)
+
+
+def test_wide_logit_spread_in_whole_pairs():
+    """Keys of every 5th row scaled by 1000: in most tiles one logit then lies
+    hundreds (base 2) above or below the others, so the pairs every row sees
+    whole take exp2s with its select below -125 (weights exactly 0), not the
+    form without it, which needs every logit of the pair within 125 of its
+    tile's max.  Integer intermediates bit-exact, out to the bar, lse to the
+    bar relative to max(1, |lse|)."""
+    _say("[chunk] wide logit spread")
+    dev, wl, ref, cache, table, slots, start, cu, q = _setup([700, 520], [96, 64], 8, 2, 97, k_scale_every=5)
+    qd = bf(q, dev)
+    max_ctx = int(wl.ctx.max())
+    out, lse = kv4.prefill_attention(cache, qd, i32(cu, dev), i32(start, dev), slots, table, max_ctx, SCALE)
+    out_d, lse_d, dbg = kv4.prefill_attention_debug(cache, qd, i32(cu, dev), i32(start, dev), slots, table,
+                                                    max_ctx, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_d) and torch.equal(lse, lse_d)
+    r_out, r_lse, r_dbg = oracle.prefill_attention(ref, q, cu, start, wl.slots, wl.page_table, 8, SCALE,
+                                                   debug=True)
+    for key in ("qcodes", "qsum", "qk", "pcode", "pv"):
+        got = dbg[key].cpu().numpy()
+        bad = np.argwhere(got != r_dbg[key])
+        assert len(bad) == 0, f"{key}: {len(bad)} mismatches, first {bad[:4].tolist()}"
+    # the case is the one meant: many main-region codes are 0 next to a 127
+    codes = r_dbg["pcode"][:, :, 16:wl.ctx.min() - 128]
+    assert (codes == 0).mean() > 0.5 and (codes == 127).any()
+    # lse is near ln 2 times the largest logit (hundreds here): FP32 resolves
+    # it to a few 1e-5 relative whatever the order of the merges, so its bar
+    # scales with it above 1
+    err = float(np.abs(out.cpu().numpy() - r_out).max())
+    lerr = float((np.abs(lse.cpu().numpy() - r_lse) / np.maximum(1.0, np.abs(r_lse))).max())
+    _say(f"[chunk] wide logit spread: out {err:.2e} lse {lerr:.2e} relative (|lse| up to "
+         f"{float(np.abs(r_lse).max()):.0f})")
+    assert err <= OUT_TOL and lerr <= LSE_TOL, (err, lerr)
 
 
 def test_benchmark_reprefill_sampled():
