@@ -161,6 +161,40 @@ def test_wide_logit_spread_in_whole_pairs():
     assert err <= OUT_TOL and lerr <= LSE_TOL, (err, lerr)
 
 
+def test_nan_key_scale_in_whole_pairs():
+    """A NaN key scale (FP16 metadata bits 0x7E00, outside what the quantizer
+    writes) at three main-region positions of sequence 0 in both caches: their
+    logits are NaN, which the tile max leaves out and exp2s maps to weight 0.
+    In the pairs every row sees whole, such a pair must take the selecting
+    exp2s: the test on the smallest logit of a tile propagates NaN.  Integer
+    intermediates bit-exact, out and lse finite and to the bar."""
+    _say("[chunk] NaN key scales")
+    dev, wl, ref, cache, table, slots, start, cu, q = _setup([700, 300], [96, 40], 8, 2, 99)
+    for pos in (40, 77, 200):
+        page, off = int(wl.page_table[0, pos // 16]), 2048 + 4 * (pos % 16)
+        ref.pages[page, :, off], ref.pages[page, :, off + 1] = 0x00, 0x7E
+        cache.pages[page, :, off], cache.pages[page, :, off + 1] = 0x00, 0x7E
+    qd = bf(q, dev)
+    max_ctx = int(wl.ctx.max())
+    out, lse = kv4.prefill_attention(cache, qd, i32(cu, dev), i32(start, dev), slots, table, max_ctx, SCALE)
+    out_d, lse_d, dbg = kv4.prefill_attention_debug(cache, qd, i32(cu, dev), i32(start, dev), slots, table,
+                                                    max_ctx, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_d) and torch.equal(lse, lse_d)
+    r_out, r_lse, r_dbg = oracle.prefill_attention(ref, q, cu, start, wl.slots, wl.page_table, 8, SCALE,
+                                                   debug=True)
+    assert np.isfinite(r_out).all() and np.isfinite(r_lse).all()
+    for key in ("qcodes", "qsum", "qk", "pcode", "pv"):
+        got = dbg[key].cpu().numpy()
+        bad = np.argwhere(got != r_dbg[key])
+        assert len(bad) == 0, f"{key}: {len(bad)} mismatches, first {bad[:4].tolist()}"
+    assert (r_dbg["pcode"][:int(cu[1]), :, [40, 77, 200]] == 0).all()
+    err = float(np.abs(out.cpu().numpy() - r_out).max())
+    lerr = float(np.abs(lse.cpu().numpy() - r_lse).max())
+    _say(f"[chunk] NaN key scales: out {err:.2e} lse {lerr:.2e}")
+    assert err <= OUT_TOL and lerr <= LSE_TOL, (err, lerr)
+
+
 def test_benchmark_reprefill_sampled():
     """The benchmark's re-prefill (8 chunks of 16,384 tokens, 32/8 heads, the
     same values and launches): the whole quantized cache (all 8 x 16,384
