@@ -49,6 +49,10 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 // times 2^-20.
 constexpr float kPvScale = 1048576.0f;
 
+// How far (base 2) a pair's max may pass a row's reference max before the
+// reference moves and the running state is rescaled.
+constexpr float kLazyZ = 8.0f;
+
 // Slot of a tile (0..15) that row m' of its half of the QK product holds:
 // register r of lane (n, kg) holds rows 8 (r / 4) + 4 kg + r % 4, i.e. slots
 // 8 kg + 4 ((r / 4) % 2) + r % 4 of tile r / 8, so that the lane's 8 values of
@@ -485,12 +489,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const h2 p2 = f16_pair(pc[2], pc[6]) * sixteen, p3 = f16_pair(pc[3], pc[7]);
       pb[t] = h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
     }
-    // running reference max of the row; rescale what is accumulated
-    // (rows with no valid position yet keep Z = -inf and a scale of 1)
-    const float Zn = fmaxf(Zr, fmaxf(zmax[0], zmax[1]));
-    const float al = Zr == Zn ? 1.0f : __builtin_amdgcn_exp2f(Zr - Zn);
-    Zr = Zn;
-    if (__builtin_amdgcn_ballot_w64(al != 1.0f)) {
+    // Running reference Z of the row: it moves to the pair's max only when
+    // that passes it by more than kLazyZ, so the tile weights exp2(z_max - Z)
+    // stay below 2^kLazyZ and what is accumulated is rescaled rarely (the
+    // log-sum-exp merge is exact for any reference).  A row with no valid
+    // position yet keeps Z = -inf and moves at its first finite max.
+    const float Zm = fmaxf(zmax[0], zmax[1]);
+    const bool move = Zm > Zr + kLazyZ;
+    const float al = move ? __builtin_amdgcn_exp2f(Zr - Zm) : 1.0f;
+    Zr = move ? Zm : Zr;
+    if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) O[s2] *= al;
     }
@@ -499,7 +507,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float wsu[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float wt = zmax[t] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(zmax[t] - Zn);
+      const float wt = zmax[t] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(zmax[t] - Zr);
       Ls = __builtin_fmaf(wt, e_t[t], Ls);
       Ms = __builtin_fmaf(wt, emv_t[t], Ms);
       wsu[t] = wt * (umax[t] * (kPvScale / 127.0f));  // (u_max / 127) * 2^20: exact rescale
