@@ -110,7 +110,8 @@ def test_random_fused_step(seed):
     assert err <= OUT_TOL and lerr <= LSE_TOL, (tag, err, lerr)
 
 
-@pytest.mark.parametrize("seed", list(range(14, 22)) + list(range(42, 50)) + list(range(118, 124)))
+@pytest.mark.parametrize("seed", list(range(14, 22)) + list(range(42, 50)) + list(range(118, 124)) +
+                         list(range(200, 220)))
 def test_random_prefill_attention(seed):
     """Chunks of random length at the end of random prefixes (several per
     call), random budget and slots."""
